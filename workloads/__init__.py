@@ -1,0 +1,274 @@
+"""Seeded synthetic inputs for the paged decode path.
+
+This module only draws random numbers and fixes the shapes of each workload.
+It holds no attention, cache-write or block-allocation arithmetic, so the
+oracle and the HIP library can both consume its output without sharing any
+of the method's code.
+
+The workloads stand in for the pages' OPT-13B serving setting: OPT-13B keeps
+keys and values of 5,120 numbers per token and layer in 16-bit floats
+(«The KV Cache and PagedAttention» › "800 KB a Token"), vLLM's default block
+holds 16 tokens and the explanatory drawings use 4 (› "Like Pages of Memory").
+The pages' request traces (ShareGPT, Alpaca) are not available; lengths are
+drawn from the fixed distributions named per workload instead.
+
+Draw order for one workload, all from one seeded stream:
+  free-list permutation -> lengths -> per sequence: prefill K then prefill V
+  -> per step: new k, new v, then q.
+Values are drawn as float32 N(0, 1), multiplied by the workload's standard
+deviation and rounded to the storage dtype (round to nearest even).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+DTYPES = ("f32", "f16", "bf16")
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    seed: int
+    num_seqs: int
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    dtype: str
+    kv_std: float
+    q_std: float
+    steps: int = 1
+    # "fixed": every sequence attends `ctx_fixed` tokens at step 0.
+    # "list": attended lengths at step 0 are `ctx_list`.
+    # "uniform": attended lengths ~ U{ctx_lo..ctx_hi} (inclusive).
+    # "sharing": groups sharing a prompt (see sharing_* fields).
+    length_kind: str = "fixed"
+    ctx_fixed: int = 0
+    ctx_list: tuple = ()
+    ctx_lo: int = 0
+    ctx_hi: int = 0
+    groups: int = 0
+    samples: int = 0
+    prompt_len: int = 0
+    suffix_lo: int = 0
+    suffix_hi: int = 0
+    description: str = ""
+
+    def scaled(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads. Attended lengths count the step's new token, whose
+# key and value are written before attention reads the cache («KV cache» ›
+# "How it works": the new position's own key is compared as well).
+TINY = Workload(
+    name="tiny_4x4x64_f32_b4", seed=1, num_seqs=4, num_heads=4, num_kv_heads=4,
+    head_dim=64, block_size=4, num_blocks=64, dtype="f32", kv_std=1.0, q_std=1.0,
+    length_kind="list", ctx_list=(5, 13, 22, 37),
+    description="4 sequences, 4 heads x 64, fp32, block 4, attended {5,13,22,37}")
+
+OPT13B_7x2048 = Workload(
+    name="opt13b_7x2048_f16_b16", seed=2, num_seqs=7, num_heads=40, num_kv_heads=40,
+    head_dim=128, block_size=16, num_blocks=983, dtype="f16",
+    kv_std=1.0 / math.sqrt(128.0), q_std=1.0, length_kind="fixed", ctx_fixed=2048,
+    description="OPT-13B one layer: 40 heads x 128, fp16, block 16, 7 x 2048 tokens, "
+                "983-block pool (12 GiB / 40 layers), random placement")
+
+OPT13B_MIXED256 = Workload(
+    name="opt13b_mixed256_f16_b16", seed=3, num_seqs=256, num_heads=40, num_kv_heads=40,
+    head_dim=128, block_size=16, num_blocks=39250, dtype="f16",
+    kv_std=1.0 / math.sqrt(128.0), q_std=1.0, length_kind="uniform", ctx_lo=16, ctx_hi=2048,
+    description="OPT-13B one layer, 256 sequences, attended lengths U{16..2048}, "
+                "39,250-block pool (15,700 x 40 token slots)")
+
+SHARING_32x8 = Workload(
+    name="sharing_32x8_bf16_b16", seed=4, num_seqs=256, num_heads=40, num_kv_heads=40,
+    head_dim=128, block_size=16, num_blocks=12288, dtype="bf16",
+    kv_std=1.0 / math.sqrt(128.0), q_std=1.0, steps=4, length_kind="sharing",
+    groups=32, samples=8, prompt_len=1024, suffix_lo=0, suffix_hi=512,
+    description="32 groups x 8 samples sharing a 1,024-token prompt, suffixes U{0..512}, "
+                "4 steps of pair fork -> append (copy-on-write) -> write -> decode")
+
+LONG_16x32K = Workload(
+    name="long_16x32k_f16_b16", seed=5, num_seqs=16, num_heads=40, num_kv_heads=40,
+    head_dim=128, block_size=16, num_blocks=32800, dtype="f16",
+    kv_std=1.0 / math.sqrt(128.0), q_std=1.0, steps=4, length_kind="fixed", ctx_fixed=32768,
+    description="16 sequences x 32,768 tokens, 4 generation steps (32,768..32,771)")
+
+ALL = (TINY, OPT13B_7x2048, OPT13B_MIXED256, SHARING_32x8, LONG_16x32K)
+BY_NAME = {w.name: w for w in ALL}
+
+
+def _np_dtype_cast(x32: np.ndarray, dtype: str):
+    """Round float32 draws to the storage dtype; returns a torch CPU tensor.
+
+    torch's CPU casts round to nearest even for fp16 and bf16.
+    """
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32))
+    return t.to({"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype])
+
+
+class Stream:
+    """One seeded stream of draws, numpy PCG64 (host) or torch Philox (device).
+
+    The host stream is used where the oracle must also see every value; the
+    device stream fills the multi-gigabyte workloads in milliseconds, and the
+    oracle then reads back only the slices it checks.
+    """
+
+    def __init__(self, seed: int, device: Optional[str] = None):
+        self.device = device
+        if device is None:
+            self.rng = np.random.Generator(np.random.PCG64(seed))
+        else:
+            import torch
+            self.gen = torch.Generator(device=device)
+            self.gen.manual_seed(seed)
+            self.rng = np.random.Generator(np.random.PCG64(seed))  # integers stay on host
+
+    def permutation(self, n: int) -> np.ndarray:
+        return self.rng.permutation(n).astype(np.int32)
+
+    def integers(self, lo: int, hi_inclusive: int, size: int) -> np.ndarray:
+        return self.rng.integers(lo, hi_inclusive + 1, size=size).astype(np.int64)
+
+    def normal(self, shape: Sequence[int], std: float, dtype: str):
+        """float32 N(0, std^2) rounded to `dtype`; a torch tensor (CPU or device)."""
+        import torch
+        if self.device is None:
+            x = self.rng.standard_normal(size=tuple(shape), dtype=np.float32)
+            if std != 1.0:
+                x *= np.float32(std)
+            return _np_dtype_cast(x, dtype)
+        x = torch.randn(tuple(shape), generator=self.gen, device=self.device, dtype=torch.float32)
+        if std != 1.0:
+            x.mul_(float(std))
+        return x.to({"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype])
+
+
+@dataclasses.dataclass
+class Draws:
+    """Every random input of one workload (torch tensors, CPU or device).
+
+    prefill_k[i] / prefill_v[i]: [n_i, H_kv, D] for prefill sequence i (the
+      prompt of group i for the sharing workload).
+    suffix_k / suffix_v (sharing only): per sample, [suffix_len, H_kv, D].
+    step_k / step_v: per step, [S, H_kv, D]; step_q: per step, [S, H, D].
+    """
+    free_order: np.ndarray
+    prefill_lens: List[int]
+    prefill_k: list
+    prefill_v: list
+    step_k: list
+    step_v: list
+    step_q: list
+    suffix_lens: List[int] = dataclasses.field(default_factory=list)
+    suffix_k: list = dataclasses.field(default_factory=list)
+    suffix_v: list = dataclasses.field(default_factory=list)
+
+
+def draw(w: Workload, device: Optional[str] = None) -> Draws:
+    """All inputs of workload `w`, in the fixed draw order of this module."""
+    st = Stream(w.seed, device)
+    free_order = st.permutation(w.num_blocks)
+    Hk, D = w.num_kv_heads, w.head_dim
+    suffix_lens: List[int] = []
+    if w.length_kind == "fixed":
+        attended = [w.ctx_fixed] * w.num_seqs
+    elif w.length_kind == "list":
+        attended = list(w.ctx_list)
+        assert len(attended) == w.num_seqs
+    elif w.length_kind == "uniform":
+        attended = [int(x) for x in st.integers(w.ctx_lo, w.ctx_hi, w.num_seqs)]
+    elif w.length_kind == "sharing":
+        assert w.groups * w.samples == w.num_seqs
+        suffix_lens = [int(x) for x in st.integers(w.suffix_lo, w.suffix_hi, w.num_seqs)]
+        attended = []
+    else:
+        raise ValueError(w.length_kind)
+
+    if w.length_kind == "sharing":
+        prefill_lens = [w.prompt_len] * w.groups
+    else:
+        prefill_lens = [a - 1 for a in attended]
+    pk, pv = [], []
+    for n in prefill_lens:
+        pk.append(st.normal((n, Hk, D), w.kv_std, w.dtype))
+        pv.append(st.normal((n, Hk, D), w.kv_std, w.dtype))
+    sk, sv = [], []
+    for n in suffix_lens:
+        sk.append(st.normal((n, Hk, D), w.kv_std, w.dtype))
+        sv.append(st.normal((n, Hk, D), w.kv_std, w.dtype))
+    step_k, step_v, step_q = [], [], []
+    for _ in range(w.steps):
+        step_k.append(st.normal((w.num_seqs, Hk, D), w.kv_std, w.dtype))
+        step_v.append(st.normal((w.num_seqs, Hk, D), w.kv_std, w.dtype))
+        step_q.append(st.normal((w.num_seqs, w.num_heads, D), w.q_std, w.dtype))
+    return Draws(free_order=free_order, prefill_lens=prefill_lens, prefill_k=pk, prefill_v=pv,
+                 step_k=step_k, step_v=step_v, step_q=step_q, suffix_lens=suffix_lens,
+                 suffix_k=sk, suffix_v=sv)
+
+
+# --- Operation scripts -------------------------------------------------------
+# A script is a list of tuples naming cache-manager operations on *slots*
+# (positions in the decode batch), never physical blocks:
+#   ("add", slot)                      new empty sequence placed at `slot`
+#   ("prefill", slot, i)               append prefill tokens i (all of them)
+#   ("suffix", slot, j)                append suffix tokens j (sharing workload)
+#   ("fork", dst_slot, src_slot)       dst becomes a sharer of src's blocks
+#   ("free", slot)                     release the sequence at `slot`
+#   ("step", t)                        append one token to every slot in order,
+#                                      write step t's k/v, decode step t's q
+# Both the oracle model and the library replay the same script.
+
+def script(w: Workload, d: Draws) -> list:
+    ops: list = []
+    if w.length_kind != "sharing":
+        for s in range(w.num_seqs):
+            ops.append(("add", s))
+            ops.append(("prefill", s, s))
+        for t in range(w.steps):
+            ops.append(("step", t))
+        return ops
+    # Sharing: per group a prompt sequence is prefilled, forked into the
+    # group's samples and released, so the prompt blocks are held by the
+    # samples only; each sample then appends its own suffix. Every step
+    # first replaces odd sample 2k+1 by a fresh fork of even sample 2k (beam
+    # search keeping the better of two beams), so the pair shares a
+    # partially filled last block when the step's token is appended.
+    G, J = w.groups, w.samples
+    for g in range(G):
+        prompt_slot = ("prompt", g)
+        ops.append(("add", prompt_slot))
+        ops.append(("prefill", prompt_slot, g))
+        for j in range(J):
+            ops.append(("fork", g * J + j, prompt_slot))
+        ops.append(("free", prompt_slot))
+    for s in range(G * J):
+        ops.append(("suffix", s, s))
+    for t in range(w.steps):
+        for g in range(G):
+            for k in range(J // 2):
+                a, b = g * J + 2 * k, g * J + 2 * k + 1
+                ops.append(("free", b))
+                ops.append(("fork", b, a))
+        ops.append(("step", t))
+    return ops
+
+
+def attended_at_step0(w: Workload, d: Draws) -> List[int]:
+    """Attended lengths at the first decode step (for sizing workspace/pools)."""
+    if w.length_kind == "sharing":
+        # after the first pair fork, odd samples inherit their even partner's length
+        out = []
+        for s in range(w.num_seqs):
+            src = s - (s % 2)
+            out.append(w.prompt_len + d.suffix_lens[src] + 1)
+        return out
+    return [n + 1 for n in d.prefill_lens]
