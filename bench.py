@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""Paged decode-attention throughput on one MI355X (gfx950).
+
+Workload: OPT-13B-shaped decode of 7 texts x 2,048 tokens (40 heads x 128, fp16,
+block 16, 983-block pools with randomly placed blocks). One step is the whole hot
+path for the batch:
+  host allocator step (one slot per text, copy-on-write pairs) -> table/slot upload
+  -> for every layer: pa_copy_blocks (when pairs exist), pa_kv_write of the new
+     token, pa_decode_attention over the cache.
+`--layers` pools share one allocator, as the layers of one model do; reading a
+different layer's pools on every launch keeps repeat reads out of the 256 MB
+Infinity Cache, so every launch streams its keys and values from HBM.
+
+Prints ONE JSON line on stdout (everything else goes to stderr):
+  value      algorithmic decode bytes (K and V of every attended token, q, out,
+             table entries) per second over the timed steps, inputs resident in HBM
+  roofline   the decode launch: algorithmic bytes per launch / its average duration
+             from HIP events around each launch on the launch stream, vs 8 TB/s
+  cpu_baseline  the fp64 CPU oracle on the same step (one layer), one thread
+"""
+from __future__ import annotations
+
+import argparse
+import dataclasses
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_320_amd", "csrc", "decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_opt13b_7x2048.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_bytes(lens, H, D, B, elt) -> int:
+    """Algorithmic bytes of one decode launch: K+V of attended tokens, q, out, table entries."""
+    S = len(lens)
+    kv = sum(int(L) for L in lens) * 2 * H * D * elt
+    qo = 2 * S * H * D * elt
+    tab = sum((int(L) + B - 1) // B for L in lens) * 4
+    return kv + qo + tab
+
+
+def src_hash() -> str:
+    return hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed counter runs, if the kernel is unchanged."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("decode_src_sha256_16") != src_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def run_probe(L, torch, gib=4):
+    n = gib << 30
+    buf = torch.empty(n // 2, dtype=torch.float16, device="cuda").normal_()
+    sink = torch.empty(L.pa_probe_sink_bytes(0), dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        L.pa_stream_read_probe(buf, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        L.pa_stream_read_probe(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf
+    return gbps
+
+
+def cpu_baseline(w, d0, seconds: float, gpu_out0):
+    """The oracle as it stands, on one layer's step-0 batch, one thread, about `seconds` long."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import workloads as wl
+    from oracle.attention import decode_attention
+    from oracle.replay import Replay
+
+    cpu = dataclasses.replace(
+        d0, prefill_k=[t.cpu() for t in d0.prefill_k], prefill_v=[t.cpu() for t in d0.prefill_v],
+        step_k=[d0.step_k[0].cpu()], step_v=[d0.step_v[0].cpu()], step_q=[d0.step_q[0].cpu()])
+    w1 = w.scaled(steps=1)
+    # the oracle allocator and cache writes build the step-0 pools and tables
+    # (attention skipped there: decode_pairs -> []); the attention itself is timed below
+    rp = Replay(w1, cpu, pool=True)
+    res = rp.run(wl.script(w1, cpu), decode_pairs=lambda t: [])[0]
+    q = cpu.step_q[0]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        reps = 0
+        out = None
+        while True:
+            out = decode_attention(q, rp.k, rp.v, res.tables, res.lens, w.block_size)
+            reps += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+    nbytes = decode_bytes(res.lens, w.num_heads, w.head_dim, w.block_size, 2)
+    err = None
+    if gpu_out0 is not None:
+        err = float(np.max(np.abs(gpu_out0.astype(np.float64) - out)))
+    return {
+        "value": round(nbytes * reps / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{w.name} one layer, step 0: all {w.num_seqs * w.num_heads} (text, head) pairs "
+                  f"x {reps} repetitions in {dt:.1f} s (fp64 numpy, BLAS limited to 1 thread)",
+        "seq_layers_per_s": round(w.num_seqs * reps / dt, 3),
+    }, err
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=8, help="pools (model layers) per step")
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the decode path shards by sequence with no exchange; see the design notes). "
+              f"Got --gpus {args.gpus}, WORLD_SIZE {world}.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from paged_kv_cache_320_amd import PagedKVCache, _lib as L
+
+    L.lib()  # fails loudly when libpagedkv.so has not been built
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    K, W, NL = args.steps, args.warmup, args.layers
+    base = wl.OPT13B_7x2048
+    w = base.scaled(steps=K + W)
+    S, H, Hkv, D, B = w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size
+    steps_room = (w.num_blocks - S * ((w.ctx_fixed + B - 1) // B)) // S * B
+    assert K + W <= steps_room, f"pool holds only {steps_room} more steps"
+
+    log(f"setup: {w.name}, {NL} layers, drawing inputs on the GPU")
+    draws = [wl.draw(w, device="cuda")]
+    for li in range(1, NL):
+        draws.append(wl.draw(w.scaled(seed=w.seed * 1000 + li), device="cuda"))
+    cache = PagedKVCache(w.num_blocks, B, Hkv, D, w.dtype, layers=NL, device="cuda",
+                         free_order=draws[0].free_order, fill=float("nan"))
+    seqs = []
+    for s in range(S):
+        sid = cache.add()
+        slots, pair = cache.alloc.append(sid, draws[0].prefill_lens[s])
+        assert pair == (-1, -1)
+        for li in range(NL):
+            cache.write(slots, draws[li].prefill_k[s], draws[li].prefill_v[s], layer=li)
+        seqs.append(sid)
+    torch.cuda.synchronize()
+
+    max_blocks = (w.ctx_fixed + K + W + B - 1) // B
+    max_ctx_bound = w.ctx_fixed + K + W
+    T = args.partition_tokens
+    ws = torch.empty(L.pa_decode_workspace_bytes(S, H, D, max_ctx_bound, T), dtype=torch.uint8,
+                     device="cuda")
+    d_slots = torch.empty(S, dtype=torch.int64, device="cuda")
+    d_tables = torch.empty((S, max_blocks), dtype=torch.int32, device="cuda")
+    d_lens = torch.empty(S, dtype=torch.int32, device="cuda")
+    d_pairs = torch.empty((S, 2), dtype=torch.int32, device="cuda")
+    R = 4  # ring of pinned staging buffers, each reused only after its upload completed
+    p_slots = [torch.empty(S, dtype=torch.int64, pin_memory=True) for _ in range(R)]
+    p_tables = [torch.empty((S, max_blocks), dtype=torch.int32, pin_memory=True) for _ in range(R)]
+    p_lens = [torch.empty(S, dtype=torch.int32, pin_memory=True) for _ in range(R)]
+    p_pairs = [torch.empty((S, 2), dtype=torch.int32, pin_memory=True) for _ in range(R)]
+    up_done = [torch.cuda.Event() for _ in range(R)]
+    outs = [torch.empty((S, H, D), dtype=torch.float16, device="cuda") for _ in range(NL)]
+    newk = [[dl.step_k[i] for i in range(K + W)] for dl in draws]
+    newv = [[dl.step_v[i] for i in range(K + W)] for dl in draws]
+    qs = [[dl.step_q[i] for i in range(K + W)] for dl in draws]
+    step_lens = []
+    ev = []  # (start, end) events around every timed decode launch
+
+    def step(i: int, timed: bool):
+        slots, pairs, done = cache.alloc.step_append(seqs)
+        r = i % R
+        up_done[r].synchronize()
+        p_slots[r].numpy()[:] = slots
+        L.pa_export_tables(cache.alloc.h, seqs, max_blocks, p_tables[r].numpy(), p_lens[r].numpy())
+        lens = p_lens[r].numpy().copy()
+        step_lens.append(lens)
+        d_slots.copy_(p_slots[r], non_blocking=True)
+        d_tables.copy_(p_tables[r], non_blocking=True)
+        d_lens.copy_(p_lens[r], non_blocking=True)
+        if pairs:
+            p_pairs[r].numpy()[:len(pairs)] = np.asarray(pairs, dtype=np.int32)
+            d_pairs.copy_(p_pairs[r], non_blocking=True)
+        up_done[r].record()
+        mctx = int(lens.max())
+        for li in range(NL):
+            if pairs:
+                L.pa_copy_blocks(cache.k[li], cache.v[li], d_pairs[:len(pairs)])
+            L.pa_kv_write(cache.k[li], cache.v[li], newk[li][i], newv[li][i], d_slots)
+            if timed:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+            L.pa_decode_attention(outs[li], qs[li][i], cache.k[li], cache.v[li], d_tables, d_lens,
+                                  mctx, ws, partition_tokens=T)
+            if timed:
+                e1.record()
+                ev.append((e0, e1))
+
+    log(f"warmup {W} steps")
+    for i in range(W):
+        step(i, False)
+        if i == 0:
+            torch.cuda.synchronize()
+            out0 = outs[0].float().cpu().numpy()
+    torch.cuda.synchronize()
+
+    log(f"timing {K} steps")
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(W, W + K):
+        step(i, True)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / K
+
+    timed_lens = step_lens[W:]
+    bytes_per_step = [decode_bytes(l, H, D, B, 2) * NL for l in timed_lens]
+    value = sum(bytes_per_step) / (total_ms * 1e-3) / 1e9
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    avg_launch_ms = float(np.mean(launch_ms))
+    bytes_per_launch = float(np.mean([decode_bytes(l, H, D, B, 2) for l in timed_lens]))
+    achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
+    traffic = measured_traffic()
+    log(f"step {ms_per_step * 1e3:.1f} us ({NL} layers), decode launch {avg_launch_ms * 1e3:.1f} us "
+        f"(min {min(launch_ms) * 1e3:.1f}), {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBPS:.1%} of 8 TB/s")
+
+    probe = None
+    if not args.no_probe:
+        probe = run_probe(L, torch)
+        log(f"stream-read probe: {probe:.0f} GB/s")
+
+    cpu = None
+    err0 = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: fp64 oracle, one layer, one thread")
+        cpu, err0 = cpu_baseline(base, draws[0], args.cpu_seconds, out0)
+        log(f"cpu baseline {cpu['value']} GB/s; step-0 max abs error vs oracle {err0:.3e}")
+
+    line = {
+        "metric": "paged decode attention: KV GB/s and % of HBM peak; sequences·layers/sec",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded N(0,1)/sqrt(128) keys/values, N(0,1) queries; random block placement)",
+        "config": {"workload": base.name, "seqs": S, "context_at_step0": w.ctx_fixed,
+                   "heads": H, "kv_heads": Hkv, "head_dim": D, "block_size": B,
+                   "pool_blocks": w.num_blocks, "layers_per_step": NL,
+                   "partition_tokens": T, "parallelism": "single GPU"},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "seq_layers_per_s": round(S * NL * K / (total_ms * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel": "pa_decode_attention (decode_partition + decode_merge)",
+                     "avg_launch_us": round(avg_launch_ms * 1e3, 2),
+                     "bytes_per_launch": int(bytes_per_launch)},
+        "probe_read_gbps": round(probe, 1) if probe else None,
+        "cpu_baseline": cpu,
+        "step0_max_abs_err_vs_oracle": err0,
+        "wall_s_timed": round(wall, 4),
+        "decode_src_sha256_16": src_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

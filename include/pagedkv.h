@@ -1,0 +1,202 @@
+/*
+ * pagedkv — paged KV cache for generation-phase attention on AMD Instinct
+ * MI355X (gfx950). C ABI of libpagedkv.so.
+ *
+ * The method (sources: «The KV Cache and PagedAttention», world.lapla.si/en/kvcache,
+ * and «KV cache», tellworld.net/learn/kv-cache):
+ *  - each text's keys and values are cut into blocks of `block_size` token
+ *    places; the text sees its blocks as consecutive logical blocks while
+ *    the physical blocks can be anywhere ("Like Pages of Memory");
+ *  - a per-text block table maps logical to physical blocks and records how
+ *    many places of each are filled; a new block is taken only when the
+ *    previous ones are full ("The Block Table");
+ *  - blocks can be shared with reference counts and are copied before a
+ *    sharer writes into them ("Shared, Copied on Write");
+ *  - every generation step writes the new token's key and value and lets
+ *    its query attend over the whole cache ("One Token at a Time"; «KV cache»
+ *    "How it works").
+ *
+ * Conventions
+ *  - Every call returns int status: PA_OK or a negative PA_E* code; nothing
+ *    aborts or throws across the ABI. pa_last_error() gives a message for the
+ *    last failing call on the calling thread.
+ *  - Host allocator functions (pa_alloc_*, pa_seq_*, pa_step_append,
+ *    pa_export_tables, ...) touch only host memory; all their pointers are
+ *    host pointers. One pa_alloc must not be used from two threads at once.
+ *  - Device functions (pa_kv_write, pa_copy_blocks, pa_decode_*) take device
+ *    pointers the caller owns, enqueue work on `stream` (a hipStream_t; NULL
+ *    is the null stream) and return without waiting. Host-side checks cover
+ *    null pointers, sizes, dtype and 16-byte alignment; indices stored in
+ *    device memory are bounds-guarded inside the kernels as stated per call.
+ *  - Layouts (row-major, contiguous):
+ *      k_cache, v_cache  [num_blocks][num_kv_heads][block_size][head_dim]
+ *      q, out            [num_seqs][num_heads][head_dim]
+ *      k_new, v_new      [num_tokens][num_kv_heads][head_dim]
+ *      block_tables      int32 [num_seqs][max_blocks_per_seq], unused entries -1
+ *      context_lens      int32 [num_seqs], tokens attended, new token included
+ *      slots             int64 [num_tokens], slot = physical_block * block_size + place
+ *      pairs             int32 [num_pairs][2] = (source block, destination block)
+ *    The K and V pools share physical block ids: one block holds the keys and
+ *    the values of the same tokens.
+ *  - Supported: dtype PA_F32 / PA_F16 / PA_BF16 (K, V, q and out share it),
+ *    head_dim 64 or 128, block_size 4, 8, 16 or 32,
+ *    num_heads a multiple of num_kv_heads (heads sharing key/value sets,
+ *    "What Came After").
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  PA_OK = 0,
+  PA_EINVAL = -1,        /* bad argument: null, out of range, misaligned */
+  PA_ENOBLOCKS = -2,     /* not enough free blocks; nothing was changed */
+  PA_ENOSEQ = -3,        /* unknown or released sequence id */
+  PA_EHIP = -4,          /* a HIP runtime call failed (message has the HIP error) */
+  PA_EUNSUPPORTED = -5   /* valid but not supported (dtype, head_dim, block_size) */
+};
+
+enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 };
+
+/* Message for the last failing call on this thread ("" if none). Owned by the library. */
+const char* pa_last_error(void);
+/* Library ABI version (major*100 + minor). */
+int pa_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Host block allocator ("The Block Table", "Shared, Copied on Write",
+ * "When Memory Runs Out").
+ *
+ * Policy (fixed so that block tables are reproducible):
+ *  - The free list is a stack. With free_order given, free_order[0] is handed
+ *    out first; without it, block 0 first. Blocks released by pa_seq_free are
+ *    pushed in logical order, so the released text's last block comes next.
+ *  - Sequence ids count up from 0 and are never reused.
+ *  - pa_seq_append gives a text a new block only when its last block is full.
+ *    If its last block is partly filled and shared (count > 1), the block is
+ *    first replaced by a fresh copy target: the caller must copy source ->
+ *    destination (pa_copy_blocks) before writing any new token. The original's
+ *    count drops by one, so the last remaining holder writes in place. A
+ *    shared block that is full is never copied.
+ *  - All-or-nothing: if the free list cannot supply every block an append
+ *    needs, PA_ENOBLOCKS is returned and nothing changes.
+ * ------------------------------------------------------------------------- */
+typedef struct pa_alloc pa_alloc;
+
+/* num_blocks >= 1, block_size >= 1; free_order: NULL or a permutation of 0..num_blocks-1. */
+int pa_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                    pa_alloc** out);
+void pa_alloc_destroy(pa_alloc* a);
+
+/* New empty text. */
+int pa_seq_add(pa_alloc* a, int32_t* seq_out);
+/* New text sharing every block of `parent` (each block's count + 1) — parallel sampling. */
+int pa_seq_fork(pa_alloc* a, int32_t parent, int32_t* child_out);
+/* Slots for n_tokens new tokens of `seq` (n_tokens >= 0), in token order.
+ * *cow_src / *cow_dst: the block to copy and its copy, or -1 / -1. */
+int pa_seq_append(pa_alloc* a, int32_t seq, int32_t n_tokens, int64_t* slots_out,
+                  int32_t* cow_src, int32_t* cow_dst);
+/* One generation step for n texts, in order: one token each (pa_seq_append(seqs[i], 1)).
+ * slots_out[n]; pairs_out[n][2] receives the copy pairs in order, *num_pairs_out their count.
+ * On PA_ENOBLOCKS the first *done_out texts have been appended (their slots and pairs are
+ * valid) and text seqs[*done_out] and later are unchanged. */
+int pa_step_append(pa_alloc* a, const int32_t* seqs, int32_t n, int64_t* slots_out,
+                   int32_t* pairs_out, int32_t* num_pairs_out, int32_t* done_out);
+/* Release a text: each of its blocks' counts - 1; blocks reaching 0 return to the free list. */
+int pa_seq_free(pa_alloc* a, int32_t seq);
+/* Tokens held and blocks used by `seq`. */
+int pa_seq_info(const pa_alloc* a, int32_t seq, int32_t* ctx_len, int32_t* n_blocks);
+/* Block-table entries of `seq`: physical block and filled places per logical block
+ * (cap = capacity of both arrays; PA_EINVAL if too small). */
+int pa_seq_block_table(const pa_alloc* a, int32_t seq, int32_t* phys_out, int32_t* filled_out,
+                       int32_t cap);
+/* Dense tables for a batch: tables_out[n][max_blocks_per_seq] (unused entries -1) and
+ * ctx_lens_out[n]. PA_EINVAL if a text has more than max_blocks_per_seq blocks. */
+int pa_export_tables(const pa_alloc* a, const int32_t* seqs, int32_t n,
+                     int32_t max_blocks_per_seq, int32_t* tables_out, int32_t* ctx_lens_out);
+/* Reference count of a physical block (0 = free). */
+int pa_block_ref(const pa_alloc* a, int32_t block, int32_t* ref_out);
+int pa_num_free(const pa_alloc* a, int32_t* n_out);
+/* Blocks in use and filled places over them (each physical block counted once):
+ * filled / (used * block_size) is the share of the cache holding tokens ("What It Does"). */
+int pa_alloc_stats(const pa_alloc* a, int64_t* used_blocks, int64_t* filled_slots);
+
+/* ---------------------------------------------------------------------------
+ * Device cache writes.
+ * ------------------------------------------------------------------------- */
+
+/* Write each new token's key and value into its slot ("One Token at a Time"):
+ *   k_cache[slot/B][h][slot%B][:] = k_new[i][h][:] for every kv head h; same for V.
+ * Bit-exact copy. Slots must be distinct. A slot outside [0, num_blocks*block_size)
+ * is skipped (nothing written for that token). num_tokens == 0 is a no-op. */
+int pa_kv_write(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                const int64_t* slots, int32_t num_tokens, int32_t num_blocks,
+                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t dtype,
+                void* stream);
+
+/* Copy whole blocks, keys and values, for copy-on-write ("Shared, Copied on Write"):
+ *   k_cache[dst] = k_cache[src], v_cache[dst] = v_cache[src] for each pair.
+ * Pairs are copied concurrently: destinations must be distinct and no block may be
+ * both a source and a destination in one call (the allocator's pairs satisfy this).
+ * A pair with an index outside [0, num_blocks) is skipped. */
+int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
+                   int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t block_size, int32_t dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Decode attention ("One Token at a Time"; «KV cache» "How it works";
+ * "The Block Table": the kernel follows the table to each block).
+ *
+ *   out[s][h][:] = sum_t p_t * V_s[t],  p = softmax_t(scale * <q[s][h], K_s[t]>),
+ *   t over the context_lens[s] tokens of text s in logical order, K_s[t] / V_s[t]
+ *   read from physical block block_tables[s][t / block_size], place t % block_size,
+ *   key/value head h / (num_heads / num_kv_heads).
+ *
+ * The work over all (text, head, 16-token chunk) units is cut into equal
+ * contiguous segments, one per wavefront; a text's chunks can span several
+ * segments, whose partial results (running max, sum, weighted values; fp32)
+ * are merged in a second pass. Accumulation is fp32; out is rounded to nearest
+ * even. The result depends only on logical positions, never on placement.
+ *
+ * partition_tokens: 0 = one segment per resident wavefront (recommended); else a
+ *   multiple of 16 giving the segment length in tokens.
+ * max_context_len: upper bound of context_lens (sizes the segment grid).
+ * context_lens[s] == 0 gives zeros. A table entry outside [0, num_blocks) for an
+ * attended token, or context_lens[s] > max_blocks_per_seq * block_size, makes
+ * out[s][:][:] NaN (nothing outside the pools is read).
+ * workspace: device memory of pa_decode_workspace_bytes(...) bytes for the same
+ * num_seqs, num_heads, head_dim, max_context_len, partition_tokens on the current
+ * device; contents need no initialisation. Calls sharing a workspace must be
+ * ordered on one stream. */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_tokens);
+int pa_decode_attention(void* out, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                        int32_t max_blocks_per_seq, int32_t max_context_len,
+                        int32_t partition_tokens, float scale, int32_t dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Measurement helpers (not part of the method): the achievable HBM read rate
+ * and a copy of known size for calibrating memory counters.
+ * ------------------------------------------------------------------------- */
+/* Stream-read `bytes` (multiple of 16) from buf; sink receives 4 bytes per workgroup
+ * (size it with pa_probe_sink_bytes). waves_per_cu 0 = 8. */
+size_t pa_probe_sink_bytes(int32_t waves_per_cu);
+int pa_stream_read_probe(const void* buf, size_t bytes, void* sink, int32_t waves_per_cu,
+                         void* stream);
+/* dst[0:bytes] = src[0:bytes] (bytes multiple of 16). */
+int pa_copy_probe(void* dst, const void* src, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAGEDKV_H */

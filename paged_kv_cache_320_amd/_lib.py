@@ -1,0 +1,273 @@
+"""ctypes binding of libpagedkv.so: argument marshalling only.
+
+Every function here has the name of the C entry point it calls (include/pagedkv.h)
+and does no computation of its own. Device arguments are torch CUDA tensors whose
+data pointers are passed through; work is enqueued on torch's current stream.
+The library must have been built (python -m paged_kv_cache_320_amd.build);
+nothing falls back to another implementation when it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpagedkv.so")
+
+PA_OK, PA_EINVAL, PA_ENOBLOCKS, PA_ENOSEQ, PA_EHIP, PA_EUNSUPPORTED = 0, -1, -2, -3, -4, -5
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+
+_c_int32_p = ctypes.POINTER(ctypes.c_int32)
+_c_int64_p = ctypes.POINTER(ctypes.c_int64)
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_sz = ctypes.c_size_t
+
+# name: (restype, argtypes)
+SIGNATURES = {
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_version": (ctypes.c_int, []),
+    "pa_alloc_create": (ctypes.c_int, [_i32, _i32, _c_int32_p, ctypes.POINTER(_vp)]),
+    "pa_alloc_destroy": (None, [_vp]),
+    "pa_seq_add": (ctypes.c_int, [_vp, _c_int32_p]),
+    "pa_seq_fork": (ctypes.c_int, [_vp, _i32, _c_int32_p]),
+    "pa_seq_append": (ctypes.c_int, [_vp, _i32, _i32, _c_int64_p, _c_int32_p, _c_int32_p]),
+    "pa_step_append": (ctypes.c_int, [_vp, _c_int32_p, _i32, _c_int64_p, _c_int32_p, _c_int32_p,
+                                      _c_int32_p]),
+    "pa_seq_free": (ctypes.c_int, [_vp, _i32]),
+    "pa_seq_info": (ctypes.c_int, [_vp, _i32, _c_int32_p, _c_int32_p]),
+    "pa_seq_block_table": (ctypes.c_int, [_vp, _i32, _c_int32_p, _c_int32_p, _i32]),
+    "pa_export_tables": (ctypes.c_int, [_vp, _c_int32_p, _i32, _i32, _c_int32_p, _c_int32_p]),
+    "pa_block_ref": (ctypes.c_int, [_vp, _i32, _c_int32_p]),
+    "pa_num_free": (ctypes.c_int, [_vp, _c_int32_p]),
+    "pa_alloc_stats": (ctypes.c_int, [_vp, _c_int64_p, _c_int64_p]),
+    "pa_kv_write": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                   _vp]),
+    "pa_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                           _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32,
+                                           _vp, _sz, _vp]),
+    "pa_probe_sink_bytes": (_sz, [_i32]),
+    "pa_stream_read_probe": (ctypes.c_int, [_vp, _sz, _vp, _i32, _vp]),
+    "pa_copy_probe": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"pagedkv error {code}: {msg}")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m paged_kv_cache_320_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != PA_OK:
+        raise PagedKVError(rc, lib().pa_last_error().decode())
+
+
+def pa_last_error() -> str:
+    return lib().pa_last_error().decode()
+
+
+def pa_version() -> int:
+    return lib().pa_version()
+
+
+# ---- host allocator ---------------------------------------------------------
+
+def pa_alloc_create(num_blocks: int, block_size: int, free_order: Optional[Sequence[int]] = None):
+    h = _vp()
+    arr = None
+    if free_order is not None:
+        arr = (ctypes.c_int32 * num_blocks)(*[int(x) for x in free_order])
+    _check(lib().pa_alloc_create(num_blocks, block_size, arr, ctypes.byref(h)))
+    return h
+
+
+def pa_alloc_destroy(h) -> None:
+    lib().pa_alloc_destroy(h)
+
+
+def pa_seq_add(h) -> int:
+    out = ctypes.c_int32()
+    _check(lib().pa_seq_add(h, ctypes.byref(out)))
+    return out.value
+
+
+def pa_seq_fork(h, parent: int) -> int:
+    out = ctypes.c_int32()
+    _check(lib().pa_seq_fork(h, parent, ctypes.byref(out)))
+    return out.value
+
+
+def pa_seq_append(h, seq: int, n_tokens: int) -> Tuple[List[int], Tuple[int, int]]:
+    slots = (ctypes.c_int64 * max(n_tokens, 1))()
+    src, dst = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().pa_seq_append(h, seq, n_tokens, slots, ctypes.byref(src), ctypes.byref(dst)))
+    return list(slots[:n_tokens]), (src.value, dst.value)
+
+
+def pa_step_append(h, seqs: Sequence[int]):
+    """Returns (slots, pairs, done); raises PagedKVError on failure."""
+    n = len(seqs)
+    arr = (ctypes.c_int32 * max(n, 1))(*seqs)
+    slots = (ctypes.c_int64 * max(n, 1))()
+    pairs = (ctypes.c_int32 * max(2 * n, 2))()
+    npairs, done = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().pa_step_append(h, arr, n, slots, pairs, ctypes.byref(npairs), ctypes.byref(done)))
+    k = npairs.value
+    return list(slots[:n]), [(pairs[2 * i], pairs[2 * i + 1]) for i in range(k)], done.value
+
+
+def pa_seq_free(h, seq: int) -> None:
+    _check(lib().pa_seq_free(h, seq))
+
+
+def pa_seq_info(h, seq: int) -> Tuple[int, int]:
+    ctx, nb = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().pa_seq_info(h, seq, ctypes.byref(ctx), ctypes.byref(nb)))
+    return ctx.value, nb.value
+
+
+def pa_seq_block_table(h, seq: int) -> List[Tuple[int, int]]:
+    _, nb = pa_seq_info(h, seq)
+    phys = (ctypes.c_int32 * max(nb, 1))()
+    filled = (ctypes.c_int32 * max(nb, 1))()
+    _check(lib().pa_seq_block_table(h, seq, phys, filled, nb))
+    return [(phys[i], filled[i]) for i in range(nb)]
+
+
+def pa_export_tables(h, seqs: Sequence[int], max_blocks: int, tables_out=None, lens_out=None):
+    """Dense tables and context lengths as numpy int32 arrays (or into given arrays)."""
+    import numpy as np
+    n = len(seqs)
+    arr = np.ascontiguousarray(np.asarray(seqs, dtype=np.int32))
+    tables = tables_out if tables_out is not None else np.empty((n, max_blocks), np.int32)
+    lens = lens_out if lens_out is not None else np.empty((n,), np.int32)
+    assert tables.dtype == np.int32 and tables.flags.c_contiguous and tables.size >= n * max_blocks
+    assert lens.dtype == np.int32 and lens.flags.c_contiguous and lens.size >= n
+    _check(lib().pa_export_tables(h, arr.ctypes.data_as(_c_int32_p), n, max_blocks,
+                                  tables.ctypes.data_as(_c_int32_p),
+                                  lens.ctypes.data_as(_c_int32_p)))
+    return tables, lens
+
+
+def pa_block_ref(h, block: int) -> int:
+    out = ctypes.c_int32()
+    _check(lib().pa_block_ref(h, block, ctypes.byref(out)))
+    return out.value
+
+
+def pa_num_free(h) -> int:
+    out = ctypes.c_int32()
+    _check(lib().pa_num_free(h, ctypes.byref(out)))
+    return out.value
+
+
+def pa_alloc_stats(h) -> Tuple[int, int]:
+    used, filled = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().pa_alloc_stats(h, ctypes.byref(used), ctypes.byref(filled)))
+    return used.value, filled.value
+
+
+# ---- device operations ------------------------------------------------------
+
+def dtype_code(t) -> int:
+    import torch
+    return {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}[t.dtype]
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dev(t, name: str):
+    if t is None or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous CUDA tensor")
+    return t.data_ptr()
+
+
+def pa_kv_write(k_cache, v_cache, k_new, v_new, slots, stream=None) -> None:
+    """k_cache/v_cache [N, Hkv, B, D]; k_new/v_new [T, Hkv, D]; slots int64 [T] (all on device)."""
+    N, Hkv, B, D = k_cache.shape
+    T = int(slots.numel())
+    if T:
+        assert tuple(k_new.shape) == (T, Hkv, D) and tuple(v_new.shape) == (T, Hkv, D)
+    _check(lib().pa_kv_write(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                             _dev(k_new, "k_new") if T else None,
+                             _dev(v_new, "v_new") if T else None,
+                             _dev(slots, "slots") if T else None, T, N, Hkv, D, B,
+                             dtype_code(k_cache), _stream(stream)))
+
+
+def pa_copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
+    """pairs: int32 [P, 2] device tensor of (source, destination)."""
+    N, Hkv, B, D = k_cache.shape
+    P = int(pairs.shape[0]) if pairs is not None else 0
+    _check(lib().pa_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                _dev(pairs, "pairs") if P else None, P, N, Hkv, D, B,
+                                dtype_code(k_cache), _stream(stream)))
+
+
+def pa_decode_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,
+                              partition_tokens: int = 0) -> int:
+    n = lib().pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len,
+                                        partition_tokens)
+    if n == 0:
+        raise PagedKVError(PA_EINVAL, pa_last_error())
+    return n
+
+
+def pa_decode_attention(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
+                        workspace, partition_tokens: int = 0, scale: Optional[float] = None,
+                        stream=None) -> None:
+    """out/q [S, H, D]; pools [N, Hkv, B, D]; block_tables int32 [S, maxb]; context_lens int32 [S]."""
+    S, H, D = q.shape
+    N, Hkv, B, Dk = k_cache.shape
+    assert Dk == D and tuple(out.shape) == (S, H, D)
+    assert block_tables.shape[0] == S and context_lens.numel() == S
+    if scale is None:
+        scale = D ** -0.5
+    _check(lib().pa_decode_attention(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), S, H, Hkv, D, B,
+        N, int(block_tables.shape[1]), int(max_context_len), int(partition_tokens), float(scale),
+        dtype_code(q), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def pa_probe_sink_bytes(waves_per_cu: int = 0) -> int:
+    return lib().pa_probe_sink_bytes(waves_per_cu)
+
+
+def pa_stream_read_probe(buf, sink, waves_per_cu: int = 0, stream=None) -> None:
+    _check(lib().pa_stream_read_probe(_dev(buf, "buf"), buf.numel() * buf.element_size(),
+                                      _dev(sink, "sink"), waves_per_cu, _stream(stream)))
+
+
+def pa_copy_probe(dst, src, stream=None) -> None:
+    n = src.numel() * src.element_size()
+    assert dst.numel() * dst.element_size() >= n
+    _check(lib().pa_copy_probe(_dev(dst, "dst"), _dev(src, "src"), n, _stream(stream)))

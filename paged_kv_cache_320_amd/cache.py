@@ -1,0 +1,183 @@
+"""A paged KV cache on one GPU: device pools plus the native block allocator.
+
+Thin layer over the C ABI (every step runs in libpagedkv.so): the allocator
+hands out slots and copy-on-write pairs on the host, the pairs and slots go to
+the device, and the device entry points copy blocks, write the new keys and
+values, and run decode attention. One decode step, in order («The KV Cache and
+PagedAttention» › "One Token at a Time", › "Shared, Copied on Write"):
+  1. pa_step_append     one slot per text; a copy pair when its last block is shared
+  2. pa_copy_blocks     copies before any new token is written
+  3. pa_kv_write        the new tokens' keys and values into their slots
+  4. pa_decode_attention over the whole cache, new token included
+Several layers may share one allocator (the same block tables address every
+layer's pools), as a model with several attention layers would.
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+from . import _lib as L
+
+_TORCH_DTYPES = None
+
+
+def torch_dtype(name: str):
+    import torch
+    return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[name]
+
+
+class BlockAllocator:
+    """Owner of a native pa_alloc handle (host memory only)."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order: Optional[Sequence[int]] = None):
+        self.num_blocks, self.block_size = num_blocks, block_size
+        self.h = L.pa_alloc_create(num_blocks, block_size, free_order)
+
+    def close(self):
+        if self.h is not None:
+            L.pa_alloc_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add(self) -> int:
+        return L.pa_seq_add(self.h)
+
+    def fork(self, parent: int) -> int:
+        return L.pa_seq_fork(self.h, parent)
+
+    def append(self, seq: int, n: int):
+        return L.pa_seq_append(self.h, seq, n)
+
+    def step_append(self, seqs: Sequence[int]):
+        return L.pa_step_append(self.h, seqs)
+
+    def free(self, seq: int) -> None:
+        L.pa_seq_free(self.h, seq)
+
+    def info(self, seq: int):
+        return L.pa_seq_info(self.h, seq)
+
+    def table(self, seq: int):
+        return L.pa_seq_block_table(self.h, seq)
+
+    def export(self, seqs: Sequence[int], max_blocks: int):
+        return L.pa_export_tables(self.h, seqs, max_blocks)
+
+    def ref(self, block: int) -> int:
+        return L.pa_block_ref(self.h, block)
+
+    def num_free(self) -> int:
+        return L.pa_num_free(self.h)
+
+    def stats(self):
+        return L.pa_alloc_stats(self.h)
+
+
+class PagedKVCache:
+    """K/V pools [num_blocks, num_kv_heads, block_size, head_dim] per layer on one device."""
+
+    def __init__(self, num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
+                 dtype: str = "f16", layers: int = 1, device: str = "cuda",
+                 free_order: Optional[Sequence[int]] = None, fill: Optional[float] = None):
+        import torch
+        self.num_blocks, self.block_size = num_blocks, block_size
+        self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
+        self.dtype, self.device = dtype, device
+        self.alloc = BlockAllocator(num_blocks, block_size, free_order)
+        shape = (num_blocks, num_kv_heads, block_size, head_dim)
+        tdt = torch_dtype(dtype)
+        if fill is None:
+            self.k = [torch.empty(shape, dtype=tdt, device=device) for _ in range(layers)]
+            self.v = [torch.empty(shape, dtype=tdt, device=device) for _ in range(layers)]
+        else:
+            self.k = [torch.full(shape, fill, dtype=tdt, device=device) for _ in range(layers)]
+            self.v = [torch.full(shape, fill, dtype=tdt, device=device) for _ in range(layers)]
+        self._ws = None
+        self._ws_key = None
+
+    # ---- cache management (host allocator + device copies/writes) ----------
+    def add(self) -> int:
+        return self.alloc.add()
+
+    def fork(self, parent: int) -> int:
+        return self.alloc.fork(parent)
+
+    def free(self, seq: int) -> None:
+        self.alloc.free(seq)
+
+    def append(self, seq: int, k, v, layer: int = 0):
+        """Append n tokens' keys/values ([n, Hkv, D] device tensors) to one text."""
+        import torch
+        n = int(k.shape[0])
+        slots, pair = self.alloc.append(seq, n)
+        if pair[0] >= 0:
+            p = torch.tensor([pair], dtype=torch.int32, device=self.device)
+            for li in range(len(self.k)):
+                L.pa_copy_blocks(self.k[li], self.v[li], p)
+        if n:
+            s = torch.tensor(slots, dtype=torch.int64, device=self.device)
+            L.pa_kv_write(self.k[layer], self.v[layer], k, v, s)
+        return slots, pair
+
+    def write(self, slots, k, v, layer: int = 0) -> None:
+        import torch
+        s = torch.as_tensor(np.asarray(slots, dtype=np.int64)).to(self.device)
+        L.pa_kv_write(self.k[layer], self.v[layer], k, v, s)
+
+    def copy(self, pairs, layer: Optional[int] = None) -> None:
+        import torch
+        if not pairs:
+            return
+        p = torch.as_tensor(np.asarray(pairs, dtype=np.int32).reshape(-1, 2)).to(self.device)
+        for li in (range(len(self.k)) if layer is None else [layer]):
+            L.pa_copy_blocks(self.k[li], self.v[li], p)
+
+    def tables(self, seqs: Sequence[int], max_blocks: Optional[int] = None):
+        """Device block tables [S, max_blocks] and context lengths [S], plus the host copies."""
+        import torch
+        if max_blocks is None:
+            max_blocks = max(1, max(self.alloc.info(s)[1] for s in seqs))
+        t, lens = self.alloc.export(seqs, max_blocks)
+        return (torch.from_numpy(t).to(self.device), torch.from_numpy(lens).to(self.device), t, lens)
+
+    # ---- attention ---------------------------------------------------------
+    def workspace(self, num_seqs: int, num_heads: int, max_context_len: int,
+                  partition_tokens: int = 0):
+        import torch
+        key = (num_seqs, num_heads, max_context_len, partition_tokens)
+        if self._ws_key != key:
+            nbytes = L.pa_decode_workspace_bytes(num_seqs, num_heads, self.head_dim,
+                                                 max_context_len, partition_tokens)
+            if self._ws is None or self._ws.numel() < nbytes:
+                self._ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            self._ws_key = key
+        return self._ws
+
+    def attend(self, q, block_tables, context_lens, max_context_len: int, out=None,
+               layer: int = 0, partition_tokens: int = 0, scale: Optional[float] = None):
+        import torch
+        S, H, D = q.shape
+        if out is None:
+            out = torch.empty_like(q)
+        ws = self.workspace(S, H, max_context_len, partition_tokens)
+        L.pa_decode_attention(out, q, self.k[layer], self.v[layer], block_tables, context_lens,
+                              max_context_len, ws, partition_tokens=partition_tokens, scale=scale)
+        return out
+
+    def step(self, seqs: Sequence[int], k_new, v_new, q, max_blocks: Optional[int] = None,
+             partition_tokens: int = 0, scale: Optional[float] = None):
+        """One decode step for `seqs` (single layer). Returns (out, slots, pairs, host tables, lens)."""
+        slots, pairs, done = self.alloc.step_append(seqs)
+        self.copy(pairs)
+        self.write(slots, k_new, v_new)
+        bt, cl, t_host, lens = self.tables(seqs, max_blocks)
+        out = self.attend(q, bt, cl, int(lens.max()), partition_tokens=partition_tokens,
+                          scale=scale)
+        return out, slots, pairs, t_host, lens

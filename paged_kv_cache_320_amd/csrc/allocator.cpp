@@ -1,0 +1,277 @@
+// Host block allocator of the paged KV cache.
+//
+// «The KV Cache and PagedAttention»:
+//  "Like Pages of Memory"      equal physical blocks; a text's logical blocks map anywhere.
+//  "The Block Table"           per-text table of (physical block, places filled); a new
+//                              block only when every earlier block is full; blocks return
+//                              to the free list when the text ends.
+//  "Shared, Copied on Write"   shared blocks carry reference counts; a sharer about to write
+//                              into a shared block gets a copy and the original's count drops.
+//  "When Memory Runs Out"      a text holds all of its blocks or none: an append that cannot
+//                              get every block it needs changes nothing.
+// The free-list order, id assignment and "first writer copies" choices are fixed in
+// pagedkv.h so that tables are reproducible.
+//
+// Plain C++17, no HIP: it builds and runs on any host.
+#include <algorithm>
+#include <cstdint>
+#include <new>
+#include <vector>
+
+#include "status.hpp"
+
+using pagedkv::fail;
+using pagedkv::ok;
+
+namespace {
+
+struct Seq {
+  bool live = false;
+  std::vector<int32_t> blocks;  // physical block per logical block
+  std::vector<int32_t> filled;  // places filled per logical block
+  int64_t ctx = 0;              // tokens held
+};
+
+}  // namespace
+
+struct pa_alloc {
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  std::vector<int32_t> free_stack;  // top = back
+  std::vector<int32_t> ref;
+  std::vector<Seq> seqs;            // index = sequence id
+
+  Seq* find(int32_t id) {
+    if (id < 0 || id >= (int32_t)seqs.size() || !seqs[id].live) return nullptr;
+    return &seqs[id];
+  }
+  const Seq* find(int32_t id) const {
+    if (id < 0 || id >= (int32_t)seqs.size() || !seqs[id].live) return nullptr;
+    return &seqs[id];
+  }
+
+  // Blocks an append of n tokens needs, and whether it copies the last block.
+  int64_t blocks_needed(const Seq& s, int64_t n, bool* copy) const {
+    *copy = false;
+    if (n == 0) return 0;
+    int64_t room = 0;
+    if (!s.blocks.empty() && s.filled.back() < block_size) {
+      room = block_size - s.filled.back();
+      *copy = ref[s.blocks.back()] > 1;
+    }
+    int64_t beyond = std::max<int64_t>(0, n - room);
+    return (*copy ? 1 : 0) + (beyond + block_size - 1) / block_size;
+  }
+
+  int append(Seq& s, int32_t n, int64_t* slots, int32_t* src, int32_t* dst) {
+    bool copy = false;
+    int64_t need = blocks_needed(s, n, &copy);
+    if (need > (int64_t)free_stack.size())
+      return fail(PA_ENOBLOCKS, "append of %d tokens needs %lld blocks, %zu free", n,
+                  (long long)need, free_stack.size());
+    *src = -1;
+    *dst = -1;
+    if (copy) {
+      int32_t old = s.blocks.back();
+      int32_t fresh = free_stack.back();
+      free_stack.pop_back();
+      ref[fresh] = 1;
+      ref[old] -= 1;
+      s.blocks.back() = fresh;
+      *src = old;
+      *dst = fresh;
+    }
+    for (int32_t i = 0; i < n; ++i) {
+      if (s.blocks.empty() || s.filled.back() == block_size) {
+        int32_t b = free_stack.back();
+        free_stack.pop_back();
+        ref[b] = 1;
+        s.blocks.push_back(b);
+        s.filled.push_back(0);
+      }
+      slots[i] = (int64_t)s.blocks.back() * block_size + s.filled.back();
+      s.filled.back() += 1;
+    }
+    s.ctx += n;
+    return ok();
+  }
+};
+
+extern "C" {
+
+int pa_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                    pa_alloc** out) {
+  if (!out) return fail(PA_EINVAL, "out is null");
+  *out = nullptr;
+  if (num_blocks < 1 || block_size < 1)
+    return fail(PA_EINVAL, "num_blocks (%d) and block_size (%d) must be >= 1", num_blocks,
+                block_size);
+  if ((int64_t)num_blocks * block_size > INT64_MAX / 2)
+    return fail(PA_EINVAL, "pool too large");
+  pa_alloc* a = new (std::nothrow) pa_alloc();
+  if (!a) return fail(PA_EINVAL, "out of host memory");
+  a->num_blocks = num_blocks;
+  a->block_size = block_size;
+  a->ref.assign(num_blocks, 0);
+  a->free_stack.resize(num_blocks);
+  if (free_order) {
+    std::vector<char> seen(num_blocks, 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      int32_t b = free_order[i];
+      if (b < 0 || b >= num_blocks || seen[b]) {
+        delete a;
+        return fail(PA_EINVAL, "free_order is not a permutation of 0..%d", num_blocks - 1);
+      }
+      seen[b] = 1;
+      a->free_stack[num_blocks - 1 - i] = b;
+    }
+  } else {
+    for (int32_t i = 0; i < num_blocks; ++i) a->free_stack[num_blocks - 1 - i] = i;
+  }
+  *out = a;
+  return ok();
+}
+
+void pa_alloc_destroy(pa_alloc* a) { delete a; }
+
+int pa_seq_add(pa_alloc* a, int32_t* seq_out) {
+  if (!a || !seq_out) return fail(PA_EINVAL, "null argument");
+  if (a->seqs.size() >= (size_t)INT32_MAX) return fail(PA_EINVAL, "sequence ids exhausted");
+  a->seqs.emplace_back();
+  a->seqs.back().live = true;
+  *seq_out = (int32_t)a->seqs.size() - 1;
+  return ok();
+}
+
+int pa_seq_fork(pa_alloc* a, int32_t parent, int32_t* child_out) {
+  if (!a || !child_out) return fail(PA_EINVAL, "null argument");
+  if (!a->find(parent)) return fail(PA_ENOSEQ, "unknown sequence %d", parent);
+  if (a->seqs.size() >= (size_t)INT32_MAX) return fail(PA_EINVAL, "sequence ids exhausted");
+  Seq child = *a->find(parent);  // copy before emplace_back may reallocate
+  for (int32_t b : child.blocks) a->ref[b] += 1;
+  a->seqs.push_back(std::move(child));
+  *child_out = (int32_t)a->seqs.size() - 1;
+  return ok();
+}
+
+int pa_seq_append(pa_alloc* a, int32_t seq, int32_t n_tokens, int64_t* slots_out,
+                  int32_t* cow_src, int32_t* cow_dst) {
+  if (!a || !cow_src || !cow_dst || (n_tokens > 0 && !slots_out))
+    return fail(PA_EINVAL, "null argument");
+  if (n_tokens < 0) return fail(PA_EINVAL, "n_tokens %d < 0", n_tokens);
+  Seq* s = a->find(seq);
+  if (!s) return fail(PA_ENOSEQ, "unknown sequence %d", seq);
+  return a->append(*s, n_tokens, slots_out, cow_src, cow_dst);
+}
+
+int pa_step_append(pa_alloc* a, const int32_t* seqs, int32_t n, int64_t* slots_out,
+                   int32_t* pairs_out, int32_t* num_pairs_out, int32_t* done_out) {
+  if (!a || !num_pairs_out || !done_out || (n > 0 && (!seqs || !slots_out || !pairs_out)))
+    return fail(PA_EINVAL, "null argument");
+  if (n < 0) return fail(PA_EINVAL, "n %d < 0", n);
+  *num_pairs_out = 0;
+  *done_out = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    Seq* s = a->find(seqs[i]);
+    if (!s) return fail(PA_ENOSEQ, "unknown sequence %d at batch index %d", seqs[i], i);
+    int32_t src, dst;
+    int rc = a->append(*s, 1, &slots_out[i], &src, &dst);
+    if (rc != PA_OK) return rc;
+    if (src >= 0) {
+      pairs_out[2 * *num_pairs_out] = src;
+      pairs_out[2 * *num_pairs_out + 1] = dst;
+      *num_pairs_out += 1;
+    }
+    *done_out = i + 1;
+  }
+  return ok();
+}
+
+int pa_seq_free(pa_alloc* a, int32_t seq) {
+  if (!a) return fail(PA_EINVAL, "null argument");
+  Seq* s = a->find(seq);
+  if (!s) return fail(PA_ENOSEQ, "unknown sequence %d", seq);
+  for (int32_t b : s->blocks) {
+    a->ref[b] -= 1;
+    if (a->ref[b] == 0) a->free_stack.push_back(b);
+  }
+  *s = Seq();  // live = false, storage released
+  return ok();
+}
+
+int pa_seq_info(const pa_alloc* a, int32_t seq, int32_t* ctx_len, int32_t* n_blocks) {
+  if (!a || !ctx_len || !n_blocks) return fail(PA_EINVAL, "null argument");
+  const Seq* s = a->find(seq);
+  if (!s) return fail(PA_ENOSEQ, "unknown sequence %d", seq);
+  if (s->ctx > INT32_MAX) return fail(PA_EINVAL, "context length exceeds int32");
+  *ctx_len = (int32_t)s->ctx;
+  *n_blocks = (int32_t)s->blocks.size();
+  return ok();
+}
+
+int pa_seq_block_table(const pa_alloc* a, int32_t seq, int32_t* phys_out, int32_t* filled_out,
+                       int32_t cap) {
+  if (!a) return fail(PA_EINVAL, "null argument");
+  const Seq* s = a->find(seq);
+  if (!s) return fail(PA_ENOSEQ, "unknown sequence %d", seq);
+  if ((int64_t)s->blocks.size() > cap)
+    return fail(PA_EINVAL, "capacity %d < %zu blocks", cap, s->blocks.size());
+  if (!s->blocks.empty() && (!phys_out || !filled_out)) return fail(PA_EINVAL, "null argument");
+  std::copy(s->blocks.begin(), s->blocks.end(), phys_out);
+  std::copy(s->filled.begin(), s->filled.end(), filled_out);
+  return ok();
+}
+
+int pa_export_tables(const pa_alloc* a, const int32_t* seqs, int32_t n,
+                     int32_t max_blocks_per_seq, int32_t* tables_out, int32_t* ctx_lens_out) {
+  if (!a || (n > 0 && (!seqs || !tables_out || !ctx_lens_out)))
+    return fail(PA_EINVAL, "null argument");
+  if (n < 0 || max_blocks_per_seq < 0) return fail(PA_EINVAL, "negative size");
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq* s = a->find(seqs[i]);
+    if (!s) return fail(PA_ENOSEQ, "unknown sequence %d at batch index %d", seqs[i], i);
+    if ((int64_t)s->blocks.size() > max_blocks_per_seq)
+      return fail(PA_EINVAL, "sequence %d has %zu blocks > max_blocks_per_seq %d", seqs[i],
+                  s->blocks.size(), max_blocks_per_seq);
+    if (s->ctx > INT32_MAX) return fail(PA_EINVAL, "context length exceeds int32");
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq* s = a->find(seqs[i]);
+    int32_t* row = tables_out + (int64_t)i * max_blocks_per_seq;
+    std::copy(s->blocks.begin(), s->blocks.end(), row);
+    std::fill(row + s->blocks.size(), row + max_blocks_per_seq, -1);
+    ctx_lens_out[i] = (int32_t)s->ctx;
+  }
+  return ok();
+}
+
+int pa_block_ref(const pa_alloc* a, int32_t block, int32_t* ref_out) {
+  if (!a || !ref_out) return fail(PA_EINVAL, "null argument");
+  if (block < 0 || block >= a->num_blocks)
+    return fail(PA_EINVAL, "block %d outside [0, %d)", block, a->num_blocks);
+  *ref_out = a->ref[block];
+  return ok();
+}
+
+int pa_num_free(const pa_alloc* a, int32_t* n_out) {
+  if (!a || !n_out) return fail(PA_EINVAL, "null argument");
+  *n_out = (int32_t)a->free_stack.size();
+  return ok();
+}
+
+int pa_alloc_stats(const pa_alloc* a, int64_t* used_blocks, int64_t* filled_slots) {
+  if (!a || !used_blocks || !filled_slots) return fail(PA_EINVAL, "null argument");
+  std::vector<int32_t> filled(a->num_blocks, -1);
+  for (const Seq& s : a->seqs) {
+    if (!s.live) continue;
+    for (size_t j = 0; j < s.blocks.size(); ++j) filled[s.blocks[j]] = s.filled[j];
+  }
+  int64_t f = 0;
+  for (int32_t x : filled)
+    if (x > 0) f += x;
+  *used_blocks = (int64_t)a->num_blocks - (int64_t)a->free_stack.size();
+  *filled_slots = f;
+  return ok();
+}
+
+}  // extern "C"

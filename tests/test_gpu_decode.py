@@ -1,0 +1,170 @@
+"""pa_decode_attention on the GPU against the fp64 oracle, through the C ABI.
+
+Small seeded cases that still span several segments and a ragged last chunk,
+every dtype / head_dim / block_size the library supports, shared key/value
+heads, and the method's degenerate cases.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_common import assert_close, say
+from oracle.attention import decode_attention
+
+pytestmark = pytest.mark.gpu
+
+TD = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def make_case(seed, lens, H, Hkv, D, B, dtype, kv_std=1.0, q_std=1.0, extra=7, fill=float("nan")):
+    """Pools with every text's tokens in randomly placed blocks; unused places = fill."""
+    g = torch.Generator().manual_seed(seed)
+    rng = np.random.default_rng(seed)
+    nblk = [(L + B - 1) // B for L in lens]
+    N = sum(nblk) + extra
+    kc = torch.full((N, Hkv, B, D), fill, dtype=TD[dtype])
+    vc = torch.full((N, Hkv, B, D), fill, dtype=TD[dtype])
+    perm = list(rng.permutation(N))
+    maxb = max(1, max(nblk))
+    tables = np.full((len(lens), maxb), -1, dtype=np.int32)
+    for s, L in enumerate(lens):
+        k = (torch.randn((L, Hkv, D), generator=g) * kv_std).to(TD[dtype])
+        v = (torch.randn((L, Hkv, D), generator=g) * kv_std).to(TD[dtype])
+        for j in range(nblk[s]):
+            tables[s, j] = perm.pop()
+        for t in range(L):
+            kc[tables[s, t // B], :, t % B] = k[t]
+            vc[tables[s, t // B], :, t % B] = v[t]
+    q = (torch.randn((len(lens), H, D), generator=g) * q_std).to(TD[dtype])
+    return q, kc, vc, tables, np.asarray(lens, dtype=np.int32)
+
+
+def run_gpu(native, q, kc, vc, tables, lens, partition_tokens=0, max_ctx=None, scale=None):
+    S, H, D = q.shape
+    if max_ctx is None:
+        max_ctx = int(lens.max()) if len(lens) else 0
+    nbytes = native.pa_decode_workspace_bytes(S, H, D, max_ctx, partition_tokens)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.full(q.shape, 7.0, dtype=q.dtype, device="cuda")
+    native.pa_decode_attention(out, q.cuda(), kc.cuda(), vc.cuda(),
+                               torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
+                               max_ctx, ws, partition_tokens=partition_tokens, scale=scale)
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+SHAPES = [(dt, D, B) for dt in ("f32", "f16", "bf16") for D in (64, 128) for B in (4, 8, 16, 32)]
+
+
+@pytest.mark.parametrize("dtype,D,B", SHAPES)
+def test_matches_oracle(native, dtype, D, B):
+    lens = [1, 5, 16, 17, 40, 129, 300, 2]
+    H = Hkv = 4
+    say(f"decode dtype={dtype} D={D} B={B} lens={lens}")
+    kv_std = 1.0 if dtype == "f32" else 1.0 / math.sqrt(D)
+    q, kc, vc, tables, L = make_case(D * 100 + B, lens, H, Hkv, D, B, dtype, kv_std=kv_std)
+    want = decode_attention(q, kc, vc, tables, L, B)
+    for T in (0, 16, 64):
+        got = run_gpu(native, q, kc, vc, tables, L, partition_tokens=T)
+        assert_close(got, want, dtype, f"partition_tokens={T}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_sharp_scores(native, dtype):
+    """Peaked softmax (q x 32, V ~ N(0,1)): a dropped or misplaced block cannot hide."""
+    lens = [33, 250, 777]
+    q, kc, vc, tables, L = make_case(7, lens, 8, 8, 128, 16, dtype, kv_std=1.0 / math.sqrt(128),
+                                     q_std=32.0)
+    vc = torch.where(torch.isnan(vc), vc, vc * math.sqrt(128))
+    want = decode_attention(q, kc, vc, tables, L, 16)
+    got = run_gpu(native, q, kc, vc, tables, L, partition_tokens=32)
+    assert_close(got, want, dtype, "sharp")
+
+
+@pytest.mark.parametrize("H,Hkv", [(8, 2), (8, 1), (40, 8)])
+def test_shared_kv_heads(native, H, Hkv):
+    lens = [3, 70, 31]
+    say(f"gqa H={H} Hkv={Hkv}")
+    q, kc, vc, tables, L = make_case(H + Hkv, lens, H, Hkv, 128, 16, "f16",
+                                     kv_std=1.0 / math.sqrt(128))
+    want = decode_attention(q, kc, vc, tables, L, 16)
+    got = run_gpu(native, q, kc, vc, tables, L)
+    assert_close(got, want, "f16", "gqa")
+
+
+def test_single_token_is_exact(native):
+    for dtype in ("f32", "f16", "bf16"):
+        q, kc, vc, tables, L = make_case(3, [1, 1, 1], 4, 4, 128, 16, dtype)
+        got = run_gpu(native, q, kc, vc, tables, L)
+        for s in range(3):
+            v0 = vc[tables[s, 0], :, 0]
+            assert torch.equal(got[s], v0), f"{dtype}: out != v_0"
+
+
+def test_empty_context_gives_zeros(native):
+    q, kc, vc, tables, L = make_case(4, [0, 9, 0], 4, 4, 64, 4, "f16")
+    got = run_gpu(native, q, kc, vc, tables, L)
+    assert torch.count_nonzero(got[0]) == 0 and torch.count_nonzero(got[2]) == 0
+    want = decode_attention(q, kc, vc, tables, L, 4)
+    assert_close(got, want, "f16", "ragged with empty texts")
+
+
+def test_placement_does_not_change_a_bit(native):
+    """The same logical cache under another block placement: identical output bits."""
+    lens = [100, 513, 47, 1000]
+    q, kc, vc, tables, L = make_case(9, lens, 8, 8, 128, 16, "f16", kv_std=1 / math.sqrt(128))
+    base = run_gpu(native, q, kc, vc, tables, L)
+    pi = torch.from_numpy(np.random.default_rng(5).permutation(kc.shape[0]))
+    kc2, vc2 = torch.empty_like(kc), torch.empty_like(vc)
+    kc2[pi], vc2[pi] = kc, vc
+    t2 = np.where(tables >= 0, pi.numpy()[np.maximum(tables, 0)], -1).astype(np.int32)
+    moved = run_gpu(native, q, kc2, vc2, t2, L)
+    assert torch.equal(base.view(torch.int16), moved.view(torch.int16))
+
+
+def test_unused_places_are_never_read(native):
+    """NaN in unfilled places and unused blocks vs zeros there: same output bits."""
+    lens = [5, 18, 33]
+    a = make_case(11, lens, 4, 4, 128, 16, "bf16", fill=float("nan"))
+    b = make_case(11, lens, 4, 4, 128, 16, "bf16", fill=0.0)
+    ga, gb = run_gpu(native, *a), run_gpu(native, *b)
+    assert torch.isfinite(ga.float()).all()
+    assert torch.equal(ga.view(torch.int16), gb.view(torch.int16))
+
+
+def test_bad_table_entry_poisons_only_its_text(native):
+    lens = [20, 20, 20]
+    q, kc, vc, tables, L = make_case(12, lens, 4, 4, 64, 16, "f32")
+    tables = tables.copy()
+    tables[1, 1] = kc.shape[0] + 100       # outside the pool
+    got = run_gpu(native, q, kc, vc, tables, L)
+    assert torch.isnan(got[1]).all()
+    want = decode_attention(q, kc, vc, tables, L, 16, pairs=[(s, h) for s in (0, 2) for h in range(4)])
+    assert_close(got, want, "f32", "other texts")
+
+
+def test_context_longer_than_table_poisons(native):
+    q, kc, vc, tables, L = make_case(13, [10, 10], 4, 4, 64, 4, "f32")
+    L = L.copy()
+    L[0] = tables.shape[1] * 4 + 1
+    got = run_gpu(native, q, kc, vc, tables, L, max_ctx=int(L.max()))
+    assert torch.isnan(got[0]).all() and torch.isfinite(got[1]).all()
+
+
+def test_long_single_text_many_segments(native):
+    """One 20,000-token text split over many waves; the merge pass combines them."""
+    q, kc, vc, tables, L = make_case(14, [20000, 3], 2, 2, 128, 16, "f16",
+                                     kv_std=1 / math.sqrt(128))
+    want = decode_attention(q, kc, vc, tables, L, 16)
+    for T in (0, 256, 4096):
+        got = run_gpu(native, q, kc, vc, tables, L, partition_tokens=T)
+        assert_close(got, want, "f16", f"T={T}")
+
+
+def test_scale_argument(native):
+    q, kc, vc, tables, L = make_case(15, [30, 61], 4, 4, 64, 8, "f32")
+    want = decode_attention(q, kc, vc, tables, L, 8, scale=0.3)
+    got = run_gpu(native, q, kc, vc, tables, L, scale=0.3)
+    assert_close(got, want, "f32", "scale 0.3")

@@ -1,0 +1,135 @@
+"""The five workloads replayed through the native path and the oracle.
+
+Tiny and scaled-down workloads: whole pools, tables, slots and copy pairs
+bit-exact, every output element checked. Full-size workloads (the launch
+configuration the bench times): tables, slots and copy pairs bit-exact at every
+step, sampled slots of the pools bit-exact against the written tokens, and
+sampled (text, head) outputs against the oracle computed one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from gpu_common import NativeReplay, assert_close, sample_pairs, say
+from oracle.replay import Replay
+
+pytestmark = pytest.mark.gpu
+
+
+def bits(t):
+    t = t.detach().cpu().contiguous()
+    return t.view(torch.int32) if t.element_size() == 4 else t.view(torch.int16)
+
+
+def compare_steps(w, nat_steps, ora_steps, pairs_for=None, strict_gate=False):
+    assert len(nat_steps) == len(ora_steps) == w.steps
+    worst = 0.0
+    for t, (n, o) in enumerate(zip(nat_steps, ora_steps)):
+        assert n.slots == o.slots, f"step {t}: slots differ"
+        assert n.pairs == [tuple(p) for p in o.pairs], f"step {t}: copy pairs differ"
+        assert np.array_equal(n.tables, o.tables), f"step {t}: block tables differ"
+        assert list(n.lens) == list(o.lens), f"step {t}: context lengths differ"
+        got = n.out.cpu().to(torch.float64).numpy()
+        want = o.out
+        if pairs_for is not None:
+            mask = np.zeros(want.shape[:2], bool)
+            for s, h in pairs_for(t):
+                mask[s, h] = True
+            got = np.where(mask[..., None], got, np.nan)
+        worst = max(worst, assert_close(got, want, w.dtype, f"{w.name} step {t}"))
+        if strict_gate:
+            m = ~np.isnan(want)
+            err = float(np.abs(got[m] - want[m]).max())
+            gate = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}[w.dtype]
+            assert err <= gate, f"{w.name} step {t}: max abs error {err:.3e} > {gate}"
+    return worst
+
+
+def test_tiny_workload_whole_pool(native):
+    w = wl.TINY
+    say(f"workload {w.name}")
+    d = wl.draw(w)
+    ops = wl.script(w, d)
+    nat = NativeReplay(w, d)
+    ns = nat.run(ops)
+    ora = Replay(w, d, pool=True)
+    os_ = ora.run(ops)
+    err = compare_steps(w, ns, os_, strict_gate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(nat.cache.k[0]), bits(ora.k)) and torch.equal(bits(nat.cache.v[0]), bits(ora.v))
+    say(f"  max abs error {err:.3e}")
+
+
+@pytest.mark.parametrize("dtype,B", [("bf16", 4), ("f16", 16), ("f32", 8)])
+def test_scaled_sharing_whole_pool(native, dtype, B):
+    """Copy-on-write every step (parallel samples / beams), small enough for whole pools."""
+    w = wl.SHARING_32x8.scaled(groups=3, samples=4, num_seqs=12, num_heads=4, num_kv_heads=4,
+                               head_dim=64, block_size=B, num_blocks=160, prompt_len=6 * B + 3,
+                               suffix_lo=0, suffix_hi=2 * B + 1, steps=4, dtype=dtype,
+                               kv_std=1.0 if dtype == "f32" else 0.125)
+    say(f"workload {w.name} scaled dtype={dtype} B={B}")
+    d = wl.draw(w)
+    ops = wl.script(w, d)
+    nat = NativeReplay(w, d)
+    ns = nat.run(ops)
+    ora = Replay(w, d, pool=True)
+    os_ = ora.run(ops)
+    compare_steps(w, ns, os_)
+    assert sum(len(s.pairs) for s in ns) > 0, "the workload must exercise copy-on-write"
+    torch.cuda.synchronize()
+    assert torch.equal(bits(nat.cache.k[0]), bits(ora.k)) and torch.equal(bits(nat.cache.v[0]), bits(ora.v))
+
+
+def check_sampled_slots(nat, ora, w, d, nsamples=256, seed=0):
+    """Pool places of sampled (text, token) positions hold exactly the written token."""
+    rng = np.random.default_rng(seed)
+    a = ora.alloc
+    live = list(a.blocks)
+    for _ in range(nsamples):
+        sid = live[int(rng.integers(len(live)))]
+        L = a.context_len(sid)
+        t = int(rng.integers(L))
+        blk = a.blocks[sid][t // w.block_size]
+        place = t % w.block_size
+        # the t-th written token of this text, from the oracle's logical record
+        chunks = ora.tokens[sid]
+        k_tok = None
+        for ck, cv in chunks:
+            if t < ck.shape[0]:
+                k_tok, v_tok = ck[t], cv[t]
+                break
+            t -= ck.shape[0]
+        got_k = nat.cache.k[0][blk, :, place]
+        got_v = nat.cache.v[0][blk, :, place]
+        assert torch.equal(bits(got_k), bits(k_tok)) and torch.equal(bits(got_v), bits(v_tok))
+
+
+FULL = [wl.OPT13B_7x2048, wl.OPT13B_MIXED256, wl.SHARING_32x8, wl.LONG_16x32K]
+
+
+@pytest.mark.parametrize("w", FULL, ids=lambda w: w.name)
+def test_full_size_workload(native, w):
+    say(f"workload {w.name} (full size)")
+    d = wl.draw(w, device="cuda")
+    ops = wl.script(w, d)
+    nat = NativeReplay(w, d)
+    ns = nat.run(ops)
+    torch.cuda.synchronize()
+    say("  native path done")
+    every = w.num_seqs * w.num_heads <= 280
+    lens0 = wl.attended_at_step0(w, d)
+
+    def pairs_for(t):
+        if every:
+            return [(s, h) for s in range(w.num_seqs) for h in range(w.num_heads)]
+        return sample_pairs(lens0, w.num_heads, 48, seed=t)
+
+    ora = Replay(w, d, pool=False)
+    os_ = ora.run(ops, decode_pairs=pairs_for)
+    say("  oracle done")
+    err = compare_steps(w, ns, os_, pairs_for=pairs_for, strict_gate=True)
+    check_sampled_slots(nat, ora, w, d)
+    if w.length_kind == "sharing":
+        assert sum(len(s.pairs) for s in ns) > 0
+    say(f"  max abs error {err:.3e}")
