@@ -65,6 +65,59 @@ def measured_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
+COPY_CAL_BYTES = 512 << 20
+
+
+def _counter_rows(d, name):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    out = []
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r.get("Counter_Name") == name:
+                out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def traffic_from_counters(fetch_dir: str, write_dir: str) -> None:
+    """HBM bytes per decode launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each
+    scaled by what the same counter reads for pa_copy_probe moving COPY_CAL_BYTES."""
+    import numpy as np
+    res = {}
+    for key, d, name in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = _counter_rows(d, name)
+        ours = [(k, v) for k, v in rows if k.startswith("pagedkv::") or "pagedkv::" in k[:40]]
+        copy = [v for k, v in ours if "copy_kernel" in k]
+        part = [v for k, v in ours if "decode_partition" in k]
+        merge = [v for k, v in ours if "decode_merge" in k]
+        if not copy or not part:
+            raise SystemExit(f"{name}: need copy_kernel and decode_partition dispatches in {d}")
+        scale = COPY_CAL_BYTES / (float(np.median(copy)) * 1024)
+        res[key] = {"counter": name, "copy_kib_median": float(np.median(copy)),
+                    "scale": scale, "partition_kib_median": float(np.median(part)),
+                    "merge_kib_median": float(np.median(merge)) if merge else 0.0,
+                    "bytes_per_launch": (float(np.median(part)) +
+                                         (float(np.median(merge)) if merge else 0.0)) * 1024 * scale}
+    rec = {"decode_src_sha256_16": src_hash(), "workload": "opt13b_7x2048_f16_b16",
+           "hbm_bytes_per_launch": int(res["fetch"]["bytes_per_launch"] + res["write"]["bytes_per_launch"]),
+           "fetch": res["fetch"], "write": res["write"],
+           "calibration": f"pa_copy_probe reading and writing {COPY_CAL_BYTES} bytes"}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    json.dump(rec, open(TRAFFIC_FILE, "w"), indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+def run_copy_calibration(L, torch):
+    src = torch.empty(COPY_CAL_BYTES // 2, dtype=torch.float16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        L.pa_copy_probe(dst, src)
+    torch.cuda.synchronize()
+
+
 def run_probe(L, torch, gib=4):
     n = gib << 30
     buf = torch.empty(n // 2, dtype=torch.float16, device="cuda").normal_()
@@ -137,7 +190,15 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run pa_copy_probe over 512 MiB (reference for memory counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "`bench.py --copy-calibration` into " + os.path.relpath(TRAFFIC_FILE, ROOT))
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from_counters(*args.traffic_from)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -179,8 +240,7 @@ def main():
     max_blocks = (w.ctx_fixed + K + W + B - 1) // B
     max_ctx_bound = w.ctx_fixed + K + W
     T = args.partition_tokens
-    ws = torch.empty(L.pa_decode_workspace_bytes(S, H, D, max_ctx_bound, T), dtype=torch.uint8,
-                     device="cuda")
+    ws = L.decode_workspace(S, H, D, max_ctx_bound, T)
     d_slots = torch.empty(S, dtype=torch.int64, device="cuda")
     d_tables = torch.empty((S, max_blocks), dtype=torch.int32, device="cuda")
     d_lens = torch.empty(S, dtype=torch.int32, device="cuda")
@@ -214,18 +274,24 @@ def main():
             d_pairs.copy_(p_pairs[r], non_blocking=True)
         up_done[r].record()
         mctx = int(lens.max())
+        # every layer's copies and new-token writes, then every layer's attention back to
+        # back: one event pair brackets the NL decode launches of the step
         for li in range(NL):
             if pairs:
                 L.pa_copy_blocks(cache.k[li], cache.v[li], d_pairs[:len(pairs)])
             L.pa_kv_write(cache.k[li], cache.v[li], newk[li][i], newv[li][i], d_slots)
-            if timed:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
+        if timed:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+        for li in range(NL):
             L.pa_decode_attention(outs[li], qs[li][i], cache.k[li], cache.v[li], d_tables, d_lens,
                                   mctx, ws, partition_tokens=T)
-            if timed:
-                e1.record()
-                ev.append((e0, e1))
+        if timed:
+            e1.record()
+            ev.append((e0, e1))
+
+    if args.copy_calibration:
+        run_copy_calibration(L, torch)
 
     log(f"warmup {W} steps")
     for i in range(W):
@@ -250,7 +316,7 @@ def main():
     timed_lens = step_lens[W:]
     bytes_per_step = [decode_bytes(l, H, D, B, 2) * NL for l in timed_lens]
     value = sum(bytes_per_step) / (total_ms * 1e-3) / 1e9
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    launch_ms = [a.elapsed_time(b) / NL for a, b in ev]   # per decode launch, per step
     avg_launch_ms = float(np.mean(launch_ms))
     bytes_per_launch = float(np.mean([decode_bytes(l, H, D, B, 2) for l in timed_lens]))
     achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
@@ -291,7 +357,7 @@ def main():
         "seq_layers_per_s": round(S * NL * K / (total_ms * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": "pa_decode_attention (decode_partition + decode_merge)",
+                     "traffic": traffic, "kernel": "pa_decode_attention = decode_partition + decode_merge",
                      "avg_launch_us": round(avg_launch_ms * 1e3, 2),
                      "bytes_per_launch": int(bytes_per_launch)},
         "probe_read_gbps": round(probe, 1) if probe else None,

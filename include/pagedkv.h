@@ -160,22 +160,27 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t n
  *
  * The work over all (text, head, 16-token chunk) units is cut into equal
  * contiguous segments, one per wavefront; a text's chunks can span several
- * segments, whose partial results (running max, sum, weighted values; fp32)
- * are merged in a second pass. Accumulation is fp32; out is rounded to nearest
- * even. The result depends only on logical positions, never on placement.
+ * segments, whose partial results (running max, sum, weighted values; fp32) are
+ * merged by a second kernel in segment order. Accumulation is fp32; out is
+ * rounded to nearest even. The result depends only on logical positions, never on
+ * block placement.
  *
- * partition_tokens: 0 = one segment per resident wavefront (recommended); else a
- *   multiple of 16 giving the segment length in tokens.
+ * partition_tokens: 0 = 4 segments per compute unit (recommended); else a multiple
+ *   of 16 giving the segment length in tokens.
  * max_context_len: upper bound of context_lens (sizes the segment grid).
  * context_lens[s] == 0 gives zeros. A table entry outside [0, num_blocks) for an
  * attended token, or context_lens[s] > max_blocks_per_seq * block_size, makes
  * out[s][:][:] NaN (nothing outside the pools is read).
- * workspace: device memory of pa_decode_workspace_bytes(...) bytes for the same
- * num_seqs, num_heads, head_dim, max_context_len, partition_tokens on the current
- * device; contents need no initialisation. Calls sharing a workspace must be
- * ordered on one stream. */
+ * workspace: device memory of at least pa_decode_workspace_bytes(...) bytes for the
+ * same num_seqs, num_heads, head_dim, max_context_len, partition_tokens on the
+ * current device; its contents need no initialisation. Calls sharing a workspace
+ * must be ordered on one stream. */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                  int32_t max_context_len, int32_t partition_tokens);
+/* Zero `workspace_bytes` bytes of a decode workspace on `stream` (a fill kernel, not a
+ * memset, so it may be recorded into a HIP graph). Optional: for byte-reproducible
+ * workspace contents. */
+int pa_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 int pa_decode_attention(void* out, const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* block_tables, const int32_t* context_lens,
                         int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,

@@ -46,6 +46,7 @@ SIGNATURES = {
                                    _vp]),
     "pa_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_workspace_init": (ctypes.c_int, [_vp, _sz, _vp]),
     "pa_decode_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                            _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32,
                                            _vp, _sz, _vp]),
@@ -238,6 +239,22 @@ def pa_decode_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_
     if n == 0:
         raise PagedKVError(PA_EINVAL, pa_last_error())
     return n
+
+
+def pa_decode_workspace_init(workspace, stream=None) -> None:
+    _check(lib().pa_decode_workspace_init(_dev(workspace, "workspace"),
+                                          workspace.numel() * workspace.element_size(),
+                                          _stream(stream)))
+
+
+def decode_workspace(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,
+                     partition_tokens: int = 0, device="cuda"):
+    """A zeroed uint8 device tensor sized for pa_decode_attention."""
+    import torch
+    n = pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition_tokens)
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    pa_decode_workspace_init(ws)
+    return ws
 
 
 def pa_decode_attention(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,

@@ -22,9 +22,15 @@
 //    scalar cache; the token index is clamped to the text's last token so no
 //    unfilled place is read.
 //  * A run (the chunks of one (text, head)) covered entirely by one wave is
-//    finished in place; otherwise each wave leaves a partial (m, l, acc) and
-//    the merge kernel combines them in segment order. The order of every sum
-//    depends only on logical positions, never on where blocks are placed.
+//    finished in place; otherwise each wave covering part of it leaves a partial
+//    (m, l, acc) and decode_merge combines a run's partials in segment order.
+//    Merging inside this kernel by the last segment to arrive was measured
+//    slower on the 7 x 2,048 OPT-13B step: with agent-scope release/acquire
+//    fences (an L2 writeback and invalidate per partial) the launch doubled;
+//    with device-coherent stores, a completion wait and a counter it still cost
+//    more than this kernel plus the merge kernel. The kernel boundary gives the
+//    merge its visibility for free. The order of every sum depends only on
+//    logical positions, never on where blocks are placed.
 #include "device.hpp"
 
 #include <cmath>
@@ -35,10 +41,19 @@ namespace {
 constexpr int kChunk = 16;                 // tokens per work unit
 constexpr int kWavesPerGroup = 4;          // wavefronts per workgroup
 constexpr int kThreads = 64 * kWavesPerGroup;
-constexpr int kMaxWavesPerCU = 16;         // auto grid: at most this many waves per CU
-constexpr int kHdrBytes = 256;
+constexpr int kWavesPerCU = 4;             // auto grid: segments per CU (measured best of 4, 6, 8, 12, 16)
+constexpr int kHdrBytes = 256;             // workspace header: total units, segment length
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Keys and values are read once per launch: non-temporal loads keep them from
+// displacing the block tables, queries and partials in the caches (measured on
+// the 7 x 2,048 OPT-13B step: 55 -> 48 us for the partition kernel).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const char* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 __host__ __device__ __forceinline__ int units_of(int L) {
   return L <= 0 ? 1 : (L + kChunk - 1) / kChunk;
@@ -139,8 +154,8 @@ __device__ __forceinline__ void load_chunk(Buf<DT, D>& b, const Cursor& c, const
       const int t = t_first + i * G::RPW + g;
       const int tc = t < last ? t : last;
       const uint32_t off = (uint32_t)(tc % B) * kRowBytes + lp * 16;
-      b.k[i] = *reinterpret_cast<const uint4*>(kb + off);
-      b.v[i] = *reinterpret_cast<const uint4*>(vb + off);
+      b.k[i] = load_stream(kb + off);
+      b.v[i] = load_stream(vb + off);
     }
   } else {
 #pragma unroll
@@ -160,8 +175,8 @@ __device__ __forceinline__ void load_chunk(Buf<DT, D>& b, const Cursor& c, const
       if (bad) blk = 0;
       const int64_t off = ((int64_t)blk * x.Hkv + kvh) * kTileBytes +
                           (uint32_t)(tc % B) * kRowBytes + lp * 16;
-      b.k[i] = *reinterpret_cast<const uint4*>(kc + off);
-      b.v[i] = *reinterpret_cast<const uint4*>(vc + off);
+      b.k[i] = load_stream(kc + off);
+      b.v[i] = load_stream(vc + off);
     }
   }
   b.q = *reinterpret_cast<const uint4*>(q + ((int64_t)c.s * x.H + c.h) * kRowBytes + lp * 16);
@@ -233,6 +248,86 @@ __device__ __forceinline__ void merge_groups(State<DT, D>& st) {
   }
 }
 
+// Output row of (s, h) from fp32 values, PER consecutive elements per lane.
+template <int DT, int PER>
+__device__ __forceinline__ void store_out(char* __restrict__ dst, const float* o) {
+  if constexpr (DT == PA_F32) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) reinterpret_cast<float*>(dst)[e] = o[e];
+  } else if constexpr (DT == PA_F16) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) reinterpret_cast<_Float16*>(dst)[e] = (_Float16)o[e];
+  } else {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)bf16_bits_rne(o[e]);
+  }
+}
+
+// Combine the partials of one run, left by segments w0..w1, in segment order.
+// Segment w0 holds the run in its slot 1 unless the run starts exactly at w0's
+// first unit (then it is w0's first run, slot 0); every later segment starts
+// inside the run, so the run is its first run (slot 0).
+// Combine the partials of one run, left by segments w0..w1, in segment order.
+// Segment w0 holds the run in its slot 1 unless the run starts exactly at w0's
+// first unit (then it is w0's first run, slot 0); every later segment starts
+// inside the run, so the run is its first run (slot 0). The partials are read
+// UNROLL at a time with all loads in flight, and combined with a running maximum
+// (the same rescaling as the online softmax), so one pass over memory suffices.
+template <int DT, int D>
+__device__ __forceinline__ void merge_run(const float* __restrict__ partials, int64_t w0,
+                                          int64_t w1, int64_t run_lo, int64_t seg,
+                                          char* __restrict__ dst_row, int lane) {
+  using G = Geo<DT, D>;
+  constexpr int PER = D / 64;   // output elements per lane
+  constexpr int UNROLL = 8;
+  auto slot_of = [&](int64_t w) -> int64_t {
+    return w * 2 + ((w == w0 && run_lo != w0 * seg) ? 1 : 0);
+  };
+  float M = -INFINITY, den = 0.f, num[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) num[e] = 0.f;
+  for (int64_t w = w0; w <= w1; w += UNROLL) {
+    float m[UNROLL], l[UNROLL], a[UNROLL][PER];
+#pragma unroll
+    for (int j = 0; j < UNROLL; ++j) {
+      // past w1: an empty partial (weight 0) instead of a load
+      m[j] = -INFINITY;
+      l[j] = 0.f;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) a[j][e] = 0.f;
+      if (w + j <= w1) {
+        const float* p = partials + slot_of(w + j) * G::PSTRIDE;
+        m[j] = p[0];
+        l[j] = p[1];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) a[j][e] = p[4 + lane * PER + e];
+      }
+    }
+    float mg = M;
+#pragma unroll
+    for (int j = 0; j < UNROLL; ++j) mg = fmaxf(mg, m[j]);
+    const float mu = mg == -INFINITY ? 0.f : mg;
+    const float r = fast_exp2(M - mu);
+    den *= r;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) num[e] *= r;
+#pragma unroll
+    for (int j = 0; j < UNROLL; ++j) {  // segment order
+      const float f = fast_exp2(m[j] - mu);
+      den += f * l[j];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) num[e] += f * a[j][e];
+    }
+    M = mg;
+  }
+  float o[PER];
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  // 0 * num: NaN stays visible for a poisoned run
+#pragma unroll
+  for (int e = 0; e < PER; ++e) o[e] = den > 0.f ? num[e] * inv : 0.f * num[e];
+  store_out<DT, PER>(dst_row + lane * PER * G::ELT, o);
+}
+
 template <int DT, int D>
 __device__ __forceinline__ void flush_run(State<DT, D>& st, const Cursor& c, int64_t seg_lo,
                                           int64_t seg_hi, int w, char* __restrict__ out,
@@ -243,11 +338,12 @@ __device__ __forceinline__ void flush_run(State<DT, D>& st, const Cursor& c, int
   const int64_t run_hi = run_lo + c.U;
   if (lane < G::LPR) {
     if (run_lo >= seg_lo && run_hi <= seg_hi) {
+      // the whole run is in this segment: finish it here
       float o[G::EPL];
       const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+      // 0 * acc: zeros when nothing was attended, NaN for a poisoned run
 #pragma unroll
       for (int e = 0; e < G::EPL; ++e) o[e] = st.l > 0.f ? st.acc[e] * inv : 0.f * st.acc[e];
-      // 0 * acc: zeros when nothing was attended, NaN for a poisoned run
       char* dst = out + (((int64_t)c.s * H + c.h) * D) * G::ELT + lane * 16;
       *reinterpret_cast<uint4*>(dst) = narrow16<DT>(o);
     } else {
@@ -407,16 +503,16 @@ __global__ __launch_bounds__(kThreads) void decode_partition(
   }
 }
 
-// Merge pass: one wave per (text, head) whose run spans several segments.
+// Merge pass: one wave per (text, head); runs finished inside one segment return at once.
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads) void decode_merge(
     char* __restrict__ out, const int32_t* __restrict__ ctx, int S, int H, int maxb, int bsz,
     const int64_t* __restrict__ hdr, const int64_t* __restrict__ excl,
     const float* __restrict__ partials) {
   using G = Geo<DT, D>;
-  constexpr int PER = D / 64;  // output elements per lane
   const int lane = threadIdx.x & 63;
-  const int64_t pair = (int64_t)blockIdx.x * kWavesPerGroup + threadIdx.x / 64;
+  const int64_t pair =
+      (int64_t)blockIdx.x * kWavesPerGroup + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (pair >= (int64_t)S * H) return;
   const int s = (int)(pair / H), h = (int)(pair - (int64_t)s * H);
   int L = ctx[s];
@@ -428,55 +524,19 @@ __global__ __launch_bounds__(kThreads) void decode_merge(
   const int64_t lo = excl[s] + (int64_t)h * U, hi = lo + U;
   const int64_t w0 = lo / seg, w1 = (hi - 1) / seg;
   if (w0 == w1) return;
-  float M = -INFINITY;
-  for (int64_t w = w0; w <= w1; ++w) {
-    const int slot = (w == w0 && lo != w0 * seg) ? 1 : 0;
-    M = fmaxf(M, partials[(w * 2 + slot) * G::PSTRIDE]);
-  }
-  const float Mu = M == -INFINITY ? 0.f : M;
-  float num[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) num[e] = 0.f;
-  float den = 0.f;
-  for (int64_t w = w0; w <= w1; ++w) {
-    const int slot = (w == w0 && lo != w0 * seg) ? 1 : 0;
-    const float* p = partials + (w * 2 + slot) * G::PSTRIDE;
-    const float f = fast_exp2(p[0] - Mu);
-    den += f * p[1];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) num[e] += f * p[4 + lane * PER + e];
-  }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
-  char* dst = out + (((int64_t)s * H + h) * D + lane * PER) * G::ELT;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const float o = den > 0.f ? num[e] * inv : 0.f * num[e];
-    if constexpr (DT == PA_F32) {
-      reinterpret_cast<float*>(dst)[e] = o;
-    } else if constexpr (DT == PA_F16) {
-      reinterpret_cast<_Float16*>(dst)[e] = (_Float16)o;
-    } else {
-      reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)bf16_bits_rne(o);
-    }
-  }
+  merge_run<DT, D>(partials, w0, w1, lo, seg, out + pair * D * G::ELT, lane);
 }
 
 // ---- host side -------------------------------------------------------------
 
+// Workspace: header (total units, segment length), int64 unit offset of each text [S],
+// fp32 partials [W][2][D+4]. Written by decode_partition, read by decode_merge.
 struct Layout {
-  int64_t W;            // wavefronts in the grid
+  int64_t W;  // wavefronts (segments) in the grid
   size_t excl_off, part_off, bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-int auto_waves(int64_t* W) {
-  int cus = 0;
-  int rc = device_cus(&cus);
-  if (rc != PA_OK) return rc;
-  *W = (int64_t)cus * kMaxWavesPerCU;
-  return PA_OK;
-}
 
 int layout(int32_t S, int32_t H, int32_t D, int32_t max_ctx, int32_t T, Layout* lay) {
   if (S < 1 || H < 1 || (D != 64 && D != 128) || max_ctx < 0 || T < 0 || T % kChunk != 0)
@@ -485,8 +545,10 @@ int layout(int32_t S, int32_t H, int32_t D, int32_t max_ctx, int32_t T, Layout* 
   const int64_t units_bound = (int64_t)S * H * units_of(max_ctx);
   int64_t W;
   if (T == 0) {
-    int rc = auto_waves(&W);
+    int cus = 0;
+    int rc = device_cus(&cus);
     if (rc != PA_OK) return rc;
+    W = (int64_t)cus * kWavesPerCU;
     if (W > units_bound) W = units_bound;
   } else {
     const int64_t seg = T / kChunk;
@@ -514,6 +576,12 @@ void launch(char* out, const char* q, const char* kc, const char* vc, const int3
   const int mgroups = (int)((pairs + kWavesPerGroup - 1) / kWavesPerGroup);
   hipLaunchKernelGGL((decode_merge<DT, D>), dim3(mgroups), dim3(kThreads), 0, st, out, ctx, S, H,
                      maxb, B, hdr, excl, part);
+}
+
+__global__ void zero_fill_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
 }
 
 template <int DT, int D>
@@ -544,6 +612,20 @@ bool dispatch_d(int D, int B, char* out, const char* q, const char* kc, const ch
 }  // namespace pagedkv
 
 using namespace pagedkv;
+
+extern "C" int pa_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace) return fail(PA_EINVAL, "null workspace");
+  if (((uintptr_t)workspace & 3u) || (workspace_bytes & 3u))
+    return fail(PA_EINVAL, "workspace must be 4-byte aligned and sized");
+  const int64_t n = (int64_t)(workspace_bytes / 4);
+  if (n == 0) return ok();
+  const int64_t want = (n + 255) / 256;
+  const int groups = (int)(want < 4096 ? want : 4096);
+  hipLaunchKernelGGL(zero_fill_kernel, dim3(groups), dim3(256), 0, (hipStream_t)stream,
+                     (uint32_t*)workspace, n);
+  PA_HIP_CHECK(hipGetLastError());
+  return ok();
+}
 
 extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads,
                                             int32_t head_dim, int32_t max_context_len,

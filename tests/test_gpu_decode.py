@@ -45,8 +45,7 @@ def run_gpu(native, q, kc, vc, tables, lens, partition_tokens=0, max_ctx=None, s
     S, H, D = q.shape
     if max_ctx is None:
         max_ctx = int(lens.max()) if len(lens) else 0
-    nbytes = native.pa_decode_workspace_bytes(S, H, D, max_ctx, partition_tokens)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ws = native.decode_workspace(S, H, D, max_ctx, partition_tokens)
     out = torch.full(q.shape, 7.0, dtype=q.dtype, device="cuda")
     native.pa_decode_attention(out, q.cuda(), kc.cuda(), vc.cuda(),
                                torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
@@ -168,3 +167,25 @@ def test_scale_argument(native):
     want = decode_attention(q, kc, vc, tables, L, 8, scale=0.3)
     got = run_gpu(native, q, kc, vc, tables, L, scale=0.3)
     assert_close(got, want, "f32", "scale 0.3")
+
+
+def test_repeated_launches_are_bit_identical(native):
+    """Many segments per text and partials merged by whichever segment finishes last:
+    thirty launches give the same bits (a race in the merge would show here)."""
+    lens = [3000] * 6 + [17, 1, 250, 4096]
+    q, kc, vc, tables, L = make_case(16, lens, 8, 8, 128, 16, "f16", kv_std=1 / math.sqrt(128))
+    want = decode_attention(q, kc, vc, tables, L, 16)
+    qd, kd, vd = q.cuda(), kc.cuda(), vc.cuda()
+    td, ld = torch.from_numpy(tables).cuda(), torch.from_numpy(L).cuda()
+    for T in (0, 32):
+        ws = native.decode_workspace(len(lens), 8, 128, int(L.max()), T)
+        outs = []
+        for _ in range(30):
+            out = torch.empty_like(qd)
+            native.pa_decode_attention(out, qd, kd, vd, td, ld, int(L.max()), ws, partition_tokens=T)
+            outs.append(out)
+        torch.cuda.synchronize()
+        first = outs[0].cpu()
+        assert_close(first, want, "f16", f"T={T}")
+        for o in outs[1:]:
+            assert torch.equal(o.cpu().view(torch.int16), first.view(torch.int16))
