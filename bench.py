@@ -33,7 +33,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_320_amd", "csrc", "decode.hip")
+CSRC = os.path.join(ROOT, "paged_kv_cache_320_amd", "csrc")
+DECODE_SRCS = [os.path.join(CSRC, f) for f in ("decode.hip", "decode_kernels.hpp",
+                                               "decode_inst.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_opt13b_7x2048.json")
 
 
@@ -41,17 +43,27 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def decode_bytes(lens, H, D, B, elt) -> int:
-    """Algorithmic bytes of one decode launch: K+V of attended tokens, q, out, table entries."""
+def decode_bytes(lens, H, D, B, elt, Hkv=None, kv_elt=None) -> int:
+    """Algorithmic bytes of one decode launch: K+V of attended tokens (each key/value head
+    once, kv_elt bytes a number), q and out (elt bytes a number), table entries."""
     S = len(lens)
-    kv = sum(int(L) for L in lens) * 2 * H * D * elt
+    kv = sum(int(L) for L in lens) * 2 * (Hkv or H) * D * (kv_elt or elt)
     qo = 2 * S * H * D * elt
     tab = sum((int(L) + B - 1) // B for L in lens) * 4
     return kv + qo + tab
 
 
 def src_hash() -> str:
-    return hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the decode source files' code (comments and blank space left out): counter
+    figures are tied to one kernel build."""
+    import re
+    h = hashlib.sha256()
+    for f in DECODE_SRCS:
+        text = open(f).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():
@@ -66,19 +78,27 @@ def measured_traffic():
 
 
 COPY_CAL_BYTES = 512 << 20
+ELT = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 
 
 def _counter_rows(d, name):
+    """(kernel name, value) per dispatch of counter `name` from a rocprofv3 --pmc output
+    folder: CSV output (*counter_collection.csv) or the default database (*_results.db)."""
     import csv
     import glob
-    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
-    if not files:
-        raise SystemExit(f"no counter_collection.csv under {d}")
+    import sqlite3
     out = []
-    for f in files:
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
             if r.get("Counter_Name") == name:
                 out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    for f in glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True):
+        db = sqlite3.connect(f)
+        out += [(k, float(v)) for k, v in db.execute(
+            "select kernel_name, value from counters_collection where counter_name = ?", (name,))]
+        db.close()
+    if not out:
+        raise SystemExit(f"no {name} records under {d}")
     return out
 
 
@@ -160,12 +180,14 @@ def cpu_baseline(w, d0, seconds: float, gpu_out0):
         reps = 0
         out = None
         while True:
-            out = decode_attention(q, rp.k, rp.v, res.tables, res.lens, w.block_size)
+            out = decode_attention(q, rp.k, rp.v, res.tables, res.lens, w.block_size,
+                                   k_scale=w.k_scale, v_scale=w.v_scale)
             reps += 1
             if time.perf_counter() - t0 >= seconds:
                 break
         dt = time.perf_counter() - t0
-    nbytes = decode_bytes(res.lens, w.num_heads, w.head_dim, w.block_size, 2)
+    nbytes = decode_bytes(res.lens, w.num_heads, w.head_dim, w.block_size, ELT[w.dtype],
+                          w.num_kv_heads, ELT[w.pool_dtype])
     err = None
     if gpu_out0 is not None:
         err = float(np.max(np.abs(gpu_out0.astype(np.float64) - out)))
@@ -185,7 +207,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--layers", type=int, default=8, help="pools (model layers) per step")
+    ap.add_argument("--workload", default="opt13b_7x2048_f16_b16",
+                    help="fixed-length workload from workloads.BY_NAME")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="pools (model layers) per step; 0 = enough for >= 2 GB of pools")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -210,12 +235,17 @@ def main():
     import torch
 
     import workloads as wl
-    from paged_kv_cache_320_amd import PagedKVCache, _lib as L
+    from paged_kv_cache_320_amd import PagedKVCache, _lib as L, torch_dtype
 
     L.lib()  # fails loudly when libpagedkv.so has not been built
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    K, W, NL = args.steps, args.warmup, args.layers
-    base = wl.OPT13B_7x2048
+    K, W = args.steps, args.warmup
+    base = wl.BY_NAME[args.workload]
+    assert base.length_kind == "fixed", "bench.py times fixed-length batches"
+    kv_elt = ELT[base.pool_dtype]
+    fp8 = base.pool_dtype == "fp8"
+    per_layer = base.num_seqs * base.ctx_fixed * 2 * base.num_kv_heads * base.head_dim * kv_elt
+    NL = args.layers or min(16, max(8, -(-2_000_000_000 // per_layer)))
     w = base.scaled(steps=K + W)
     S, H, Hkv, D, B = w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size
     steps_room = (w.num_blocks - S * ((w.ctx_fixed + B - 1) // B)) // S * B
@@ -225,8 +255,9 @@ def main():
     draws = [wl.draw(w, device="cuda")]
     for li in range(1, NL):
         draws.append(wl.draw(w.scaled(seed=w.seed * 1000 + li), device="cuda"))
-    cache = PagedKVCache(w.num_blocks, B, Hkv, D, w.dtype, layers=NL, device="cuda",
-                         free_order=draws[0].free_order, fill=float("nan"))
+    cache = PagedKVCache(w.num_blocks, B, Hkv, D, w.pool_dtype, layers=NL, device="cuda",
+                         free_order=draws[0].free_order, fill=float("nan"),
+                         k_scale=w.k_scale, v_scale=w.v_scale)
     seqs = []
     for s in range(S):
         sid = cache.add()
@@ -251,7 +282,7 @@ def main():
     p_lens = [torch.empty(S, dtype=torch.int32, pin_memory=True) for _ in range(R)]
     p_pairs = [torch.empty((S, 2), dtype=torch.int32, pin_memory=True) for _ in range(R)]
     up_done = [torch.cuda.Event() for _ in range(R)]
-    outs = [torch.empty((S, H, D), dtype=torch.float16, device="cuda") for _ in range(NL)]
+    outs = [torch.empty((S, H, D), dtype=torch_dtype(w.dtype), device="cuda") for _ in range(NL)]
     newk = [[dl.step_k[i] for i in range(K + W)] for dl in draws]
     newv = [[dl.step_v[i] for i in range(K + W)] for dl in draws]
     qs = [[dl.step_q[i] for i in range(K + W)] for dl in draws]
@@ -279,13 +310,17 @@ def main():
         for li in range(NL):
             if pairs:
                 L.pa_copy_blocks(cache.k[li], cache.v[li], d_pairs[:len(pairs)])
-            L.pa_kv_write(cache.k[li], cache.v[li], newk[li][i], newv[li][i], d_slots)
+            cache.write(d_slots, newk[li][i], newv[li][i], layer=li)
         if timed:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
         for li in range(NL):
-            L.pa_decode_attention(outs[li], qs[li][i], cache.k[li], cache.v[li], d_tables, d_lens,
-                                  mctx, ws, partition_tokens=T)
+            if fp8:
+                L.pa_decode_attention_fp8(outs[li], qs[li][i], cache.k[li], cache.v[li], d_tables,
+                                          d_lens, mctx, ws, w.k_scale, w.v_scale, partition_tokens=T)
+            else:
+                L.pa_decode_attention(outs[li], qs[li][i], cache.k[li], cache.v[li], d_tables,
+                                      d_lens, mctx, ws, partition_tokens=T)
         if timed:
             e1.record()
             ev.append((e0, e1))
@@ -314,13 +349,15 @@ def main():
     ms_per_step = total_ms / K
 
     timed_lens = step_lens[W:]
-    bytes_per_step = [decode_bytes(l, H, D, B, 2) * NL for l in timed_lens]
+    elt = ELT[w.dtype]
+    bytes_per_step = [decode_bytes(l, H, D, B, elt, Hkv, kv_elt) * NL for l in timed_lens]
     value = sum(bytes_per_step) / (total_ms * 1e-3) / 1e9
     launch_ms = [a.elapsed_time(b) / NL for a, b in ev]   # per decode launch, per step
     avg_launch_ms = float(np.mean(launch_ms))
-    bytes_per_launch = float(np.mean([decode_bytes(l, H, D, B, 2) for l in timed_lens]))
+    bytes_per_launch = float(np.mean([decode_bytes(l, H, D, B, elt, Hkv, kv_elt)
+                                      for l in timed_lens]))
     achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
-    traffic = measured_traffic()
+    traffic = measured_traffic() if base.name == "opt13b_7x2048_f16_b16" else None
     log(f"step {ms_per_step * 1e3:.1f} us ({NL} layers), decode launch {avg_launch_ms * 1e3:.1f} us "
         f"(min {min(launch_ms) * 1e3:.1f}), {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBPS:.1%} of 8 TB/s")
 
@@ -347,10 +384,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
-        "data": "synthetic (seeded N(0,1)/sqrt(128) keys/values, N(0,1) queries; random block placement)",
+        "dtype": w.dtype,
+        "data": f"synthetic (seeded N(0,1)*{w.kv_std:.4g} keys/values, N(0,{w.q_std:g}) queries; "
+                "random block placement)",
         "config": {"workload": base.name, "seqs": S, "context_at_step0": w.ctx_fixed,
                    "heads": H, "kv_heads": Hkv, "head_dim": D, "block_size": B,
+                   "kv_cache_dtype": "fp8_e4m3" if fp8 else w.dtype,
                    "pool_blocks": w.num_blocks, "layers_per_step": NL,
                    "partition_tokens": T, "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),

@@ -62,7 +62,9 @@ enum {
   PA_EUNSUPPORTED = -5   /* valid but not supported (dtype, head_dim, block_size) */
 };
 
-enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 };
+/* Element formats. PA_FP8_E4M3 (OCP FP8 E4M3, one byte a number) is for key/value pools
+ * only: see pa_kv_write_fp8 and pa_decode_attention_fp8. */
+enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 };
 
 /* Message for the last failing call on this thread ("" if none). Owned by the library. */
 const char* pa_last_error(void);
@@ -144,10 +146,20 @@ int pa_kv_write(void* k_cache, void* v_cache, const void* k_new, const void* v_n
  *   k_cache[dst] = k_cache[src], v_cache[dst] = v_cache[src] for each pair.
  * Pairs are copied concurrently: destinations must be distinct and no block may be
  * both a source and a destination in one call (the allocator's pairs satisfy this).
- * A pair with an index outside [0, num_blocks) is skipped. */
+ * A pair with an index outside [0, num_blocks) is skipped. dtype may be PA_FP8_E4M3. */
 int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
                    int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
                    int32_t block_size, int32_t dtype, void* stream);
+
+/* Like pa_kv_write into PA_FP8_E4M3 pools ("What Came After": the cache kept in 8-bit
+ * floating point, one byte a number). k_new / v_new hold src_dtype values (PA_F32,
+ * PA_F16 or PA_BF16); each is stored as the E4M3 code of fp32(x) * fp32(1 / scale)
+ * (k_scale for keys, v_scale for values): round to nearest even, magnitudes beyond 448
+ * saturate to 448, NaN stays NaN. Scales must be finite and > 0. */
+int pa_kv_write_fp8(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                    const int64_t* slots, int32_t num_tokens, int32_t num_blocks,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int32_t src_dtype, float k_scale, float v_scale, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Decode attention ("One Token at a Time"; «KV cache» "How it works";
@@ -188,6 +200,18 @@ int pa_decode_attention(void* out, const void* q, const void* k_cache, const voi
                         int32_t max_blocks_per_seq, int32_t max_context_len,
                         int32_t partition_tokens, float scale, int32_t dtype,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Decode attention over PA_FP8_E4M3 pools: every stored key is decode(code) * k_scale,
+ * every value decode(code) * v_scale; q and out are q_dtype (PA_F16 or PA_BF16).
+ * Otherwise as pa_decode_attention (same workspace sizing). */
+int pa_decode_attention_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                            int32_t max_blocks_per_seq, int32_t max_context_len,
+                            int32_t partition_tokens, float scale, float k_scale, float v_scale,
+                            int32_t q_dtype, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /* ---------------------------------------------------------------------------
  * Measurement helpers (not part of the method): the achievable HBM read rate

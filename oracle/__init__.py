@@ -2,6 +2,8 @@
 
 A plain, slow, obviously correct model of what the paged KV cache computes:
   attention.py   generation-phase attention, gathered through block tables (fp64)
+  prefill.py     prompt-phase causal attention over the same paged cache (fp64)
+  fp8.py         the 8-bit (E4M3) storage format of an 8-bit key/value cache
   cache_ops.py   the new token's key/value write and the copy-on-write block copy
   allocator.py   the block allocator: free list, reference counts, copy-on-write
   sizing.py      the pages' cache-size arithmetic

@@ -16,7 +16,10 @@ Readings where the pages are silent:
   * heads are independent; with fewer key/value heads than query heads
     (heads sharing one set of keys and values, › "What Came After"), query
     head h reads key/value head h // (num_heads // num_kv_heads);
-  * a text with no cached token yields zeros.
+  * a text with no cached token yields zeros;
+  * pools stored in 8-bit floating point (uint8 codes, see oracle/fp8.py) hold
+    decode(code) * scale, with one scale for the key pool and one for the value
+    pool; attention runs on those values.
 """
 from __future__ import annotations
 
@@ -64,18 +67,34 @@ def softmax_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float)
     return p @ V
 
 
+def pool_values(pool, pool_scale: float = 1.0) -> np.ndarray:
+    """float64 values of a key or value pool; uint8 pools are E4M3 codes times pool_scale."""
+    try:
+        import torch
+        if isinstance(pool, torch.Tensor) and pool.dtype == torch.uint8:
+            pool = pool.numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    if isinstance(pool, np.ndarray) and pool.dtype == np.uint8:
+        from . import fp8
+        return fp8.dequantize(pool, pool_scale)
+    return to_f64(pool)
+
+
 def decode_attention(q, k_cache, v_cache, block_tables, context_lens, block_size: int,
-                     scale: float | None = None, pairs=None) -> np.ndarray:
+                     scale: float | None = None, pairs=None, k_scale: float = 1.0,
+                     v_scale: float = 1.0) -> np.ndarray:
     """Paged decode attention for a batch: out[s, h, :] as float64.
 
     q: [S, H, D]; k_cache, v_cache: [N, H_kv, B, D]; block_tables: [S, max_blocks]
     (entries past a text's last block are never read); context_lens: [S], the
     number of tokens each text attends, counting the step's new token.
+    k_scale, v_scale: pool scales, used when the pools hold uint8 E4M3 codes.
     `pairs`: optional list of (s, h) to compute; other outputs stay NaN.
     """
     qd = to_f64(q)
-    kd = to_f64(k_cache)
-    vd = to_f64(v_cache)
+    kd = pool_values(k_cache, k_scale)
+    vd = pool_values(v_cache, v_scale)
     tables = np.asarray(block_tables)
     lens = np.asarray(context_lens, dtype=np.int64)
     S, H, D = qd.shape

@@ -36,3 +36,28 @@ def copy_blocks(k_cache, v_cache, pairs) -> None:
     for src, dst in pairs:
         k_cache[int(dst)] = k_cache[int(src)].clone()
         v_cache[int(dst)] = v_cache[int(src)].clone()
+
+
+def quantize_rows(x, scale: float):
+    """E4M3 codes of values x stored with `scale`, rounding decided in float32.
+
+    The code of x is encode(float32(x) * float32(1 / scale)): one float32
+    multiply by the float32 reciprocal of the scale (each rounded to nearest
+    even), then the E4M3 rounding of that float32 value (oracle/fp8.py).
+    """
+    import numpy as np
+    import torch
+
+    from . import fp8
+    x32 = x.detach().to("cpu", torch.float32).numpy()
+    inv = np.float32(1.0) / np.float32(scale)
+    y = (x32 * inv).astype(np.float32)
+    return torch.from_numpy(fp8.encode(y.astype(np.float64)))
+
+
+def kv_write_fp8(k_cache, v_cache, k_new, v_new, slots, block_size: int, k_scale: float,
+                 v_scale: float) -> None:
+    """kv_write into uint8 E4M3 pools: each new value is quantized with its pool's scale
+    («The KV Cache and PagedAttention» › "What Came After": one byte a number)."""
+    kv_write(k_cache, v_cache, quantize_rows(k_new, k_scale), quantize_rows(v_new, v_scale),
+             slots, block_size)

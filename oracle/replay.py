@@ -14,7 +14,8 @@ Two modes:
               through the exported block tables.
   pool=False  no pools (multi-gigabyte workloads): each text keeps the
               ordered list of the token data written to it, and attention for
-              the requested (text, head) pairs runs on that contiguous copy.
+              the requested (text, head) pairs runs on that contiguous copy
+              (for E4M3 pools, on the values that data is stored as).
               The allocator still runs, so its tables can be compared.
 """
 from __future__ import annotations
@@ -46,18 +47,38 @@ class Replay:
         self.slot_of: Dict[object, int] = {}  # batch position -> sequence id
         self.tokens: Dict[int, list] = {}      # logical mode: seq id -> [(k, v) chunks]
         self.max_blocks = max_blocks
+        self.fp8 = getattr(w, "pool_dtype", w.dtype) == "fp8"
         tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
         if pool:
             shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
-            self.k = torch.full(shape, float("nan"), dtype=tdt)
-            self.v = torch.full(shape, float("nan"), dtype=tdt)
+            if self.fp8:  # E4M3 codes; 0x7F (NaN) where nothing was written
+                self.k = torch.full(shape, 0x7F, dtype=torch.uint8)
+                self.v = torch.full(shape, 0x7F, dtype=torch.uint8)
+            else:
+                self.k = torch.full(shape, float("nan"), dtype=tdt)
+                self.v = torch.full(shape, float("nan"), dtype=tdt)
         self.steps: List[StepResult] = []
+
+    def _cache_write(self, k, v, slots):
+        if self.fp8:
+            cache_ops.kv_write_fp8(self.k, self.v, k.cpu(), v.cpu(), slots, self.w.block_size,
+                                   self.w.k_scale, self.w.v_scale)
+        else:
+            cache_ops.kv_write(self.k, self.v, k.cpu(), v.cpu(), slots, self.w.block_size)
+
+    def stored_values(self, x, scale: float) -> np.ndarray:
+        """fp64 values the cache holds for written data x (E4M3 pools: quantized with
+        `scale`, then dequantized; other pools: x itself)."""
+        if not self.fp8:
+            return attention.to_f64(x)
+        from . import fp8
+        return fp8.dequantize(cache_ops.quantize_rows(x, scale).numpy(), scale)
 
     def _write(self, sid: int, k, v, slots, pair):
         if self.pool:
             if pair[0] >= 0:
                 cache_ops.copy_blocks(self.k, self.v, [pair])
-            cache_ops.kv_write(self.k, self.v, k.cpu(), v.cpu(), slots, self.w.block_size)
+            self._cache_write(k, v, slots)
         else:
             self.tokens[sid].append((k, v))
 
@@ -104,7 +125,7 @@ class Replay:
         k_new, v_new, q = d.step_k[t], d.step_v[t], d.step_q[t].cpu()
         if self.pool:
             cache_ops.copy_blocks(self.k, self.v, r.pairs)
-            cache_ops.kv_write(self.k, self.v, k_new.cpu(), v_new.cpu(), r.slots, w.block_size)
+            self._cache_write(k_new, v_new, r.slots)
         else:
             for i, sid in enumerate(r.seq_ids):
                 self.tokens[sid].append((k_new[i:i + 1], v_new[i:i + 1]))
@@ -115,7 +136,9 @@ class Replay:
         pairs = decode_pairs(t) if decode_pairs is not None else None
         if self.pool:
             r.out = attention.decode_attention(q, self.k, self.v, r.tables, lens,
-                                               w.block_size, pairs=pairs)
+                                               w.block_size, pairs=pairs,
+                                               k_scale=getattr(w, "k_scale", 1.0),
+                                               v_scale=getattr(w, "v_scale", 1.0))
         else:
             r.out = self.logical_attention(q, r.seq_ids, pairs)
         return r
@@ -137,9 +160,9 @@ class Replay:
             chunks = self.tokens[seq_ids[s]]
             for h in heads:
                 kvh = h // group
-                kh = attention.to_f64(torch.cat([c[0][:, kvh].cpu() for c in chunks])) \
-                    if chunks else np.zeros((0, D))
-                vh = attention.to_f64(torch.cat([c[1][:, kvh].cpu() for c in chunks])) \
-                    if chunks else np.zeros((0, D))
+                kh = self.stored_values(torch.cat([c[0][:, kvh].cpu() for c in chunks]),
+                                        w.k_scale) if chunks else np.zeros((0, D))
+                vh = self.stored_values(torch.cat([c[1][:, kvh].cpu() for c in chunks]),
+                                        w.v_scale) if chunks else np.zeros((0, D))
                 out[s, h] = attention.softmax_attention(qd[s, h], kh, vh, scale)
         return out

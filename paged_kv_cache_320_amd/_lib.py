@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpagedkv.so")
 
 PA_OK, PA_EINVAL, PA_ENOBLOCKS, PA_ENOSEQ, PA_EHIP, PA_EUNSUPPORTED = 0, -1, -2, -3, -4, -5
-PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 
 _c_int32_p = ctypes.POINTER(ctypes.c_int32)
 _c_int64_p = ctypes.POINTER(ctypes.c_int64)
@@ -45,11 +45,17 @@ SIGNATURES = {
     "pa_kv_write": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                    _vp]),
     "pa_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pa_kv_write_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                       ctypes.c_float, ctypes.c_float, _vp]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pa_decode_workspace_init": (ctypes.c_int, [_vp, _sz, _vp]),
     "pa_decode_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                            _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32,
                                            _vp, _sz, _vp]),
+    "pa_decode_attention_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                               _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float,
+                                               ctypes.c_float, ctypes.c_float, _i32, _vp, _sz,
+                                               _vp]),
     "pa_probe_sink_bytes": (_sz, [_i32]),
     "pa_stream_read_probe": (ctypes.c_int, [_vp, _sz, _vp, _i32, _vp]),
     "pa_copy_probe": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
@@ -193,8 +199,10 @@ def pa_alloc_stats(h) -> Tuple[int, int]:
 # ---- device operations ------------------------------------------------------
 
 def dtype_code(t) -> int:
+    """Element-format code of a tensor; uint8 tensors are E4M3 pools."""
     import torch
-    return {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}[t.dtype]
+    return {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
+            torch.uint8: PA_FP8_E4M3}[t.dtype]
 
 
 def _stream(stream) -> Optional[int]:
@@ -221,6 +229,21 @@ def pa_kv_write(k_cache, v_cache, k_new, v_new, slots, stream=None) -> None:
                              _dev(v_new, "v_new") if T else None,
                              _dev(slots, "slots") if T else None, T, N, Hkv, D, B,
                              dtype_code(k_cache), _stream(stream)))
+
+
+def pa_kv_write_fp8(k_cache, v_cache, k_new, v_new, slots, k_scale: float = 1.0,
+                    v_scale: float = 1.0, stream=None) -> None:
+    """E4M3 (uint8) pools [N, Hkv, B, D]; k_new/v_new [T, Hkv, D] in f32/f16/bf16."""
+    N, Hkv, B, D = k_cache.shape
+    T = int(slots.numel())
+    if T:
+        assert tuple(k_new.shape) == (T, Hkv, D) and tuple(v_new.shape) == (T, Hkv, D)
+    _check(lib().pa_kv_write_fp8(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                 _dev(k_new, "k_new") if T else None,
+                                 _dev(v_new, "v_new") if T else None,
+                                 _dev(slots, "slots") if T else None, T, N, Hkv, D, B,
+                                 dtype_code(k_new) if T else PA_F16, float(k_scale),
+                                 float(v_scale), _stream(stream)))
 
 
 def pa_copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
@@ -273,6 +296,25 @@ def pa_decode_attention(out, q, k_cache, v_cache, block_tables, context_lens, ma
         N, int(block_tables.shape[1]), int(max_context_len), int(partition_tokens), float(scale),
         dtype_code(q), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+
+
+def pa_decode_attention_fp8(out, q, k_cache, v_cache, block_tables, context_lens,
+                            max_context_len: int, workspace, k_scale: float = 1.0,
+                            v_scale: float = 1.0, partition_tokens: int = 0,
+                            scale: Optional[float] = None, stream=None) -> None:
+    """Decode over E4M3 (uint8) pools; q/out f16 or bf16."""
+    S, H, D = q.shape
+    N, Hkv, B, Dk = k_cache.shape
+    assert Dk == D and tuple(out.shape) == (S, H, D) and out.dtype == q.dtype
+    assert block_tables.shape[0] == S and context_lens.numel() == S
+    if scale is None:
+        scale = D ** -0.5
+    _check(lib().pa_decode_attention_fp8(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), S, H, Hkv, D, B,
+        N, int(block_tables.shape[1]), int(max_context_len), int(partition_tokens), float(scale),
+        float(k_scale), float(v_scale), dtype_code(q), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def pa_probe_sink_bytes(waves_per_cu: int = 0) -> int:

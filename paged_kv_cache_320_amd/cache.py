@@ -24,8 +24,10 @@ _TORCH_DTYPES = None
 
 
 def torch_dtype(name: str):
+    """torch dtype of a format name; "fp8" pools hold E4M3 codes as uint8."""
     import torch
-    return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[name]
+    return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+            "fp8": torch.uint8}[name]
 
 
 class BlockAllocator:
@@ -81,18 +83,27 @@ class BlockAllocator:
 
 
 class PagedKVCache:
-    """K/V pools [num_blocks, num_kv_heads, block_size, head_dim] per layer on one device."""
+    """K/V pools [num_blocks, num_kv_heads, block_size, head_dim] per layer on one device.
+
+    dtype "fp8" keeps E4M3 codes (one byte a number) with one scale per pool; new keys
+    and values (any 16/32-bit format) are quantized as they are written.
+    """
 
     def __init__(self, num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
                  dtype: str = "f16", layers: int = 1, device: str = "cuda",
-                 free_order: Optional[Sequence[int]] = None, fill: Optional[float] = None):
+                 free_order: Optional[Sequence[int]] = None, fill: Optional[float] = None,
+                 k_scale: float = 1.0, v_scale: float = 1.0):
         import torch
         self.num_blocks, self.block_size = num_blocks, block_size
         self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
         self.dtype, self.device = dtype, device
+        self.fp8 = dtype == "fp8"
+        self.k_scale, self.v_scale = k_scale, v_scale
         self.alloc = BlockAllocator(num_blocks, block_size, free_order)
         shape = (num_blocks, num_kv_heads, block_size, head_dim)
         tdt = torch_dtype(dtype)
+        if self.fp8 and fill is not None:
+            fill = 0x7F  # the E4M3 NaN code marks places never written
         if fill is None:
             self.k = [torch.empty(shape, dtype=tdt, device=device) for _ in range(layers)]
             self.v = [torch.empty(shape, dtype=tdt, device=device) for _ in range(layers)]
@@ -122,14 +133,17 @@ class PagedKVCache:
             for li in range(len(self.k)):
                 L.pa_copy_blocks(self.k[li], self.v[li], p)
         if n:
-            s = torch.tensor(slots, dtype=torch.int64, device=self.device)
-            L.pa_kv_write(self.k[layer], self.v[layer], k, v, s)
+            self.write(slots, k, v, layer)
         return slots, pair
 
     def write(self, slots, k, v, layer: int = 0) -> None:
         import torch
-        s = torch.as_tensor(np.asarray(slots, dtype=np.int64)).to(self.device)
-        L.pa_kv_write(self.k[layer], self.v[layer], k, v, s)
+        s = slots if isinstance(slots, torch.Tensor) else \
+            torch.as_tensor(np.asarray(slots, dtype=np.int64)).to(self.device)
+        if self.fp8:
+            L.pa_kv_write_fp8(self.k[layer], self.v[layer], k, v, s, self.k_scale, self.v_scale)
+        else:
+            L.pa_kv_write(self.k[layer], self.v[layer], k, v, s)
 
     def copy(self, pairs, layer: Optional[int] = None) -> None:
         import torch
@@ -167,8 +181,14 @@ class PagedKVCache:
         if out is None:
             out = torch.empty_like(q)
         ws = self.workspace(S, H, max_context_len, partition_tokens)
-        L.pa_decode_attention(out, q, self.k[layer], self.v[layer], block_tables, context_lens,
-                              max_context_len, ws, partition_tokens=partition_tokens, scale=scale)
+        if self.fp8:
+            L.pa_decode_attention_fp8(out, q, self.k[layer], self.v[layer], block_tables,
+                                      context_lens, max_context_len, ws, self.k_scale,
+                                      self.v_scale, partition_tokens=partition_tokens, scale=scale)
+        else:
+            L.pa_decode_attention(out, q, self.k[layer], self.v[layer], block_tables,
+                                  context_lens, max_context_len, ws,
+                                  partition_tokens=partition_tokens, scale=scale)
         return out
 
     def step(self, seqs: Sequence[int], k_new, v_new, q, max_blocks: Optional[int] = None,

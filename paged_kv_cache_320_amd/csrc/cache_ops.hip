@@ -6,6 +6,8 @@
 // shared block is copied whole before a sharer writes into it.
 #include "device.hpp"
 
+#include <cmath>
+
 namespace pagedkv {
 namespace {
 
@@ -48,8 +50,50 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
   }
 }
 
+// Quantizing write into E4M3 pools: one thread turns 16 source values of one (token,
+// kv head) row into 16 codes (16 bytes) for K and for V. rows = num_tokens * Hkv,
+// row = D codes = lpr 16-byte pieces; SRC is the source element format.
+template <int SRC>
+__global__ __launch_bounds__(kThreads) void kv_write_fp8_kernel(
+    uint4* __restrict__ kc, uint4* __restrict__ vc, const uint4* __restrict__ kn,
+    const uint4* __restrict__ vn, const int64_t* __restrict__ slots, int64_t pieces, int lpr,
+    int hkv, int bsz, int64_t num_slots, float k_inv, float v_inv) {
+  constexpr int IN = 16 * elt_size<SRC>() / 16;  // 16-byte source pieces per 16 codes
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < pieces;
+       i += (int64_t)gridDim.x * kThreads) {
+    const int64_t row = i / lpr;
+    const int piece = (int)(i - row * lpr);
+    const int64_t tok = row / hkv;
+    const int head = (int)(row - tok * hkv);
+    const int64_t slot = slots[tok];
+    if (slot < 0 || slot >= num_slots) continue;
+    const int64_t blk = slot / bsz;
+    const int place = (int)(slot - blk * bsz);
+    const int64_t dst = (((blk * hkv + head) * bsz + place) * lpr) + piece;
+    float kf[16], vf[16];
+#pragma unroll
+    for (int j = 0; j < IN; ++j) {
+      widen16<SRC>(kn[i * IN + j], kf + j * (16 / IN));
+      widen16<SRC>(vn[i * IN + j], vf + j * (16 / IN));
+    }
+    uint32_t kw[4], vw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      kw[j] = vw[j] = 0u;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        kw[j] |= e4m3_from_f32(kf[4 * j + b] * k_inv) << (8 * b);
+        vw[j] |= e4m3_from_f32(vf[4 * j + b] * v_inv) << (8 * b);
+      }
+    }
+    kc[dst] = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+    vc[dst] = make_uint4(vw[0], vw[1], vw[2], vw[3]);
+  }
+}
+
 int check_shape(int32_t num_blocks, int32_t hkv, int32_t d, int32_t bsz, int32_t dtype) {
-  if (!dtype_ok(dtype)) return fail(PA_EINVAL, "dtype %d is not PA_F32/PA_F16/PA_BF16", dtype);
+  if (!pool_dtype_ok(dtype))
+    return fail(PA_EINVAL, "dtype %d is not PA_F32/PA_F16/PA_BF16/PA_FP8_E4M3", dtype);
   if (d != 64 && d != 128) return fail(PA_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", d);
   if (bsz != 4 && bsz != 8 && bsz != 16 && bsz != 32)
     return fail(PA_EUNSUPPORTED, "block_size %d (supported: 4, 8, 16, 32)", bsz);
@@ -70,10 +114,52 @@ int grid_for(int64_t pieces) {
 
 using namespace pagedkv;
 
+extern "C" int pa_kv_write_fp8(void* k_cache, void* v_cache, const void* k_new,
+                               const void* v_new, const int64_t* slots, int32_t num_tokens,
+                               int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t src_dtype, float k_scale,
+                               float v_scale, void* stream) {
+  int rc = check_shape(num_blocks, num_kv_heads, head_dim, block_size, PA_FP8_E4M3);
+  if (rc != PA_OK) return rc;
+  if (!dtype_ok(src_dtype))
+    return fail(PA_EINVAL, "src_dtype %d is not PA_F32/PA_F16/PA_BF16", src_dtype);
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(PA_EINVAL, "scales must be finite and > 0");
+  if (num_tokens < 0) return fail(PA_EINVAL, "num_tokens %d < 0", num_tokens);
+  if (num_tokens == 0) return ok();
+  if (!k_cache || !v_cache || !k_new || !v_new || !slots) return fail(PA_EINVAL, "null pointer");
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
+    return fail(PA_EINVAL, "pools and new rows must be 16-byte aligned");
+  if (((uintptr_t)slots & 7u) != 0) return fail(PA_EINVAL, "slots must be 8-byte aligned");
+  const int lpr = head_dim / 16;  // 16 codes per piece
+  const int64_t pieces = (int64_t)num_tokens * num_kv_heads * lpr;
+  // the rounding of x / scale is decided as fp32(x) * fp32(1 / scale)
+  const float k_inv = 1.0f / k_scale, v_inv = 1.0f / v_scale;
+  const int64_t num_slots = (int64_t)num_blocks * block_size;
+  const dim3 grid(grid_for(pieces)), block(kThreads);
+  hipStream_t st = (hipStream_t)stream;
+  if (src_dtype == PA_F32)
+    hipLaunchKernelGGL(kv_write_fp8_kernel<PA_F32>, grid, block, 0, st, (uint4*)k_cache,
+                       (uint4*)v_cache, (const uint4*)k_new, (const uint4*)v_new, slots, pieces,
+                       lpr, (int)num_kv_heads, (int)block_size, num_slots, k_inv, v_inv);
+  else if (src_dtype == PA_F16)
+    hipLaunchKernelGGL(kv_write_fp8_kernel<PA_F16>, grid, block, 0, st, (uint4*)k_cache,
+                       (uint4*)v_cache, (const uint4*)k_new, (const uint4*)v_new, slots, pieces,
+                       lpr, (int)num_kv_heads, (int)block_size, num_slots, k_inv, v_inv);
+  else
+    hipLaunchKernelGGL(kv_write_fp8_kernel<PA_BF16>, grid, block, 0, st, (uint4*)k_cache,
+                       (uint4*)v_cache, (const uint4*)k_new, (const uint4*)v_new, slots, pieces,
+                       lpr, (int)num_kv_heads, (int)block_size, num_slots, k_inv, v_inv);
+  PA_HIP_CHECK(hipGetLastError());
+  return ok();
+}
+
 extern "C" int pa_kv_write(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                            const int64_t* slots, int32_t num_tokens, int32_t num_blocks,
                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                            int32_t dtype, void* stream) {
+  if (dtype == PA_FP8_E4M3)
+    return fail(PA_EINVAL, "E4M3 pools are written with pa_kv_write_fp8");
   int rc = check_shape(num_blocks, num_kv_heads, head_dim, block_size, dtype);
   if (rc != PA_OK) return rc;
   if (num_tokens < 0) return fail(PA_EINVAL, "num_tokens %d < 0", num_tokens);

@@ -1,0 +1,693 @@
+// Paged decode attention for gfx950: kernels and their launch templates.
+// decode_inst.hip instantiates them once per (key/value format, query format,
+// head_dim), one compile unit each; the C entry points are in decode.hip.
+//
+// What is computed: «KV cache» › "How it works" — the new position's query is
+// compared with every cached key of its text (its own included) and the softmax
+// weights mix the values. «The KV Cache and PagedAttention» › "The Block Table" —
+// the kernel follows each text's block table to its blocks, wherever they sit.
+// › "What Came After": several query heads may share one set of keys and values.
+//
+// How (design for MI355X; decode is bound by HBM bandwidth, so no MFMA):
+//  * A wave serves GS query heads that share one key/value head (GS = 1, 2, 4 or
+//    8), so each key/value row is read from HBM once per GS heads. A "run" is
+//    one text's chunks for one such head group.
+//  * Work unit = one 16-token chunk of one run. All units of the batch are
+//    numbered text-major, head group, chunk, and cut into equal contiguous
+//    segments, one per wavefront ("split-context" with equal work per wave, so
+//    any mix of lengths fills the 256 CUs evenly).
+//  * Inside a wave, a K or V row of head_dim elements is read by LPR lanes with
+//    16-byte loads; the wave covers RPW = 64 / LPR rows per load instruction, so
+//    a block's rows stream as fully coalesced 1 KiB wave loads. The lanes of a
+//    row form a group; each dot product is summed over the group with DPP.
+//  * Each row group keeps its own online softmax (running max m, sum l, weighted
+//    values acc) per query head in the exp2 domain; groups are merged at the end
+//    of a run. The loads of the next chunk are in flight while the current chunk
+//    is computed (two register buffers).
+//  * E4M3 (8-bit) pools: keys and values are widened to fp32 in registers by
+//    the hardware conversion; the key scale is folded into the score scale and
+//    the value scale applied once to the output, so the hot loop is unchanged.
+//  * Block ids are wave-uniform per load instruction and come through the
+//    scalar cache; the token index is clamped to the text's last token so no
+//    unfilled place is read.
+//  * A run covered entirely by one wave is finished in place; otherwise each
+//    wave covering part of it leaves a partial (m, l, acc) and decode_merge
+//    combines a run's partials in segment order. Merging inside this kernel by
+//    the last segment to arrive was measured slower on the 7 x 2,048 OPT-13B
+//    step: with agent-scope release/acquire fences (an L2 writeback and
+//    invalidate per partial) the launch doubled; with device-coherent stores, a
+//    completion wait and a counter it still cost more than this kernel plus the
+//    merge kernel. The kernel boundary gives the merge its visibility for free.
+//    The order of every sum depends only on logical positions, never on where
+//    blocks are placed.
+#pragma once
+
+#include "device.hpp"
+
+#include <cmath>
+
+namespace pagedkv {
+namespace decode_impl {
+
+
+constexpr int kChunk = 16;         // tokens per work unit
+constexpr int kWavesPerGroup = 4;  // wavefronts per workgroup
+constexpr int kThreads = 64 * kWavesPerGroup;
+constexpr int kWavesPerCU = 4;     // auto grid: segments per CU (measured best of 4, 6, 8, 12, 16)
+constexpr int kHdrBytes = 256;     // workspace header: total units, segment length
+constexpr int kMaxGS = 8;          // query heads per wave, at most
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Keys and values are read once per launch: non-temporal loads keep them from
+// displacing the block tables, queries and partials in the caches (measured on
+// the 7 x 2,048 OPT-13B step: 55 -> 48 us for the partition kernel).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const char* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__host__ __device__ __forceinline__ int units_of(int L) {
+  return L <= 0 ? 1 : (L + kChunk - 1) / kChunk;
+}
+
+// KT: storage format of keys and values; QT: format of queries and outputs (the same
+// except for E4M3 pools, whose queries and outputs are 16-bit).
+template <int KT, int D>
+struct Geo {
+  static constexpr int ELT = elt_size<KT>();
+  static constexpr int EPL = 16 / ELT;      // elements per lane per load
+  static constexpr int LPR = D / EPL;       // lanes per row
+  static constexpr int RPW = 64 / LPR;      // rows per wave load
+  static constexpr int NLD = kChunk / RPW;  // load instructions per chunk and tensor
+  static constexpr int PSTRIDE = D + 4;     // floats per partial: m, l, pad, pad, acc[D]
+};
+
+// Wave-uniform position in the unit numbering.
+struct Cursor {
+  int s, r, u;      // text, run (head group) within the text, chunk within the run
+  int U, L;         // chunks in the run, attended tokens (clamped to the table's capacity)
+  int over;         // context_lens[s] exceeded the table's capacity
+  int64_t excl;     // number of the first unit of text s
+};
+
+struct Ctx {
+  int S, H, Hkv;
+  int G;            // query heads per key/value head
+  int NG;           // head groups per key/value head (G / GS)
+  int R;            // runs per text (Hkv * NG)
+  int maxb, num_blocks;
+  int64_t capacity;  // max_blocks_per_seq * block_size
+  const int32_t* __restrict__ ctx;
+};
+
+__device__ __forceinline__ void set_text(Cursor& c, const Ctx& x, int s) {
+  c.s = s;
+  int L = s < x.S ? x.ctx[s] : 0;
+  if (L < 0) L = 0;
+  c.over = L > x.capacity;
+  if (c.over) L = (int)x.capacity;
+  c.L = L;
+  c.U = units_of(L);
+}
+
+__device__ __forceinline__ void advance(Cursor& c, const Ctx& x) {
+  if (++c.u == c.U) {
+    c.u = 0;
+    if (++c.r == x.R) {
+      c.r = 0;
+      c.excl += (int64_t)x.R * c.U;
+      set_text(c, x, c.s + 1);
+    }
+  }
+}
+
+// Key/value head of run r, and the first of its GS query heads.
+template <int GS>
+__device__ __forceinline__ int kv_head_of(int r, const Ctx& x) {
+  return GS == 1 ? r / x.G : r / x.NG;
+}
+template <int GS>
+__device__ __forceinline__ int first_head_of(int r, const Ctx& x) {
+  return GS == 1 ? r : (r / x.NG) * x.G + (r % x.NG) * GS;
+}
+
+// 16-byte pieces of QT per lane holding the lane's EPL query (or output) elements
+template <int KT, int QT, int D>
+constexpr int q_pieces() { return Geo<KT, D>::EPL * elt_size<QT>() / 16; }
+
+template <int KT, int QT, int D, int GS>
+struct Buf {
+  uint4 k[Geo<KT, D>::NLD];
+  uint4 v[Geo<KT, D>::NLD];
+  uint4 q[GS][q_pieces<KT, QT, D>()];
+  bool bad;  // a table entry outside the pool, or a context longer than the table
+};
+
+template <int KT, int D, int GS>
+struct State {
+  float m[GS], l[GS];
+  float acc[GS][Geo<KT, D>::EPL];
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int j = 0; j < GS; ++j) {
+      m[j] = -INFINITY;
+      l[j] = 0.f;
+#pragma unroll
+      for (int e = 0; e < Geo<KT, D>::EPL; ++e) acc[j][e] = 0.f;
+    }
+  }
+};
+
+template <int KT, int QT, int D, int B, int GS>
+__device__ __forceinline__ void load_chunk(Buf<KT, QT, D, GS>& b, const Cursor& c, const Ctx& x,
+                                           const char* __restrict__ kc,
+                                           const char* __restrict__ vc,
+                                           const char* __restrict__ q,
+                                           const int32_t* __restrict__ tables, int lane) {
+  using G = Geo<KT, D>;
+  constexpr int kRowBytes = D * G::ELT;
+  constexpr int64_t kTileBytes = (int64_t)B * kRowBytes;  // one (block, kv head) tile
+  constexpr int QP = q_pieces<KT, QT, D>();
+  constexpr int kQRowBytes = D * elt_size<QT>();
+  const int g = lane / G::LPR, lp = lane % G::LPR;
+  const int kvh = kv_head_of<GS>(c.r, x);
+  const int last = c.L > 0 ? c.L - 1 : 0;
+  const int32_t* trow = tables + (int64_t)c.s * x.maxb;
+  const int t_first = c.u * kChunk;
+  b.bad = c.over;
+  if constexpr (B >= kChunk) {
+    // the whole chunk lies in one block: one scalar table lookup, a scalar tile base
+    // and 32-bit lane offsets
+    int blk = trow[t_first / B];
+    const bool bad = (unsigned)blk >= (unsigned)x.num_blocks;
+    b.bad |= bad;
+    if (bad) blk = 0;  // read block 0 instead; the result is poisoned
+    const int64_t tile = ((int64_t)blk * x.Hkv + kvh) * kTileBytes;
+    const char* kb = kc + tile;
+    const char* vb = vc + tile;
+#pragma unroll
+    for (int i = 0; i < G::NLD; ++i) {
+      const int t = t_first + i * G::RPW + g;
+      const int tc = t < last ? t : last;
+      const uint32_t off = (uint32_t)(tc % B) * kRowBytes + lp * 16;
+      b.k[i] = load_stream(kb + off);
+      b.v[i] = load_stream(vb + off);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < G::NLD; ++i) {
+      const int t = t_first + i * G::RPW + g;
+      const int tc = t < last ? t : last;
+      int blk;
+      if constexpr (B >= G::RPW) {
+        // the rows of one load instruction lie in one block: a scalar lookup
+        const int t0 = min(t_first + i * G::RPW, last);
+        blk = trow[t0 / B];
+      } else {
+        blk = trow[tc / B];
+      }
+      const bool bad = (unsigned)blk >= (unsigned)x.num_blocks;
+      b.bad |= bad;
+      if (bad) blk = 0;
+      const int64_t off = ((int64_t)blk * x.Hkv + kvh) * kTileBytes +
+                          (uint32_t)(tc % B) * kRowBytes + lp * 16;
+      b.k[i] = load_stream(kc + off);
+      b.v[i] = load_stream(vc + off);
+    }
+  }
+  // the GS query rows (cache hits after the run's first chunk)
+  const char* qrow =
+      q + ((int64_t)c.s * x.H + first_head_of<GS>(c.r, x)) * kQRowBytes + lp * QP * 16;
+#pragma unroll
+  for (int j = 0; j < GS; ++j)
+#pragma unroll
+    for (int p = 0; p < QP; ++p)
+      b.q[j][p] = *reinterpret_cast<const uint4*>(qrow + j * kQRowBytes + p * 16);
+}
+
+template <int KT, int QT, int D, int GS>
+__device__ __forceinline__ void compute_chunk(const Buf<KT, QT, D, GS>& b, const Cursor& c,
+                                              State<KT, D, GS>& st, float scale_log2, int lane) {
+  using G = Geo<KT, D>;
+  constexpr int QP = q_pieces<KT, QT, D>();
+  if (c.L == 0) return;  // nothing attended: the run's result is zeros
+  const int g = lane / G::LPR;
+  float kf[G::NLD][G::EPL];
+#pragma unroll
+  for (int i = 0; i < G::NLD; ++i) widen16<KT>(b.k[i], kf[i]);
+  float vf[G::NLD][G::EPL];
+#pragma unroll
+  for (int i = 0; i < G::NLD; ++i) widen16<KT>(b.v[i], vf[i]);
+#pragma unroll
+  for (int j = 0; j < GS; ++j) {
+    float qf[G::EPL];
+#pragma unroll
+    for (int p = 0; p < QP; ++p) widen16<QT>(b.q[j][p], qf + p * (G::EPL / QP));
+    float sc[G::NLD];
+    float mc = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < G::NLD; ++i) {
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < G::EPL; ++e) d = fmaf(qf[e], kf[i][e], d);
+      d = group_sum<G::LPR>(d) * scale_log2;
+      const int t = c.u * kChunk + i * G::RPW + g;
+      if (t >= c.L) d = -INFINITY;
+      sc[i] = d;
+      mc = fmaxf(mc, d);
+    }
+    const float mn = fmaxf(st.m[j], mc);
+    const float mu = mn == -INFINITY ? 0.f : mn;
+    const float alpha = fast_exp2(st.m[j] - mu);
+    st.l[j] *= alpha;
+#pragma unroll
+    for (int e = 0; e < G::EPL; ++e) st.acc[j][e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < G::NLD; ++i) {
+      const float p = fast_exp2(sc[i] - mu);
+      st.l[j] += p;
+#pragma unroll
+      for (int e = 0; e < G::EPL; ++e) st.acc[j][e] = fmaf(p, vf[i][e], st.acc[j][e]);
+    }
+    st.m[j] = mn;
+    if (b.bad) {
+#pragma unroll
+      for (int e = 0; e < G::EPL; ++e) st.acc[j][e] = __builtin_nanf("");
+    }
+  }
+}
+
+// Merge the row groups of a wave (fixed butterfly order); every lane ends with the result.
+template <int KT, int D, int GS>
+__device__ __forceinline__ void merge_groups(State<KT, D, GS>& st) {
+  using G = Geo<KT, D>;
+#pragma unroll
+  for (int j = 0; j < GS; ++j) {
+#pragma unroll
+    for (int off = G::LPR; off < 64; off <<= 1) {
+      const float m2 = __shfl_xor(st.m[j], off);
+      const float l2 = __shfl_xor(st.l[j], off);
+      const float mn = fmaxf(st.m[j], m2);
+      const float mu = mn == -INFINITY ? 0.f : mn;
+      const float a = fast_exp2(st.m[j] - mu), b = fast_exp2(m2 - mu);
+      st.l[j] = st.l[j] * a + l2 * b;
+#pragma unroll
+      for (int e = 0; e < G::EPL; ++e) {
+        const float x2 = __shfl_xor(st.acc[j][e], off);
+        st.acc[j][e] = st.acc[j][e] * a + x2 * b;
+      }
+      st.m[j] = mn;
+    }
+  }
+}
+
+// Output row of (s, h) from fp32 values, PER consecutive elements per lane.
+template <int DT, int PER>
+__device__ __forceinline__ void store_out(char* __restrict__ dst, const float* o) {
+  if constexpr (DT == PA_F32) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) reinterpret_cast<float*>(dst)[e] = o[e];
+  } else if constexpr (DT == PA_F16) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) reinterpret_cast<_Float16*>(dst)[e] = (_Float16)o[e];
+  } else {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)bf16_bits_rne(o[e]);
+  }
+}
+
+// Partial record of query head j of segment w's slot (0: the segment's first run,
+// 1: its last run).
+template <int D, int GS>
+__device__ __forceinline__ int64_t partial_index(int64_t w, int slot, int j) {
+  return ((w * 2 + slot) * GS + j) * (int64_t)(D + 4);
+}
+
+template <int KT, int QT, int D, int GS>
+__device__ __forceinline__ void flush_run(State<KT, D, GS>& st, const Cursor& c, const Ctx& x,
+                                          int64_t seg_lo, int64_t seg_hi, int w,
+                                          char* __restrict__ out, float* __restrict__ partials,
+                                          float v_scale, int lane) {
+  using G = Geo<KT, D>;
+  constexpr int QP = q_pieces<KT, QT, D>();
+  merge_groups<KT, D, GS>(st);
+  const int64_t run_lo = c.excl + (int64_t)c.r * c.U;
+  const int64_t run_hi = run_lo + c.U;
+  const int h0 = first_head_of<GS>(c.r, x);
+  if (lane < G::LPR) {
+    if (run_lo >= seg_lo && run_hi <= seg_hi) {
+      // the whole run is in this segment: finish it here
+#pragma unroll
+      for (int j = 0; j < GS; ++j) {
+        float o[G::EPL];
+        const float inv = st.l[j] > 0.f ? v_scale / st.l[j] : 0.f;
+        // 0 * acc: zeros when nothing was attended, NaN for a poisoned run
+#pragma unroll
+        for (int e = 0; e < G::EPL; ++e)
+          o[e] = st.l[j] > 0.f ? st.acc[j][e] * inv : 0.f * st.acc[j][e];
+        char* dst = out + ((int64_t)c.s * x.H + h0 + j) * D * elt_size<QT>() + lane * QP * 16;
+#pragma unroll
+        for (int p = 0; p < QP; ++p)
+          reinterpret_cast<uint4*>(dst)[p] = narrow16<QT>(o + p * (G::EPL / QP));
+      }
+    } else {
+      const int slot = run_lo <= seg_lo ? 0 : 1;
+#pragma unroll
+      for (int j = 0; j < GS; ++j) {
+        float* p = partials + partial_index<D, GS>(w, slot, j);
+        if (lane == 0) {
+          p[0] = st.m[j];
+          p[1] = st.l[j];
+        }
+        float4* a4 = reinterpret_cast<float4*>(p + 4 + lane * G::EPL);
+#pragma unroll
+        for (int e = 0; e < G::EPL; e += 4)
+          a4[e / 4] = make_float4(st.acc[j][e], st.acc[j][e + 1], st.acc[j][e + 2], st.acc[j][e + 3]);
+      }
+    }
+  }
+  st.reset();
+}
+
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Sum over the workgroup (every thread gets it).
+__device__ __forceinline__ int64_t block_sum(int64_t x, int64_t* sh) {
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  const int wave = threadIdx.x / 64;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[wave] = x;
+  __syncthreads();
+  int64_t t = 0;
+#pragma unroll
+  for (int j = 0; j < kWavesPerGroup; ++j) t += sh[j];
+  return t;
+}
+
+template <int KT, int QT, int D, int B, int GS>
+__global__ __launch_bounds__(kThreads) void decode_partition(
+    char* __restrict__ out, const char* __restrict__ q, const char* __restrict__ kc,
+    const char* __restrict__ vc, const int32_t* __restrict__ tables,
+    const int32_t* __restrict__ ctx, int S, int H, int Hkv, int maxb, int num_blocks, int W,
+    int seg_fixed, float scale_log2, float v_scale, int64_t* __restrict__ hdr,
+    int64_t* __restrict__ excl_out, float* __restrict__ partials) {
+  __shared__ int64_t sh_red[kWavesPerGroup];
+  __shared__ int sh_seq[kWavesPerGroup];
+  __shared__ int64_t sh_off[kWavesPerGroup];
+  __shared__ int64_t sh_excl[kWavesPerGroup];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t capacity = (int64_t)maxb * B;
+  const int Gq = H / Hkv;
+  const int R = Hkv * (Gq / GS);
+  auto units_at = [&](int i) -> int64_t {
+    int L = ctx[i];
+    if (L < 0) L = 0;
+    if (L > capacity) L = (int)capacity;
+    return (int64_t)R * units_of(L);
+  };
+
+  // ---- locate each wave's segment: total units, then an exclusive scan ----
+  int64_t local = 0;
+  for (int i = tid; i < S; i += kThreads) local += units_at(i);
+  const int64_t total = uniform64(block_sum(local, sh_red));
+  const int64_t seg = seg_fixed > 0 ? seg_fixed : (total + W - 1) / W;
+  if (blockIdx.x == 0 && tid == 0) {
+    hdr[0] = total;
+    hdr[1] = seg;
+  }
+  int64_t carry = 0;
+  for (int base = 0; base < S; base += kThreads) {
+    const int i = base + tid;
+    const int64_t n = i < S ? units_at(i) : 0;
+    int64_t incl = n;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    __syncthreads();
+    if (lane == 63) sh_red[wave] = incl;
+    __syncthreads();
+    int64_t before = 0, all = 0;
+#pragma unroll
+    for (int j = 0; j < kWavesPerGroup; ++j) {
+      before += j < wave ? sh_red[j] : 0;
+      all += sh_red[j];
+    }
+    const int64_t ex = carry + before + incl - n;
+    if (i < S) {
+      if (blockIdx.x == 0) excl_out[i] = ex;
+#pragma unroll
+      for (int j = 0; j < kWavesPerGroup; ++j) {
+        const int64_t c0 = ((int64_t)blockIdx.x * kWavesPerGroup + j) * seg;
+        if (c0 >= ex && c0 < ex + n) {
+          sh_seq[j] = i;
+          sh_off[j] = c0 - ex;
+          sh_excl[j] = ex;
+        }
+      }
+    }
+    carry += all;
+  }
+  __syncthreads();
+
+  const int w = blockIdx.x * kWavesPerGroup + wave;
+  const int64_t seg_lo = (int64_t)w * seg;
+  if (w >= W || seg_lo >= total) return;
+  const int64_t seg_hi = seg_lo + seg < total ? seg_lo + seg : total;
+  const int n = (int)(seg_hi - seg_lo);
+
+  const Ctx x{S, H, Hkv, Gq, Gq / GS, R, maxb, num_blocks, capacity, ctx};
+  Cursor cur;
+  // values read from LDS are the same in every lane: keep them in scalar registers
+  cur.excl = uniform64(sh_excl[wave]);
+  set_text(cur, x, __builtin_amdgcn_readfirstlane(sh_seq[wave]));
+  {
+    const int64_t off = uniform64(sh_off[wave]);
+    cur.r = (int)(off / cur.U);
+    cur.u = (int)(off - (int64_t)cur.r * cur.U);
+  }
+  Cursor ld = cur;
+  const float sl = scale_log2;
+
+  State<KT, D, GS> st;
+  st.reset();
+  Buf<KT, QT, D, GS> A, Bb;
+  load_chunk<KT, QT, D, B, GS>(A, ld, x, kc, vc, q, tables, lane);
+  advance(ld, x);
+
+  auto finish = [&](int i) {
+    // last chunk of the run, or of the segment
+    if (cur.u == cur.U - 1 || i == n - 1)
+      flush_run<KT, QT, D, GS>(st, cur, x, seg_lo, seg_hi, w, out, partials, v_scale, lane);
+    advance(cur, x);
+  };
+
+  // steady state: both loads unconditional, so the next chunk's loads stay in
+  // flight while the current one is computed
+  int i = 0;
+  while (i + 2 < n) {
+    load_chunk<KT, QT, D, B, GS>(Bb, ld, x, kc, vc, q, tables, lane);
+    advance(ld, x);
+    compute_chunk<KT, QT, D, GS>(A, cur, st, sl, lane);
+    finish(i);
+    load_chunk<KT, QT, D, B, GS>(A, ld, x, kc, vc, q, tables, lane);
+    advance(ld, x);
+    compute_chunk<KT, QT, D, GS>(Bb, cur, st, sl, lane);
+    finish(i + 1);
+    i += 2;
+  }
+  if (i + 1 < n) {
+    load_chunk<KT, QT, D, B, GS>(Bb, ld, x, kc, vc, q, tables, lane);
+    compute_chunk<KT, QT, D, GS>(A, cur, st, sl, lane);
+    finish(i);
+    compute_chunk<KT, QT, D, GS>(Bb, cur, st, sl, lane);
+    finish(i + 1);
+  } else {
+    compute_chunk<KT, QT, D, GS>(A, cur, st, sl, lane);
+    finish(i);
+  }
+}
+
+// Combine the partials of one run for query head j (of the run's GS), left by
+// segments w0..w1, in segment order. Segment w0 holds the run in its slot 1 unless
+// the run starts exactly at w0's first unit (then it is w0's first run, slot 0);
+// every later segment starts inside the run, so the run is its first run (slot 0).
+// The partials are read UNROLL at a time with all loads in flight and combined
+// with a running maximum (the rescaling of the online softmax), in one pass.
+template <int QT, int D, int GS>
+__device__ __forceinline__ void merge_run(const float* __restrict__ partials, int64_t w0,
+                                          int64_t w1, int64_t run_lo, int64_t seg, int j,
+                                          float v_scale, char* __restrict__ dst_row, int lane) {
+  constexpr int PER = D / 64;  // output elements per lane
+  constexpr int UNROLL = 8;
+  auto index_of = [&](int64_t w) -> int64_t {
+    return partial_index<D, GS>(w, (w == w0 && run_lo != w0 * seg) ? 1 : 0, j);
+  };
+  float M = -INFINITY, den = 0.f, num[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) num[e] = 0.f;
+  for (int64_t w = w0; w <= w1; w += UNROLL) {
+    float m[UNROLL], l[UNROLL], a[UNROLL][PER];
+#pragma unroll
+    for (int k = 0; k < UNROLL; ++k) {
+      // past w1: an empty partial (weight 0) instead of a load
+      m[k] = -INFINITY;
+      l[k] = 0.f;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) a[k][e] = 0.f;
+      if (w + k <= w1) {
+        const float* p = partials + index_of(w + k);
+        m[k] = p[0];
+        l[k] = p[1];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) a[k][e] = p[4 + lane * PER + e];
+      }
+    }
+    float mg = M;
+#pragma unroll
+    for (int k = 0; k < UNROLL; ++k) mg = fmaxf(mg, m[k]);
+    const float mu = mg == -INFINITY ? 0.f : mg;
+    const float r = fast_exp2(M - mu);
+    den *= r;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) num[e] *= r;
+#pragma unroll
+    for (int k = 0; k < UNROLL; ++k) {  // segment order
+      const float f = fast_exp2(m[k] - mu);
+      den += f * l[k];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) num[e] += f * a[k][e];
+    }
+    M = mg;
+  }
+  float o[PER];
+  const float inv = den > 0.f ? v_scale / den : 0.f;
+  // 0 * num: NaN stays visible for a poisoned run
+#pragma unroll
+  for (int e = 0; e < PER; ++e) o[e] = den > 0.f ? num[e] * inv : 0.f * num[e];
+  store_out<QT, PER>(dst_row + lane * PER * elt_size<QT>(), o);
+}
+
+// Merge pass: one wave per (text, query head); runs finished inside one segment
+// return at once.
+template <int QT, int D, int GS>
+__global__ __launch_bounds__(kThreads) void decode_merge(
+    char* __restrict__ out, const int32_t* __restrict__ ctx, int S, int H, int Hkv, int maxb,
+    int bsz, float v_scale, const int64_t* __restrict__ hdr, const int64_t* __restrict__ excl,
+    const float* __restrict__ partials) {
+  const int lane = threadIdx.x & 63;
+  const int64_t pair =
+      (int64_t)blockIdx.x * kWavesPerGroup + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (pair >= (int64_t)S * H) return;
+  const int s = (int)(pair / H), h = (int)(pair - (int64_t)s * H);
+  const int Gq = H / Hkv, NG = Gq / GS;
+  const int kvh = h / Gq, within = h - kvh * Gq;
+  const int r = kvh * NG + within / GS, j = within % GS;
+  int L = ctx[s];
+  if (L < 0) L = 0;
+  const int64_t capacity = (int64_t)maxb * bsz;
+  if (L > capacity) L = (int)capacity;
+  const int U = units_of(L);
+  const int64_t seg = hdr[1];
+  const int64_t lo = excl[s] + (int64_t)r * U, hi = lo + U;
+  const int64_t w0 = lo / seg, w1 = (hi - 1) / seg;
+  if (w0 == w1) return;
+  merge_run<QT, D, GS>(partials, w0, w1, lo, seg, j, v_scale, out + pair * D * elt_size<QT>(),
+                       lane);
+}
+
+// ---- launch ------------------------------------------------------------------
+
+// Workspace: header (total units, segment length), int64 unit offset of each text [S],
+// fp32 partials [W][2][GS][D+4] (sized for GS = 8). Written by decode_partition, read
+// by decode_merge.
+struct Layout {
+  int64_t W;  // wavefronts (segments) in the grid
+  size_t excl_off, part_off, bytes;
+};
+
+struct Launch {
+  char* out;
+  const char* q;
+  const char* kc;
+  const char* vc;
+  const int32_t* tables;
+  const int32_t* ctx;
+  int S, H, Hkv, maxb, nb, W, seg_fixed;
+  float sl;       // scale * k_scale * log2(e)
+  float v_scale;
+  char* ws;
+  Layout lay;
+  hipStream_t st;
+};
+
+template <int KT, int QT, int D, int B, int GS>
+void launch(const Launch& a) {
+  int64_t* hdr = reinterpret_cast<int64_t*>(a.ws);
+  int64_t* excl = reinterpret_cast<int64_t*>(a.ws + a.lay.excl_off);
+  float* part = reinterpret_cast<float*>(a.ws + a.lay.part_off);
+  const int groups = (a.W + kWavesPerGroup - 1) / kWavesPerGroup;
+  hipLaunchKernelGGL((decode_partition<KT, QT, D, B, GS>), dim3(groups), dim3(kThreads), 0, a.st,
+                     a.out, a.q, a.kc, a.vc, a.tables, a.ctx, a.S, a.H, a.Hkv, a.maxb, a.nb, a.W,
+                     a.seg_fixed, a.sl, a.v_scale, hdr, excl, part);
+  const int64_t pairs = (int64_t)a.S * a.H;
+  const int mgroups = (int)((pairs + kWavesPerGroup - 1) / kWavesPerGroup);
+  hipLaunchKernelGGL((decode_merge<QT, D, GS>), dim3(mgroups), dim3(kThreads), 0, a.st, a.out,
+                     a.ctx, a.S, a.H, a.Hkv, a.maxb, B, a.v_scale, hdr, excl, part);
+}
+
+template <int KT, int QT, int D, int B>
+bool dispatch_gs(int GS, const Launch& a) {
+  switch (GS) {
+    case 1: launch<KT, QT, D, B, 1>(a); return true;
+    case 2: launch<KT, QT, D, B, 2>(a); return true;
+    case 4: launch<KT, QT, D, B, 4>(a); return true;
+    case 8: launch<KT, QT, D, B, 8>(a); return true;
+  }
+  return false;
+}
+
+template <int KT, int QT, int D>
+bool dispatch_b(int B, int GS, const Launch& a) {
+  switch (B) {
+    case 4: return dispatch_gs<KT, QT, D, 4>(GS, a);
+    case 8: return dispatch_gs<KT, QT, D, 8>(GS, a);
+    case 16: return dispatch_gs<KT, QT, D, 16>(GS, a);
+    case 32: return dispatch_gs<KT, QT, D, 32>(GS, a);
+  }
+  return false;
+}
+
+template <int KT, int QT>
+bool dispatch_d(int D, int B, int GS, const Launch& a) {
+  if (D == 64) return dispatch_b<KT, QT, 64>(B, GS, a);
+  if (D == 128) return dispatch_b<KT, QT, 128>(B, GS, a);
+  return false;
+}
+
+}  // namespace decode_impl
+
+// One instance per (key/value format, query/output format, head_dim), from decode_inst.hip.
+#define PA_DECL_INST(kt, qt, d) \
+  bool decode_launch_##kt##_##qt##_d##d(int B, int GS, const decode_impl::Launch& a);
+PA_DECL_INST(PA_F32, PA_F32, 64)
+PA_DECL_INST(PA_F32, PA_F32, 128)
+PA_DECL_INST(PA_F16, PA_F16, 64)
+PA_DECL_INST(PA_F16, PA_F16, 128)
+PA_DECL_INST(PA_BF16, PA_BF16, 64)
+PA_DECL_INST(PA_BF16, PA_BF16, 128)
+PA_DECL_INST(PA_FP8_E4M3, PA_F16, 64)
+PA_DECL_INST(PA_FP8_E4M3, PA_F16, 128)
+PA_DECL_INST(PA_FP8_E4M3, PA_BF16, 64)
+PA_DECL_INST(PA_FP8_E4M3, PA_BF16, 128)
+#undef PA_DECL_INST
+
+}  // namespace pagedkv

@@ -17,8 +17,12 @@ namespace pagedkv {
       return ::pagedkv::fail(PA_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_)); \
   } while (0)
 
-inline int elt_bytes(int dtype) { return dtype == PA_F32 ? 4 : 2; }
+inline int elt_bytes(int dtype) { return dtype == PA_F32 ? 4 : dtype == PA_FP8_E4M3 ? 1 : 2; }
 inline bool dtype_ok(int dtype) { return dtype == PA_F32 || dtype == PA_F16 || dtype == PA_BF16; }
+inline bool pool_dtype_ok(int dtype) { return dtype_ok(dtype) || dtype == PA_FP8_E4M3; }
+
+template <int DT>
+constexpr int elt_size() { return DT == PA_F32 ? 4 : DT == PA_FP8_E4M3 ? 1 : 2; }
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Compute units of the current device (cached per device id).
@@ -26,11 +30,23 @@ int device_cus(int* cus);
 
 // ---- element formats -------------------------------------------------------
 
-// 16 bytes of storage = 4 fp32, or 8 fp16 / bf16 values, widened exactly to fp32.
+// 16 bytes of storage = 4 fp32, 8 fp16 / bf16 or 16 E4M3 values, widened exactly to fp32.
+// E4M3 uses gfx950's conversion instruction, which reads the OCP E4M3 format.
 template <int DT>
 __device__ __forceinline__ void widen16(const uint4& x, float* f) {
   const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-  if constexpr (DT == PA_F32) {
+  if constexpr (DT == PA_FP8_E4M3) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+      f[4 * i] = lo.x;
+      f[4 * i + 1] = lo.y;
+      f[4 * i + 2] = hi.x;
+      f[4 * i + 3] = hi.y;
+    }
+  } else if constexpr (DT == PA_F32) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
   } else if constexpr (DT == PA_F16) {
@@ -54,6 +70,25 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
   u += 0x7fffu + ((u >> 16) & 1u);
   return u >> 16;
+}
+
+// fp32 -> OCP E4M3 code: round to nearest, ties to even, magnitudes >= 448 saturate to
+// 448, NaN -> 0x7F, the sign of values rounding to zero kept. Bit operations only, so
+// the code is the same on every device (E4M3: bias 7, 3 mantissa bits, smallest normal
+// 2^-6, subnormal steps of 2^-9).
+__device__ __forceinline__ uint32_t e4m3_from_f32(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;            // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;     // >= 448, infinities included
+  if (a >= 0x3c800000u) {                         // >= 2^-6: normal
+    const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);  // keep 3 mantissa bits, RNE
+    const uint32_t code = (r >> 20) - (120u << 3);        // exponent bias 127 -> 7
+    return sign | (code > 0x7eu ? 0x7eu : code);
+  }
+  // below 2^-6: multiples of 2^-9 (the scaling by 512 is exact), nearest even
+  return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
 }
 
 // 4 fp32 (or 8 for 16-bit formats) -> 16 bytes of storage, round to nearest even.

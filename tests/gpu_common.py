@@ -62,7 +62,8 @@ class NativeReplay:
     def __init__(self, w, d, fill=float("nan"), partition_tokens: int = 0):
         self.w, self.d = w, d
         self.cache = PagedKVCache(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim,
-                                  w.dtype, free_order=d.free_order, fill=fill)
+                                  w.pool_dtype, free_order=d.free_order, fill=fill,
+                                  k_scale=w.k_scale, v_scale=w.v_scale)
         self.slot_of = {}
         self.partition_tokens = partition_tokens
         self.steps = []

@@ -82,15 +82,33 @@ def test_sharp_scores(native, dtype):
     assert_close(got, want, dtype, "sharp")
 
 
-@pytest.mark.parametrize("H,Hkv", [(8, 2), (8, 1), (40, 8)])
+@pytest.mark.parametrize("H,Hkv", [(8, 2), (8, 1), (40, 8), (32, 2), (64, 8), (12, 4), (6, 3)])
 def test_shared_kv_heads(native, H, Hkv):
-    lens = [3, 70, 31]
+    """Query heads sharing key/value heads: one stream of a K/V head serves 1, 2, 4 or 8 of
+    them (G = 5 and 3 fall back to one head per wave; G = 16 uses two groups of 8)."""
+    lens = [3, 70, 31, 400]
     say(f"gqa H={H} Hkv={Hkv}")
     q, kc, vc, tables, L = make_case(H + Hkv, lens, H, Hkv, 128, 16, "f16",
                                      kv_std=1.0 / math.sqrt(128))
     want = decode_attention(q, kc, vc, tables, L, 16)
-    got = run_gpu(native, q, kc, vc, tables, L)
-    assert_close(got, want, "f16", "gqa")
+    for T in (0, 32):
+        got = run_gpu(native, q, kc, vc, tables, L, partition_tokens=T)
+        assert_close(got, want, "f16", f"gqa T={T}")
+
+
+@pytest.mark.parametrize("dtype,D,B", [("f32", 64, 4), ("bf16", 128, 32), ("f16", 64, 8),
+                                       ("bf16", 64, 16), ("f32", 128, 16)])
+@pytest.mark.parametrize("G", [2, 4, 8])
+def test_shared_kv_heads_all_formats(native, dtype, D, B, G):
+    lens = [1, 17, 129, 300]
+    Hkv = 2
+    kv_std = 1.0 if dtype == "f32" else 1.0 / math.sqrt(D)
+    say(f"gqa dtype={dtype} D={D} B={B} G={G}")
+    q, kc, vc, tables, L = make_case(G * 10 + D + B, lens, G * Hkv, Hkv, D, B, dtype, kv_std=kv_std)
+    want = decode_attention(q, kc, vc, tables, L, B)
+    for T in (0, 16):
+        got = run_gpu(native, q, kc, vc, tables, L, partition_tokens=T)
+        assert_close(got, want, dtype, f"T={T}")
 
 
 def test_single_token_is_exact(native):

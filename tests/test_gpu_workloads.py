@@ -12,6 +12,7 @@ import torch
 
 import workloads as wl
 from gpu_common import NativeReplay, assert_close, sample_pairs, say
+from oracle import cache_ops
 from oracle.replay import Replay
 
 pytestmark = pytest.mark.gpu
@@ -19,6 +20,8 @@ pytestmark = pytest.mark.gpu
 
 def bits(t):
     t = t.detach().cpu().contiguous()
+    if t.element_size() == 1:
+        return t
     return t.view(torch.int32) if t.element_size() == 4 else t.view(torch.int16)
 
 
@@ -61,13 +64,15 @@ def test_tiny_workload_whole_pool(native):
     say(f"  max abs error {err:.3e}")
 
 
-@pytest.mark.parametrize("dtype,B", [("bf16", 4), ("f16", 16), ("f32", 8)])
-def test_scaled_sharing_whole_pool(native, dtype, B):
+@pytest.mark.parametrize("dtype,B,cache", [("bf16", 4, ""), ("f16", 16, ""), ("f32", 8, ""),
+                                           ("f16", 16, "fp8"), ("bf16", 4, "fp8")])
+def test_scaled_sharing_whole_pool(native, dtype, B, cache):
     """Copy-on-write every step (parallel samples / beams), small enough for whole pools."""
     w = wl.SHARING_32x8.scaled(groups=3, samples=4, num_seqs=12, num_heads=4, num_kv_heads=4,
                                head_dim=64, block_size=B, num_blocks=160, prompt_len=6 * B + 3,
                                suffix_lo=0, suffix_hi=2 * B + 1, steps=4, dtype=dtype,
-                               kv_std=1.0 if dtype == "f32" else 0.125)
+                               kv_std=1.0 if dtype == "f32" else 0.125, cache_dtype=cache,
+                               k_scale=1 / 64 if cache else 1.0, v_scale=1 / 32 if cache else 1.0)
     say(f"workload {w.name} scaled dtype={dtype} B={B}")
     d = wl.draw(w)
     ops = wl.script(w, d)
@@ -102,10 +107,16 @@ def check_sampled_slots(nat, ora, w, d, nsamples=256, seed=0):
             t -= ck.shape[0]
         got_k = nat.cache.k[0][blk, :, place]
         got_v = nat.cache.v[0][blk, :, place]
-        assert torch.equal(bits(got_k), bits(k_tok)) and torch.equal(bits(got_v), bits(v_tok))
+        if w.pool_dtype == "fp8":
+            # E4M3 pools: the stored codes are the oracle's quantization of the token
+            assert torch.equal(got_k.cpu(), cache_ops.quantize_rows(k_tok, w.k_scale)) and \
+                torch.equal(got_v.cpu(), cache_ops.quantize_rows(v_tok, w.v_scale))
+        else:
+            assert torch.equal(bits(got_k), bits(k_tok)) and torch.equal(bits(got_v), bits(v_tok))
 
 
-FULL = [wl.OPT13B_7x2048, wl.OPT13B_MIXED256, wl.SHARING_32x8, wl.LONG_16x32K]
+FULL = [wl.OPT13B_7x2048, wl.OPT13B_MIXED256, wl.SHARING_32x8, wl.LONG_16x32K,
+        wl.LLAMA70B_32x4096, wl.OPT13B_7x2048_FP8]
 
 
 @pytest.mark.parametrize("w", FULL, ids=lambda w: w.name)

@@ -26,7 +26,9 @@ def test_tiny_lengths_and_fresh_blocks():
 
 
 def test_pool_and_logical_modes_agree():
-    for w in (wl.TINY, small_sharing()):
+    fp8_sharing = small_sharing().scaled(dtype="f16", cache_dtype="fp8", kv_std=0.3,
+                                         k_scale=1 / 64, v_scale=1 / 16)
+    for w in (wl.TINY, small_sharing(), fp8_sharing):
         d = wl.draw(w)
         a = Replay(w, d, pool=True).run(wl.script(w, d))
         b = Replay(w, d, pool=False).run(wl.script(w, d))

@@ -57,7 +57,16 @@ class Workload:
     prompt_len: int = 0
     suffix_lo: int = 0
     suffix_hi: int = 0
+    # key/value pool format when it differs from `dtype` ("fp8": OCP E4M3 codes with one
+    # scale per pool; the drawn keys/values are `dtype` values quantized on write)
+    cache_dtype: str = ""
+    k_scale: float = 1.0
+    v_scale: float = 1.0
     description: str = ""
+
+    @property
+    def pool_dtype(self) -> str:
+        return self.cache_dtype or self.dtype
 
     def scaled(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -100,8 +109,29 @@ LONG_16x32K = Workload(
     kv_std=1.0 / math.sqrt(128.0), q_std=1.0, steps=4, length_kind="fixed", ctx_fixed=32768,
     description="16 sequences x 32,768 tokens, 4 generation steps (32,768..32,771)")
 
+# Heads sharing key/value sets (P1 "What Came After": Llama 2 70B gives its 64 heads 8
+# sets). One layer of that shape: 64 query heads, 8 key/value heads of 128, fp16, block 16,
+# 32 texts x 4,096 tokens (the model's context length); not one of the five workloads above,
+# it measures the shared-head path.
+LLAMA70B_32x4096 = Workload(
+    name="llama2_70b_32x4096_f16_b16", seed=6, num_seqs=32, num_heads=64, num_kv_heads=8,
+    head_dim=128, block_size=16, num_blocks=32 * 257 + 64, dtype="f16",
+    kv_std=1.0 / math.sqrt(128.0), q_std=1.0, length_kind="fixed", ctx_fixed=4096,
+    description="Llama-2-70B-shaped layer: 64 query heads sharing 8 key/value heads of 128, "
+                "fp16, block 16, 32 x 4,096 tokens")
+
+# The cache kept in 8-bit floating point (P1 "What Came After": one byte a number, about
+# twice the tokens in the same memory): the OPT-13B 7 x 2,048 step with E4M3 pools. The
+# scales 1/256 (exact reciprocals) map the drawn keys/values (std 0.088) well inside E4M3's
+# range (448 * 1/256 = 1.75, about 20 standard deviations).
+OPT13B_7x2048_FP8 = OPT13B_7x2048.scaled(
+    name="opt13b_7x2048_fp8_b16", cache_dtype="fp8", k_scale=1 / 256, v_scale=1 / 256,
+    description="OPT-13B one layer with an E4M3 cache: 40 heads x 128, fp16 queries, "
+                "block 16, 7 x 2048 tokens, pool scales 1/256")
+
 ALL = (TINY, OPT13B_7x2048, OPT13B_MIXED256, SHARING_32x8, LONG_16x32K)
-BY_NAME = {w.name: w for w in ALL}
+EXTRA = (LLAMA70B_32x4096, OPT13B_7x2048_FP8)
+BY_NAME = {w.name: w for w in ALL + EXTRA}
 
 
 def _np_dtype_cast(x32: np.ndarray, dtype: str):
