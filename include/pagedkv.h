@@ -214,6 +214,40 @@ int pa_decode_attention_fp8(void* out, const void* q, const void* k_cache, const
                             void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Prompt phase ("One Token at a Time": a text's whole prompt at once; "What It
+ * Does": each token attends every token before it; «KV cache» "How it works":
+ * and its own). Causal attention of packed prompt queries over the paged cache.
+ *
+ *   rows q_start[s] .. q_start[s+1]-1 of q / out are text s's queries, its last
+ *   n_s = q_start[s+1] - q_start[s] positions: row q_start[s] + i sits at position
+ *   p = context_lens[s] - n_s + i and
+ *   out[row][h][:] = sum_{t<=p} w_t * V_s[t],  w = softmax_{t<=p}(scale * <q[row][h], K_s[t]>),
+ *   K_s / V_s read through the block table as in pa_decode_attention, key/value head
+ *   h / (num_heads / num_kv_heads).
+ * So the keys and values of the queries' own positions must already be in the cache
+ * (write them with pa_kv_write first); positions before the queries are a cached
+ * prefix (a reused prompt prefix, "What Came After"), possibly empty.
+ *
+ * q, out: [num_rows][num_heads][head_dim], dtype PA_F16 or PA_BF16 (pools the same);
+ * q_start: int32 [num_seqs + 1], non-decreasing, 0 <= q_start[s] and
+ * q_start[num_seqs] <= num_rows. Texts with q_start[s+1] <= q_start[s] are skipped;
+ * rows of a text whose range leaves [0, num_rows) are not written.
+ * max_q_len: the largest n_s (sizes the grid; larger n_s are still computed, slower).
+ * Products run on the matrix cores with fp32 accumulation; the softmax weights are
+ * rounded to the input format before they multiply the values; out is rounded to
+ * nearest even. n_s > context_lens[s], context_lens[s] > max_blocks_per_seq *
+ * block_size, or a table entry outside [0, num_blocks) for a needed position makes
+ * that text's rows NaN (nothing outside the pools is read).
+ * Returns PA_EUNSUPPORTED for other dtypes, head_dim other than 64/128, block_size
+ * other than 4/8/16/32. No workspace. */
+int pa_prefill_attention(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         const int32_t* q_start, int32_t num_seqs, int32_t num_rows,
+                         int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                         int32_t max_q_len, float scale, int32_t dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Measurement helpers (not part of the method): the achievable HBM read rate
  * and a copy of known size for calibrating memory counters.
  * ------------------------------------------------------------------------- */

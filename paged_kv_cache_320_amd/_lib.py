@@ -52,6 +52,9 @@ SIGNATURES = {
     "pa_decode_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                            _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32,
                                            _vp, _sz, _vp]),
+    "pa_prefill_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                            _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float,
+                                            _i32, _vp]),
     "pa_decode_attention_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                                _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float,
                                                ctypes.c_float, ctypes.c_float, _i32, _vp, _sz,
@@ -315,6 +318,25 @@ def pa_decode_attention_fp8(out, q, k_cache, v_cache, block_tables, context_lens
         N, int(block_tables.shape[1]), int(max_context_len), int(partition_tokens), float(scale),
         float(k_scale), float(v_scale), dtype_code(q), _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def pa_prefill_attention(out, q, k_cache, v_cache, block_tables, context_lens, q_start,
+                         max_q_len: int, scale: Optional[float] = None, stream=None) -> None:
+    """Causal prompt attention. out/q [T, H, D] (f16/bf16); pools [N, Hkv, B, D];
+    block_tables int32 [S, maxb]; context_lens int32 [S]; q_start int32 [S+1]."""
+    T, H, D = q.shape
+    N, Hkv, B, Dk = k_cache.shape
+    S = int(context_lens.numel())
+    assert Dk == D and tuple(out.shape) == (T, H, D) and out.dtype == q.dtype
+    assert block_tables.shape[0] == S and q_start.numel() == S + 1
+    if scale is None:
+        scale = D ** -0.5
+    _check(lib().pa_prefill_attention(
+        _dev(out, "out") if T else None, _dev(q, "q") if T else None, _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
+        _dev(context_lens, "context_lens"), _dev(q_start, "q_start"), S, T, H, Hkv, D, B, N,
+        int(block_tables.shape[1]), int(max_q_len), float(scale), dtype_code(q),
+        _stream(stream)))
 
 
 def pa_probe_sink_bytes(waves_per_cu: int = 0) -> int:

@@ -26,7 +26,7 @@ DECODE_INSTANCES = [(kt, qt, d) for kt, qt in (("PA_F32", "PA_F32"), ("PA_F16", 
                                                ("PA_FP8_E4M3", "PA_BF16"))
                     for d in (64, 128)]
 UNITS = [(src, os.path.splitext(src)[0], []) for src in
-         ("api.cpp", "allocator.cpp", "cache_ops.hip", "decode.hip", "probe.hip")] + \
+         ("api.cpp", "allocator.cpp", "cache_ops.hip", "decode.hip", "prefill.hip", "probe.hip")] + \
         [("decode_inst.hip", f"decode_inst_{kt}_{qt}_d{d}".lower(),
           [f"-DPA_INST_KT={kt}", f"-DPA_INST_QT={qt}", f"-DPA_INST_D={d}"])
          for kt, qt, d in DECODE_INSTANCES]

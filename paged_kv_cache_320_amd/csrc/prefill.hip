@@ -1,0 +1,322 @@
+// Prompt-phase (causal) attention over the paged cache on gfx950 matrix cores.
+//
+// What is computed: «The KV Cache and PagedAttention» › "One Token at a Time" — the
+// prompt phase handles a text's whole prompt at once; each position's query attends
+// the keys and values of every position up to and including its own (› "What It
+// Does"; «KV cache» › "How it works"). The queries are the last n positions of a
+// text, so a prompt may follow a cached prefix (› "What Came After") or recompute a
+// text's cache in one go (› "When Memory Runs Out"). Keys and values, the prompt's
+// own included, are read through the block table (› "The Block Table").
+//
+// How (design for MI355X): with up to thousands of queries per key this is a dense
+// contraction, so both products run on the matrix cores (v_mfma_f32_32x32x16 for
+// fp16 and bf16, fp32 accumulation).
+//  * A workgroup of 4 waves takes 128 consecutive queries of one (text, head); wave w
+//    holds queries 32w..32w+31 as the 32 columns of its MFMA tiles.
+//  * Keys stream in tiles of 32 positions. The workgroup copies a tile's keys and
+//    values from their blocks (16-byte loads, one table entry per block) into LDS;
+//    rows past the last position any query of the workgroup needs are zero.
+//  * S^T = K Q^T puts keys on the rows and queries on the columns, so a lane holds
+//    16 scores of one query and its partner lane (lane ^ 32) the other 16: the row
+//    maximum and sum need one exchange between the pair, no wider reduction.
+//  * Online softmax in the exp2 domain (scale * log2(e) folded in). The weights are
+//    rounded to the input format and O^T += V^T P^T runs on MFMA; the order in which
+//    each lane holds its scores is the order of the P^T operand's k index, so the
+//    weights never leave their registers; V^T is read from LDS.
+//  * Waves whose queries all precede a key tile skip its arithmetic (causal skip);
+//    the longest query tiles of a text are dispatched first.
+#include "device.hpp"
+
+#include <cmath>
+
+namespace pagedkv {
+namespace prefill_impl {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kQRows = 32 * kWaves;  // queries per workgroup
+constexpr int kKeys = 32;            // key positions per tile
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int DT>
+struct Mma;
+
+template <>
+struct Mma<PA_F16> {
+  typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+  static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t bits(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+  }
+};
+
+template <>
+struct Mma<PA_BF16> {
+  typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+  static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t bits(float x) { return bf16_bits_rne(x); }
+};
+
+// Key position held in accumulator register r of a lane in half `half` (0: lanes 0-31,
+// 1: lanes 32-63) of the 32x32 MFMA output, relative to the tile.
+__device__ __forceinline__ int key_of(int r, int half) { return (r >> 2) * 8 + half * 4 + (r & 3); }
+
+template <int DT, int D, int B>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(
+    char* __restrict__ out, const char* __restrict__ q, const char* __restrict__ kc,
+    const char* __restrict__ vc, const int32_t* __restrict__ tables,
+    const int32_t* __restrict__ ctx, const int32_t* __restrict__ q_start, int T, int H, int Hkv,
+    int maxb, int num_blocks, int qtiles, float scale_log2) {
+  using M = Mma<DT>;
+  typedef typename M::v8 v8;
+  constexpr int KS = D + 8;                      // 16-bit elements per LDS row
+  constexpr int CPR = D / 8;                     // 16-byte pieces per key row
+  constexpr int NC = kKeys * CPR / kThreads;     // pieces per thread and tile, each of K and V
+  constexpr int NQ = D / 16;                     // MFMA k-steps of S^T
+  constexpr int NM = D / 32;                     // 32-row tiles of O^T
+  static_assert(NC * kThreads == kKeys * CPR, "tile copy must cover the tile exactly");
+  __shared__ __align__(16) uint16_t ks[kKeys * KS];
+  __shared__ __align__(16) uint16_t vs[kKeys * KS];
+  __shared__ int bad_sh;
+
+  const int s = blockIdx.x / qtiles;
+  const int h = blockIdx.y;
+  const int kvh = h / (H / Hkv);
+  const int r0 = q_start[s], r1 = q_start[s + 1];
+  const int n = r1 - r0;
+  if (r0 < 0 || r1 > T || n <= 0) return;  // no rows of `out` to write
+  int L = ctx[s];
+  const int64_t cap = (int64_t)maxb * B;
+  const bool bad_shape = L < n || (int64_t)L > cap;
+  if ((int64_t)L > cap) L = (int)cap;
+  const int first = L - n;  // position of the text's first query
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int32_t* trow = tables + (int64_t)s * maxb;
+  if (tid == 0) bad_sh = 0;
+
+  for (int qt = qtiles - 1 - (int)(blockIdx.x % qtiles); qt * kQRows < n; qt += qtiles) {
+    const int row_lo = qt * kQRows;
+    const int row_hi = min(n, row_lo + kQRows);
+    const int kv_end = first + row_hi;           // positions [0, kv_end) are needed
+    const int kv_lim = min(kv_end, L);
+    const int wrow0 = row_lo + wave * 32;
+    const bool wave_on = wrow0 < row_hi;
+    const int wave_last = first + min(row_hi, wrow0 + 32) - 1;
+    const int row = wrow0 + col;
+    const bool row_ok = row < row_hi;
+    const int pos = row_ok ? first + row : -1;   // -1 attends nothing
+
+    // queries: lane holds q[row][16c + 8 half .. +7] for k-step c
+    v8 qv[NQ];
+    {
+      const char* qp = q + ((int64_t)(r0 + (row_ok ? row : row_lo)) * H + h) * (D * 2);
+#pragma unroll
+      for (int c = 0; c < NQ; ++c) {
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (row_ok) x = *(const u32x4*)(qp + (16 * c + 8 * half) * 2);
+        qv[c] = __builtin_bit_cast(v8, x);
+      }
+    }
+    f32x16 o[NM];
+#pragma unroll
+    for (int mt = 0; mt < NM; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[mt][r] = 0.f;
+    float m = -INFINITY, l = 0.f;
+
+    const int ntiles = kv_end > 0 ? (kv_end + kKeys - 1) / kKeys : 0;
+    for (int kt = 0; kt < ntiles; ++kt) {
+      __syncthreads();  // every wave is done with the previous tile
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        const int c = tid + j * kThreads;
+        const int key = c / CPR, pc = c % CPR;
+        const int kp = kt * kKeys + key;
+        u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
+        if (kp < kv_lim) {
+          int blk = trow[kp / B];
+          if ((unsigned)blk >= (unsigned)num_blocks) {
+            bad_sh = 1;  // read block 0 instead; the text's output is poisoned
+            blk = 0;
+          }
+          const int64_t off = (((int64_t)blk * Hkv + kvh) * B + kp % B) * (D * 2) + pc * 16;
+          kx = *(const u32x4*)(kc + off);
+          vx = *(const u32x4*)(vc + off);
+        }
+        *(u32x4*)(ks + key * KS + pc * 8) = kx;
+        *(u32x4*)(vs + key * KS + pc * 8) = vx;
+      }
+      __syncthreads();
+      if (!wave_on || kt * kKeys > wave_last) continue;  // causal skip (wave-uniform)
+
+      // S^T = K Q^T: A = 32 keys x 16 dims from LDS, B = the wave's queries
+      f32x16 sacc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+#pragma unroll
+      for (int c = 0; c < NQ; ++c) {
+        const v8 a = __builtin_bit_cast(v8, *(const u32x4*)(ks + col * KS + 16 * c + 8 * half));
+        sacc = M::mfma(a, qv[c], sacc);
+      }
+      float z[16];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        z[r] = kt * kKeys + key_of(r, half) <= pos ? sacc[r] * scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, z[r]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m, tmax);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m - m_use);
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        z[r] = fast_exp2(z[r] - m_use);
+        psum += z[r];
+      }
+      l = l * alpha + psum;
+      m = m_new;
+#pragma unroll
+      for (int mt = 0; mt < NM; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[mt][r] *= alpha;
+
+      // P^T operand of k-step kk: the lane's scores r = 8kk .. 8kk+7 (keys key_of(r, half))
+      v8 pb[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        u32x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          w[j] = M::bits(z[8 * kk + 2 * j]) | (M::bits(z[8 * kk + 2 * j + 1]) << 16);
+        pb[kk] = __builtin_bit_cast(v8, w);
+      }
+      // O^T += V^T P^T: A = V^T rows d = 32 mt + col over the same 8 keys per k-step
+#pragma unroll
+      for (int mt = 0; mt < NM; ++mt) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          u32x4 w;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t e0 = vs[key_of(8 * kk + 2 * j, half) * KS + 32 * mt + col];
+            const uint32_t e1 = vs[key_of(8 * kk + 2 * j + 1, half) * KS + 32 * mt + col];
+            w[j] = e0 | (e1 << 16);
+          }
+          o[mt] = M::mfma(__builtin_bit_cast(v8, w), pb[kk], o[mt]);
+        }
+      }
+    }
+    __syncthreads();  // bad_sh is final for this tile
+    const float lt = l + __shfl_xor(l, 32);
+    float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (bad_shape || bad_sh) inv = __builtin_nanf("");
+    if (row_ok) {
+      char* op = out + ((int64_t)(r0 + row) * H + h) * (D * 2);
+#pragma unroll
+      for (int mt = 0; mt < NM; ++mt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * mt + 8 * g + 4 * half;  // registers 4g..4g+3: dims d..d+3
+          uint2 w;
+          w.x = M::bits(o[mt][4 * g] * inv) | (M::bits(o[mt][4 * g + 1] * inv) << 16);
+          w.y = M::bits(o[mt][4 * g + 2] * inv) | (M::bits(o[mt][4 * g + 3] * inv) << 16);
+          *(uint2*)(op + d * 2) = w;
+        }
+    }
+  }
+}
+
+struct Args {
+  char* out;
+  const char *q, *kc, *vc;
+  const int32_t *tables, *ctx, *q_start;
+  int S, T, H, Hkv, maxb, num_blocks, qtiles;
+  float scale_log2;
+  hipStream_t st;
+};
+
+template <int DT, int D, int B>
+void launch(const Args& a) {
+  const dim3 grid((unsigned)(a.S * a.qtiles), (unsigned)a.H), block(kThreads);
+  hipLaunchKernelGGL((prefill_kernel<DT, D, B>), grid, block, 0, a.st, a.out, a.q, a.kc, a.vc,
+                     a.tables, a.ctx, a.q_start, a.T, a.H, a.Hkv, a.maxb, a.num_blocks,
+                     a.qtiles, a.scale_log2);
+}
+
+template <int DT, int D>
+void launch_b(int B, const Args& a) {
+  switch (B) {
+    case 4: launch<DT, D, 4>(a); break;
+    case 8: launch<DT, D, 8>(a); break;
+    case 16: launch<DT, D, 16>(a); break;
+    default: launch<DT, D, 32>(a); break;
+  }
+}
+
+template <int DT>
+void launch_d(int D, int B, const Args& a) {
+  if (D == 64) launch_b<DT, 64>(B, a);
+  else launch_b<DT, 128>(B, a);
+}
+
+}  // namespace prefill_impl
+}  // namespace pagedkv
+
+using namespace pagedkv;
+
+extern "C" int pa_prefill_attention(void* out, const void* q, const void* k_cache,
+                                    const void* v_cache, const int32_t* block_tables,
+                                    const int32_t* context_lens, const int32_t* q_start,
+                                    int32_t num_seqs, int32_t num_rows, int32_t num_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                    int32_t num_blocks, int32_t max_blocks_per_seq,
+                                    int32_t max_q_len, float scale, int32_t dtype, void* stream) {
+  using namespace prefill_impl;
+  if (dtype != PA_F16 && dtype != PA_BF16)
+    return fail(PA_EUNSUPPORTED, "prefill dtype %d (supported: PA_F16, PA_BF16)", dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
+  if (block_size != 4 && block_size != 8 && block_size != 16 && block_size != 32)
+    return fail(PA_EUNSUPPORTED, "block_size %d (supported: 4, 8, 16, 32)", block_size);
+  if (num_seqs < 1 || num_heads < 1 || num_kv_heads < 1 || num_blocks < 1 ||
+      max_blocks_per_seq < 1)
+    return fail(PA_EINVAL, "num_seqs, num_heads, num_kv_heads, num_blocks and "
+                "max_blocks_per_seq must be >= 1");
+  if (num_heads % num_kv_heads != 0)
+    return fail(PA_EINVAL, "num_heads %d is not a multiple of num_kv_heads %d", num_heads,
+                num_kv_heads);
+  if (num_heads > 65535) return fail(PA_EINVAL, "num_heads %d > 65535", num_heads);
+  if (num_rows < 0 || max_q_len < 0) return fail(PA_EINVAL, "num_rows and max_q_len must be >= 0");
+  if (!std::isfinite(scale)) return fail(PA_EINVAL, "scale is not finite");
+  if (num_rows == 0 || max_q_len == 0) return ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !q_start)
+    return fail(PA_EINVAL, "null pointer");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_EINVAL, "out, q and pools must be 16-byte aligned");
+  if (((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u) ||
+      ((uintptr_t)q_start & 3u))
+    return fail(PA_EINVAL, "tables, context_lens and q_start must be 4-byte aligned");
+  const int64_t qtiles = ((int64_t)max_q_len + kQRows - 1) / kQRows;
+  if ((int64_t)num_seqs * qtiles > 0x7fffffffLL)
+    return fail(PA_EINVAL, "num_seqs * ceil(max_q_len / %d) exceeds the grid", kQRows);
+  const Args a{(char*)out, (const char*)q, (const char*)k_cache, (const char*)v_cache,
+               block_tables, context_lens, q_start, num_seqs, num_rows, num_heads,
+               num_kv_heads, max_blocks_per_seq, num_blocks, (int)qtiles,
+               scale * 1.4426950408889634f, (hipStream_t)stream};
+  if (dtype == PA_F16) launch_d<PA_F16>(head_dim, block_size, a);
+  else launch_d<PA_BF16>(head_dim, block_size, a);
+  PA_HIP_CHECK(hipGetLastError());
+  return ok();
+}
