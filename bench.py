@@ -202,6 +202,203 @@ def cpu_baseline(w, d0, seconds: float, gpu_out0):
     }, err
 
 
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}   # dense fp16/bf16 matrix-core peak
+
+
+def prompt_flops(prompt_lens, prefix_len, H, D) -> int:
+    """Algorithmic flops of one prompt-phase launch: the query at position p takes
+    2*D flops per attended key for q.k and 2*D for the weighted sum of values."""
+    keys = sum(n * prefix_len + n * (n + 1) // 2 for n in prompt_lens)
+    return 4 * D * H * keys
+
+
+def bench_prompt(args, w) -> None:
+    """The prompt phase: per step, every text is added (after the shared cached prefix,
+    if any), its prompt's keys and values are written, and pa_prefill_attention runs."""
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from paged_kv_cache_320_amd import PagedKVCache, _lib as L, torch_dtype
+
+    K, W = args.steps, args.warmup
+    S, H, Hkv, D, B = w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size
+    NL = args.layers or 4
+    log(f"setup: {w.name}, {NL} layers, drawing inputs on the GPU")
+    d = wl.draw_prompt(w, device="cuda")
+    lens = d.prompt_lens
+    T = sum(lens)
+    cache = PagedKVCache(w.num_blocks, B, Hkv, D, w.dtype, layers=NL, device="cuda",
+                         free_order=d.free_order, fill=float("nan"))
+    prefix_seq = None
+    if w.prefix_len:
+        prefix_seq = cache.add()
+        slots, _ = cache.alloc.append(prefix_seq, w.prefix_len)
+        for li in range(NL):
+            cache.write(slots, d.prefix_k, d.prefix_v, layer=li)
+    pk = torch.cat(d.prompt_k).contiguous()
+    pv = torch.cat(d.prompt_v).contiguous()
+    q = d.q
+    q_start = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32,
+                           device="cuda")
+    max_blocks = (w.prefix_len + max(lens) + B - 1) // B
+    d_slots = torch.empty(T, dtype=torch.int64, device="cuda")
+    d_tables = torch.empty((S, max_blocks), dtype=torch.int32, device="cuda")
+    d_lens = torch.empty(S, dtype=torch.int32, device="cuda")
+    outs = [torch.empty((T, H, D), dtype=torch_dtype(w.dtype), device="cuda") for _ in range(NL)]
+    R = 4
+    p_slots = [torch.empty(T, dtype=torch.int64, pin_memory=True) for _ in range(R)]
+    p_tables = [torch.empty((S, max_blocks), dtype=torch.int32, pin_memory=True) for _ in range(R)]
+    p_lens = [torch.empty(S, dtype=torch.int32, pin_memory=True) for _ in range(R)]
+    up_done = [torch.cuda.Event() for _ in range(R)]
+    ev = []
+    tables0 = {}
+
+    def step(i: int, timed: bool):
+        seqs = [cache.fork(prefix_seq) if prefix_seq is not None else cache.add() for _ in lens]
+        r = i % R
+        up_done[r].synchronize()
+        off = 0
+        for sid, n in zip(seqs, lens):
+            slots, pair = cache.alloc.append(sid, n)
+            assert pair == (-1, -1), "the cached prefix ends on a block boundary"
+            p_slots[r].numpy()[off:off + n] = slots
+            off += n
+        L.pa_export_tables(cache.alloc.h, seqs, max_blocks, p_tables[r].numpy(), p_lens[r].numpy())
+        if i == 0:
+            tables0["tables"] = p_tables[r].numpy().copy()
+            tables0["lens"] = p_lens[r].numpy().copy()
+        d_slots.copy_(p_slots[r], non_blocking=True)
+        d_tables.copy_(p_tables[r], non_blocking=True)
+        d_lens.copy_(p_lens[r], non_blocking=True)
+        up_done[r].record()
+        for li in range(NL):
+            cache.write(d_slots, pk, pv, layer=li)
+        if timed:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+        for li in range(NL):
+            L.pa_prefill_attention(outs[li], q, cache.k[li], cache.v[li], d_tables, d_lens,
+                                   q_start, max(lens))
+        if timed:
+            e1.record()
+            ev.append((e0, e1))
+        for sid in seqs:
+            cache.free(sid)
+
+    log(f"warmup {W} steps")
+    for i in range(W):
+        step(i, False)
+        if i == 0:
+            torch.cuda.synchronize()
+            out0 = outs[0].float().cpu().numpy()
+    torch.cuda.synchronize()
+    log(f"timing {K} steps")
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(W, W + K):
+        step(i, True)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    flops = prompt_flops(lens, w.prefix_len, H, D)
+    launch_ms = [a.elapsed_time(b) / NL for a, b in ev]
+    avg = float(np.mean(launch_ms))
+    achieved = flops / (avg * 1e-3) / 1e12
+    value = flops * NL * K / (total_ms * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[w.dtype]
+    log(f"step {total_ms / K * 1e3:.1f} us ({NL} layers), prefill launch {avg * 1e3:.1f} us "
+        f"(min {min(launch_ms) * 1e3:.1f}), {achieved:.1f} TFLOP/s = {achieved / peak:.1%} of "
+        f"{peak:.0f}")
+
+    cpu, err0 = None, None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: fp64 oracle, sampled query rows of one layer, one thread")
+        cpu, err0 = cpu_baseline_prompt(w, d, tables0, args.cpu_seconds, out0)
+        log(f"cpu baseline {cpu['value']} GFLOP/s; sampled max abs error vs oracle {err0:.3e}")
+    line = {
+        "metric": "prompt-phase paged attention: TFLOP/s and % of the fp16/bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(total_ms / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": f"synthetic (seeded N(0,1)*{w.kv_std:.4g} keys/values, N(0,{w.q_std:g}) queries; "
+                "random block placement)",
+        "config": {"workload": w.name, "seqs": S, "prompt_tokens": T, "prefix_len": w.prefix_len,
+                   "heads": H, "kv_heads": Hkv, "head_dim": D, "block_size": B,
+                   "pool_blocks": w.num_blocks, "layers_per_step": NL,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": "pa_prefill_attention (prefill_kernel)",
+                     "avg_launch_us": round(avg * 1e3, 2), "flops_per_launch": flops},
+        "cpu_baseline": cpu,
+        "sampled_max_abs_err_vs_oracle": err0,
+        "wall_s_timed": round(wall, 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_prompt(w, d, tables0, seconds: float, gpu_out0):
+    """The prompt oracle on seeded sampled (row, head) pairs of step 0, one layer, one thread,
+    about `seconds` long; also the GPU's error on those pairs."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from oracle.prefill import prefill_attention
+
+    lens = d.prompt_lens
+    B, Hkv, D = w.block_size, w.num_kv_heads, w.head_dim
+    tables, ctx = tables0["tables"], tables0["lens"]
+    # the pools as the step-0 writes left them, built on the host from the same draws
+    N = w.num_blocks
+    kc = torch.full((N, Hkv, B, D), float("nan"), dtype=d.q.dtype)
+    vc = torch.full((N, Hkv, B, D), float("nan"), dtype=d.q.dtype)
+    for s in range(len(lens)):
+        ks = torch.cat([d.prefix_k.cpu(), d.prompt_k[s].cpu()])
+        vs = torch.cat([d.prefix_v.cpu(), d.prompt_v[s].cpu()])
+        t = torch.arange(ks.shape[0])
+        blk = torch.from_numpy(tables[s].astype(np.int64))[t // B]
+        kc[blk, :, t % B] = ks
+        vc[blk, :, t % B] = vs
+    q = d.q.cpu()
+    q_start = np.concatenate([[0], np.cumsum(lens)])
+    rng = np.random.default_rng(0)
+    rows = [(int(rng.integers(q.shape[0])), int(rng.integers(w.num_heads))) for _ in range(4096)]
+    rows += [(int(q_start[s + 1] - 1), 0) for s in range(len(lens))]  # every text's last row
+    done, got, t0 = [], {}, time.perf_counter()
+    with threadpool_limits(limits=1):
+        for i in range(0, len(rows), 512):
+            part = rows[i:i + 512]
+            o = prefill_attention(q, kc, vc, tables, ctx, q_start, B, rows=part)
+            for r, h in part:
+                got[(r, h)] = o[r, h].copy()
+            del o
+            done += part
+            if time.perf_counter() - t0 >= seconds:
+                break
+    dt = time.perf_counter() - t0
+    where = {}
+    for s in range(len(lens)):
+        for i in range(lens[s]):
+            where[int(q_start[s] + i)] = w.prefix_len + i
+    keys = sum(where[r] + 1 for r, _ in done)
+    flops = 4 * D * keys
+    err = float(max(np.abs(gpu_out0[r, h].astype(np.float64) - got[(r, h)]).max() for r, h in done))
+    return {"value": round(flops / dt / 1e9, 4), "unit": "GFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{w.name} one layer, step 0: {len(done)} seeded (query row, head) pairs "
+                      f"in {dt:.1f} s (fp64 numpy, BLAS limited to 1 thread)"}, err
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -241,6 +438,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     K, W = args.steps, args.warmup
     base = wl.BY_NAME[args.workload]
+    if isinstance(base, wl.PromptWorkload):
+        return bench_prompt(args, base)
     assert base.length_kind == "fixed", "bench.py times fixed-length batches"
     kv_elt = ELT[base.pool_dtype]
     fp8 = base.pool_dtype == "fp8"

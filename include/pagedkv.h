@@ -214,6 +214,37 @@ int pa_decode_attention_fp8(void* out, const void* q, const void* k_cache, const
                             void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Prefix caching ("What Came After": every full block gets a hash of its tokens and
+ * of everything before them; a request that begins the same way reuses the blocks,
+ * which saves prompt-phase work only).
+ *
+ * Hash: 64-bit FNV-1a chained over blocks,
+ *   h_j = FNV-1a(le64(h_{j-1}) || le32(tok[jB]) || ... || le32(tok[jB+B-1])),  h_{-1} = parent,
+ * for the n_tokens / block_size full blocks (parent = 0 at a text's start).
+ * Registered blocks: a hash maps to at most one block and a block carries at most
+ * one hash. A registered block whose count drops to 0 stays registered and goes to
+ * the bottom of the free stack (below every unregistered free block; of one text's
+ * blocks the later ones above the earlier), so it is handed out last; handing it
+ * out again drops its registration. Without registered blocks nothing changes in
+ * the policy above.
+ * ------------------------------------------------------------------------- */
+int pa_hash_blocks(const int32_t* tokens, int32_t n_tokens, int32_t block_size,
+                   uint64_t parent, uint64_t* hashes_out);
+/* A new sequence starting on the registered blocks matching hashes[0], hashes[1], ...
+ * up to the first miss (each count + 1; a free registered block is taken back out of
+ * the free stack). *n_cached_out = blocks reused; the sequence holds
+ * *n_cached_out * block_size tokens. To leave a prompt's last token to compute, pass
+ * at most (prompt_len - 1) / block_size hashes. */
+int pa_seq_add_cached(pa_alloc* a, const uint64_t* hashes, int32_t n_hashes, int32_t* seq_out,
+                      int32_t* n_cached_out);
+/* Register the sequence's first n blocks (all full, keys and values written) under
+ * hashes[0..n-1]; a hash already registered or a block already registered is skipped.
+ * PA_EINVAL (nothing changed) if n exceeds the sequence's blocks or one is not full. */
+int pa_seq_cache_blocks(pa_alloc* a, int32_t seq, const uint64_t* hashes, int32_t n);
+/* Registered blocks, and how many of them are free (count 0). */
+int pa_cache_stats(const pa_alloc* a, int32_t* registered_out, int32_t* registered_free_out);
+
+/* ---------------------------------------------------------------------------
  * Prompt phase ("One Token at a Time": a text's whole prompt at once; "What It
  * Does": each token attends every token before it; «KV cache» "How it works":
  * and its own). Causal attention of packed prompt queries over the paged cache.
@@ -238,8 +269,8 @@ int pa_decode_attention_fp8(void* out, const void* q, const void* k_cache, const
  * nearest even. n_s > context_lens[s], context_lens[s] > max_blocks_per_seq *
  * block_size, or a table entry outside [0, num_blocks) for a needed position makes
  * that text's rows NaN (nothing outside the pools is read).
- * Returns PA_EUNSUPPORTED for other dtypes, head_dim other than 64/128, block_size
- * other than 4/8/16/32. No workspace. */
+ * scale must be finite and > 0. Returns PA_EUNSUPPORTED for other dtypes, head_dim
+ * other than 64/128, block_size other than 4/8/16/32. No workspace. */
 int pa_prefill_attention(void* out, const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_tables, const int32_t* context_lens,
                          const int32_t* q_start, int32_t num_seqs, int32_t num_rows,

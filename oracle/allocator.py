@@ -26,6 +26,22 @@ same ones, so block tables can be compared bit for bit):
     count is back to 1 the remaining holder writes in place. A shared block
     that is already full is never copied: the append opens a new block.
   * One append of n tokens can copy at most one block (the last one).
+
+Prefix caching (› "What Came After": a full block gets a hash of its tokens
+and everything before them; a request that begins the same way reuses the
+blocks). Readings where the page is silent:
+  * blocks are registered explicitly (`cache_blocks`) once their keys and
+    values are written; a hash already registered, or a block already
+    carrying a hash, is left as it is;
+  * `add_cached` starts a text on the longest run of registered blocks
+    matching its leading block hashes, each block's count + 1; a registered
+    block whose count had dropped to 0 is taken back out of the free list;
+  * a registered block whose count drops to 0 stays registered and goes to
+    the bottom of the free stack, after every unregistered free block, so
+    cached blocks are handed out last: least recently freed first, and of one
+    text's blocks the later ones first. Handing a registered block out again
+    drops its registration (eviction).
+Without registered blocks every behaviour above is unchanged.
 """
 from __future__ import annotations
 
@@ -50,6 +66,8 @@ class BlockAllocator:
         self.blocks: Dict[int, List[int]] = {}
         self.filled: Dict[int, List[int]] = {}
         self.next_id = 0
+        self.hash_of: Dict[int, int] = {}    # registered block -> its hash
+        self.block_of: Dict[int, int] = {}   # hash -> registered block
 
     # -- texts --------------------------------------------------------------
     def add(self) -> int:
@@ -89,29 +107,75 @@ class BlockAllocator:
         pair = (-1, -1)
         if copy:
             src = blocks[-1]
-            dst = self.free.pop()
-            self.ref[dst] = 1
+            dst = self._take()
             self.ref[src] -= 1
             blocks[-1] = dst
             pair = (src, dst)
         slots = []
         for _ in range(n):
             if not blocks or filled[-1] == B:
-                b = self.free.pop()
-                self.ref[b] = 1
+                b = self._take()
                 blocks.append(b)
                 filled.append(0)
             slots.append(blocks[-1] * B + filled[-1])
             filled[-1] += 1
         return slots, pair
 
+    def _take(self) -> int:
+        """Top of the free stack, with count 1; a registered block loses its registration."""
+        b = self.free.pop()
+        if b in self.hash_of:
+            del self.block_of[self.hash_of.pop(b)]
+        self.ref[b] = 1
+        return b
+
     def free_seq(self, sid: int) -> None:
+        cached = []
         for b in self.blocks[sid]:
             self.ref[b] -= 1
             if self.ref[b] == 0:
-                self.free.append(b)
+                if b in self.hash_of:
+                    cached.append(b)
+                else:
+                    self.free.append(b)
+        for b in reversed(cached):
+            self.free.insert(0, b)  # bottom of the stack: handed out after all others
         del self.blocks[sid]
         del self.filled[sid]
+
+    # -- prefix caching -----------------------------------------------------
+    def add_cached(self, hashes: Sequence[int]) -> Tuple[int, int]:
+        """A new text starting on the registered blocks that match its leading block
+        hashes; returns (text id, blocks reused)."""
+        sid = self.add()
+        n = 0
+        for h in hashes:
+            b = self.block_of.get(int(h))
+            if b is None:
+                break
+            if self.ref[b] == 0:
+                self.free.remove(b)
+            self.ref[b] += 1
+            self.blocks[sid].append(b)
+            self.filled[sid].append(self.block_size)
+            n += 1
+        return sid, n
+
+    def cache_blocks(self, sid: int, hashes: Sequence[int]) -> None:
+        """Register the text's first len(hashes) blocks, which must be full."""
+        bl, fl = self.blocks[sid], self.filled[sid]
+        if len(hashes) > len(bl) or any(f != self.block_size for f in fl[:len(hashes)]):
+            raise ValueError("only full blocks of the text can be registered")
+        for b, h in zip(bl, hashes):
+            h = int(h)
+            if h in self.block_of or b in self.hash_of:
+                continue
+            self.block_of[h] = b
+            self.hash_of[b] = h
+
+    def cached_blocks(self) -> Tuple[int, int]:
+        """(registered blocks, registered blocks that are free)."""
+        return len(self.hash_of), sum(1 for b in self.hash_of if self.ref[b] == 0)
 
     # -- views --------------------------------------------------------------
     def context_len(self, sid: int) -> int:

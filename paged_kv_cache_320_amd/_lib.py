@@ -52,6 +52,10 @@ SIGNATURES = {
     "pa_decode_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                            _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32,
                                            _vp, _sz, _vp]),
+    "pa_hash_blocks": (ctypes.c_int, [_vp, _i32, _i32, ctypes.c_uint64, _vp]),
+    "pa_seq_add_cached": (ctypes.c_int, [_vp, _vp, _i32, _c_int32_p, _c_int32_p]),
+    "pa_seq_cache_blocks": (ctypes.c_int, [_vp, _i32, _vp, _i32]),
+    "pa_cache_stats": (ctypes.c_int, [_vp, _c_int32_p, _c_int32_p]),
     "pa_prefill_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                             _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float,
                                             _i32, _vp]),
@@ -197,6 +201,40 @@ def pa_alloc_stats(h) -> Tuple[int, int]:
     used, filled = ctypes.c_int64(), ctypes.c_int64()
     _check(lib().pa_alloc_stats(h, ctypes.byref(used), ctypes.byref(filled)))
     return used.value, filled.value
+
+
+# ---- prefix caching (host) ----------------------------------------------------
+
+def pa_hash_blocks(tokens, block_size: int, parent: int = 0) -> List[int]:
+    """Chained FNV-1a hashes of the full blocks of `tokens` (int sequence)."""
+    import numpy as np
+    t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64).astype(np.int32))
+    nb = len(t) // block_size if block_size > 0 else 0
+    out = np.zeros(max(nb, 1), dtype=np.uint64)
+    _check(lib().pa_hash_blocks(t.ctypes.data if len(t) else None, len(t), block_size,
+                                ctypes.c_uint64(parent & (2 ** 64 - 1)), out.ctypes.data))
+    return [int(x) for x in out[:nb]]
+
+
+def pa_seq_add_cached(h, hashes: Sequence[int]) -> Tuple[int, int]:
+    import numpy as np
+    arr = np.ascontiguousarray(np.asarray([int(x) for x in hashes], dtype=np.uint64))
+    seq, n = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().pa_seq_add_cached(h, arr.ctypes.data if len(arr) else None, len(arr),
+                                   ctypes.byref(seq), ctypes.byref(n)))
+    return seq.value, n.value
+
+
+def pa_seq_cache_blocks(h, seq: int, hashes: Sequence[int]) -> None:
+    import numpy as np
+    arr = np.ascontiguousarray(np.asarray([int(x) for x in hashes], dtype=np.uint64))
+    _check(lib().pa_seq_cache_blocks(h, seq, arr.ctypes.data if len(arr) else None, len(arr)))
+
+
+def pa_cache_stats(h) -> Tuple[int, int]:
+    r, f = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().pa_cache_stats(h, ctypes.byref(r), ctypes.byref(f)))
+    return r.value, f.value
 
 
 # ---- device operations ------------------------------------------------------

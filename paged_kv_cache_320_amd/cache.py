@@ -81,6 +81,17 @@ class BlockAllocator:
     def stats(self):
         return L.pa_alloc_stats(self.h)
 
+    # prefix caching
+    def add_cached(self, hashes: Sequence[int]):
+        """New text on the registered blocks matching its leading hashes: (id, blocks reused)."""
+        return L.pa_seq_add_cached(self.h, hashes)
+
+    def cache_blocks(self, seq: int, hashes: Sequence[int]) -> None:
+        L.pa_seq_cache_blocks(self.h, seq, hashes)
+
+    def cache_stats(self):
+        return L.pa_cache_stats(self.h)
+
 
 class PagedKVCache:
     """K/V pools [num_blocks, num_kv_heads, block_size, head_dim] per layer on one device.

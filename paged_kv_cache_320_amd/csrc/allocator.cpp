@@ -9,6 +9,9 @@
 //                              into a shared block gets a copy and the original's count drops.
 //  "When Memory Runs Out"      a text holds all of its blocks or none: an append that cannot
 //                              get every block it needs changes nothing.
+//  "What Came After"           prefix caching: full blocks registered under a chained hash of
+//                              their tokens are reused by texts that begin the same way;
+//                              registered blocks nobody holds are handed out last.
 // The free-list order, id assignment and "first writer copies" choices are fixed in
 // pagedkv.h so that tables are reproducible.
 //
@@ -16,6 +19,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <new>
+#include <unordered_map>
 #include <vector>
 
 #include "status.hpp"
@@ -32,14 +36,71 @@ struct Seq {
   int64_t ctx = 0;              // tokens held
 };
 
+// The free blocks as a stack that also takes blocks at its bottom and gives up any
+// block in O(1) (a doubly linked list over block ids; `down` points toward the bottom).
+struct FreeStack {
+  std::vector<int32_t> up, down;
+  int32_t top = -1, bottom = -1, size = 0;
+
+  void init(int32_t n) {
+    up.assign(n, -1);
+    down.assign(n, -1);
+  }
+  void push_top(int32_t b) {
+    up[b] = -1;
+    down[b] = top;
+    if (top >= 0) up[top] = b;
+    else bottom = b;
+    top = b;
+    ++size;
+  }
+  void push_bottom(int32_t b) {
+    down[b] = -1;
+    up[b] = bottom;
+    if (bottom >= 0) down[bottom] = b;
+    else top = b;
+    bottom = b;
+    ++size;
+  }
+  void remove(int32_t b) {
+    const int32_t u = up[b], d = down[b];
+    if (u >= 0) down[u] = d;
+    else top = d;
+    if (d >= 0) up[d] = u;
+    else bottom = u;
+    up[b] = down[b] = -1;
+    --size;
+  }
+  int32_t pop_top() {
+    const int32_t b = top;
+    remove(b);
+    return b;
+  }
+};
+
 }  // namespace
 
 struct pa_alloc {
   int32_t num_blocks = 0;
   int32_t block_size = 0;
-  std::vector<int32_t> free_stack;  // top = back
+  FreeStack free_stack;
   std::vector<int32_t> ref;
   std::vector<Seq> seqs;            // index = sequence id
+  // prefix caching: registered blocks and their hashes
+  std::unordered_map<uint64_t, int32_t> block_of;
+  std::vector<uint64_t> hash_of;
+  std::vector<char> registered;
+
+  // Top of the free stack with count 1; a registered block loses its registration.
+  int32_t take() {
+    const int32_t b = free_stack.pop_top();
+    if (registered[b]) {
+      block_of.erase(hash_of[b]);
+      registered[b] = 0;
+    }
+    ref[b] = 1;
+    return b;
+  }
 
   Seq* find(int32_t id) {
     if (id < 0 || id >= (int32_t)seqs.size() || !seqs[id].live) return nullptr;
@@ -66,16 +127,14 @@ struct pa_alloc {
   int append(Seq& s, int32_t n, int64_t* slots, int32_t* src, int32_t* dst) {
     bool copy = false;
     int64_t need = blocks_needed(s, n, &copy);
-    if (need > (int64_t)free_stack.size())
-      return fail(PA_ENOBLOCKS, "append of %d tokens needs %lld blocks, %zu free", n,
-                  (long long)need, free_stack.size());
+    if (need > (int64_t)free_stack.size)
+      return fail(PA_ENOBLOCKS, "append of %d tokens needs %lld blocks, %d free", n,
+                  (long long)need, free_stack.size);
     *src = -1;
     *dst = -1;
     if (copy) {
       int32_t old = s.blocks.back();
-      int32_t fresh = free_stack.back();
-      free_stack.pop_back();
-      ref[fresh] = 1;
+      int32_t fresh = take();
       ref[old] -= 1;
       s.blocks.back() = fresh;
       *src = old;
@@ -83,9 +142,7 @@ struct pa_alloc {
     }
     for (int32_t i = 0; i < n; ++i) {
       if (s.blocks.empty() || s.filled.back() == block_size) {
-        int32_t b = free_stack.back();
-        free_stack.pop_back();
-        ref[b] = 1;
+        int32_t b = take();
         s.blocks.push_back(b);
         s.filled.push_back(0);
       }
@@ -113,7 +170,9 @@ int pa_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* free_
   a->num_blocks = num_blocks;
   a->block_size = block_size;
   a->ref.assign(num_blocks, 0);
-  a->free_stack.resize(num_blocks);
+  a->hash_of.assign(num_blocks, 0);
+  a->registered.assign(num_blocks, 0);
+  a->free_stack.init(num_blocks);
   if (free_order) {
     std::vector<char> seen(num_blocks, 0);
     for (int32_t i = 0; i < num_blocks; ++i) {
@@ -123,10 +182,10 @@ int pa_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* free_
         return fail(PA_EINVAL, "free_order is not a permutation of 0..%d", num_blocks - 1);
       }
       seen[b] = 1;
-      a->free_stack[num_blocks - 1 - i] = b;
     }
+    for (int32_t i = 0; i < num_blocks; ++i) a->free_stack.push_bottom(free_order[i]);
   } else {
-    for (int32_t i = 0; i < num_blocks; ++i) a->free_stack[num_blocks - 1 - i] = i;
+    for (int32_t i = 0; i < num_blocks; ++i) a->free_stack.push_bottom(i);
   }
   *out = a;
   return ok();
@@ -191,10 +250,17 @@ int pa_seq_free(pa_alloc* a, int32_t seq) {
   if (!a) return fail(PA_EINVAL, "null argument");
   Seq* s = a->find(seq);
   if (!s) return fail(PA_ENOSEQ, "unknown sequence %d", seq);
+  std::vector<int32_t> cached;
   for (int32_t b : s->blocks) {
     a->ref[b] -= 1;
-    if (a->ref[b] == 0) a->free_stack.push_back(b);
+    if (a->ref[b] == 0) {
+      if (a->registered[b]) cached.push_back(b);
+      else a->free_stack.push_top(b);
+    }
   }
+  // registered blocks go below every other free block: the text's later blocks above
+  // its earlier ones, all above blocks freed before
+  for (auto it = cached.rbegin(); it != cached.rend(); ++it) a->free_stack.push_bottom(*it);
   *s = Seq();  // live = false, storage released
   return ok();
 }
@@ -255,7 +321,7 @@ int pa_block_ref(const pa_alloc* a, int32_t block, int32_t* ref_out) {
 
 int pa_num_free(const pa_alloc* a, int32_t* n_out) {
   if (!a || !n_out) return fail(PA_EINVAL, "null argument");
-  *n_out = (int32_t)a->free_stack.size();
+  *n_out = a->free_stack.size;
   return ok();
 }
 
@@ -269,8 +335,97 @@ int pa_alloc_stats(const pa_alloc* a, int64_t* used_blocks, int64_t* filled_slot
   int64_t f = 0;
   for (int32_t x : filled)
     if (x > 0) f += x;
-  *used_blocks = (int64_t)a->num_blocks - (int64_t)a->free_stack.size();
+  *used_blocks = (int64_t)a->num_blocks - (int64_t)a->free_stack.size;
   *filled_slots = f;
+  return ok();
+}
+
+// ---- prefix caching ("What Came After") ---------------------------------------
+
+// 64-bit FNV-1a (offset basis 0xcbf29ce484222325, prime 0x100000001b3) over `n` bytes,
+// continuing from state h.
+static uint64_t fnv1a64(uint64_t h, const unsigned char* p, size_t n) {
+  for (size_t i = 0; i < n; ++i) {
+    h ^= p[i];
+    h *= 0x100000001b3ull;
+  }
+  return h;
+}
+
+int pa_hash_blocks(const int32_t* tokens, int32_t n_tokens, int32_t block_size, uint64_t parent,
+                   uint64_t* hashes_out) {
+  if (n_tokens < 0 || block_size < 1) return fail(PA_EINVAL, "n_tokens < 0 or block_size < 1");
+  const int32_t nb = n_tokens / block_size;
+  if (nb > 0 && (!tokens || !hashes_out)) return fail(PA_EINVAL, "null argument");
+  uint64_t h = parent;
+  for (int32_t j = 0; j < nb; ++j) {
+    unsigned char le[8];
+    for (int k = 0; k < 8; ++k) le[k] = (unsigned char)(h >> (8 * k));
+    uint64_t x = fnv1a64(0xcbf29ce484222325ull, le, 8);
+    for (int32_t t = 0; t < block_size; ++t) {
+      const uint32_t tok = (uint32_t)tokens[(int64_t)j * block_size + t];
+      unsigned char tb[4] = {(unsigned char)tok, (unsigned char)(tok >> 8),
+                             (unsigned char)(tok >> 16), (unsigned char)(tok >> 24)};
+      x = fnv1a64(x, tb, 4);
+    }
+    hashes_out[j] = h = x;
+  }
+  return ok();
+}
+
+int pa_seq_add_cached(pa_alloc* a, const uint64_t* hashes, int32_t n_hashes, int32_t* seq_out,
+                      int32_t* n_cached_out) {
+  if (!a || !seq_out || !n_cached_out || (n_hashes > 0 && !hashes))
+    return fail(PA_EINVAL, "null argument");
+  if (n_hashes < 0) return fail(PA_EINVAL, "n_hashes %d < 0", n_hashes);
+  if (a->seqs.size() >= (size_t)INT32_MAX) return fail(PA_EINVAL, "sequence ids exhausted");
+  Seq s;
+  s.live = true;
+  for (int32_t j = 0; j < n_hashes; ++j) {
+    auto it = a->block_of.find(hashes[j]);
+    if (it == a->block_of.end()) break;
+    const int32_t b = it->second;
+    if (a->ref[b] == 0) a->free_stack.remove(b);
+    a->ref[b] += 1;
+    s.blocks.push_back(b);
+    s.filled.push_back(a->block_size);
+    s.ctx += a->block_size;
+  }
+  *n_cached_out = (int32_t)s.blocks.size();
+  a->seqs.push_back(std::move(s));
+  *seq_out = (int32_t)a->seqs.size() - 1;
+  return ok();
+}
+
+int pa_seq_cache_blocks(pa_alloc* a, int32_t seq, const uint64_t* hashes, int32_t n) {
+  if (!a || (n > 0 && !hashes)) return fail(PA_EINVAL, "null argument");
+  Seq* s = a->find(seq);
+  if (!s) return fail(PA_ENOSEQ, "unknown sequence %d", seq);
+  if (n < 0 || n > (int32_t)s->blocks.size())
+    return fail(PA_EINVAL, "n %d outside [0, %zu]", n, s->blocks.size());
+  for (int32_t j = 0; j < n; ++j)
+    if (s->filled[j] != a->block_size)
+      return fail(PA_EINVAL, "logical block %d of sequence %d is not full", j, seq);
+  for (int32_t j = 0; j < n; ++j) {
+    const int32_t b = s->blocks[j];
+    if (a->registered[b] || a->block_of.count(hashes[j])) continue;
+    a->block_of.emplace(hashes[j], b);
+    a->hash_of[b] = hashes[j];
+    a->registered[b] = 1;
+  }
+  return ok();
+}
+
+int pa_cache_stats(const pa_alloc* a, int32_t* registered_out, int32_t* registered_free_out) {
+  if (!a || !registered_out || !registered_free_out) return fail(PA_EINVAL, "null argument");
+  int32_t r = 0, f = 0;
+  for (int32_t b = 0; b < a->num_blocks; ++b)
+    if (a->registered[b]) {
+      ++r;
+      if (a->ref[b] == 0) ++f;
+    }
+  *registered_out = r;
+  *registered_free_out = f;
   return ok();
 }
 

@@ -22,7 +22,8 @@
 //  * Online softmax in the exp2 domain (scale * log2(e) folded in). The weights are
 //    rounded to the input format and O^T += V^T P^T runs on MFMA; the order in which
 //    each lane holds its scores is the order of the P^T operand's k index, so the
-//    weights never leave their registers; V^T is read from LDS.
+//    weights never leave their registers. V^T comes from the row-major value tile
+//    through gfx950's transposing LDS read (two reads per MFMA operand).
 //  * Waves whose queries all precede a key tile skip its arithmetic (causal skip);
 //    the longest query tiles of a text are dispatched first.
 #include "device.hpp"
@@ -51,8 +52,12 @@ struct Mma<PA_F16> {
   static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
-  static __device__ __forceinline__ uint32_t bits(float x) {
-    return __builtin_bit_cast(uint16_t, (_Float16)x);
+  static constexpr float kSlack = 8.f;  // log2 of the largest softmax weight held
+  // two fp32 -> two fp16 in one word (round to nearest even), first in the low half
+  static __device__ __forceinline__ uint32_t pack2(float x, float y) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){x, y}, h2));
   }
 };
 
@@ -62,15 +67,45 @@ struct Mma<PA_BF16> {
   static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
-  static __device__ __forceinline__ uint32_t bits(float x) { return bf16_bits_rne(x); }
+  static constexpr float kSlack = 0.f;
+  static __device__ __forceinline__ uint32_t pack2(float x, float y) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){x, y}, b2));
+  }
 };
 
 // Key position held in accumulator register r of a lane in half `half` (0: lanes 0-31,
 // 1: lanes 32-63) of the 32x32 MFMA output, relative to the tile.
 __device__ __forceinline__ int key_of(int r, int half) { return (r >> 2) * 8 + half * 4 + (r & 3); }
 
+// A operand of O^T += V^T P^T for 32-row tile mt and k-step kk: lane l needs
+// V[key_of(8 kk + j, l / 32)][32 mt + l % 32] for j = 0..7. gfx950's ds_read_b64_tr_b16
+// reads, per group of 16 lanes, the 4 x 16-bit pieces that lane j of the group
+// addresses and hands lane i element i % 4 of lane 4k + i / 4's piece as its value k.
+// So lane j of a group addresses key (its value k = j / 4) at dims 4 (j % 4) .. +3
+// of the group's 16 dims, and lane i receives 4 keys at dim (group base) + i. Two
+// reads give the 8 keys: 16 kk + 4 half + (0..3), then the same + 8.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+template <int KS>
+__device__ __forceinline__ u32x4 vt_operand(const uint16_t* vs, int mt, int kk, int lane) {
+  const int grp = lane >> 4, j = lane & 15;
+  const int dim = 32 * mt + 16 * (grp & 1) + 4 * (j & 3);
+  const int key = 16 * kk + 4 * (grp >> 1) + (j >> 2);
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + key * KS + dim));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + (key + 8) * KS + dim));
+  u32x4 w;
+  w[0] = (uint16_t)a[0] | ((uint32_t)(uint16_t)a[1] << 16);
+  w[1] = (uint16_t)a[2] | ((uint32_t)(uint16_t)a[3] << 16);
+  w[2] = (uint16_t)b[0] | ((uint32_t)(uint16_t)b[1] << 16);
+  w[3] = (uint16_t)b[2] | ((uint32_t)(uint16_t)b[3] << 16);
+  return w;
+}
+
 template <int DT, int D, int B>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(
     char* __restrict__ out, const char* __restrict__ q, const char* __restrict__ kc,
     const char* __restrict__ vc, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ ctx, const int32_t* __restrict__ q_start, int T, int H, int Hkv,
@@ -83,8 +118,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   constexpr int NQ = D / 16;                     // MFMA k-steps of S^T
   constexpr int NM = D / 32;                     // 32-row tiles of O^T
   static_assert(NC * kThreads == kKeys * CPR, "tile copy must cover the tile exactly");
-  __shared__ __align__(16) uint16_t ks[kKeys * KS];
-  __shared__ __align__(16) uint16_t vs[kKeys * KS];
+  __shared__ __align__(16) uint16_t ks[2][kKeys * KS];  // two buffers: compute one tile
+  __shared__ __align__(16) uint16_t vs[2][kKeys * KS];  // while the next is stored
+
   __shared__ int bad_sh;
 
   const int s = blockIdx.x / qtiles;
@@ -99,10 +135,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   if ((int64_t)L > cap) L = (int)cap;
   const int first = L - n;  // position of the text's first query
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int col = lane & 31, half = lane >> 5;
   const int32_t* trow = tables + (int64_t)s * maxb;
   if (tid == 0) bad_sh = 0;
+  __syncthreads();  // cleared before any tile load can set it
 
   for (int qt = qtiles - 1 - (int)(blockIdx.x % qtiles); qt * kQRows < n; qt += qtiles) {
     const int row_lo = qt * kQRows;
@@ -135,90 +173,131 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     float m = -INFINITY, l = 0.f;
 
     const int ntiles = kv_end > 0 ? (kv_end + kKeys - 1) / kKeys : 0;
-    for (int kt = 0; kt < ntiles; ++kt) {
-      __syncthreads();  // every wave is done with the previous tile
+    const int wave_first = first + wrow0;  // position of the wave's first query
+    // Register copies of the next tile's keys and values: the global loads of tile kt+1
+    // are in flight while tile kt is computed from the other LDS buffer. The block ids of
+    // a tile are read one tile earlier still, so no load waits on a table lookup.
+    u32x4 kx[NC], vx[NC];
+    int tb[NC];
+    auto load_table = [&](int kt) {
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        const int kp = kt * kKeys + (tid + j * kThreads) / CPR;
+        tb[j] = kp < kv_lim ? trow[kp / B] : 0;
+      }
+    };
+    auto fetch = [&](int kt) {
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
         const int c = tid + j * kThreads;
         const int key = c / CPR, pc = c % CPR;
         const int kp = kt * kKeys + key;
-        u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
+        kx[j] = u32x4{0u, 0u, 0u, 0u};
+        vx[j] = u32x4{0u, 0u, 0u, 0u};
         if (kp < kv_lim) {
-          int blk = trow[kp / B];
+          int blk = tb[j];
           if ((unsigned)blk >= (unsigned)num_blocks) {
             bad_sh = 1;  // read block 0 instead; the text's output is poisoned
             blk = 0;
           }
           const int64_t off = (((int64_t)blk * Hkv + kvh) * B + kp % B) * (D * 2) + pc * 16;
-          kx = *(const u32x4*)(kc + off);
-          vx = *(const u32x4*)(vc + off);
+          kx[j] = *(const u32x4*)(kc + off);
+          vx[j] = *(const u32x4*)(vc + off);
         }
-        *(u32x4*)(ks + key * KS + pc * 8) = kx;
-        *(u32x4*)(vs + key * KS + pc * 8) = vx;
       }
-      __syncthreads();
-      if (!wave_on || kt * kKeys > wave_last) continue;  // causal skip (wave-uniform)
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        const int c = tid + j * kThreads;
+        const int key = c / CPR, pc = c % CPR;
+        *(u32x4*)(ks[buf] + key * KS + pc * 8) = kx[j];
+        *(u32x4*)(vs[buf] + key * KS + pc * 8) = vx[j];
+      }
+    };
+    if (ntiles > 0) {
+      load_table(0);
+      fetch(0);
+      stash(0);
+      if (ntiles > 1) load_table(1);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < ntiles; ++kt) {
+      const int buf = kt & 1;
+      if (kt + 1 < ntiles) fetch(kt + 1);
+      if (kt + 2 < ntiles) load_table(kt + 2);
+      if (wave_on && kt * kKeys <= wave_last) {  // causal skip (wave-uniform)
+        const uint16_t* kb = ks[buf];
+        const uint16_t* vb = vs[buf];
+        // S^T = K Q^T: A = 32 keys x 16 dims from LDS, B = the wave's queries
+        f32x16 sacc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) {
+          const v8 a = __builtin_bit_cast(v8, *(const u32x4*)(kb + col * KS + 16 * c + 8 * half));
+          sacc = M::mfma(a, qv[c], sacc);
+        }
+        // raw scores (scale_log2 > 0 keeps their order); on a diagonal tile, keys after
+        // a query's own position get no weight
+        if (kt * kKeys + kKeys - 1 > wave_first) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kt * kKeys + key_of(r, half) > pos) sacc[r] = -INFINITY;
+        }
+        float tmax = sacc[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, sacc[r]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * scale_log2;
+        // fp16 weights: the reference maximum m moves only when a score exceeds it by
+        // more than 2^8 (or on the first key), so weights stay below 256 and most tiles
+        // skip the rescaling of the accumulators; any reference gives the same result
+        // in exact arithmetic, since l and O are scaled alike. bf16 weights (8-bit
+        // significand): m is the exact running maximum, so the largest weight is 1 and
+        // exact, and rounding touches only the smaller ones.
+        const bool move = tmax > m + M::kSlack;
+        if (__any(move)) {
+          const float m_new = move ? tmax : m;
+          const float alpha = fast_exp2(m - m_new);  // m = -inf: 0
+          l *= alpha;
+#pragma unroll
+          for (int mt = 0; mt < NM; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[mt][r] *= alpha;
+          m = m_new;
+        }
+        const float m_use = m == -INFINITY ? 0.f : m;
+        float z[16];
+        float psum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          z[r] = fast_exp2(__builtin_fmaf(sacc[r], scale_log2, -m_use));
+          psum += z[r];
+        }
+        l += psum;
 
-      // S^T = K Q^T: A = 32 keys x 16 dims from LDS, B = the wave's queries
-      f32x16 sacc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-#pragma unroll
-      for (int c = 0; c < NQ; ++c) {
-        const v8 a = __builtin_bit_cast(v8, *(const u32x4*)(ks + col * KS + 16 * c + 8 * half));
-        sacc = M::mfma(a, qv[c], sacc);
-      }
-      float z[16];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        z[r] = kt * kKeys + key_of(r, half) <= pos ? sacc[r] * scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, z[r]);
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m, tmax);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m - m_use);
-      float psum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        z[r] = fast_exp2(z[r] - m_use);
-        psum += z[r];
-      }
-      l = l * alpha + psum;
-      m = m_new;
-#pragma unroll
-      for (int mt = 0; mt < NM; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[mt][r] *= alpha;
-
-      // P^T operand of k-step kk: the lane's scores r = 8kk .. 8kk+7 (keys key_of(r, half))
-      v8 pb[2];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        u32x4 w;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          w[j] = M::bits(z[8 * kk + 2 * j]) | (M::bits(z[8 * kk + 2 * j + 1]) << 16);
-        pb[kk] = __builtin_bit_cast(v8, w);
-      }
-      // O^T += V^T P^T: A = V^T rows d = 32 mt + col over the same 8 keys per k-step
-#pragma unroll
-      for (int mt = 0; mt < NM; ++mt) {
+        // P^T operand of k-step kk: the lane's scores r = 8kk .. 8kk+7 (keys key_of(r, half))
+        v8 pb[2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           u32x4 w;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t e0 = vs[key_of(8 * kk + 2 * j, half) * KS + 32 * mt + col];
-            const uint32_t e1 = vs[key_of(8 * kk + 2 * j + 1, half) * KS + 32 * mt + col];
-            w[j] = e0 | (e1 << 16);
-          }
-          o[mt] = M::mfma(__builtin_bit_cast(v8, w), pb[kk], o[mt]);
+          for (int j = 0; j < 4; ++j) w[j] = M::pack2(z[8 * kk + 2 * j], z[8 * kk + 2 * j + 1]);
+          pb[kk] = __builtin_bit_cast(v8, w);
+        }
+        // O^T += V^T P^T: A = V^T rows d = 32 mt + col over the same 8 keys per k-step,
+        // read from the row-major value tile by the transposing LDS read
+#pragma unroll
+        for (int mt = 0; mt < NM; ++mt) {
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
+            o[mt] = M::mfma(__builtin_bit_cast(v8, vt_operand<KS>(vb, mt, kk, lane)), pb[kk],
+                            o[mt]);
         }
       }
+      if (kt + 1 < ntiles) stash(buf ^ 1);
+      __syncthreads();  // the next tile is in LDS; this one is no longer read
     }
-    __syncthreads();  // bad_sh is final for this tile
     const float lt = l + __shfl_xor(l, 32);
     float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (bad_shape || bad_sh) inv = __builtin_nanf("");
@@ -230,8 +309,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
         for (int g = 0; g < 4; ++g) {
           const int d = 32 * mt + 8 * g + 4 * half;  // registers 4g..4g+3: dims d..d+3
           uint2 w;
-          w.x = M::bits(o[mt][4 * g] * inv) | (M::bits(o[mt][4 * g + 1] * inv) << 16);
-          w.y = M::bits(o[mt][4 * g + 2] * inv) | (M::bits(o[mt][4 * g + 3] * inv) << 16);
+          w.x = M::pack2(o[mt][4 * g] * inv, o[mt][4 * g + 1] * inv);
+          w.y = M::pack2(o[mt][4 * g + 2] * inv, o[mt][4 * g + 3] * inv);
           *(uint2*)(op + d * 2) = w;
         }
     }
@@ -299,7 +378,8 @@ extern "C" int pa_prefill_attention(void* out, const void* q, const void* k_cach
                 num_kv_heads);
   if (num_heads > 65535) return fail(PA_EINVAL, "num_heads %d > 65535", num_heads);
   if (num_rows < 0 || max_q_len < 0) return fail(PA_EINVAL, "num_rows and max_q_len must be >= 0");
-  if (!std::isfinite(scale)) return fail(PA_EINVAL, "scale is not finite");
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(PA_EINVAL, "scale must be finite and > 0");
   if (num_rows == 0 || max_q_len == 0) return ok();
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !q_start)
     return fail(PA_EINVAL, "null pointer");

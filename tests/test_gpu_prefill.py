@@ -179,7 +179,10 @@ def test_rejects_unsupported(native):
 
 
 def test_scale_argument(native):
+    """Any scale > 0 (the score order is kept); 0 and negative scales are rejected."""
     ctx = [50]
     q, kc, vc, tables, L, qs = make_case(12, ctx, ctx, 2, 2, 128, 16, "f16")
     want = prefill_attention(q, kc, vc, tables, L, qs, 16, scale=0.3)
     assert_close(run_gpu(native, q, kc, vc, tables, L, qs, scale=0.3), want, "f16")
+    with pytest.raises(native.PagedKVError):
+        run_gpu(native, q, kc, vc, tables, L, qs, scale=-0.3)

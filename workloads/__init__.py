@@ -130,8 +130,62 @@ OPT13B_7x2048_FP8 = OPT13B_7x2048.scaled(
                 "block 16, 7 x 2048 tokens, pool scales 1/256")
 
 ALL = (TINY, OPT13B_7x2048, OPT13B_MIXED256, SHARING_32x8, LONG_16x32K)
+
+
+# --- Prompt-phase workloads ----------------------------------------------------
+# The prompt phase takes each text's whole prompt at once («The KV Cache and
+# PagedAttention» › "One Token at a Time"); a prompt may follow cached tokens, e.g.
+# a shared prefix whose blocks are reused (› "What Came After").
+
+@dataclasses.dataclass(frozen=True)
+class PromptWorkload:
+    name: str
+    seed: int
+    num_seqs: int
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    dtype: str
+    kv_std: float
+    q_std: float
+    prompt_lo: int           # prompt lengths ~ U{prompt_lo..prompt_hi} (equal: fixed)
+    prompt_hi: int
+    prefix_len: int = 0      # cached tokens, the same for every text, before each prompt
+    description: str = ""
+
+    def scaled(self, **kw) -> "PromptWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+OPT13B_PROMPT_7x2048 = PromptWorkload(
+    name="opt13b_prompt_7x2048_f16_b16", seed=12, num_seqs=7, num_heads=40, num_kv_heads=40,
+    head_dim=128, block_size=16, num_blocks=983, dtype="f16", kv_std=1 / math.sqrt(128),
+    q_std=1.0, prompt_lo=2048, prompt_hi=2048,
+    description="prompt phase of the OPT-13B 7 x 2048 batch: 7 fresh 2,048-token prompts, "
+                "40 heads x 128, fp16, block 16")
+OPT13B_PROMPT_MIXED64 = PromptWorkload(
+    name="opt13b_prompt_mixed64_f16_b16", seed=13, num_seqs=64, num_heads=40, num_kv_heads=40,
+    head_dim=128, block_size=16, num_blocks=8300, dtype="f16", kv_std=1 / math.sqrt(128),
+    q_std=1.0, prompt_lo=16, prompt_hi=2048,
+    description="64 fresh prompts of U{16..2048} tokens, OPT-13B shapes, fp16, block 16")
+LLAMA70B_PROMPT_8x4096 = PromptWorkload(
+    name="llama2_70b_prompt_8x4096_f16_b16", seed=14, num_seqs=8, num_heads=64, num_kv_heads=8,
+    head_dim=128, block_size=16, num_blocks=8 * 256 + 64, dtype="f16",
+    kv_std=1 / math.sqrt(128), q_std=1.0, prompt_lo=4096, prompt_hi=4096,
+    description="shared K/V heads: 64 query heads over 8 K/V heads x 128, 8 fresh "
+                "4,096-token prompts, fp16, block 16")
+OPT13B_PREFIX_32x1024 = PromptWorkload(
+    name="opt13b_prefix_32x1024p512_f16_b16", seed=15, num_seqs=32, num_heads=40,
+    num_kv_heads=40, head_dim=128, block_size=16, num_blocks=64 + 32 * 32 + 64, dtype="f16",
+    kv_std=1 / math.sqrt(128), q_std=1.0, prompt_lo=512, prompt_hi=512, prefix_len=1024,
+    description="32 prompts of 512 new tokens after one shared, cached 1,024-token prefix "
+                "(64 blocks held by all 32 texts), OPT-13B shapes, fp16, block 16")
+PROMPT = (OPT13B_PROMPT_7x2048, OPT13B_PROMPT_MIXED64, LLAMA70B_PROMPT_8x4096,
+          OPT13B_PREFIX_32x1024)
 EXTRA = (LLAMA70B_32x4096, OPT13B_7x2048_FP8)
-BY_NAME = {w.name: w for w in ALL + EXTRA}
+BY_NAME = {w.name: w for w in ALL + EXTRA + PROMPT}
 
 
 def _np_dtype_cast(x32: np.ndarray, dtype: str):
@@ -302,3 +356,129 @@ def attended_at_step0(w: Workload, d: Draws) -> List[int]:
             out.append(w.prompt_len + d.suffix_lens[src] + 1)
         return out
     return [n + 1 for n in d.prefill_lens]
+
+
+@dataclasses.dataclass
+class PromptDraws:
+    """Every random input of a prompt workload (torch tensors, CPU or device).
+
+    prefix_k / prefix_v: [prefix_len, H_kv, D], the cached tokens before every prompt;
+    prompt_k / prompt_v[s]: [n_s, H_kv, D]; q: [sum n_s, H, D], texts' rows one after another.
+    """
+    free_order: np.ndarray
+    prompt_lens: List[int]
+    prefix_k: list
+    prefix_v: list
+    prompt_k: list
+    prompt_v: list
+    q: object
+
+
+def draw_prompt(w: PromptWorkload, device: Optional[str] = None) -> PromptDraws:
+    """Inputs of a prompt workload: free-list permutation -> prompt lengths -> prefix K,
+    prefix V -> per text: prompt K, prompt V -> the packed queries."""
+    st = Stream(w.seed, device)
+    free_order = st.permutation(w.num_blocks)
+    lens = [int(x) for x in st.integers(w.prompt_lo, w.prompt_hi, w.num_seqs)]
+    Hk, D = w.num_kv_heads, w.head_dim
+    xk = st.normal((w.prefix_len, Hk, D), w.kv_std, w.dtype)
+    xv = st.normal((w.prefix_len, Hk, D), w.kv_std, w.dtype)
+    pk, pv = [], []
+    for n in lens:
+        pk.append(st.normal((n, Hk, D), w.kv_std, w.dtype))
+        pv.append(st.normal((n, Hk, D), w.kv_std, w.dtype))
+    q = st.normal((sum(lens), w.num_heads, D), w.q_std, w.dtype)
+    return PromptDraws(free_order=free_order, prompt_lens=lens, prefix_k=xk, prefix_v=xv,
+                       prompt_k=pk, prompt_v=pv, q=q)
+
+
+# --- Prefix-caching workloads -------------------------------------------------
+# Requests that begin with one of a few shared system prompts and go on with their own
+# tokens (› "What Came After": many requests begin the same way). Token ids are drawn
+# as well as keys and values, so that the block hashes of the prefix cache can be formed.
+
+@dataclasses.dataclass(frozen=True)
+class PrefixWorkload:
+    name: str
+    seed: int
+    prompt_lens: tuple       # shared system prompts
+    num_requests: int
+    user_lo: int             # each request's own tokens ~ U{user_lo..user_hi}
+    user_hi: int
+    batch: int               # requests per prompt-phase call
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    dtype: str
+    kv_std: float
+    q_std: float
+    vocab: int = 50000
+    description: str = ""
+
+    def scaled(self, **kw) -> "PrefixWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+PREFIX_CHAT = PrefixWorkload(
+    name="prefix_chat_f16_b16", seed=21, prompt_lens=(100, 64, 37), num_requests=24,
+    user_lo=5, user_hi=60, batch=6, num_heads=4, num_kv_heads=2, head_dim=64, block_size=16,
+    num_blocks=64, dtype="f16", kv_std=0.5, q_std=1.0,
+    description="24 requests after one of 3 shared system prompts (100, 64, 37 tokens), "
+                "5-60 own tokens each, prompt phase in batches of 6; a 64-block pool, so "
+                "cached blocks are also evicted")
+
+
+@dataclasses.dataclass
+class PrefixDraws:
+    """sys_tokens[i] (int64 numpy), sys_k / sys_v[i]: [len_i, H_kv, D]; per request r:
+    req_sys[r] (its system prompt), user_tokens[r], user_k / user_v[r]: [u_r, H_kv, D],
+    q[r]: [len_i + u_r, H, D] (a query for every position of the request)."""
+    free_order: np.ndarray
+    sys_tokens: list
+    sys_k: list
+    sys_v: list
+    req_sys: List[int]
+    user_tokens: list
+    user_k: list
+    user_v: list
+    q: list
+
+
+def draw_prefix(w: PrefixWorkload, device: Optional[str] = None) -> PrefixDraws:
+    """free-list permutation -> per system prompt: tokens, K, V -> per request: its
+    system prompt, own length, tokens, K, V, queries."""
+    st = Stream(w.seed, device)
+    free_order = st.permutation(w.num_blocks)
+    Hk, D = w.num_kv_heads, w.head_dim
+    sys_t, sys_k, sys_v = [], [], []
+    for n in w.prompt_lens:
+        sys_t.append(st.integers(0, w.vocab - 1, n))
+        sys_k.append(st.normal((n, Hk, D), w.kv_std, w.dtype))
+        sys_v.append(st.normal((n, Hk, D), w.kv_std, w.dtype))
+    req_sys, ut, uk, uv, qs = [], [], [], [], []
+    for _ in range(w.num_requests):
+        i = int(st.integers(0, len(w.prompt_lens) - 1, 1)[0])
+        u = int(st.integers(w.user_lo, w.user_hi, 1)[0])
+        req_sys.append(i)
+        ut.append(st.integers(0, w.vocab - 1, u))
+        uk.append(st.normal((u, Hk, D), w.kv_std, w.dtype))
+        uv.append(st.normal((u, Hk, D), w.kv_std, w.dtype))
+        qs.append(st.normal((w.prompt_lens[i] + u, w.num_heads, D), w.q_std, w.dtype))
+    return PrefixDraws(free_order=free_order, sys_tokens=sys_t, sys_k=sys_k, sys_v=sys_v,
+                       req_sys=req_sys, user_tokens=ut, user_k=uk, user_v=uv, q=qs)
+
+
+def prefix_schedule(w: PrefixWorkload) -> list:
+    """Batches of `batch` consecutive requests; after a batch's prompt phase its blocks
+    are registered, then the requests of the batch before it finish (are freed)."""
+    ops = []
+    batches = [list(range(i, min(i + w.batch, w.num_requests)))
+               for i in range(0, w.num_requests, w.batch)]
+    for b, reqs in enumerate(batches):
+        ops.append(("batch", reqs))
+        if b > 0:
+            ops.append(("finish", batches[b - 1]))
+    ops.append(("finish", batches[-1]))
+    return ops
