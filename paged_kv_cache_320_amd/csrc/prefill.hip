@@ -179,53 +179,57 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // a tile are read one tile earlier still, so no load waits on a table lookup.
     u32x4 kx[NC], vx[NC];
     int tb[NC];
+    // Every lane loads, whether its key position is needed or not: positions past the
+    // last needed one read that one again (a valid place) and store zeros, so no load
+    // sits under a branch.
+    const int kv_last = max(kv_lim - 1, 0);
     auto load_table = [&](int kt) {
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
         const int kp = kt * kKeys + (tid + j * kThreads) / CPR;
-        tb[j] = kp < kv_lim ? trow[kp / B] : 0;
+        tb[j] = trow[min(kp, kv_last) / B];
       }
     };
     auto fetch = [&](int kt) {
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
         const int c = tid + j * kThreads;
-        const int key = c / CPR, pc = c % CPR;
-        const int kp = kt * kKeys + key;
-        kx[j] = u32x4{0u, 0u, 0u, 0u};
-        vx[j] = u32x4{0u, 0u, 0u, 0u};
-        if (kp < kv_lim) {
-          int blk = tb[j];
-          if ((unsigned)blk >= (unsigned)num_blocks) {
-            bad_sh = 1;  // read block 0 instead; the text's output is poisoned
-            blk = 0;
-          }
-          const int64_t off = (((int64_t)blk * Hkv + kvh) * B + kp % B) * (D * 2) + pc * 16;
-          kx[j] = *(const u32x4*)(kc + off);
-          vx[j] = *(const u32x4*)(vc + off);
+        const int kp = kt * kKeys + c / CPR;
+        int blk = tb[j];
+        if ((unsigned)blk >= (unsigned)num_blocks) {
+          if (kp < kv_lim) bad_sh = 1;  // read block 0 instead; the text's output is poisoned
+          blk = 0;
         }
+        const int64_t off =
+            (((int64_t)blk * Hkv + kvh) * B + min(kp, kv_last) % B) * (D * 2) + (c % CPR) * 16;
+        kx[j] = *(const u32x4*)(kc + off);
+        vx[j] = *(const u32x4*)(vc + off);
       }
     };
-    auto stash = [&](int buf) {
+    auto stash = [&](int buf, int kt) {
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
         const int c = tid + j * kThreads;
         const int key = c / CPR, pc = c % CPR;
-        *(u32x4*)(ks[buf] + key * KS + pc * 8) = kx[j];
-        *(u32x4*)(vs[buf] + key * KS + pc * 8) = vx[j];
+        const bool use = kt * kKeys + key < kv_lim;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        *(u32x4*)(ks[buf] + key * KS + pc * 8) = use ? kx[j] : zero;
+        *(u32x4*)(vs[buf] + key * KS + pc * 8) = use ? vx[j] : zero;
       }
     };
-    if (ntiles > 0) {
-      load_table(0);
-      fetch(0);
-      stash(0);
-      if (ntiles > 1) load_table(1);
-    }
+    // Loads, table reads and LDS stores run unconditionally (their addresses are guarded
+    // per lane: past the last needed position nothing is read and zeros are stored), so
+    // the compiler's wait counters never see a path with an unfinished load and the
+    // matrix products never wait for the next tile's loads.
+    load_table(0);
+    fetch(0);
+    stash(0, 0);
+    load_table(1);
     __syncthreads();
     for (int kt = 0; kt < ntiles; ++kt) {
       const int buf = kt & 1;
-      if (kt + 1 < ntiles) fetch(kt + 1);
-      if (kt + 2 < ntiles) load_table(kt + 2);
+      fetch(kt + 1);
+      load_table(kt + 2);
       if (wave_on && kt * kKeys <= wave_last) {  // causal skip (wave-uniform)
         const uint16_t* kb = ks[buf];
         const uint16_t* vb = vs[buf];
@@ -295,7 +299,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                             o[mt]);
         }
       }
-      if (kt + 1 < ntiles) stash(buf ^ 1);
+      stash(buf ^ 1, kt + 1);
       __syncthreads();  // the next tile is in LDS; this one is no longer read
     }
     const float lt = l + __shfl_xor(l, 32);
