@@ -36,7 +36,8 @@ namespace prefill_impl {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQRows = 32 * kWaves;  // queries per workgroup
-constexpr int kKeys = 32;            // key positions per tile
+constexpr int kKeys = 64;            // key positions per tile (two 32-key MFMA subtiles)
+constexpr int kSub = kKeys / 32;     // 32-key subtiles per tile
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -233,25 +234,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       if (wave_on && kt * kKeys <= wave_last) {  // causal skip (wave-uniform)
         const uint16_t* kb = ks[buf];
         const uint16_t* vb = vs[buf];
-        // S^T = K Q^T: A = 32 keys x 16 dims from LDS, B = the wave's queries
-        f32x16 sacc;
+        // S^T = K Q^T per 32-key subtile: A = 32 keys x 16 dims from LDS, B = the wave's
+        // queries; the subtiles' products are independent, so they overlap
+        f32x16 sacc[kSub];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+        for (int st = 0; st < kSub; ++st) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[st][r] = 0.f;
+        }
 #pragma unroll
         for (int c = 0; c < NQ; ++c) {
-          const v8 a = __builtin_bit_cast(v8, *(const u32x4*)(kb + col * KS + 16 * c + 8 * half));
-          sacc = M::mfma(a, qv[c], sacc);
+#pragma unroll
+          for (int st = 0; st < kSub; ++st) {
+            const v8 a = __builtin_bit_cast(
+                v8, *(const u32x4*)(kb + (32 * st + col) * KS + 16 * c + 8 * half));
+            sacc[st] = M::mfma(a, qv[c], sacc[st]);
+          }
         }
         // raw scores (scale_log2 > 0 keeps their order); on a diagonal tile, keys after
         // a query's own position get no weight
         if (kt * kKeys + kKeys - 1 > wave_first) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (kt * kKeys + key_of(r, half) > pos) sacc[r] = -INFINITY;
-        }
-        float tmax = sacc[0];
+          for (int st = 0; st < kSub; ++st)
 #pragma unroll
-        for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, sacc[r]);
+            for (int r = 0; r < 16; ++r)
+              if (kt * kKeys + 32 * st + key_of(r, half) > pos) sacc[st][r] = -INFINITY;
+        }
+        float tmax = sacc[0][0];
+#pragma unroll
+        for (int st = 0; st < kSub; ++st)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[st][r]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * scale_log2;
         // fp16 weights: the reference maximum m moves only when a score exceeds it by
         // more than 2^8 (or on the first key), so weights stay below 256 and most tiles
@@ -271,33 +284,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
           m = m_new;
         }
         const float m_use = m == -INFINITY ? 0.f : m;
-        float z[16];
         float psum = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          z[r] = fast_exp2(__builtin_fmaf(sacc[r], scale_log2, -m_use));
-          psum += z[r];
+        for (int st = 0; st < kSub; ++st) {
+          // P^T operand of k-step kk: the lane's scores r = 8kk .. 8kk+7 (keys
+          // 32 st + key_of(r, half))
+          v8 pb[2];
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            float z[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              z[j] = fast_exp2(__builtin_fmaf(sacc[st][8 * kk + j], scale_log2, -m_use));
+              psum += z[j];
+            }
+            u32x4 w;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) w[j] = M::pack2(z[2 * j], z[2 * j + 1]);
+            pb[kk] = __builtin_bit_cast(v8, w);
+          }
+          // O^T += V^T P^T: A = V^T rows d = 32 mt + col over the same 8 keys per k-step,
+          // read from the row-major value tile by the transposing LDS read
+#pragma unroll
+          for (int mt = 0; mt < NM; ++mt) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+              o[mt] = M::mfma(
+                  __builtin_bit_cast(v8, vt_operand<KS>(vb + 32 * st * KS, mt, kk, lane)),
+                  pb[kk], o[mt]);
+          }
         }
         l += psum;
-
-        // P^T operand of k-step kk: the lane's scores r = 8kk .. 8kk+7 (keys key_of(r, half))
-        v8 pb[2];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          u32x4 w;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) w[j] = M::pack2(z[8 * kk + 2 * j], z[8 * kk + 2 * j + 1]);
-          pb[kk] = __builtin_bit_cast(v8, w);
-        }
-        // O^T += V^T P^T: A = V^T rows d = 32 mt + col over the same 8 keys per k-step,
-        // read from the row-major value tile by the transposing LDS read
-#pragma unroll
-        for (int mt = 0; mt < NM; ++mt) {
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk)
-            o[mt] = M::mfma(__builtin_bit_cast(v8, vt_operand<KS>(vb, mt, kk, lane)), pb[kk],
-                            o[mt]);
-        }
       }
       stash(buf ^ 1, kt + 1);
       __syncthreads();  // the next tile is in LDS; this one is no longer read
