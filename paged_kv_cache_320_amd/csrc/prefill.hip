@@ -110,22 +110,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     char* __restrict__ out, const char* __restrict__ q, const char* __restrict__ kc,
     const char* __restrict__ vc, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ ctx, const int32_t* __restrict__ q_start, int T, int H, int Hkv,
-    int maxb, int num_blocks, int qtiles, float scale_log2) {
+    int maxb, int num_blocks, int qtiles, int nwork, float scale_log2) {
   using M = Mma<DT>;
   typedef typename M::v8 v8;
-  constexpr int KS = D + 8;                      // 16-bit elements per LDS row
+  // 16-bit elements per LDS row: a key row shifts 4 banks from the one before, so the 16
+  // rows of a 16-lane key-operand read hit 64 distinct banks; a value row shifts 8 banks,
+  // so the 4 rows x 32 bytes of a 16-lane transposing read hit 32 distinct banks
+  constexpr int KS = D + 8;
+  constexpr int VS = D + 16;
   constexpr int CPR = D / 8;                     // 16-byte pieces per key row
   constexpr int NC = kKeys * CPR / kThreads;     // pieces per thread and tile, each of K and V
   constexpr int NQ = D / 16;                     // MFMA k-steps of S^T
   constexpr int NM = D / 32;                     // 32-row tiles of O^T
   static_assert(NC * kThreads == kKeys * CPR, "tile copy must cover the tile exactly");
   __shared__ __align__(16) uint16_t ks[2][kKeys * KS];  // two buffers: compute one tile
-  __shared__ __align__(16) uint16_t vs[2][kKeys * KS];  // while the next is stored
+  __shared__ __align__(16) uint16_t vs[2][kKeys * VS];  // while the next is stored
 
   __shared__ int bad_sh;
 
-  const int s = blockIdx.x / qtiles;
-  const int h = blockIdx.y;
+  // Work item w = (text, head, query tile), numbered so that one (text, head)'s query
+  // tiles are consecutive. Workgroups are dealt to the 8 XCDs in turn (workgroup b to
+  // XCD b % 8), so w takes b's XCD-major rank: each XCD walks its own contiguous range of
+  // work items and a head's keys and values are read by workgroups sharing one L2.
+  const int per = (nwork + 7) >> 3;
+  const int w = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+  if (w >= nwork) return;
+  const int qt0 = qtiles - 1 - w % qtiles;  // the longest query tiles of a text first
+  const int s = w / qtiles / H;
+  const int h = w / qtiles % H;
   const int kvh = h / (H / Hkv);
   const int r0 = q_start[s], r1 = q_start[s + 1];
   const int n = r1 - r0;
@@ -143,7 +155,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   if (tid == 0) bad_sh = 0;
   __syncthreads();  // cleared before any tile load can set it
 
-  for (int qt = qtiles - 1 - (int)(blockIdx.x % qtiles); qt * kQRows < n; qt += qtiles) {
+  for (int qt = qt0; qt * kQRows < n; qt += qtiles) {
     const int row_lo = qt * kQRows;
     const int row_hi = min(n, row_lo + kQRows);
     const int kv_end = first + row_hi;           // positions [0, kv_end) are needed
@@ -215,7 +227,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         const bool use = kt * kKeys + key < kv_lim;
         const u32x4 zero = {0u, 0u, 0u, 0u};
         *(u32x4*)(ks[buf] + key * KS + pc * 8) = use ? kx[j] : zero;
-        *(u32x4*)(vs[buf] + key * KS + pc * 8) = use ? vx[j] : zero;
+        *(u32x4*)(vs[buf] + key * VS + pc * 8) = use ? vx[j] : zero;
       }
     };
     // Loads, table reads and LDS stores run unconditionally (their addresses are guarded
@@ -310,7 +322,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
               o[mt] = M::mfma(
-                  __builtin_bit_cast(v8, vt_operand<KS>(vb + 32 * st * KS, mt, kk, lane)),
+                  __builtin_bit_cast(v8, vt_operand<VS>(vb + 32 * st * VS, mt, kk, lane)),
                   pb[kk], o[mt]);
           }
         }
@@ -342,17 +354,17 @@ struct Args {
   char* out;
   const char *q, *kc, *vc;
   const int32_t *tables, *ctx, *q_start;
-  int S, T, H, Hkv, maxb, num_blocks, qtiles;
+  int S, T, H, Hkv, maxb, num_blocks, qtiles, nwork;
   float scale_log2;
   hipStream_t st;
 };
 
 template <int DT, int D, int B>
 void launch(const Args& a) {
-  const dim3 grid((unsigned)(a.S * a.qtiles), (unsigned)a.H), block(kThreads);
+  const dim3 grid((unsigned)(8 * ((a.nwork + 7) / 8))), block(kThreads);
   hipLaunchKernelGGL((prefill_kernel<DT, D, B>), grid, block, 0, a.st, a.out, a.q, a.kc, a.vc,
                      a.tables, a.ctx, a.q_start, a.T, a.H, a.Hkv, a.maxb, a.num_blocks,
-                     a.qtiles, a.scale_log2);
+                     a.qtiles, a.nwork, a.scale_log2);
 }
 
 template <int DT, int D>
@@ -410,11 +422,13 @@ extern "C" int pa_prefill_attention(void* out, const void* q, const void* k_cach
       ((uintptr_t)q_start & 3u))
     return fail(PA_EINVAL, "tables, context_lens and q_start must be 4-byte aligned");
   const int64_t qtiles = ((int64_t)max_q_len + kQRows - 1) / kQRows;
-  if ((int64_t)num_seqs * qtiles > 0x7fffffffLL)
-    return fail(PA_EINVAL, "num_seqs * ceil(max_q_len / %d) exceeds the grid", kQRows);
+  if ((int64_t)num_seqs * num_heads * qtiles > 0x7ffffff0LL)
+    return fail(PA_EINVAL, "num_seqs * num_heads * ceil(max_q_len / %d) exceeds the grid",
+                kQRows);
   const Args a{(char*)out, (const char*)q, (const char*)k_cache, (const char*)v_cache,
                block_tables, context_lens, q_start, num_seqs, num_rows, num_heads,
                num_kv_heads, max_blocks_per_seq, num_blocks, (int)qtiles,
+               (int)(num_seqs * num_heads * qtiles),
                scale * 1.4426950408889634f, (hipStream_t)stream};
   if (dtype == PA_F16) launch_d<PA_F16>(head_dim, block_size, a);
   else launch_d<PA_BF16>(head_dim, block_size, a);
