@@ -390,13 +390,22 @@ __device__ __forceinline__ int64_t block_sum(int64_t x, int64_t* sh) {
   return t;
 }
 
-template <int KT, int QT, int D, int B, int GS>
-__global__ __launch_bounds__(kThreads) void decode_partition(
-    char* __restrict__ out, const char* __restrict__ q, const char* __restrict__ kc,
-    const char* __restrict__ vc, const int32_t* __restrict__ tables,
-    const int32_t* __restrict__ ctx, int S, int H, int Hkv, int maxb, int num_blocks, int W,
-    int seg_fixed, float scale_log2, float v_scale, int64_t* __restrict__ hdr,
-    int64_t* __restrict__ excl_out, float* __restrict__ partials) {
+// This wave's segment of the unit numbering: every workgroup sums the texts' units and
+// scans them to find where its waves' segments start. Returns false when the wave has
+// no units; otherwise sets the segment [seg_lo, seg_hi), the context and the cursor at
+// the segment's first unit (all wave-uniform).
+struct Segment {
+  int w;
+  int64_t seg_lo, seg_hi;
+  int n;
+};
+
+template <int B, int GS>
+__device__ __forceinline__ bool start_segment(const int32_t* __restrict__ ctx, int S, int H,
+                                              int Hkv, int maxb, int num_blocks, int W,
+                                              int seg_fixed, int64_t* __restrict__ hdr,
+                                              int64_t* __restrict__ excl_out, Segment& sg,
+                                              Ctx& x, Cursor& cur) {
   __shared__ int64_t sh_red[kWavesPerGroup];
   __shared__ int sh_seq[kWavesPerGroup];
   __shared__ int64_t sh_off[kWavesPerGroup];
@@ -458,22 +467,39 @@ __global__ __launch_bounds__(kThreads) void decode_partition(
   }
   __syncthreads();
 
-  const int w = blockIdx.x * kWavesPerGroup + wave;
-  const int64_t seg_lo = (int64_t)w * seg;
-  if (w >= W || seg_lo >= total) return;
-  const int64_t seg_hi = seg_lo + seg < total ? seg_lo + seg : total;
-  const int n = (int)(seg_hi - seg_lo);
+  sg.w = blockIdx.x * kWavesPerGroup + wave;
+  sg.seg_lo = (int64_t)sg.w * seg;
+  if (sg.w >= W || sg.seg_lo >= total) return false;
+  sg.seg_hi = sg.seg_lo + seg < total ? sg.seg_lo + seg : total;
+  sg.n = (int)(sg.seg_hi - sg.seg_lo);
 
-  const Ctx x{S, H, Hkv, Gq, Gq / GS, R, maxb, num_blocks, capacity, ctx};
-  Cursor cur;
+  x = Ctx{S, H, Hkv, Gq, Gq / GS, R, maxb, num_blocks, capacity, ctx};
   // values read from LDS are the same in every lane: keep them in scalar registers
   cur.excl = uniform64(sh_excl[wave]);
   set_text(cur, x, __builtin_amdgcn_readfirstlane(sh_seq[wave]));
-  {
-    const int64_t off = uniform64(sh_off[wave]);
-    cur.r = (int)(off / cur.U);
-    cur.u = (int)(off - (int64_t)cur.r * cur.U);
-  }
+  const int64_t off = uniform64(sh_off[wave]);
+  cur.r = (int)(off / cur.U);
+  cur.u = (int)(off - (int64_t)cur.r * cur.U);
+  return true;
+}
+
+template <int KT, int QT, int D, int B, int GS>
+__global__ __launch_bounds__(kThreads) void decode_partition(
+    char* __restrict__ out, const char* __restrict__ q, const char* __restrict__ kc,
+    const char* __restrict__ vc, const int32_t* __restrict__ tables,
+    const int32_t* __restrict__ ctx, int S, int H, int Hkv, int maxb, int num_blocks, int W,
+    int seg_fixed, float scale_log2, float v_scale, int64_t* __restrict__ hdr,
+    int64_t* __restrict__ excl_out, float* __restrict__ partials) {
+  const int lane = threadIdx.x & 63;
+  Segment sg;
+  Ctx x;
+  Cursor cur;
+  if (!start_segment<B, GS>(ctx, S, H, Hkv, maxb, num_blocks, W, seg_fixed, hdr, excl_out, sg,
+                            x, cur))
+    return;
+  const int w = sg.w;
+  const int64_t seg_lo = sg.seg_lo, seg_hi = sg.seg_hi;
+  const int n = sg.n;
   Cursor ld = cur;
   const float sl = scale_log2;
 
@@ -604,6 +630,295 @@ __global__ __launch_bounds__(kThreads) void decode_merge(
                        lane);
 }
 
+// ---- shared key/value heads on the matrix cores --------------------------------
+//
+// With 8 query heads per key/value head, every key and value row feeds 8 dot products
+// and 8 weighted sums: about 8 flop per byte, which the vector ALUs cannot sustain at
+// HBM speed. Here a wave's 8 heads are the columns of 16x16 MFMA tiles (8 of 16 used):
+//   S^T (16 tokens x heads) = K (16 tokens x 32 dims) . Q^T     v_mfma_f32_16x16x32
+//   O^T (16 dims x heads)  += V^T (16 dims x 16 tokens) . P^T  v_mfma_f32_16x16x16
+// Lane l (col = l % 16, grp = l / 16) loads 16 bytes of token col's key and value rows at
+// dims 8 grp + 32 c, which is the K operand's layout as loaded; its S^T results are head
+// col's scores for tokens 4 grp .. 4 grp + 3, which is the P^T operand's layout. The
+// values go through the wave's own LDS rows once, for the transposing read that builds
+// the V^T operand. Segmentation, partials and the merge are those of decode_partition.
+
+template <int QT>
+struct Mma16;
+
+template <>
+struct Mma16<PA_F16> {
+  typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 v4 __attribute__((ext_vector_type(4)));
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ f4 qk(v8 a, v8 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f4 pv(v4 a, v4 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float x, float y) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){x, y}, h2));
+  }
+};
+
+template <>
+struct Mma16<PA_BF16> {
+  typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+  typedef short v4 __attribute__((ext_vector_type(4)));
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ f4 qk(v8 a, v8 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f4 pv(v4 a, v4 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float x, float y) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){x, y}, b2));
+  }
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+template <int D>
+struct MmaBuf {
+  uint4 k[D / 32];
+  uint4 v[D / 32];
+  bool bad;
+};
+
+template <int D>
+struct MmaState {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  f4 o[D / 16];  // O^T tile mt: dims 16 mt + 4 grp + r, head col
+  float m, l;    // head col's running maximum; sum over this lane's tokens
+  __device__ __forceinline__ void reset() {
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) o[mt] = f4{0.f, 0.f, 0.f, 0.f};
+  }
+};
+
+template <int QT, int D, int B>
+__device__ __forceinline__ void load_chunk_mma(MmaBuf<D>& b, const Cursor& c, const Ctx& x,
+                                               const char* __restrict__ kc,
+                                               const char* __restrict__ vc,
+                                               const int32_t* __restrict__ tables, int lane) {
+  constexpr int kRowBytes = D * 2;
+  constexpr int64_t kTileBytes = (int64_t)B * kRowBytes;
+  const int col = lane & 15, grp = lane >> 4;
+  const int kvh = kv_head_of<8>(c.r, x);
+  const int last = c.L > 0 ? c.L - 1 : 0;
+  const int32_t* trow = tables + (int64_t)c.s * x.maxb;
+  const int t = c.u * kChunk + col;
+  const int tc = t < last ? t : last;
+  int blk;
+  if constexpr (B >= kChunk) {
+    const int t0 = min(c.u * kChunk, last);  // the chunk lies in one block
+    blk = trow[t0 / B];
+  } else {
+    blk = trow[tc / B];
+  }
+  const bool bad = (unsigned)blk >= (unsigned)x.num_blocks;
+  b.bad = c.over || bad;
+  if (bad) blk = 0;  // read block 0 instead; the result is poisoned
+  const int64_t row = ((int64_t)blk * x.Hkv + kvh) * kTileBytes + (int64_t)(tc % B) * kRowBytes;
+#pragma unroll
+  for (int cc = 0; cc < D / 32; ++cc) {
+    b.k[cc] = load_stream(kc + row + (8 * grp + 32 * cc) * 2);
+    b.v[cc] = load_stream(vc + row + (8 * grp + 32 * cc) * 2);
+  }
+}
+
+template <int QT, int D>
+__device__ __forceinline__ void compute_chunk_mma(const MmaBuf<D>& b, const Cursor& c,
+                                                  MmaState<D>& st,
+                                                  const typename Mma16<QT>::v8* qv,
+                                                  uint16_t* __restrict__ vrow, float scale_log2,
+                                                  int lane) {
+  using M = Mma16<QT>;
+  typedef typename M::v8 v8;
+  typedef typename M::v4 v4;
+  typedef typename M::f4 f4;
+  constexpr int VS = D + 16;  // LDS row: 8-bank shift per row for the transposing read
+  if (c.L == 0) return;  // nothing attended: the run's result is zeros
+  const int col = lane & 15, grp = lane >> 4;
+  // values into this wave's LDS rows (token col), read back transposed below
+#pragma unroll
+  for (int cc = 0; cc < D / 32; ++cc)
+    *reinterpret_cast<uint4*>(vrow + col * VS + 8 * grp + 32 * cc) = b.v[cc];
+  f4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int cc = 0; cc < D / 32; ++cc) s = M::qk(__builtin_bit_cast(v8, b.k[cc]), qv[cc], s);
+  float z[4];
+  float cm = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = c.u * kChunk + 4 * grp + r;
+    z[r] = t < c.L ? s[r] * scale_log2 : -INFINITY;
+    cm = fmaxf(cm, z[r]);
+  }
+  cm = fmaxf(cm, __shfl_xor(cm, 16));
+  cm = fmaxf(cm, __shfl_xor(cm, 32));
+  const float mn = fmaxf(st.m, cm);
+  if (__any(mn > st.m)) {
+    const float mu = mn == -INFINITY ? 0.f : mn;
+    const float alpha = fast_exp2(st.m - mu);  // m = -inf: 0
+    st.l *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) st.o[mt] *= alpha;
+    st.m = mn;
+  }
+  const float mu = st.m == -INFINITY ? 0.f : st.m;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    z[r] = fast_exp2(z[r] - mu);
+    st.l += z[r];
+  }
+  const uint2 pw = make_uint2(M::pack2(z[0], z[1]), M::pack2(z[2], z[3]));
+  const v4 pb = __builtin_bit_cast(v4, pw);
+  // V^T operand of dims 16 mt + col: lane j of a 16-lane group addresses token
+  // 4 grp + j / 4 at dims 16 mt + 4 (j % 4); the transposing read hands lane i the
+  // 4 tokens at dim 16 mt + i
+  const uint16_t* vsrc = vrow + (4 * grp + (col >> 2)) * VS + 4 * (col & 3);
+#pragma unroll
+  for (int mt = 0; mt < D / 16; ++mt) {
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vsrc + 16 * mt));
+    st.o[mt] = M::pv(__builtin_bit_cast(v4, a), pb, st.o[mt]);
+  }
+  if (b.bad) {
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) st.o[mt] = f4{1.f, 1.f, 1.f, 1.f} * __builtin_nanf("");
+  }
+}
+
+template <int QT, int D>
+__device__ __forceinline__ void flush_run_mma(MmaState<D>& st, const Cursor& c, const Ctx& x,
+                                              int64_t seg_lo, int64_t seg_hi, int w,
+                                              char* __restrict__ out, float* __restrict__ partials,
+                                              float v_scale, int lane) {
+  constexpr int GS = 8;
+  const int col = lane & 15, grp = lane >> 4;
+  float l = st.l;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  const int64_t run_lo = c.excl + (int64_t)c.r * c.U;
+  const int64_t run_hi = run_lo + c.U;
+  const int h0 = first_head_of<GS>(c.r, x);
+  if (col < GS) {
+    if (run_lo >= seg_lo && run_hi <= seg_hi) {
+      // the whole run is in this segment: finish it here
+      const float inv = l > 0.f ? v_scale / l : 0.f;
+      char* dst = out + ((int64_t)c.s * x.H + h0 + col) * D * elt_size<QT>();
+#pragma unroll
+      for (int mt = 0; mt < D / 16; ++mt) {
+        float o[4];
+        // 0 * acc: zeros when nothing was attended, NaN for a poisoned run
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = l > 0.f ? st.o[mt][r] * inv : 0.f * st.o[mt][r];
+        store_out<QT, 4>(dst + (16 * mt + 4 * grp) * elt_size<QT>(), o);
+      }
+    } else {
+      const int slot = run_lo <= seg_lo ? 0 : 1;
+      float* p = partials + partial_index<D, GS>(w, slot, col);
+      if (grp == 0) {
+        p[0] = st.m;
+        p[1] = l;
+      }
+#pragma unroll
+      for (int mt = 0; mt < D / 16; ++mt)
+        *reinterpret_cast<float4*>(p + 4 + 16 * mt + 4 * grp) =
+            make_float4(st.o[mt][0], st.o[mt][1], st.o[mt][2], st.o[mt][3]);
+    }
+  }
+  st.reset();
+}
+
+template <int QT, int D, int B>
+__global__ __launch_bounds__(kThreads) void decode_partition_mma(
+    char* __restrict__ out, const char* __restrict__ q, const char* __restrict__ kc,
+    const char* __restrict__ vc, const int32_t* __restrict__ tables,
+    const int32_t* __restrict__ ctx, int S, int H, int Hkv, int maxb, int num_blocks, int W,
+    int seg_fixed, float scale_log2, float v_scale, int64_t* __restrict__ hdr,
+    int64_t* __restrict__ excl_out, float* __restrict__ partials) {
+  constexpr int GS = 8;
+  constexpr int VS = D + 16;
+  using M = Mma16<QT>;
+  typedef typename M::v8 v8;
+  __shared__ __align__(16) uint16_t vlds[kWavesPerGroup][kChunk * VS];
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  Segment sg;
+  Ctx x;
+  Cursor cur;
+  if (!start_segment<B, GS>(ctx, S, H, Hkv, maxb, num_blocks, W, seg_fixed, hdr, excl_out, sg,
+                            x, cur))
+    return;
+  const int w = sg.w;
+  const int64_t seg_lo = sg.seg_lo, seg_hi = sg.seg_hi;
+  const int n = sg.n;
+  uint16_t* vrow = vlds[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
+
+  // Q^T operand of the run's 8 heads: lane holds q[h0 + col][8 grp + 32 c .. +7]; the
+  // unused columns 8..15 are zero
+  v8 qv[D / 32];
+  int q_run = -1, q_text = -1;
+  auto load_q = [&](const Cursor& c) {
+    if (c.r == q_run && c.s == q_text) return;
+    q_run = c.r;
+    q_text = c.s;
+    const char* qrow = q + ((int64_t)c.s * x.H + first_head_of<GS>(c.r, x) + (col & 7)) * D * 2;
+#pragma unroll
+    for (int cc = 0; cc < D / 32; ++cc) {
+      uint4 v = *reinterpret_cast<const uint4*>(qrow + (8 * grp + 32 * cc) * 2);
+      if (col >= GS) v = make_uint4(0u, 0u, 0u, 0u);
+      qv[cc] = __builtin_bit_cast(v8, v);
+    }
+  };
+
+  Cursor ld = cur;
+  MmaState<D> st;
+  st.reset();
+  MmaBuf<D> A, Bb;
+  load_chunk_mma<QT, D, B>(A, ld, x, kc, vc, tables, lane);
+  advance(ld, x);
+
+  auto step = [&](const MmaBuf<D>& b, int i) {
+    load_q(cur);
+    compute_chunk_mma<QT, D>(b, cur, st, qv, vrow, scale_log2, lane);
+    // last chunk of the run, or of the segment
+    if (cur.u == cur.U - 1 || i == n - 1)
+      flush_run_mma<QT, D>(st, cur, x, seg_lo, seg_hi, w, out, partials, v_scale, lane);
+    advance(cur, x);
+  };
+
+  // steady state: both loads unconditional, so the next chunk's loads stay in flight
+  // while the current one is computed
+  int i = 0;
+  while (i + 2 < n) {
+    load_chunk_mma<QT, D, B>(Bb, ld, x, kc, vc, tables, lane);
+    advance(ld, x);
+    step(A, i);
+    load_chunk_mma<QT, D, B>(A, ld, x, kc, vc, tables, lane);
+    advance(ld, x);
+    step(Bb, i + 1);
+    i += 2;
+  }
+  if (i + 1 < n) {
+    load_chunk_mma<QT, D, B>(Bb, ld, x, kc, vc, tables, lane);
+    step(A, i);
+    step(Bb, i + 1);
+  } else {
+    step(A, i);
+  }
+}
+
 // ---- launch ------------------------------------------------------------------
 
 // Workspace: header (total units, segment length), int64 unit offset of each text [S],
@@ -635,9 +950,14 @@ void launch(const Launch& a) {
   int64_t* excl = reinterpret_cast<int64_t*>(a.ws + a.lay.excl_off);
   float* part = reinterpret_cast<float*>(a.ws + a.lay.part_off);
   const int groups = (a.W + kWavesPerGroup - 1) / kWavesPerGroup;
-  hipLaunchKernelGGL((decode_partition<KT, QT, D, B, GS>), dim3(groups), dim3(kThreads), 0, a.st,
-                     a.out, a.q, a.kc, a.vc, a.tables, a.ctx, a.S, a.H, a.Hkv, a.maxb, a.nb, a.W,
-                     a.seg_fixed, a.sl, a.v_scale, hdr, excl, part);
+  if constexpr (GS == 8 && KT == QT && (KT == PA_F16 || KT == PA_BF16))
+    hipLaunchKernelGGL((decode_partition_mma<QT, D, B>), dim3(groups), dim3(kThreads), 0, a.st,
+                       a.out, a.q, a.kc, a.vc, a.tables, a.ctx, a.S, a.H, a.Hkv, a.maxb, a.nb,
+                       a.W, a.seg_fixed, a.sl, a.v_scale, hdr, excl, part);
+  else
+    hipLaunchKernelGGL((decode_partition<KT, QT, D, B, GS>), dim3(groups), dim3(kThreads), 0,
+                       a.st, a.out, a.q, a.kc, a.vc, a.tables, a.ctx, a.S, a.H, a.Hkv, a.maxb,
+                       a.nb, a.W, a.seg_fixed, a.sl, a.v_scale, hdr, excl, part);
   const int64_t pairs = (int64_t)a.S * a.H;
   const int mgroups = (int)((pairs + kWavesPerGroup - 1) / kWavesPerGroup);
   hipLaunchKernelGGL((decode_merge<QT, D, GS>), dim3(mgroups), dim3(kThreads), 0, a.st, a.out,

@@ -111,6 +111,45 @@ def test_shared_kv_heads_all_formats(native, dtype, D, B, G):
         assert_close(got, want, dtype, f"T={T}")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("D,B", [(64, 4), (64, 16), (128, 8), (128, 16), (128, 32)])
+@pytest.mark.parametrize("G", [8, 16])
+def test_eight_heads_per_kv_head_on_matrix_cores(native, dtype, D, B, G):
+    """8 query heads per wave on MFMA (16-bit formats): every block size, ragged chunks,
+    runs split over segments and whole runs in one segment."""
+    lens = [1, 15, 16, 17, 129, 300, 1025]
+    Hkv = 2
+    say(f"gqa mfma dtype={dtype} D={D} B={B} G={G}")
+    q, kc, vc, tables, L = make_case(G + D + B, lens, G * Hkv, Hkv, D, B, dtype,
+                                     kv_std=1.0 / math.sqrt(D))
+    want = decode_attention(q, kc, vc, tables, L, B)
+    for T in (0, 16, 48, 2048):
+        got = run_gpu(native, q, kc, vc, tables, L, partition_tokens=T)
+        assert_close(got, want, dtype, f"T={T}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_eight_heads_sharp_and_degenerate(native, dtype):
+    """MFMA path: peaked softmax, one-token texts (exact), empty texts (zeros) and a bad
+    table entry (only its text is NaN)."""
+    lens = [33, 1, 0, 250, 777]
+    q, kc, vc, tables, L = make_case(77, lens, 16, 2, 128, 16, dtype,
+                                     kv_std=1.0 / math.sqrt(128), q_std=32.0)
+    vc = torch.where(torch.isnan(vc), vc, vc * math.sqrt(128))
+    want = decode_attention(q, kc, vc, tables, L, 16)
+    got = run_gpu(native, q, kc, vc, tables, L, partition_tokens=32)
+    assert_close(got, want, dtype, "sharp")
+    for h in range(16):
+        assert torch.equal(got[1, h], vc[tables[1, 0], h // 8, 0])
+    assert (got[2].float() == 0).all()
+    bad = tables.copy()
+    bad[3, 5] = kc.shape[0] + 3
+    got = run_gpu(native, q, kc, vc, bad, L, partition_tokens=32).float()
+    assert torch.isnan(got[3]).all()
+    keep = [0, 1, 2, 4]
+    assert_close(got[keep], want[keep], dtype, "others")
+
+
 def test_single_token_is_exact(native):
     for dtype in ("f32", "f16", "bf16"):
         q, kc, vc, tables, L = make_case(3, [1, 1, 1], 4, 4, 128, 16, dtype)
