@@ -7,6 +7,9 @@ path for the batch:
   host allocator step (one slot per text, copy-on-write pairs) -> table/slot upload
   -> for every layer: pa_copy_blocks (when pairs exist), pa_kv_write of the new
      token, pa_decode_attention over the cache.
+The writes and the decode launches of a step are replayed from two HIP graphs captured
+over fixed staging buffers (the step's new keys, values and queries are copied in
+first); `--no-graph` launches them one by one instead.
 `--layers` pools share one allocator, as the layers of one model do; reading a
 different layer's pools on every launch keeps repeat reads out of the 256 MB
 Infinity Cache, so every launch streams its keys and values from HBM.
@@ -412,6 +415,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch every decode step's kernels eagerly instead of replaying "
+                         "HIP graphs of the step's writes and decode launches")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run pa_copy_probe over 512 MiB (reference for memory counters)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -487,6 +493,37 @@ def main():
     qs = [[dl.step_q[i] for i in range(K + W)] for dl in draws]
     step_lens = []
     ev = []  # (start, end) events around every timed decode launch
+    graphs = {}
+
+    def decode_all(qsrc, mctx):
+        for li in range(NL):
+            if fp8:
+                L.pa_decode_attention_fp8(outs[li], qsrc[li], cache.k[li], cache.v[li], d_tables,
+                                          d_lens, mctx, ws, w.k_scale, w.v_scale, partition_tokens=T)
+            else:
+                L.pa_decode_attention(outs[li], qsrc[li], cache.k[li], cache.v[li], d_tables,
+                                      d_lens, mctx, ws, partition_tokens=T)
+
+    def capture():
+        """The step's device work as two HIP graphs over fixed staging buffers: the NL
+        new-token writes, then the NL decode launches (max_context_len = the bound the
+        workspace was sized for; the kernels read the true lengths from d_lens)."""
+        stk = {"k": torch.stack([torch.stack([newk[li][i] for li in range(NL)])
+                                 for i in range(K + W)]),
+               "v": torch.stack([torch.stack([newv[li][i] for li in range(NL)])
+                                 for i in range(K + W)]),
+               "q": torch.stack([torch.stack([qs[li][i] for li in range(NL)])
+                                 for i in range(K + W)])}
+        stage = {n: torch.empty_like(t[0]) for n, t in stk.items()}
+        torch.cuda.synchronize()
+        g_write, g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_write):
+            for li in range(NL):
+                cache.write(d_slots, stage["k"][li], stage["v"][li], layer=li)
+        with torch.cuda.graph(g_dec):
+            decode_all(stage["q"], max_ctx_bound)
+        torch.cuda.synchronize()
+        graphs.update(stk=stk, stage=stage, write=g_write, dec=g_dec)
 
     def step(i: int, timed: bool):
         slots, pairs, done = cache.alloc.step_append(seqs)
@@ -506,20 +543,23 @@ def main():
         mctx = int(lens.max())
         # every layer's copies and new-token writes, then every layer's attention back to
         # back: one event pair brackets the NL decode launches of the step
-        for li in range(NL):
-            if pairs:
+        if pairs:
+            for li in range(NL):
                 L.pa_copy_blocks(cache.k[li], cache.v[li], d_pairs[:len(pairs)])
-            cache.write(d_slots, newk[li][i], newv[li][i], layer=li)
+        if graphs:
+            for n in ("k", "v", "q"):
+                graphs["stage"][n].copy_(graphs["stk"][n][i])
+            graphs["write"].replay()
+        else:
+            for li in range(NL):
+                cache.write(d_slots, newk[li][i], newv[li][i], layer=li)
         if timed:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-        for li in range(NL):
-            if fp8:
-                L.pa_decode_attention_fp8(outs[li], qs[li][i], cache.k[li], cache.v[li], d_tables,
-                                          d_lens, mctx, ws, w.k_scale, w.v_scale, partition_tokens=T)
-            else:
-                L.pa_decode_attention(outs[li], qs[li][i], cache.k[li], cache.v[li], d_tables,
-                                      d_lens, mctx, ws, partition_tokens=T)
+        if graphs:
+            graphs["dec"].replay()
+        else:
+            decode_all([qs[li][i] for li in range(NL)], mctx)
         if timed:
             e1.record()
             ev.append((e0, e1))
@@ -529,13 +569,15 @@ def main():
 
     log(f"warmup {W} steps")
     for i in range(W):
+        if i == 1 and not args.no_graph:
+            capture()
         step(i, False)
         if i == 0:
             torch.cuda.synchronize()
             out0 = outs[0].float().cpu().numpy()
     torch.cuda.synchronize()
 
-    log(f"timing {K} steps")
+    log(f"timing {K} steps ({'HIP graph replay' if graphs else 'eager launches'})")
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t_start.record()
@@ -590,7 +632,8 @@ def main():
                    "heads": H, "kv_heads": Hkv, "head_dim": D, "block_size": B,
                    "kv_cache_dtype": "fp8_e4m3" if fp8 else w.dtype,
                    "pool_blocks": w.num_blocks, "layers_per_step": NL,
-                   "partition_tokens": T, "parallelism": "single GPU"},
+                   "partition_tokens": T, "parallelism": "single GPU",
+                   "launch": "HIP graph replay" if graphs else "eager"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "seq_layers_per_s": round(S * NL * K / (total_ms * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
