@@ -25,6 +25,7 @@ from __future__ import annotations
 
 import argparse
 import dataclasses
+import gc
 import hashlib
 import json
 import math
@@ -44,6 +45,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_opt13b_7x2048.json
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def quiet_gc():
+    """Collect once and pause Python's cyclic garbage collector for the timed steps: a
+    full collection over the setup's objects stalls the host for milliseconds at random
+    steps (measured: one 6 ms step among 12 of the Llama-shaped decode)."""
+    gc.collect()
+    gc.freeze()
+    gc.disable()
 
 
 def decode_bytes(lens, H, D, B, elt, Hkv=None, kv_elt=None) -> int:
@@ -249,7 +259,7 @@ def bench_prompt(args, w) -> None:
     d_tables = torch.empty((S, max_blocks), dtype=torch.int32, device="cuda")
     d_lens = torch.empty(S, dtype=torch.int32, device="cuda")
     outs = [torch.empty((T, H, D), dtype=torch_dtype(w.dtype), device="cuda") for _ in range(NL)]
-    R = 4
+    R = K + W  # one pinned staging buffer per step: the host never waits on an upload
     p_slots = [torch.empty(T, dtype=torch.int64, pin_memory=True) for _ in range(R)]
     p_tables = [torch.empty((S, max_blocks), dtype=torch.int32, pin_memory=True) for _ in range(R)]
     p_lens = [torch.empty(S, dtype=torch.int32, pin_memory=True) for _ in range(R)]
@@ -298,6 +308,7 @@ def bench_prompt(args, w) -> None:
     torch.cuda.synchronize()
     log(f"timing {K} steps")
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    quiet_gc()
     wall0 = time.perf_counter()
     t0.record()
     for i in range(W, W + K):
@@ -305,6 +316,7 @@ def bench_prompt(args, w) -> None:
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    gc.enable()
     total_ms = t0.elapsed_time(t1)
     flops = prompt_flops(lens, w.prefix_len, H, D)
     launch_ms = [a.elapsed_time(b) / NL for a, b in ev]
@@ -481,7 +493,10 @@ def main():
     d_tables = torch.empty((S, max_blocks), dtype=torch.int32, device="cuda")
     d_lens = torch.empty(S, dtype=torch.int32, device="cuda")
     d_pairs = torch.empty((S, 2), dtype=torch.int32, device="cuda")
-    R = 4  # ring of pinned staging buffers, each reused only after its upload completed
+    # one pinned staging buffer per step: the host allocator runs ahead of the GPU and never
+    # waits on an upload event (waiting on a ring slot let the host sleep for milliseconds
+    # past the event and the GPU run dry)
+    R = K + W
     p_slots = [torch.empty(S, dtype=torch.int64, pin_memory=True) for _ in range(R)]
     p_tables = [torch.empty((S, max_blocks), dtype=torch.int32, pin_memory=True) for _ in range(R)]
     p_lens = [torch.empty(S, dtype=torch.int32, pin_memory=True) for _ in range(R)]
@@ -579,6 +594,7 @@ def main():
 
     log(f"timing {K} steps ({'HIP graph replay' if graphs else 'eager launches'})")
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    quiet_gc()
     wall0 = time.perf_counter()
     t_start.record()
     for i in range(W, W + K):
@@ -586,6 +602,7 @@ def main():
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    gc.enable()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / K
 
