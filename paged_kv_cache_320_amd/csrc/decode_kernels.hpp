@@ -632,9 +632,9 @@ __global__ __launch_bounds__(kThreads) void decode_merge(
 
 // ---- shared key/value heads on the matrix cores --------------------------------
 //
-// With 8 query heads per key/value head, every key and value row feeds 8 dot products
-// and 8 weighted sums: about 8 flop per byte, which the vector ALUs cannot sustain at
-// HBM speed. Here a wave's 8 heads are the columns of 16x16 MFMA tiles (8 of 16 used):
+// With 8 (or 4) query heads per key/value head, every key and value row feeds 8 (4) dot
+// products and as many weighted sums: 4-8 flop per byte, which the vector ALUs cannot sustain at
+// HBM speed. Here a wave's GS = 8 (or 4) heads are the columns of 16x16 MFMA tiles:
 //   S^T (16 tokens x heads) = K (16 tokens x 32 dims) . Q^T     v_mfma_f32_16x16x32
 //   O^T (16 dims x heads)  += V^T (16 dims x 16 tokens) . P^T  v_mfma_f32_16x16x16
 // Lane l (col = l % 16, grp = l / 16) loads 16 bytes of token col's key and value rows at
@@ -705,7 +705,7 @@ struct MmaState {
   }
 };
 
-template <int QT, int D, int B>
+template <int QT, int D, int B, int GS>
 __device__ __forceinline__ void load_chunk_mma(MmaBuf<D>& b, const Cursor& c, const Ctx& x,
                                                const char* __restrict__ kc,
                                                const char* __restrict__ vc,
@@ -713,7 +713,7 @@ __device__ __forceinline__ void load_chunk_mma(MmaBuf<D>& b, const Cursor& c, co
   constexpr int kRowBytes = D * 2;
   constexpr int64_t kTileBytes = (int64_t)B * kRowBytes;
   const int col = lane & 15, grp = lane >> 4;
-  const int kvh = kv_head_of<8>(c.r, x);
+  const int kvh = kv_head_of<GS>(c.r, x);
   const int last = c.L > 0 ? c.L - 1 : 0;
   const int32_t* trow = tables + (int64_t)c.s * x.maxb;
   const int t = c.u * kChunk + col;
@@ -798,12 +798,11 @@ __device__ __forceinline__ void compute_chunk_mma(const MmaBuf<D>& b, const Curs
   }
 }
 
-template <int QT, int D>
+template <int QT, int D, int GS>
 __device__ __forceinline__ void flush_run_mma(MmaState<D>& st, const Cursor& c, const Ctx& x,
                                               int64_t seg_lo, int64_t seg_hi, int w,
                                               char* __restrict__ out, float* __restrict__ partials,
                                               float v_scale, int lane) {
-  constexpr int GS = 8;
   const int col = lane & 15, grp = lane >> 4;
   float l = st.l;
   l += __shfl_xor(l, 16);
@@ -840,14 +839,14 @@ __device__ __forceinline__ void flush_run_mma(MmaState<D>& st, const Cursor& c, 
   st.reset();
 }
 
-template <int QT, int D, int B>
+template <int QT, int D, int B, int GS>
 __global__ __launch_bounds__(kThreads) void decode_partition_mma(
     char* __restrict__ out, const char* __restrict__ q, const char* __restrict__ kc,
     const char* __restrict__ vc, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ ctx, int S, int H, int Hkv, int maxb, int num_blocks, int W,
     int seg_fixed, float scale_log2, float v_scale, int64_t* __restrict__ hdr,
     int64_t* __restrict__ excl_out, float* __restrict__ partials) {
-  constexpr int GS = 8;
+  static_assert(GS == 4 || GS == 8, "4 or 8 query heads per wave");
   constexpr int VS = D + 16;
   using M = Mma16<QT>;
   typedef typename M::v8 v8;
@@ -873,7 +872,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mma(
     if (c.r == q_run && c.s == q_text) return;
     q_run = c.r;
     q_text = c.s;
-    const char* qrow = q + ((int64_t)c.s * x.H + first_head_of<GS>(c.r, x) + (col & 7)) * D * 2;
+    const char* qrow =
+        q + ((int64_t)c.s * x.H + first_head_of<GS>(c.r, x) + (col & (GS - 1))) * D * 2;
 #pragma unroll
     for (int cc = 0; cc < D / 32; ++cc) {
       uint4 v = *reinterpret_cast<const uint4*>(qrow + (8 * grp + 32 * cc) * 2);
@@ -886,7 +886,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mma(
   MmaState<D> st;
   st.reset();
   MmaBuf<D> A, Bb;
-  load_chunk_mma<QT, D, B>(A, ld, x, kc, vc, tables, lane);
+  load_chunk_mma<QT, D, B, GS>(A, ld, x, kc, vc, tables, lane);
   advance(ld, x);
 
   auto step = [&](const MmaBuf<D>& b, int i) {
@@ -894,7 +894,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mma(
     compute_chunk_mma<QT, D>(b, cur, st, qv, vrow, scale_log2, lane);
     // last chunk of the run, or of the segment
     if (cur.u == cur.U - 1 || i == n - 1)
-      flush_run_mma<QT, D>(st, cur, x, seg_lo, seg_hi, w, out, partials, v_scale, lane);
+      flush_run_mma<QT, D, GS>(st, cur, x, seg_lo, seg_hi, w, out, partials, v_scale, lane);
     advance(cur, x);
   };
 
@@ -902,16 +902,16 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mma(
   // while the current one is computed
   int i = 0;
   while (i + 2 < n) {
-    load_chunk_mma<QT, D, B>(Bb, ld, x, kc, vc, tables, lane);
+    load_chunk_mma<QT, D, B, GS>(Bb, ld, x, kc, vc, tables, lane);
     advance(ld, x);
     step(A, i);
-    load_chunk_mma<QT, D, B>(A, ld, x, kc, vc, tables, lane);
+    load_chunk_mma<QT, D, B, GS>(A, ld, x, kc, vc, tables, lane);
     advance(ld, x);
     step(Bb, i + 1);
     i += 2;
   }
   if (i + 1 < n) {
-    load_chunk_mma<QT, D, B>(Bb, ld, x, kc, vc, tables, lane);
+    load_chunk_mma<QT, D, B, GS>(Bb, ld, x, kc, vc, tables, lane);
     step(A, i);
     step(Bb, i + 1);
   } else {
@@ -950,8 +950,8 @@ void launch(const Launch& a) {
   int64_t* excl = reinterpret_cast<int64_t*>(a.ws + a.lay.excl_off);
   float* part = reinterpret_cast<float*>(a.ws + a.lay.part_off);
   const int groups = (a.W + kWavesPerGroup - 1) / kWavesPerGroup;
-  if constexpr (GS == 8 && KT == QT && (KT == PA_F16 || KT == PA_BF16))
-    hipLaunchKernelGGL((decode_partition_mma<QT, D, B>), dim3(groups), dim3(kThreads), 0, a.st,
+  if constexpr ((GS == 4 || GS == 8) && KT == QT && (KT == PA_F16 || KT == PA_BF16))
+    hipLaunchKernelGGL((decode_partition_mma<QT, D, B, GS>), dim3(groups), dim3(kThreads), 0, a.st,
                        a.out, a.q, a.kc, a.vc, a.tables, a.ctx, a.S, a.H, a.Hkv, a.maxb, a.nb,
                        a.W, a.seg_fixed, a.sl, a.v_scale, hdr, excl, part);
   else

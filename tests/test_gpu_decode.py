@@ -113,10 +113,10 @@ def test_shared_kv_heads_all_formats(native, dtype, D, B, G):
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("D,B", [(64, 4), (64, 16), (128, 8), (128, 16), (128, 32)])
-@pytest.mark.parametrize("G", [8, 16])
+@pytest.mark.parametrize("G", [4, 8, 16])
 def test_eight_heads_per_kv_head_on_matrix_cores(native, dtype, D, B, G):
-    """8 query heads per wave on MFMA (16-bit formats): every block size, ragged chunks,
-    runs split over segments and whole runs in one segment."""
+    """4 or 8 query heads per wave on MFMA (16-bit formats): every block size, ragged
+    chunks, runs split over segments and whole runs in one segment."""
     lens = [1, 15, 16, 17, 129, 300, 1025]
     Hkv = 2
     say(f"gqa mfma dtype={dtype} D={D} B={B} G={G}")

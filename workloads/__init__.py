@@ -124,6 +124,12 @@ LLAMA70B_32x4096 = Workload(
 # twice the tokens in the same memory): the OPT-13B 7 x 2,048 step with E4M3 pools. The
 # scales 1/256 (exact reciprocals) map the drawn keys/values (std 0.088) well inside E4M3's
 # range (448 * 1/256 = 1.75, about 20 standard deviations).
+GQA4_32x4096 = Workload(
+    name="gqa4_32x4096_f16_b16", seed=7, num_seqs=32, num_heads=32, num_kv_heads=8,
+    head_dim=128, block_size=16, num_blocks=32 * 257 + 64, dtype="f16",
+    kv_std=1 / math.sqrt(128), q_std=1.0, steps=4, length_kind="fixed", ctx_fixed=4096,
+    description="shared K/V heads, 4 query heads per K/V head: 32 query heads over 8 K/V "
+                "heads x 128, fp16, block 16, 32 texts x 4096 tokens")
 OPT13B_7x2048_FP8 = OPT13B_7x2048.scaled(
     name="opt13b_7x2048_fp8_b16", cache_dtype="fp8", k_scale=1 / 256, v_scale=1 / 256,
     description="OPT-13B one layer with an E4M3 cache: 40 heads x 128, fp16 queries, "
@@ -184,7 +190,7 @@ OPT13B_PREFIX_32x1024 = PromptWorkload(
                 "(64 blocks held by all 32 texts), OPT-13B shapes, fp16, block 16")
 PROMPT = (OPT13B_PROMPT_7x2048, OPT13B_PROMPT_MIXED64, LLAMA70B_PROMPT_8x4096,
           OPT13B_PREFIX_32x1024)
-EXTRA = (LLAMA70B_32x4096, OPT13B_7x2048_FP8)
+EXTRA = (LLAMA70B_32x4096, OPT13B_7x2048_FP8, GQA4_32x4096)
 BY_NAME = {w.name: w for w in ALL + EXTRA + PROMPT}
 
 
