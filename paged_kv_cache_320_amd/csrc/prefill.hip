@@ -13,9 +13,14 @@
 // fp16 and bf16, fp32 accumulation).
 //  * A workgroup of 4 waves takes 128 consecutive queries of one (text, head); wave w
 //    holds queries 32w..32w+31 as the 32 columns of its MFMA tiles.
-//  * Keys stream in tiles of 32 positions. The workgroup copies a tile's keys and
-//    values from their blocks (16-byte loads, one table entry per block) into LDS;
-//    rows past the last position any query of the workgroup needs are zero.
+//  * Keys stream in tiles of 64 positions, double-buffered in LDS. gfx950's LDS DMA
+//    (global_load_lds_dwordx4) moves each 16-byte piece of a tile's keys and values
+//    from its block straight into LDS, without a trip through registers, while the
+//    previous tile is being multiplied. Rows past the last position any query of the
+//    workgroup needs repeat that position (finite, and given no weight).
+//  * A DMA writes a wave's 64 pieces to 1 KiB of consecutive LDS, so conflict-free
+//    operand reads come from an XOR swizzle of the 16-byte pieces within a row instead
+//    of row padding.
 //  * S^T = K Q^T puts keys on the rows and queries on the columns, so a lane holds
 //    16 scores of one query and its partner lane (lane ^ 32) the other 16: the row
 //    maximum and sum need one exchange between the pair, no wider reduction.
@@ -80,29 +85,52 @@ struct Mma<PA_BF16> {
 // 1: lanes 32-63) of the 32x32 MFMA output, relative to the tile.
 __device__ __forceinline__ int key_of(int r, int half) { return (r >> 2) * 8 + half * 4 + (r & 3); }
 
-// A operand of O^T += V^T P^T for 32-row tile mt and k-step kk: lane l needs
-// V[key_of(8 kk + j, l / 32)][32 mt + l % 32] for j = 0..7. gfx950's ds_read_b64_tr_b16
-// reads, per group of 16 lanes, the 4 x 16-bit pieces that lane j of the group
-// addresses and hands lane i element i % 4 of lane 4k + i / 4's piece as its value k.
-// So lane j of a group addresses key (its value k = j / 4) at dims 4 (j % 4) .. +3
-// of the group's 16 dims, and lane i receives 4 keys at dim (group base) + i. Two
+// LDS tile layout: key or value row r (of kKeys) holds D 16-bit elements as CPR = D / 8
+// pieces of 16 bytes; logical piece c of row r sits in slot c ^ swz(r). For keys
+// swz(r) = r mod CPR: the 16 rows of a 16-lane key-operand read (one piece each) fall in
+// 16 distinct slots, 256 distinct bytes. For values swz(r) = 2r mod CPR: the 4 rows x 2
+// pieces of a 16-lane transposing read fall in 8 distinct slots.
+template <int CPR>
+__device__ __forceinline__ int swz_k(int r) { return r & (CPR - 1); }
+template <int CPR>
+__device__ __forceinline__ int swz_v(int r) { return (2 * r) & (CPR - 1); }
+
+// A operand of O^T += V^T P^T for 32-key subtile st, 32-row tile mt and k-step kk: lane l
+// needs V[key_of(8 kk + j, l / 32)][32 mt + l % 32] for j = 0..7. gfx950's
+// ds_read_b64_tr_b16 reads, per group of 16 lanes, the 4 x 16-bit pieces that lane j of
+// the group addresses and hands lane i element i % 4 of lane 4k + i / 4's piece as its
+// value k. So lane j of a group addresses key (its value k = j / 4) at dims 4 (j % 4) ..
+// +3 of the group's 16 dims, and lane i receives 4 keys at dim (group base) + i. Two
 // reads give the 8 keys: 16 kk + 4 half + (0..3), then the same + 8.
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <int KS>
-__device__ __forceinline__ u32x4 vt_operand(const uint16_t* vs, int mt, int kk, int lane) {
+template <int D>
+__device__ __forceinline__ const uint16_t* v_piece(const uint16_t* vs, int key, int dim) {
+  constexpr int CPR = D / 8;
+  return vs + key * D + (((dim >> 3) ^ swz_v<CPR>(key)) << 3) + (dim & 7);
+}
+
+template <int D>
+__device__ __forceinline__ u32x4 vt_operand(const uint16_t* vs, int st, int mt, int kk, int lane) {
   const int grp = lane >> 4, j = lane & 15;
   const int dim = 32 * mt + 16 * (grp & 1) + 4 * (j & 3);
-  const int key = 16 * kk + 4 * (grp >> 1) + (j >> 2);
-  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + key * KS + dim));
-  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + (key + 8) * KS + dim));
+  const int key = 32 * st + 16 * kk + 4 * (grp >> 1) + (j >> 2);
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)v_piece<D>(vs, key, dim));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)v_piece<D>(vs, key + 8, dim));
   u32x4 w;
   w[0] = (uint16_t)a[0] | ((uint32_t)(uint16_t)a[1] << 16);
   w[1] = (uint16_t)a[2] | ((uint32_t)(uint16_t)a[3] << 16);
   w[2] = (uint16_t)b[0] | ((uint32_t)(uint16_t)b[1] << 16);
   w[3] = (uint16_t)b[2] | ((uint32_t)(uint16_t)b[3] << 16);
   return w;
+}
+
+// gfx950 LDS DMA: each lane's 16 bytes from `src` land at lds + 16 * lane (lds must be
+// the same for every lane of the wave).
+__device__ __forceinline__ void dma16(const char* src, uint16_t* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
 template <int DT, int D, int B>
@@ -113,18 +141,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     int maxb, int num_blocks, int qtiles, int nwork, float scale_log2) {
   using M = Mma<DT>;
   typedef typename M::v8 v8;
-  // 16-bit elements per LDS row: a key row shifts 4 banks from the one before, so the 16
-  // rows of a 16-lane key-operand read hit 64 distinct banks; a value row shifts 8 banks,
-  // so the 4 rows x 32 bytes of a 16-lane transposing read hit 32 distinct banks
-  constexpr int KS = D + 8;
-  constexpr int VS = D + 16;
   constexpr int CPR = D / 8;                     // 16-byte pieces per key row
-  constexpr int NC = kKeys * CPR / kThreads;     // pieces per thread and tile, each of K and V
   constexpr int NQ = D / 16;                     // MFMA k-steps of S^T
   constexpr int NM = D / 32;                     // 32-row tiles of O^T
-  static_assert(NC * kThreads == kKeys * CPR, "tile copy must cover the tile exactly");
-  __shared__ __align__(16) uint16_t ks[2][kKeys * KS];  // two buffers: compute one tile
-  __shared__ __align__(16) uint16_t vs[2][kKeys * VS];  // while the next is stored
+  constexpr int NI = kKeys * CPR / 64 / kWaves;  // DMAs per wave, tensor and tile
+  static_assert(NI * 64 * kWaves == kKeys * CPR, "tile copy must cover the tile exactly");
+  // Two named buffers rather than one indexed array: the compiler then sees that the
+  // next tile's DMA never writes what this tile's operand reads read, and does not make
+  // those reads wait for it.
+  __shared__ __align__(16) uint16_t k0[kKeys * D], k1[kKeys * D];  // two buffers: compute
+  __shared__ __align__(16) uint16_t v0[kKeys * D], v1[kKeys * D];  // one tile, load the next
 
   __shared__ int bad_sh;
 
@@ -187,65 +213,44 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
     const int ntiles = kv_end > 0 ? (kv_end + kKeys - 1) / kKeys : 0;
     const int wave_first = first + wrow0;  // position of the wave's first query
-    // Register copies of the next tile's keys and values: the global loads of tile kt+1
-    // are in flight while tile kt is computed from the other LDS buffer. The block ids of
-    // a tile are read one tile earlier still, so no load waits on a table lookup.
-    u32x4 kx[NC], vx[NC];
-    int tb[NC];
-    // Every lane loads, whether its key position is needed or not: positions past the
-    // last needed one read that one again (a valid place) and store zeros, so no load
-    // sits under a branch.
+    int tb[NI];
     const int kv_last = max(kv_lim - 1, 0);
     auto load_table = [&](int kt) {
 #pragma unroll
-      for (int j = 0; j < NC; ++j) {
-        const int kp = kt * kKeys + (tid + j * kThreads) / CPR;
-        tb[j] = trow[min(kp, kv_last) / B];
+      for (int j = 0; j < NI; ++j) {
+        const int row = ((wave * NI + j) * 64 + lane) / CPR;
+        tb[j] = trow[min(kt * kKeys + row, kv_last) / B];
       }
     };
-    auto fetch = [&](int kt) {
+    bool bad = false;
+    auto dma = [&](int kt, uint16_t* kd, uint16_t* vd) {
+      // every address first (the table entries arrived during the previous tile), so
+      // no wait for a table entry falls between two tile loads
+      const char* ksrc[NI];
+      const char* vsrc[NI];
 #pragma unroll
-      for (int j = 0; j < NC; ++j) {
-        const int c = tid + j * kThreads;
-        const int kp = kt * kKeys + c / CPR;
-        int blk = tb[j];
-        if ((unsigned)blk >= (unsigned)num_blocks) {
-          if (kp < kv_lim) bad_sh = 1;  // read block 0 instead; the text's output is poisoned
-          blk = 0;
-        }
-        const int64_t off =
-            (((int64_t)blk * Hkv + kvh) * B + min(kp, kv_last) % B) * (D * 2) + (c % CPR) * 16;
-        kx[j] = *(const u32x4*)(kc + off);
-        vx[j] = *(const u32x4*)(vc + off);
+      for (int j = 0; j < NI; ++j) {
+        const int chunk = (wave * NI + j) * 64 + lane;
+        const int row = chunk / CPR, slot = chunk % CPR;
+        const int kp = kt * kKeys + row;
+        const bool out_of_pool = (unsigned)tb[j] >= (unsigned)num_blocks;
+        bad |= out_of_pool && kp < kv_lim;
+        const int blk = out_of_pool ? 0 : tb[j];
+        const int64_t off = (((int64_t)blk * Hkv + kvh) * B + min(kp, kv_last) % B) * (D * 2);
+        ksrc[j] = kc + off + ((slot ^ swz_k<CPR>(row)) * 16);
+        vsrc[j] = vc + off + ((slot ^ swz_v<CPR>(row)) * 16);
       }
-    };
-    auto stash = [&](int buf, int kt) {
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < NC; ++j) {
-        const int c = tid + j * kThreads;
-        const int key = c / CPR, pc = c % CPR;
-        const bool use = kt * kKeys + key < kv_lim;
-        const u32x4 zero = {0u, 0u, 0u, 0u};
-        *(u32x4*)(ks[buf] + key * KS + pc * 8) = use ? kx[j] : zero;
-        *(u32x4*)(vs[buf] + key * VS + pc * 8) = use ? vx[j] : zero;
+      for (int j = 0; j < NI; ++j) {
+        dma16(ksrc[j], kd + (wave * NI + j) * 512);
+        dma16(vsrc[j], vd + (wave * NI + j) * 512);
       }
     };
-    // Loads, table reads and LDS stores run unconditionally (their addresses are guarded
-    // per lane: past the last needed position nothing is read and zeros are stored), so
-    // the compiler's wait counters never see a path with an unfinished load and the
-    // matrix products never wait for the next tile's loads.
-    load_table(0);
-    fetch(0);
-    stash(0, 0);
-    load_table(1);
-    __syncthreads();
-    for (int kt = 0; kt < ntiles; ++kt) {
-      const int buf = kt & 1;
-      fetch(kt + 1);
+    auto tile = [&](int kt, const uint16_t* kb, const uint16_t* vb, uint16_t* kn, uint16_t* vn) {
+      dma(kt + 1, kn, vn);
       load_table(kt + 2);
       if (wave_on && kt * kKeys <= wave_last) {  // causal skip (wave-uniform)
-        const uint16_t* kb = ks[buf];
-        const uint16_t* vb = vs[buf];
         // S^T = K Q^T per 32-key subtile: A = 32 keys x 16 dims from LDS, B = the wave's
         // queries; the subtiles' products are independent, so they overlap
         f32x16 sacc[kSub];
@@ -258,8 +263,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         for (int c = 0; c < NQ; ++c) {
 #pragma unroll
           for (int st = 0; st < kSub; ++st) {
+            const int row = 32 * st + col;
             const v8 a = __builtin_bit_cast(
-                v8, *(const u32x4*)(kb + (32 * st + col) * KS + 16 * c + 8 * half));
+                v8, *(const u32x4*)(kb + row * D + (((2 * c + half) ^ swz_k<CPR>(row)) * 8)));
             sacc[st] = M::mfma(a, qv[c], sacc[st]);
           }
         }
@@ -322,15 +328,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
               o[mt] = M::mfma(
-                  __builtin_bit_cast(v8, vt_operand<VS>(vb + 32 * st * VS, mt, kk, lane)),
+                  __builtin_bit_cast(v8, vt_operand<D>(vb, st, mt, kk, lane)),
                   pb[kk], o[mt]);
           }
         }
         l += psum;
       }
-      stash(buf ^ 1, kt + 1);
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();  // the next tile is in LDS; this one is no longer read
+    };
+    load_table(0);
+    dma(0, k0, v0);
+    load_table(1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kt = 0; kt < ntiles; kt += 2) {
+      tile(kt, k0, v0, k1, v1);
+      if (kt + 1 < ntiles) tile(kt + 1, k1, v1, k0, v0);
     }
+    if (bad) bad_sh = 1;
+    __syncthreads();
     const float lt = l + __shfl_xor(l, 32);
     float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (bad_shape || bad_sh) inv = __builtin_nanf("");
