@@ -7,9 +7,10 @@ path for the batch:
   host allocator step (one slot per text, copy-on-write pairs) -> table/slot upload
   -> for every layer: pa_copy_blocks (when pairs exist), pa_kv_write of the new
      token, pa_decode_attention over the cache.
-The writes and the decode launches of a step are replayed from two HIP graphs captured
-over fixed staging buffers (the step's new keys, values and queries are copied in
-first); `--no-graph` launches them one by one instead.
+Kernels are launched one by one (the host runs ahead of the GPU; the slots and lengths
+of a step arrive in one upload). `--graph` replays each step's writes and its decode
+launches from two HIP graphs captured for that step instead (measured slower here:
+about 20 us per step goes to the hand-over between two graph launches).
 `--layers` pools share one allocator, as the layers of one model do; reading a
 different layer's pools on every launch keeps repeat reads out of the 256 MB
 Infinity Cache, so every launch streams its keys and values from HBM.
@@ -427,9 +428,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="launch every decode step's kernels eagerly instead of replaying "
-                         "HIP graphs of the step's writes and decode launches")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each decode step's writes and decode launches from HIP graphs "
+                         "captured for that step instead of launching them one by one")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run pa_copy_probe over 512 MiB (reference for memory counters)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -489,17 +490,21 @@ def main():
     max_ctx_bound = w.ctx_fixed + K + W
     T = args.partition_tokens
     ws = L.decode_workspace(S, H, D, max_ctx_bound, T)
-    d_slots = torch.empty(S, dtype=torch.int64, device="cuda")
+    # a step's slots (int64) and lengths (int32) share one buffer: one upload per step
+    meta_bytes = 12 * S
+    d_meta = torch.empty(meta_bytes, dtype=torch.uint8, device="cuda")
+    d_slots = d_meta[:8 * S].view(torch.int64)
+    d_lens = d_meta[8 * S:].view(torch.int32)
     d_tables = torch.empty((S, max_blocks), dtype=torch.int32, device="cuda")
-    d_lens = torch.empty(S, dtype=torch.int32, device="cuda")
     d_pairs = torch.empty((S, 2), dtype=torch.int32, device="cuda")
     # one pinned staging buffer per step: the host allocator runs ahead of the GPU and never
     # waits on an upload event (waiting on a ring slot let the host sleep for milliseconds
     # past the event and the GPU run dry)
     R = K + W
-    p_slots = [torch.empty(S, dtype=torch.int64, pin_memory=True) for _ in range(R)]
+    p_meta = [torch.empty(meta_bytes, dtype=torch.uint8, pin_memory=True) for _ in range(R)]
+    p_slots = [m[:8 * S].view(torch.int64) for m in p_meta]
+    p_lens = [m[8 * S:].view(torch.int32) for m in p_meta]
     p_tables = [torch.empty((S, max_blocks), dtype=torch.int32, pin_memory=True) for _ in range(R)]
-    p_lens = [torch.empty(S, dtype=torch.int32, pin_memory=True) for _ in range(R)]
     p_pairs = [torch.empty((S, 2), dtype=torch.int32, pin_memory=True) for _ in range(R)]
     up_done = [torch.cuda.Event() for _ in range(R)]
     outs = [torch.empty((S, H, D), dtype=torch_dtype(w.dtype), device="cuda") for _ in range(NL)]
@@ -520,25 +525,19 @@ def main():
                                       d_lens, mctx, ws, partition_tokens=T)
 
     def capture():
-        """The step's device work as two HIP graphs over fixed staging buffers: the NL
-        new-token writes, then the NL decode launches (max_context_len = the bound the
-        workspace was sized for; the kernels read the true lengths from d_lens)."""
-        stk = {"k": torch.stack([torch.stack([newk[li][i] for li in range(NL)])
-                                 for i in range(K + W)]),
-               "v": torch.stack([torch.stack([newv[li][i] for li in range(NL)])
-                                 for i in range(K + W)]),
-               "q": torch.stack([torch.stack([qs[li][i] for li in range(NL)])
-                                 for i in range(K + W)])}
-        stage = {n: torch.empty_like(t[0]) for n, t in stk.items()}
+        """Two HIP graphs for every step from the second on, over that step's own inputs:
+        its NL new-token writes, then its NL decode launches (max_context_len = the bound
+        the workspace was sized for; the kernels read the true lengths from d_lens)."""
         torch.cuda.synchronize()
-        g_write, g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_write):
-            for li in range(NL):
-                cache.write(d_slots, stage["k"][li], stage["v"][li], layer=li)
-        with torch.cuda.graph(g_dec):
-            decode_all(stage["q"], max_ctx_bound)
+        for i in range(1, K + W):
+            g_write, g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_write):
+                for li in range(NL):
+                    cache.write(d_slots, newk[li][i], newv[li][i], layer=li)
+            with torch.cuda.graph(g_dec):
+                decode_all([qs[li][i] for li in range(NL)], max_ctx_bound)
+            graphs[i] = (g_write, g_dec)
         torch.cuda.synchronize()
-        graphs.update(stk=stk, stage=stage, write=g_write, dec=g_dec)
 
     last_tables = None
 
@@ -551,14 +550,13 @@ def main():
         L.pa_export_tables(cache.alloc.h, seqs, max_blocks, p_tables[r].numpy(), p_lens[r].numpy())
         lens = p_lens[r].numpy().copy()
         step_lens.append(lens)
-        d_slots.copy_(p_slots[r], non_blocking=True)
+        d_meta.copy_(p_meta[r], non_blocking=True)
         # the tables change only when a text opens a new block (every block_size steps):
         # upload them only then (an upload of the unchanged 33 KB tables of the 32-text
         # workloads stalled the host for ~6 ms every ten-odd steps)
         if last_tables is None or not np.array_equal(last_tables, p_tables[r].numpy()):
             d_tables.copy_(p_tables[r], non_blocking=True)
             last_tables = p_tables[r].numpy().copy()
-        d_lens.copy_(p_lens[r], non_blocking=True)
         if pairs:
             p_pairs[r].numpy()[:len(pairs)] = np.asarray(pairs, dtype=np.int32)
             d_pairs.copy_(p_pairs[r], non_blocking=True)
@@ -569,18 +567,16 @@ def main():
         if pairs:
             for li in range(NL):
                 L.pa_copy_blocks(cache.k[li], cache.v[li], d_pairs[:len(pairs)])
-        if graphs:
-            for n in ("k", "v", "q"):
-                graphs["stage"][n].copy_(graphs["stk"][n][i])
-            graphs["write"].replay()
+        if i in graphs:
+            graphs[i][0].replay()
         else:
             for li in range(NL):
                 cache.write(d_slots, newk[li][i], newv[li][i], layer=li)
         if timed:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-        if graphs:
-            graphs["dec"].replay()
+        if i in graphs:
+            graphs[i][1].replay()
         else:
             decode_all([qs[li][i] for li in range(NL)], mctx)
         if timed:
@@ -592,7 +588,7 @@ def main():
 
     log(f"warmup {W} steps")
     for i in range(W):
-        if i == 1 and not args.no_graph:
+        if i == 1 and args.graph:
             capture()
         step(i, False)
         if i == 0:
@@ -605,8 +601,11 @@ def main():
     quiet_gc()
     wall0 = time.perf_counter()
     t_start.record()
+    host_s = 0.0
     for i in range(W, W + K):
+        h0 = time.perf_counter()
         step(i, True)
+        host_s += time.perf_counter() - h0
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -624,6 +623,7 @@ def main():
                                       for l in timed_lens]))
     achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
     traffic = measured_traffic() if base.name == "opt13b_7x2048_f16_b16" else None
+    log(f"host time per step (allocator, uploads, launches) {host_s / K * 1e6:.1f} us")
     log(f"step {ms_per_step * 1e3:.1f} us ({NL} layers), decode launch {avg_launch_ms * 1e3:.1f} us "
         f"(min {min(launch_ms) * 1e3:.1f}), {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBPS:.1%} of 8 TB/s")
 
