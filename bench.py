@@ -171,6 +171,40 @@ def run_probe(L, torch, gib=4):
     return gbps
 
 
+def run_tile_probe(L, torch, tile_bytes: int, bytes_per_launch: int, gib=4):
+    """The decode's own read volume in randomly placed tiles of its (block, head) tile size:
+    each launch reads a disjoint random set of tiles of a 4 GiB buffer (more than the
+    256 MB Infinity Cache holds between two uses of a set). Mean GB/s."""
+    n = gib << 30
+    buf = torch.empty(n // 2, dtype=torch.float16, device="cuda").normal_()
+    sink = torch.empty(L.pa_probe_sink_bytes(4), dtype=torch.uint8, device="cuda")
+    per = max(1, bytes_per_launch // tile_bytes)
+    g = torch.Generator().manual_seed(0)
+    perm = torch.randperm(n // tile_bytes, generator=g).to(torch.int32)
+    sets = [perm[k * per:(k + 1) * per].cuda() for k in range(len(perm) // per)]
+    L.pa_tile_read_probe(buf, tile_bytes, sets[0], sink)  # checked call through the binding
+    torch.cuda.synchronize()
+    # then the raw entry point with the pointers taken once (the binding's per-call work
+    # would otherwise starve the GPU between 50 us launches), and one launch ahead of the
+    # first event so no host time falls inside the timed region
+    fn, stream = L.lib().pa_tile_read_probe, torch.cuda.current_stream().cuda_stream
+    calls = [(buf.data_ptr(), n, tile_bytes, ids.data_ptr(), ids.numel(), sink.data_ptr(), stream)
+             for ids in sets]
+    # one untimed pass over every set first: the decode steps run over pools they have
+    # touched before, and the first touch of a page costs address-translation misses
+    for c in calls:
+        assert fn(*c) == 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for c in calls[1:]:
+        fn(*c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (len(sets) - 1)
+    del buf
+    return per * tile_bytes / (ms * 1e-3) / 1e9
+
+
 def cpu_baseline(w, d0, seconds: float, gpu_out0):
     """The oracle as it stands, on one layer's step-0 batch, one thread, about `seconds` long."""
     import numpy as np
@@ -627,10 +661,13 @@ def main():
     log(f"step {ms_per_step * 1e3:.1f} us ({NL} layers), decode launch {avg_launch_ms * 1e3:.1f} us "
         f"(min {min(launch_ms) * 1e3:.1f}), {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBPS:.1%} of 8 TB/s")
 
-    probe = None
+    probe = tprobe = None
     if not args.no_probe:
         probe = run_probe(L, torch)
         log(f"stream-read probe: {probe:.0f} GB/s")
+        tprobe = run_tile_probe(L, torch, B * D * kv_elt, int(bytes_per_launch))
+        log(f"same-pattern probe ({int(bytes_per_launch) >> 20} MiB per launch in random "
+            f"{B * D * kv_elt} B tiles): {tprobe:.0f} GB/s")
 
     cpu = None
     err0 = None
@@ -667,6 +704,7 @@ def main():
                      "avg_launch_us": round(avg_launch_ms * 1e3, 2),
                      "bytes_per_launch": int(bytes_per_launch)},
         "probe_read_gbps": round(probe, 1) if probe else None,
+        "probe_same_pattern_gbps": round(tprobe, 1) if tprobe else None,
         "cpu_baseline": cpu,
         "step0_max_abs_err_vs_oracle": err0,
         "wall_s_timed": round(wall, 4),

@@ -282,11 +282,18 @@ int pa_prefill_attention(void* out, const void* q, const void* k_cache, const vo
  * Measurement helpers (not part of the method): the achievable HBM read rate
  * and a copy of known size for calibrating memory counters.
  * ------------------------------------------------------------------------- */
-/* Stream-read `bytes` (multiple of 16) from buf; sink receives 4 bytes per workgroup
- * (size it with pa_probe_sink_bytes). waves_per_cu 0 = 8. */
+/* Stream-read `bytes` (multiple of 16) from buf: each workgroup one contiguous range,
+ * 16 non-temporal 16-byte loads in flight per lane; sink receives 4 bytes per workgroup
+ * (size it with pa_probe_sink_bytes). waves_per_cu 0 = 4. */
 size_t pa_probe_sink_bytes(int32_t waves_per_cu);
 int pa_stream_read_probe(const void* buf, size_t bytes, void* sink, int32_t waves_per_cu,
                          void* stream);
+/* Read the tiles tile_ids[0 .. n_ids) of tile_bytes each (2048, 4096, 8192 or 16384) from
+ * buf, the access pattern of decode attention over randomly placed blocks: each of 4 waves
+ * per CU reads a contiguous share of the list, 32 KiB in flight, non-temporal 16-byte
+ * loads. Ids are clamped into [0, buf_bytes / tile_bytes). sink: pa_probe_sink_bytes(4). */
+int pa_tile_read_probe(const void* buf, size_t buf_bytes, int32_t tile_bytes,
+                       const int32_t* tile_ids, int64_t n_ids, void* sink, void* stream);
 /* dst[0:bytes] = src[0:bytes] (bytes multiple of 16). */
 int pa_copy_probe(void* dst, const void* src, size_t bytes, void* stream);
 

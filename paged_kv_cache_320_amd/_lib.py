@@ -65,6 +65,7 @@ SIGNATURES = {
                                                _vp]),
     "pa_probe_sink_bytes": (_sz, [_i32]),
     "pa_stream_read_probe": (ctypes.c_int, [_vp, _sz, _vp, _i32, _vp]),
+    "pa_tile_read_probe": (ctypes.c_int, [_vp, _sz, _i32, _vp, ctypes.c_int64, _vp, _vp]),
     "pa_copy_probe": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
 }
 
@@ -384,6 +385,14 @@ def pa_probe_sink_bytes(waves_per_cu: int = 0) -> int:
 def pa_stream_read_probe(buf, sink, waves_per_cu: int = 0, stream=None) -> None:
     _check(lib().pa_stream_read_probe(_dev(buf, "buf"), buf.numel() * buf.element_size(),
                                       _dev(sink, "sink"), waves_per_cu, _stream(stream)))
+
+
+def pa_tile_read_probe(buf, tile_bytes: int, tile_ids, sink, stream=None) -> None:
+    import torch
+    assert tile_ids.dtype == torch.int32
+    _check(lib().pa_tile_read_probe(_dev(buf, "buf"), buf.numel() * buf.element_size(),
+                                    int(tile_bytes), _dev(tile_ids, "tile_ids"),
+                                    int(tile_ids.numel()), _dev(sink, "sink"), _stream(stream)))
 
 
 def pa_copy_probe(dst, src, stream=None) -> None:

@@ -86,14 +86,18 @@ struct Mma<PA_BF16> {
 __device__ __forceinline__ int key_of(int r, int half) { return (r >> 2) * 8 + half * 4 + (r & 3); }
 
 // LDS tile layout: key or value row r (of kKeys) holds D 16-bit elements as CPR = D / 8
-// pieces of 16 bytes; logical piece c of row r sits in slot c ^ swz(r). For keys
-// swz(r) = r mod CPR: the 16 rows of a 16-lane key-operand read (one piece each) fall in
-// 16 distinct slots, 256 distinct bytes. For values swz(r) = 2r mod CPR: the 4 rows x 2
-// pieces of a 16-lane transposing read fall in 8 distinct slots.
+// pieces of 16 bytes; logical piece c of row r sits in slot c ^ swz(r). LDS has 64 banks
+// of 4 bytes, so a piece's bank group (of 16) is (r * CPR + slot) mod 16.
+//  * Keys: a 16-lane key-operand read takes one piece p of rows r0 .. r0 + 15. With
+//    swz(r) = r mod 16 (D = 128) or (r / 2) mod 8 (D = 64, where odd rows already sit
+//    8 groups further) the 16 rows land in 16 distinct bank groups.
+//  * Values: a 32-lane half of a transposing read takes pieces 4m .. 4m + 3 of rows
+//    r0 .. r0 + 3 (r0 a multiple of 4). With swz(r) = 4 (r mod 4) (D = 128) or
+//    4 ((r / 2) mod 2) (D = 64) the 4 rows take 4 disjoint groups of 4: 16 distinct.
 template <int CPR>
-__device__ __forceinline__ int swz_k(int r) { return r & (CPR - 1); }
+__device__ __forceinline__ int swz_k(int r) { return CPR == 16 ? (r & 15) : ((r >> 1) & 7); }
 template <int CPR>
-__device__ __forceinline__ int swz_v(int r) { return (2 * r) & (CPR - 1); }
+__device__ __forceinline__ int swz_v(int r) { return CPR == 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
 // A operand of O^T += V^T P^T for 32-key subtile st, 32-row tile mt and k-step kk: lane l
 // needs V[key_of(8 kk + j, l / 32)][32 mt + l % 32] for j = 0..7. gfx950's

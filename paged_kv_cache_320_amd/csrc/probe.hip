@@ -7,29 +7,95 @@ namespace pagedkv {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 16;
 
-// Each thread reads 16-byte pieces with a grid-wide stride, kUnroll loads in flight.
+// Each workgroup reads its own contiguous range in 16-byte pieces, kUnroll non-temporal
+// loads in flight per lane (64 KiB per workgroup). Measured on this part: with 4 waves
+// per CU this pattern reads ~7.1 TB/s, plain loads or 4 loads in flight ~6.2-6.3 TB/s.
 __global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __restrict__ buf,
                                                                int64_t pieces,
                                                                uint32_t* __restrict__ sink) {
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4* p = reinterpret_cast<const u32x4*>(buf);
+  const int64_t per = (pieces + gridDim.x - 1) / gridDim.x;
+  const int64_t lo = (int64_t)blockIdx.x * per;
+  const int64_t hi = lo + per < pieces ? lo + per : pieces;
+  int64_t i = lo + threadIdx.x;
   uint32_t x = 0;
-  for (; i + (kUnroll - 1) * stride < pieces; i += kUnroll * stride) {
-    uint4 v[kUnroll];
+  for (; i + (kUnroll - 1) * kThreads < hi; i += kUnroll * kThreads) {
+    u32x4 v[kUnroll];
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) v[j] = buf[i + j * stride];
+    for (int j = 0; j < kUnroll; ++j) v[j] = __builtin_nontemporal_load(p + i + j * kThreads);
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) x ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
   }
-  for (; i < pieces; i += stride) {
-    const uint4 v = buf[i];
+  for (; i < hi; i += kThreads) {
+    const u32x4 v = __builtin_nontemporal_load(p + i);
     x ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o);
   __shared__ uint32_t sh[kThreads / 64];
   if ((threadIdx.x & 63) == 0) sh[threadIdx.x / 64] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = sh[0] ^ sh[1] ^ sh[2] ^ sh[3];
+}
+
+// Random-tile read: the tiles named by ids (whole tiles of TB bytes, 1 KiB wave loads),
+// each wave a contiguous share of the list with 32 KiB in flight; ids are clamped into
+// the buffer.
+template <int TB>
+__global__ __launch_bounds__(kThreads) void tile_read_kernel(const char* __restrict__ buf,
+                                                             int64_t nbuf,
+                                                             const int32_t* __restrict__ ids,
+                                                             int64_t n, uint32_t* __restrict__ sink) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int LPT = TB / 1024, TU = 32768 / TB;
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = (int64_t)gridDim.x * (kThreads / 64);
+  const int64_t wv = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int64_t lo = n * wv / nw, hi = n * (wv + 1) / nw;
+  auto tile_base = [&](int64_t t) {
+    int64_t id = ids[t];
+    id = id < 0 ? 0 : id >= nbuf ? nbuf - 1 : id;
+    return reinterpret_cast<const u32x4*>(buf + id * TB);
+  };
+  auto tile = [&](int64_t t) { return tile_base(t) + lane; };
+  uint32_t x = 0;
+  int64_t t = lo;
+  for (; t + TU <= hi; t += TU) {
+    u32x4 v[TU][LPT];
+#pragma unroll
+    for (int u = 0; u < TU; ++u) {
+      const u32x4* p = tile(t + u);
+#pragma unroll
+      for (int j = 0; j < LPT; ++j) v[u][j] = __builtin_nontemporal_load(p + 64 * j);
+    }
+#pragma unroll
+    for (int u = 0; u < TU; ++u)
+#pragma unroll
+      for (int j = 0; j < LPT; ++j) x ^= v[u][j].x ^ v[u][j].y ^ v[u][j].z ^ v[u][j].w;
+  }
+  if (t < hi) {
+    // the last, partial group with its loads in flight together; past hi every lane
+    // reads the same 16 bytes (not counted)
+    u32x4 v[TU][LPT];
+#pragma unroll
+    for (int u = 0; u < TU; ++u) {
+      const bool real = t + u < hi;
+      const u32x4* p = real ? tile(t + u) : tile_base(hi - 1);
+#pragma unroll
+      for (int j = 0; j < LPT; ++j) v[u][j] = __builtin_nontemporal_load(p + (real ? 64 * j : 0));
+    }
+#pragma unroll
+    for (int u = 0; u < TU; ++u)
+      if (t + u < hi) {
+#pragma unroll
+        for (int j = 0; j < LPT; ++j) x ^= v[u][j].x ^ v[u][j].y ^ v[u][j].z ^ v[u][j].w;
+      }
+  }
+  for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o);
+  __shared__ uint32_t sh[kThreads / 64];
+  if (lane == 0) sh[threadIdx.x / 64] = x;
   __syncthreads();
   if (threadIdx.x == 0) sink[blockIdx.x] = sh[0] ^ sh[1] ^ sh[2] ^ sh[3];
 }
@@ -46,7 +112,7 @@ int probe_groups(int32_t waves_per_cu, int* groups) {
   int cus = 0;
   int rc = device_cus(&cus);
   if (rc != PA_OK) return rc;
-  if (waves_per_cu <= 0) waves_per_cu = 8;
+  if (waves_per_cu <= 0) waves_per_cu = 4;
   *groups = cus * ((waves_per_cu + 3) / 4);
   return PA_OK;
 }
@@ -72,6 +138,32 @@ extern "C" int pa_stream_read_probe(const void* buf, size_t bytes, void* sink,
   if (rc != PA_OK) return rc;
   hipLaunchKernelGGL(stream_read_kernel, dim3(groups), dim3(kThreads), 0, (hipStream_t)stream,
                      (const uint4*)buf, (int64_t)(bytes / 16), (uint32_t*)sink);
+  PA_HIP_CHECK(hipGetLastError());
+  return ok();
+}
+
+extern "C" int pa_tile_read_probe(const void* buf, size_t buf_bytes, int32_t tile_bytes,
+                                  const int32_t* tile_ids, int64_t n_ids, void* sink,
+                                  void* stream) {
+  if (!buf || !tile_ids || !sink) return fail(PA_EINVAL, "null pointer");
+  if (tile_bytes != 2048 && tile_bytes != 4096 && tile_bytes != 8192 && tile_bytes != 16384)
+    return fail(PA_EINVAL, "tile_bytes %d not 2048, 4096, 8192 or 16384", tile_bytes);
+  if (!aligned16(buf) || buf_bytes < (size_t)tile_bytes || n_ids < 0)
+    return fail(PA_EINVAL, "buf must be 16-byte aligned and hold a tile; n_ids >= 0");
+  if (n_ids == 0) return ok();
+  int groups = 0;
+  int rc = probe_groups(4, &groups);
+  if (rc != PA_OK) return rc;
+  const int64_t nbuf = (int64_t)(buf_bytes / (size_t)tile_bytes);
+  hipStream_t st = (hipStream_t)stream;
+  const char* b = (const char*)buf;
+  uint32_t* sk = (uint32_t*)sink;
+  switch (tile_bytes) {
+    case 2048: hipLaunchKernelGGL(tile_read_kernel<2048>, dim3(groups), dim3(kThreads), 0, st, b, nbuf, tile_ids, n_ids, sk); break;
+    case 4096: hipLaunchKernelGGL(tile_read_kernel<4096>, dim3(groups), dim3(kThreads), 0, st, b, nbuf, tile_ids, n_ids, sk); break;
+    case 8192: hipLaunchKernelGGL(tile_read_kernel<8192>, dim3(groups), dim3(kThreads), 0, st, b, nbuf, tile_ids, n_ids, sk); break;
+    default: hipLaunchKernelGGL(tile_read_kernel<16384>, dim3(groups), dim3(kThreads), 0, st, b, nbuf, tile_ids, n_ids, sk); break;
+  }
   PA_HIP_CHECK(hipGetLastError());
   return ok();
 }
