@@ -217,13 +217,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
     const int ntiles = kv_end > 0 ? (kv_end + kKeys - 1) / kKeys : 0;
     const int wave_first = first + wrow0;  // position of the wave's first query
-    int tb[NI];
     const int kv_last = max(kv_lim - 1, 0);
+    // A wave moves rows 16 wave .. 16 wave + 15 of every tile. With block_size >= 16 they lie
+    // in one block: one table entry per wave and tile (a scalar), and each lane's offset in
+    // the (block, head) tile is fixed but for rows past the last needed position, which
+    // re-read that position. Smaller blocks take one entry per lane and load.
+    constexpr bool kWaveBlock = B >= 16;
+    static_assert(NI * 64 == 16 * CPR, "a wave moves 16 rows of each tile");
+    int tb[NI];
+    int tbw = 0;
     auto load_table = [&](int kt) {
+      if constexpr (kWaveBlock) {
+        tbw = trow[min(kt * kKeys + 16 * wave, kv_last) / B];
+      } else {
 #pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        const int row = ((wave * NI + j) * 64 + lane) / CPR;
-        tb[j] = trow[min(kt * kKeys + row, kv_last) / B];
+        for (int j = 0; j < NI; ++j) {
+          const int row = ((wave * NI + j) * 64 + lane) / CPR;
+          tb[j] = trow[min(kt * kKeys + row, kv_last) / B];
+        }
       }
     };
     bool bad = false;
@@ -232,17 +243,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       // no wait for a table entry falls between two tile loads
       const char* ksrc[NI];
       const char* vsrc[NI];
+      if constexpr (kWaveBlock) {
+        const int pos0 = kt * kKeys + 16 * wave;
+        const bool out_of_pool = (unsigned)tbw >= (unsigned)num_blocks;
+        bad |= out_of_pool && pos0 < kv_lim;
+        const int64_t tile_off = ((int64_t)(out_of_pool ? 0 : tbw) * Hkv + kvh) * (B * D * 2);
 #pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        const int chunk = (wave * NI + j) * 64 + lane;
-        const int row = chunk / CPR, slot = chunk % CPR;
-        const int kp = kt * kKeys + row;
-        const bool out_of_pool = (unsigned)tb[j] >= (unsigned)num_blocks;
-        bad |= out_of_pool && kp < kv_lim;
-        const int blk = out_of_pool ? 0 : tb[j];
-        const int64_t off = (((int64_t)blk * Hkv + kvh) * B + min(kp, kv_last) % B) * (D * 2);
-        ksrc[j] = kc + off + ((slot ^ swz_k<CPR>(row)) * 16);
-        vsrc[j] = vc + off + ((slot ^ swz_v<CPR>(row)) * 16);
+        for (int j = 0; j < NI; ++j) {
+          const int r = (j * 64 + lane) / CPR, slot = (j * 64 + lane) % CPR;
+          const int row = 16 * wave + r;
+          const uint32_t in_tile = (uint32_t)(min(pos0 + r, kv_last) & (B - 1)) * (D * 2);
+          ksrc[j] = kc + tile_off + (in_tile + (uint32_t)((slot ^ swz_k<CPR>(row)) * 16));
+          vsrc[j] = vc + tile_off + (in_tile + (uint32_t)((slot ^ swz_v<CPR>(row)) * 16));
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          const int chunk = (wave * NI + j) * 64 + lane;
+          const int row = chunk / CPR, slot = chunk % CPR;
+          const int kp = kt * kKeys + row;
+          const bool out_of_pool = (unsigned)tb[j] >= (unsigned)num_blocks;
+          bad |= out_of_pool && kp < kv_lim;
+          const int blk = out_of_pool ? 0 : tb[j];
+          const int64_t off = (((int64_t)blk * Hkv + kvh) * B + min(kp, kv_last) % B) * (D * 2);
+          ksrc[j] = kc + off + ((slot ^ swz_k<CPR>(row)) * 16);
+          vsrc[j] = vc + off + ((slot ^ swz_v<CPR>(row)) * 16);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
