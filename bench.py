@@ -171,11 +171,12 @@ def run_probe(L, torch, gib=4):
     return gbps
 
 
-def run_tile_probe(L, torch, tile_bytes: int, bytes_per_launch: int, gib=4):
+def run_tile_probe(L, torch, tile_bytes: int, bytes_per_launch: int):
     """The decode's own read volume in randomly placed tiles of its (block, head) tile size:
-    each launch reads a disjoint random set of tiles of a 4 GiB buffer (more than the
-    256 MB Infinity Cache holds between two uses of a set). Mean GB/s."""
-    n = gib << 30
+    each launch reads a disjoint random set of tiles of a buffer of at least 4 GiB and 4
+    launches' worth (more than the 256 MB Infinity Cache holds between two uses of a
+    set). Mean GB/s."""
+    n = max(4 << 30, (4 * bytes_per_launch + (1 << 30) - 1) >> 30 << 30)  # >= 4 sets
     buf = torch.empty(n // 2, dtype=torch.float16, device="cuda").normal_()
     sink = torch.empty(L.pa_probe_sink_bytes(4), dtype=torch.uint8, device="cuda")
     per = max(1, bytes_per_launch // tile_bytes)
@@ -493,20 +494,25 @@ def main():
     base = wl.BY_NAME[args.workload]
     if isinstance(base, wl.PromptWorkload):
         return bench_prompt(args, base)
-    assert base.length_kind == "fixed", "bench.py times fixed-length batches"
+    assert base.length_kind in ("fixed", "uniform", "list"), \
+        "bench.py times batches whose texts each decode one token per step (no forks)"
     kv_elt = ELT[base.pool_dtype]
     fp8 = base.pool_dtype == "fp8"
-    per_layer = base.num_seqs * base.ctx_fixed * 2 * base.num_kv_heads * base.head_dim * kv_elt
-    NL = args.layers or min(16, max(8, -(-2_000_000_000 // per_layer)))
     w = base.scaled(steps=K + W)
     S, H, Hkv, D, B = w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size
-    steps_room = (w.num_blocks - S * ((w.ctx_fixed + B - 1) // B)) // S * B
-    assert K + W <= steps_room, f"pool holds only {steps_room} more steps"
 
-    log(f"setup: {w.name}, {NL} layers, drawing inputs on the GPU")
+    log(f"setup: {w.name}, drawing inputs on the GPU")
     draws = [wl.draw(w, device="cuda")]
+    lens0 = [n + 1 for n in draws[0].prefill_lens]  # attended at step 0
+    per_layer = sum(lens0) * 2 * Hkv * D * kv_elt
+    NL = args.layers or min(16, max(8, -(-2_000_000_000 // per_layer)))
+    need = sum((n + K + W + B - 1) // B for n in draws[0].prefill_lens)
+    assert need <= w.num_blocks, f"the pool holds {w.num_blocks} blocks; {K + W} steps need {need}"
+    log(f"{NL} layers")
     for li in range(1, NL):
-        draws.append(wl.draw(w.scaled(seed=w.seed * 1000 + li), device="cuda"))
+        # every layer holds the same texts (lengths), with its own keys, values and queries
+        draws.append(wl.draw(w.scaled(seed=w.seed * 1000 + li, length_kind="list",
+                                      ctx_list=tuple(lens0)), device="cuda"))
     cache = PagedKVCache(w.num_blocks, B, Hkv, D, w.pool_dtype, layers=NL, device="cuda",
                          free_order=draws[0].free_order, fill=float("nan"),
                          k_scale=w.k_scale, v_scale=w.v_scale)
@@ -520,8 +526,8 @@ def main():
         seqs.append(sid)
     torch.cuda.synchronize()
 
-    max_blocks = (w.ctx_fixed + K + W + B - 1) // B
-    max_ctx_bound = w.ctx_fixed + K + W
+    max_blocks = (max(lens0) + K + W + B - 1) // B
+    max_ctx_bound = max(lens0) + K + W
     T = args.partition_tokens
     ws = L.decode_workspace(S, H, D, max_ctx_bound, T)
     # a step's slots (int64) and lengths (int32) share one buffer: one upload per step
@@ -690,7 +696,9 @@ def main():
         "dtype": w.dtype,
         "data": f"synthetic (seeded N(0,1)*{w.kv_std:.4g} keys/values, N(0,{w.q_std:g}) queries; "
                 "random block placement)",
-        "config": {"workload": base.name, "seqs": S, "context_at_step0": w.ctx_fixed,
+        "config": {"workload": base.name, "seqs": S,
+                   "context_at_step0": (lens0[0] if len(set(lens0)) == 1 else
+                                        f"{min(lens0)}..{max(lens0)}, mean {np.mean(lens0):.0f}"),
                    "heads": H, "kv_heads": Hkv, "head_dim": D, "block_size": B,
                    "kv_cache_dtype": "fp8_e4m3" if fp8 else w.dtype,
                    "pool_blocks": w.num_blocks, "layers_per_step": NL,
