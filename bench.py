@@ -5,12 +5,13 @@ Workload: OPT-13B-shaped decode of 7 texts x 2,048 tokens (40 heads x 128, fp16,
 block 16, 983-block pools with randomly placed blocks). One step is the whole hot
 path for the batch:
   host allocator step (one slot per text, copy-on-write pairs) -> table/slot upload
-  -> for every layer: pa_copy_blocks (when pairs exist), pa_kv_write of the new
-     token, pa_decode_attention over the cache.
+  -> for every layer: pa_copy_blocks (when pairs exist), the write of the new token
+     and decode attention over the cache, in one launch (pa_decode_attention_write;
+     `--separate-write`, and E4M3 pools: pa_kv_write then pa_decode_attention).
 Kernels are launched one by one (the host runs ahead of the GPU; the slots and lengths
-of a step arrive in one upload). `--graph` replays each step's writes and its decode
-launches from two HIP graphs captured for that step instead (measured slower here:
-about 20 us per step goes to the hand-over between two graph launches).
+of a step arrive in one upload). `--graph` replays each step's launches from HIP graphs
+captured for that step instead (measured slower here: tens of us per step go to the
+hand-over between graph launches).
 `--layers` pools share one allocator, as the layers of one model do; reading a
 different layer's pools on every launch keeps repeat reads out of the 256 MB
 Infinity Cache, so every launch streams its keys and values from HBM.
@@ -80,13 +81,14 @@ def src_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per decode launch from the committed counter runs, if the kernel is unchanged."""
+def measured_traffic(fused: bool):
+    """HBM bytes per decode launch from the committed counter runs, if the kernel is unchanged
+    (same sources, and the same variant: with or without the fused new-token write)."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if rec.get("decode_src_sha256_16") != src_hash():
+    if rec.get("decode_src_sha256_16") != src_hash() or rec.get("fused_write", False) != fused:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -121,11 +123,14 @@ def traffic_from_counters(fetch_dir: str, write_dir: str) -> None:
     scaled by what the same counter reads for pa_copy_probe moving COPY_CAL_BYTES."""
     import numpy as np
     res = {}
+    fused = set()
     for key, d, name in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         rows = _counter_rows(d, name)
         ours = [(k, v) for k, v in rows if k.startswith("pagedkv::") or "pagedkv::" in k[:40]]
         copy = [v for k, v in ours if "copy_kernel" in k]
         part = [v for k, v in ours if "decode_partition" in k]
+        # the fused variant's template arguments end in "true>"
+        fused |= {"true>" in k for k, v in ours if "decode_partition" in k}
         merge = [v for k, v in ours if "decode_merge" in k]
         if not copy or not part:
             raise SystemExit(f"{name}: need copy_kernel and decode_partition dispatches in {d}")
@@ -135,7 +140,10 @@ def traffic_from_counters(fetch_dir: str, write_dir: str) -> None:
                     "merge_kib_median": float(np.median(merge)) if merge else 0.0,
                     "bytes_per_launch": (float(np.median(part)) +
                                          (float(np.median(merge)) if merge else 0.0)) * 1024 * scale}
+    if len(fused) != 1:
+        raise SystemExit("counter runs mix the decode kernel with and without the fused write")
     rec = {"decode_src_sha256_16": src_hash(), "workload": "opt13b_7x2048_f16_b16",
+           "fused_write": fused.pop(),
            "hbm_bytes_per_launch": int(res["fetch"]["bytes_per_launch"] + res["write"]["bytes_per_launch"]),
            "fetch": res["fetch"], "write": res["write"],
            "calibration": f"pa_copy_probe reading and writing {COPY_CAL_BYTES} bytes"}
@@ -463,6 +471,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="write each layer's new token with pa_kv_write before its decode launch "
+                         "instead of inside it (pa_decode_attention_write)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each decode step's writes and decode launches from HIP graphs "
                          "captured for that step instead of launching them one by one")
@@ -555,27 +566,40 @@ def main():
     ev = []  # (start, end) events around every timed decode launch
     graphs = {}
 
-    def decode_all(qsrc, mctx):
+    # 16- and 32-bit pools: each layer's new-token write runs inside its decode launch
+    # (pa_decode_attention_write); E4M3 pools quantize the new rows in pa_kv_write_fp8 first
+    fused = not fp8 and not args.separate_write
+
+    def write_all(i):
+        for li in range(NL):
+            cache.write(d_slots, newk[li][i], newv[li][i], layer=li)
+
+    def decode_all(i, mctx):
         for li in range(NL):
             if fp8:
-                L.pa_decode_attention_fp8(outs[li], qsrc[li], cache.k[li], cache.v[li], d_tables,
+                L.pa_decode_attention_fp8(outs[li], qs[li][i], cache.k[li], cache.v[li], d_tables,
                                           d_lens, mctx, ws, w.k_scale, w.v_scale, partition_tokens=T)
+            elif fused:
+                L.pa_decode_attention_write(outs[li], qs[li][i], cache.k[li], cache.v[li],
+                                            newk[li][i], newv[li][i], d_slots, d_tables, d_lens,
+                                            mctx, ws, partition_tokens=T)
             else:
-                L.pa_decode_attention(outs[li], qsrc[li], cache.k[li], cache.v[li], d_tables,
+                L.pa_decode_attention(outs[li], qs[li][i], cache.k[li], cache.v[li], d_tables,
                                       d_lens, mctx, ws, partition_tokens=T)
 
     def capture():
-        """Two HIP graphs for every step from the second on, over that step's own inputs:
-        its NL new-token writes, then its NL decode launches (max_context_len = the bound
-        the workspace was sized for; the kernels read the true lengths from d_lens)."""
+        """HIP graphs for every step from the second on, over that step's own inputs: its
+        NL new-token writes (unless fused), then its NL decode launches (max_context_len =
+        the bound the workspace was sized for; the kernels read the true lengths from d_lens)."""
         torch.cuda.synchronize()
         for i in range(1, K + W):
-            g_write, g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g_write):
-                for li in range(NL):
-                    cache.write(d_slots, newk[li][i], newv[li][i], layer=li)
+            g_write, g_dec = None, torch.cuda.CUDAGraph()
+            if not fused:
+                g_write = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g_write):
+                    write_all(i)
             with torch.cuda.graph(g_dec):
-                decode_all([qs[li][i] for li in range(NL)], max_ctx_bound)
+                decode_all(i, max_ctx_bound)
             graphs[i] = (g_write, g_dec)
         torch.cuda.synchronize()
 
@@ -607,18 +631,19 @@ def main():
         if pairs:
             for li in range(NL):
                 L.pa_copy_blocks(cache.k[li], cache.v[li], d_pairs[:len(pairs)])
-        if i in graphs:
+        if fused:
+            pass
+        elif i in graphs:
             graphs[i][0].replay()
         else:
-            for li in range(NL):
-                cache.write(d_slots, newk[li][i], newv[li][i], layer=li)
+            write_all(i)
         if timed:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
         if i in graphs:
             graphs[i][1].replay()
         else:
-            decode_all([qs[li][i] for li in range(NL)], mctx)
+            decode_all(i, mctx)
         if timed:
             e1.record()
             ev.append((e0, e1))
@@ -662,7 +687,7 @@ def main():
     bytes_per_launch = float(np.mean([decode_bytes(l, H, D, B, elt, Hkv, kv_elt)
                                       for l in timed_lens]))
     achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
-    traffic = measured_traffic() if base.name == "opt13b_7x2048_f16_b16" else None
+    traffic = measured_traffic(fused) if base.name == "opt13b_7x2048_f16_b16" else None
     log(f"host time per step (allocator, uploads, launches) {host_s / K * 1e6:.1f} us")
     log(f"step {ms_per_step * 1e3:.1f} us ({NL} layers), decode launch {avg_launch_ms * 1e3:.1f} us "
         f"(min {min(launch_ms) * 1e3:.1f}), {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBPS:.1%} of 8 TB/s")
@@ -703,12 +728,16 @@ def main():
                    "kv_cache_dtype": "fp8_e4m3" if fp8 else w.dtype,
                    "pool_blocks": w.num_blocks, "layers_per_step": NL,
                    "partition_tokens": T, "parallelism": "single GPU",
-                   "launch": "HIP graph replay" if graphs else "eager"},
+                   "launch": "HIP graph replay" if graphs else "eager",
+                   "new_token_write": "fused into decode" if fused else "pa_kv_write"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "seq_layers_per_s": round(S * NL * K / (total_ms * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": "pa_decode_attention = decode_partition + decode_merge",
+                     "traffic": traffic,
+                     "kernel": ("pa_decode_attention_write = decode_partition (new-token write "
+                                "fused) + decode_merge") if fused else
+                               "pa_decode_attention = decode_partition + decode_merge",
                      "avg_launch_us": round(avg_launch_ms * 1e3, 2),
                      "bytes_per_launch": int(bytes_per_launch)},
         "probe_read_gbps": round(probe, 1) if probe else None,

@@ -213,6 +213,34 @@ int pa_decode_attention_fp8(void* out, const void* q, const void* k_cache, const
                             int32_t q_dtype, void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/* Decode attention with the step's new-token write fused in (one launch instead of
+ * pa_kv_write then pa_decode_attention; «KV cache» "How it works": the new position's
+ * key and value join the cache and are attended in the same step).
+ *
+ * Result, bit for bit, that of
+ *   pa_kv_write(k_cache, v_cache, k_new, v_new, slots', num_seqs, ...);
+ *   pa_decode_attention(out, q, k_cache, v_cache, ...);
+ * with slots'[s] = slots[s] for texts with context_lens[s] >= 1 and -1 (skipped) for the
+ * others, provided slots[s] is the place of position context_lens[s] - 1 of text s in
+ * its block table (what pa_step_append hands out) and no text of the batch attends
+ * another text's new place (copy-on-write guarantees it). The last position's key and
+ * value are read from k_new / v_new; one wave per (text, key/value head) stores them
+ * into the pools during the launch, for later steps. Slots outside
+ * [0, num_blocks * block_size) are skipped.
+ *
+ * k_new, v_new: [num_seqs][num_kv_heads][head_dim] in dtype, 16-byte aligned; slots:
+ * int64 [num_seqs]. dtype PA_F32, PA_F16 or PA_BF16 (E4M3 pools: pa_kv_write_fp8, then
+ * pa_decode_attention_fp8). Everything else, the workspace included, as
+ * pa_decode_attention. */
+int pa_decode_attention_write(void* out, const void* q, void* k_cache, void* v_cache,
+                              const void* k_new, const void* v_new, const int64_t* slots,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              int32_t max_blocks_per_seq, int32_t max_context_len,
+                              int32_t partition_tokens, float scale, int32_t dtype,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Prefix caching ("What Came After": every full block gets a hash of its tokens and
  * of everything before them; a request that begins the same way reuses the blocks,

@@ -52,6 +52,9 @@ SIGNATURES = {
     "pa_decode_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                            _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32,
                                            _vp, _sz, _vp]),
+    "pa_decode_attention_write": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                 _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                 _i32, ctypes.c_float, _i32, _vp, _sz, _vp]),
     "pa_hash_blocks": (ctypes.c_int, [_vp, _i32, _i32, ctypes.c_uint64, _vp]),
     "pa_seq_add_cached": (ctypes.c_int, [_vp, _vp, _i32, _c_int32_p, _c_int32_p]),
     "pa_seq_cache_blocks": (ctypes.c_int, [_vp, _i32, _vp, _i32]),
@@ -334,6 +337,29 @@ def pa_decode_attention(out, q, k_cache, v_cache, block_tables, context_lens, ma
         scale = D ** -0.5
     _check(lib().pa_decode_attention(
         _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), S, H, Hkv, D, B,
+        N, int(block_tables.shape[1]), int(max_context_len), int(partition_tokens), float(scale),
+        dtype_code(q), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def pa_decode_attention_write(out, q, k_cache, v_cache, k_new, v_new, slots, block_tables,
+                              context_lens, max_context_len: int, workspace,
+                              partition_tokens: int = 0, scale: Optional[float] = None,
+                              stream=None) -> None:
+    """pa_kv_write of the step's new rows k_new/v_new [S, Hkv, D] at slots (int64 [S]) fused
+    into pa_decode_attention."""
+    S, H, D = q.shape
+    N, Hkv, B, Dk = k_cache.shape
+    assert Dk == D and tuple(out.shape) == (S, H, D)
+    assert tuple(k_new.shape) == (S, Hkv, D) and tuple(v_new.shape) == (S, Hkv, D)
+    assert k_new.dtype == k_cache.dtype == q.dtype and slots.numel() == S
+    assert block_tables.shape[0] == S and context_lens.numel() == S
+    if scale is None:
+        scale = D ** -0.5
+    _check(lib().pa_decode_attention_write(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(slots, "slots"),
         _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), S, H, Hkv, D, B,
         N, int(block_tables.shape[1]), int(max_context_len), int(partition_tokens), float(scale),
         dtype_code(q), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),

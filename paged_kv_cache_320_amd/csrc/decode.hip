@@ -94,7 +94,7 @@ int decode_common(void* out, const void* q, const void* k_cache, const void* v_c
                   int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                   int32_t partition_tokens, float scale, float k_scale, float v_scale,
                   int32_t kv_dtype, int32_t q_dtype, void* workspace, size_t workspace_bytes,
-                  void* stream) {
+                  void* stream, const decode_impl::NewRows& nr = decode_impl::NewRows{}) {
   if (head_dim != 64 && head_dim != 128)
     return fail(PA_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
   if (block_size != 4 && block_size != 8 && block_size != 16 && block_size != 32)
@@ -129,7 +129,7 @@ int decode_common(void* out, const void* q, const void* k_cache, const void* v_c
                  max_blocks_per_seq, num_blocks, (int)lay.W, partition_tokens / kChunk,
                  // scale * k_scale * log2(e): scores in the exp2 domain, key scale folded in
                  scale * k_scale * 1.4426950408889634f, v_scale,
-                 (char*)workspace, lay, (hipStream_t)stream};
+                 (char*)workspace, lay, (hipStream_t)stream, nr};
   const int GS = heads_per_wave(num_heads / num_kv_heads);
   bool done = false;
   const bool d64 = head_dim == 64;
@@ -184,4 +184,25 @@ extern "C" int pa_decode_attention_fp8(void* out, const void* q, const void* k_c
                        num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                        max_context_len, partition_tokens, scale, k_scale, v_scale, PA_FP8_E4M3,
                        q_dtype, workspace, workspace_bytes, stream);
+}
+
+extern "C" int pa_decode_attention_write(void* out, const void* q, void* k_cache, void* v_cache,
+                                         const void* k_new, const void* v_new,
+                                         const int64_t* slots, const int32_t* block_tables,
+                                         const int32_t* context_lens, int32_t num_seqs,
+                                         int32_t num_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                         int32_t max_blocks_per_seq, int32_t max_context_len,
+                                         int32_t partition_tokens, float scale, int32_t dtype,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return fail(PA_EINVAL, "dtype %d is not PA_F32/PA_F16/PA_BF16", dtype);
+  if (!k_new || !v_new || !slots) return fail(PA_EINVAL, "null pointer");
+  if (!aligned16(k_new) || !aligned16(v_new) || ((uintptr_t)slots & 7u))
+    return fail(PA_EINVAL, "k_new and v_new must be 16-byte aligned, slots 8-byte aligned");
+  const decode_impl::NewRows nr{(const char*)k_new, (const char*)v_new, slots, (char*)k_cache,
+                                (char*)v_cache};
+  return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
+                       num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                       max_context_len, partition_tokens, scale, 1.0f, 1.0f, dtype, dtype,
+                       workspace, workspace_bytes, stream, nr);
 }

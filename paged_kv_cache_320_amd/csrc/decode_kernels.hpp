@@ -40,6 +40,10 @@
 //    merge kernel. The kernel boundary gives the merge its visibility for free.
 //    The order of every sum depends only on logical positions, never on where
 //    blocks are placed.
+//  * Fused new-token write (pa_decode_attention_write): the step's new key and value
+//    rows are read straight from k_new / v_new for the last position (and written
+//    into the cache by one run per key/value head, for later steps), so the separate
+//    write kernel and its launch go away. No wave reads that place from the cache.
 #pragma once
 
 #include "device.hpp"
@@ -102,6 +106,16 @@ struct Ctx {
   const int32_t* __restrict__ ctx;
 };
 
+// The step's new rows, for the fused write: k_new / v_new [S][Hkv][D] in the pools'
+// format, slots [S] (block * B + place), the pools to write.
+struct NewRows {
+  const char* __restrict__ k;
+  const char* __restrict__ v;
+  const int64_t* __restrict__ slots;
+  char* kc;
+  char* vc;
+};
+
 __device__ __forceinline__ void set_text(Cursor& c, const Ctx& x, int s) {
   c.s = s;
   int L = s < x.S ? x.ctx[s] : 0;
@@ -160,12 +174,13 @@ struct State {
   }
 };
 
-template <int KT, int QT, int D, int B, int GS>
+template <int KT, int QT, int D, int B, int GS, bool FUSED>
 __device__ __forceinline__ void load_chunk(Buf<KT, QT, D, GS>& b, const Cursor& c, const Ctx& x,
                                            const char* __restrict__ kc,
                                            const char* __restrict__ vc,
                                            const char* __restrict__ q,
-                                           const int32_t* __restrict__ tables, int lane) {
+                                           const int32_t* __restrict__ tables,
+                                           const NewRows& nr, int lane) {
   using G = Geo<KT, D>;
   constexpr int kRowBytes = D * G::ELT;
   constexpr int64_t kTileBytes = (int64_t)B * kRowBytes;  // one (block, kv head) tile
@@ -176,6 +191,8 @@ __device__ __forceinline__ void load_chunk(Buf<KT, QT, D, GS>& b, const Cursor& 
   const int last = c.L > 0 ? c.L - 1 : 0;
   const int32_t* trow = tables + (int64_t)c.s * x.maxb;
   const int t_first = c.u * kChunk;
+  // fused write: the last position's rows come from k_new / v_new
+  const int64_t new_row = ((int64_t)c.s * x.Hkv + kvh) * kRowBytes + lp * 16;
   b.bad = c.over;
   if constexpr (B >= kChunk) {
     // the whole chunk lies in one block: one scalar table lookup, a scalar tile base
@@ -192,8 +209,14 @@ __device__ __forceinline__ void load_chunk(Buf<KT, QT, D, GS>& b, const Cursor& 
       const int t = t_first + i * G::RPW + g;
       const int tc = t < last ? t : last;
       const uint32_t off = (uint32_t)(tc % B) * kRowBytes + lp * 16;
-      b.k[i] = load_stream(kb + off);
-      b.v[i] = load_stream(vb + off);
+      if constexpr (FUSED) {
+        const bool fresh = tc == last;
+        b.k[i] = load_stream(fresh ? nr.k + new_row : kb + off);
+        b.v[i] = load_stream(fresh ? nr.v + new_row : vb + off);
+      } else {
+        b.k[i] = load_stream(kb + off);
+        b.v[i] = load_stream(vb + off);
+      }
     }
   } else {
 #pragma unroll
@@ -213,8 +236,14 @@ __device__ __forceinline__ void load_chunk(Buf<KT, QT, D, GS>& b, const Cursor& 
       if (bad) blk = 0;
       const int64_t off = ((int64_t)blk * x.Hkv + kvh) * kTileBytes +
                           (uint32_t)(tc % B) * kRowBytes + lp * 16;
-      b.k[i] = load_stream(kc + off);
-      b.v[i] = load_stream(vc + off);
+      if constexpr (FUSED) {
+        const bool fresh = tc == last;
+        b.k[i] = load_stream(fresh ? nr.k + new_row : kc + off);
+        b.v[i] = load_stream(fresh ? nr.v + new_row : vc + off);
+      } else {
+        b.k[i] = load_stream(kc + off);
+        b.v[i] = load_stream(vc + off);
+      }
     }
   }
   // the GS query rows (cache hits after the run's first chunk)
@@ -225,6 +254,62 @@ __device__ __forceinline__ void load_chunk(Buf<KT, QT, D, GS>& b, const Cursor& 
 #pragma unroll
     for (int p = 0; p < QP; ++p)
       b.q[j][p] = *reinterpret_cast<const uint4*>(qrow + j * kQRowBytes + p * 16);
+}
+
+// Fused write in the vector kernel: when a writing run's last chunk is computed, the lanes
+// holding the new position's rows (just loaded from k_new / v_new) store them into their
+// place, if it is in the pool. The first run of each key/value head writes.
+template <int B, int GS>
+__device__ __forceinline__ bool writes_new_row(const Cursor& c, const Ctx& x) {
+  return c.L > 0 && c.u == c.U - 1 && (GS == 1 ? c.r % x.G : c.r % x.NG) == 0;
+}
+template <int D, int ELT, int B, int GS>
+__device__ __forceinline__ void store_new_piece(const NewRows& nr, const Cursor& c, const Ctx& x,
+                                                int col, const uint4& k, const uint4& v) {
+  constexpr int kRowBytes = D * ELT;
+  const int64_t slot = nr.slots[c.s];
+  if (slot < 0 || slot >= (int64_t)x.num_blocks * B) return;
+  const int kvh = kv_head_of<GS>(c.r, x);
+  const int64_t row = ((slot / B) * x.Hkv + kvh) * B + slot % B;
+  *reinterpret_cast<uint4*>(nr.kc + row * kRowBytes + col) = k;
+  *reinterpret_cast<uint4*>(nr.vc + row * kRowBytes + col) = v;
+}
+
+// Fused write in the matrix-core kernel, after the segment's last chunk (stores inside
+// its streaming loop made the compiler's wait counts conservative): for every run whose last unit lies in
+// this segment, the first run of each key/value head copies the text's new key and value
+// rows from k_new / v_new into their place, when that place is in the pool. Each run's
+// last unit lies in exactly one segment, so each row is written once.
+template <int D, int ELT, int B, int GS>
+__device__ __forceinline__ void write_new_rows(const NewRows& nr, Cursor c, const Ctx& x,
+                                               int64_t seg_lo, int64_t seg_hi, int lane) {
+  constexpr int kRowBytes = D * ELT;
+  static_assert(kRowBytes <= 64 * 16, "one 16-byte piece per lane");
+  const int col = lane * 16;
+  while (c.s < x.S) {
+    const int64_t run_lo = c.excl + (int64_t)c.r * c.U;
+    if (run_lo >= seg_hi) break;
+    const int64_t run_last = run_lo + c.U - 1;
+    if (run_last >= seg_lo && run_last < seg_hi && c.L > 0 &&
+        (GS == 1 ? c.r % x.G : c.r % x.NG) == 0) {
+      const int64_t slot = nr.slots[c.s];
+      if (slot >= 0 && slot < (int64_t)x.num_blocks * B && col < kRowBytes) {
+        const int kvh = kv_head_of<GS>(c.r, x);
+        const int64_t src = ((int64_t)c.s * x.Hkv + kvh) * kRowBytes + col;
+        const int64_t dst = (((slot / B) * x.Hkv + kvh) * B + slot % B) * kRowBytes + col;
+        const uint4 k = *reinterpret_cast<const uint4*>(nr.k + src);
+        const uint4 v = *reinterpret_cast<const uint4*>(nr.v + src);
+        *reinterpret_cast<uint4*>(nr.kc + dst) = k;
+        *reinterpret_cast<uint4*>(nr.vc + dst) = v;
+      }
+    }
+    c.u = 0;
+    if (++c.r == x.R) {
+      c.r = 0;
+      c.excl += (int64_t)x.R * c.U;
+      set_text(c, x, c.s + 1);
+    }
+  }
 }
 
 template <int KT, int QT, int D, int GS>
@@ -483,13 +568,13 @@ __device__ __forceinline__ bool start_segment(const int32_t* __restrict__ ctx, i
   return true;
 }
 
-template <int KT, int QT, int D, int B, int GS>
+template <int KT, int QT, int D, int B, int GS, bool FUSED>
 __global__ __launch_bounds__(kThreads) void decode_partition(
     char* __restrict__ out, const char* __restrict__ q, const char* __restrict__ kc,
     const char* __restrict__ vc, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ ctx, int S, int H, int Hkv, int maxb, int num_blocks, int W,
     int seg_fixed, float scale_log2, float v_scale, int64_t* __restrict__ hdr,
-    int64_t* __restrict__ excl_out, float* __restrict__ partials) {
+    int64_t* __restrict__ excl_out, float* __restrict__ partials, NewRows nr) {
   const int lane = threadIdx.x & 63;
   Segment sg;
   Ctx x;
@@ -506,9 +591,22 @@ __global__ __launch_bounds__(kThreads) void decode_partition(
   State<KT, D, GS> st;
   st.reset();
   Buf<KT, QT, D, GS> A, Bb;
-  load_chunk<KT, QT, D, B, GS>(A, ld, x, kc, vc, q, tables, lane);
+  load_chunk<KT, QT, D, B, GS, FUSED>(A, ld, x, kc, vc, q, tables, nr, lane);
   advance(ld, x);
 
+  auto compute = [&](const Buf<KT, QT, D, GS>& b) {
+    compute_chunk<KT, QT, D, GS>(b, cur, st, sl, lane);
+    if constexpr (FUSED) {
+      using G = Geo<KT, D>;
+      if (writes_new_row<B, GS>(cur, x)) {
+        const int g = lane / G::LPR;
+#pragma unroll
+        for (int i = 0; i < G::NLD; ++i)
+          if (cur.u * kChunk + i * G::RPW + g == cur.L - 1)
+            store_new_piece<D, G::ELT, B, GS>(nr, cur, x, (lane % G::LPR) * 16, b.k[i], b.v[i]);
+      }
+    }
+  };
   auto finish = [&](int i) {
     // last chunk of the run, or of the segment
     if (cur.u == cur.U - 1 || i == n - 1)
@@ -520,24 +618,24 @@ __global__ __launch_bounds__(kThreads) void decode_partition(
   // flight while the current one is computed
   int i = 0;
   while (i + 2 < n) {
-    load_chunk<KT, QT, D, B, GS>(Bb, ld, x, kc, vc, q, tables, lane);
+    load_chunk<KT, QT, D, B, GS, FUSED>(Bb, ld, x, kc, vc, q, tables, nr, lane);
     advance(ld, x);
-    compute_chunk<KT, QT, D, GS>(A, cur, st, sl, lane);
+    compute(A);
     finish(i);
-    load_chunk<KT, QT, D, B, GS>(A, ld, x, kc, vc, q, tables, lane);
+    load_chunk<KT, QT, D, B, GS, FUSED>(A, ld, x, kc, vc, q, tables, nr, lane);
     advance(ld, x);
-    compute_chunk<KT, QT, D, GS>(Bb, cur, st, sl, lane);
+    compute(Bb);
     finish(i + 1);
     i += 2;
   }
   if (i + 1 < n) {
-    load_chunk<KT, QT, D, B, GS>(Bb, ld, x, kc, vc, q, tables, lane);
-    compute_chunk<KT, QT, D, GS>(A, cur, st, sl, lane);
+    load_chunk<KT, QT, D, B, GS, FUSED>(Bb, ld, x, kc, vc, q, tables, nr, lane);
+    compute(A);
     finish(i);
-    compute_chunk<KT, QT, D, GS>(Bb, cur, st, sl, lane);
+    compute(Bb);
     finish(i + 1);
   } else {
-    compute_chunk<KT, QT, D, GS>(A, cur, st, sl, lane);
+    compute(A);
     finish(i);
   }
 }
@@ -705,11 +803,12 @@ struct MmaState {
   }
 };
 
-template <int QT, int D, int B, int GS>
+template <int QT, int D, int B, int GS, bool FUSED>
 __device__ __forceinline__ void load_chunk_mma(MmaBuf<D>& b, const Cursor& c, const Ctx& x,
                                                const char* __restrict__ kc,
                                                const char* __restrict__ vc,
-                                               const int32_t* __restrict__ tables, int lane) {
+                                               const int32_t* __restrict__ tables,
+                                               const NewRows& nr, int lane) {
   constexpr int kRowBytes = D * 2;
   constexpr int64_t kTileBytes = (int64_t)B * kRowBytes;
   const int col = lane & 15, grp = lane >> 4;
@@ -729,10 +828,14 @@ __device__ __forceinline__ void load_chunk_mma(MmaBuf<D>& b, const Cursor& c, co
   b.bad = c.over || bad;
   if (bad) blk = 0;  // read block 0 instead; the result is poisoned
   const int64_t row = ((int64_t)blk * x.Hkv + kvh) * kTileBytes + (int64_t)(tc % B) * kRowBytes;
+  // fused write: the last position's rows come from k_new / v_new
+  const bool fresh = FUSED && tc == last;
+  const char* ksrc = fresh ? nr.k + ((int64_t)c.s * x.Hkv + kvh) * kRowBytes : kc + row;
+  const char* vsrc = fresh ? nr.v + ((int64_t)c.s * x.Hkv + kvh) * kRowBytes : vc + row;
 #pragma unroll
   for (int cc = 0; cc < D / 32; ++cc) {
-    b.k[cc] = load_stream(kc + row + (8 * grp + 32 * cc) * 2);
-    b.v[cc] = load_stream(vc + row + (8 * grp + 32 * cc) * 2);
+    b.k[cc] = load_stream(ksrc + (8 * grp + 32 * cc) * 2);
+    b.v[cc] = load_stream(vsrc + (8 * grp + 32 * cc) * 2);
   }
 }
 
@@ -839,13 +942,13 @@ __device__ __forceinline__ void flush_run_mma(MmaState<D>& st, const Cursor& c, 
   st.reset();
 }
 
-template <int QT, int D, int B, int GS>
+template <int QT, int D, int B, int GS, bool FUSED>
 __global__ __launch_bounds__(kThreads) void decode_partition_mma(
     char* __restrict__ out, const char* __restrict__ q, const char* __restrict__ kc,
     const char* __restrict__ vc, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ ctx, int S, int H, int Hkv, int maxb, int num_blocks, int W,
     int seg_fixed, float scale_log2, float v_scale, int64_t* __restrict__ hdr,
-    int64_t* __restrict__ excl_out, float* __restrict__ partials) {
+    int64_t* __restrict__ excl_out, float* __restrict__ partials, NewRows nr) {
   static_assert(GS == 4 || GS == 8, "4 or 8 query heads per wave");
   constexpr int VS = D + 16;
   using M = Mma16<QT>;
@@ -883,10 +986,11 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mma(
   };
 
   Cursor ld = cur;
+  const Cursor seg_first = cur;
   MmaState<D> st;
   st.reset();
   MmaBuf<D> A, Bb;
-  load_chunk_mma<QT, D, B, GS>(A, ld, x, kc, vc, tables, lane);
+  load_chunk_mma<QT, D, B, GS, FUSED>(A, ld, x, kc, vc, tables, nr, lane);
   advance(ld, x);
 
   auto step = [&](const MmaBuf<D>& b, int i) {
@@ -902,21 +1006,22 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mma(
   // while the current one is computed
   int i = 0;
   while (i + 2 < n) {
-    load_chunk_mma<QT, D, B, GS>(Bb, ld, x, kc, vc, tables, lane);
+    load_chunk_mma<QT, D, B, GS, FUSED>(Bb, ld, x, kc, vc, tables, nr, lane);
     advance(ld, x);
     step(A, i);
-    load_chunk_mma<QT, D, B, GS>(A, ld, x, kc, vc, tables, lane);
+    load_chunk_mma<QT, D, B, GS, FUSED>(A, ld, x, kc, vc, tables, nr, lane);
     advance(ld, x);
     step(Bb, i + 1);
     i += 2;
   }
   if (i + 1 < n) {
-    load_chunk_mma<QT, D, B, GS>(Bb, ld, x, kc, vc, tables, lane);
+    load_chunk_mma<QT, D, B, GS, FUSED>(Bb, ld, x, kc, vc, tables, nr, lane);
     step(A, i);
     step(Bb, i + 1);
   } else {
     step(A, i);
   }
+  if constexpr (FUSED) write_new_rows<D, 2, B, GS>(nr, seg_first, x, seg_lo, seg_hi, lane);
 }
 
 // ---- launch ------------------------------------------------------------------
@@ -942,35 +1047,49 @@ struct Launch {
   char* ws;
   Layout lay;
   hipStream_t st;
+  NewRows nr;  // fused new-token write when nr.k != nullptr
 };
 
+template <int KT, int QT, int D, int B, int GS, bool FUSED>
+void launch_partition(const Launch& a, int64_t* hdr, int64_t* excl, float* part) {
+  const int groups = (a.W + kWavesPerGroup - 1) / kWavesPerGroup;
+  if constexpr ((GS == 4 || GS == 8) && KT == QT && (KT == PA_F16 || KT == PA_BF16))
+    hipLaunchKernelGGL((decode_partition_mma<QT, D, B, GS, FUSED>), dim3(groups), dim3(kThreads),
+                       0, a.st, a.out, a.q, a.kc, a.vc, a.tables, a.ctx, a.S, a.H, a.Hkv, a.maxb,
+                       a.nb, a.W, a.seg_fixed, a.sl, a.v_scale, hdr, excl, part, a.nr);
+  else
+    hipLaunchKernelGGL((decode_partition<KT, QT, D, B, GS, FUSED>), dim3(groups), dim3(kThreads),
+                       0, a.st, a.out, a.q, a.kc, a.vc, a.tables, a.ctx, a.S, a.H, a.Hkv, a.maxb,
+                       a.nb, a.W, a.seg_fixed, a.sl, a.v_scale, hdr, excl, part, a.nr);
+}
+
 template <int KT, int QT, int D, int B, int GS>
-void launch(const Launch& a) {
+bool launch(const Launch& a) {
   int64_t* hdr = reinterpret_cast<int64_t*>(a.ws);
   int64_t* excl = reinterpret_cast<int64_t*>(a.ws + a.lay.excl_off);
   float* part = reinterpret_cast<float*>(a.ws + a.lay.part_off);
-  const int groups = (a.W + kWavesPerGroup - 1) / kWavesPerGroup;
-  if constexpr ((GS == 4 || GS == 8) && KT == QT && (KT == PA_F16 || KT == PA_BF16))
-    hipLaunchKernelGGL((decode_partition_mma<QT, D, B, GS>), dim3(groups), dim3(kThreads), 0, a.st,
-                       a.out, a.q, a.kc, a.vc, a.tables, a.ctx, a.S, a.H, a.Hkv, a.maxb, a.nb,
-                       a.W, a.seg_fixed, a.sl, a.v_scale, hdr, excl, part);
-  else
-    hipLaunchKernelGGL((decode_partition<KT, QT, D, B, GS>), dim3(groups), dim3(kThreads), 0,
-                       a.st, a.out, a.q, a.kc, a.vc, a.tables, a.ctx, a.S, a.H, a.Hkv, a.maxb,
-                       a.nb, a.W, a.seg_fixed, a.sl, a.v_scale, hdr, excl, part);
+  if (a.nr.k) {
+    // the fused write stores rows in the pools' own format: not for E4M3 pools, whose
+    // new rows arrive in 16 bits and are quantized by pa_kv_write_fp8
+    if constexpr (KT == QT) launch_partition<KT, QT, D, B, GS, true>(a, hdr, excl, part);
+    else return false;
+  } else {
+    launch_partition<KT, QT, D, B, GS, false>(a, hdr, excl, part);
+  }
   const int64_t pairs = (int64_t)a.S * a.H;
   const int mgroups = (int)((pairs + kWavesPerGroup - 1) / kWavesPerGroup);
   hipLaunchKernelGGL((decode_merge<QT, D, GS>), dim3(mgroups), dim3(kThreads), 0, a.st, a.out,
                      a.ctx, a.S, a.H, a.Hkv, a.maxb, B, a.v_scale, hdr, excl, part);
+  return true;
 }
 
 template <int KT, int QT, int D, int B>
 bool dispatch_gs(int GS, const Launch& a) {
   switch (GS) {
-    case 1: launch<KT, QT, D, B, 1>(a); return true;
-    case 2: launch<KT, QT, D, B, 2>(a); return true;
-    case 4: launch<KT, QT, D, B, 4>(a); return true;
-    case 8: launch<KT, QT, D, B, 8>(a); return true;
+    case 1: return launch<KT, QT, D, B, 1>(a);
+    case 2: return launch<KT, QT, D, B, 2>(a);
+    case 4: return launch<KT, QT, D, B, 4>(a);
+    case 8: return launch<KT, QT, D, B, 8>(a);
   }
   return false;
 }
