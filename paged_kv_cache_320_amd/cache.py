@@ -203,12 +203,25 @@ class PagedKVCache:
         return out
 
     def step(self, seqs: Sequence[int], k_new, v_new, q, max_blocks: Optional[int] = None,
-             partition_tokens: int = 0, scale: Optional[float] = None):
-        """One decode step for `seqs` (single layer). Returns (out, slots, pairs, host tables, lens)."""
+             partition_tokens: int = 0, scale: Optional[float] = None, fused: bool = True):
+        """One decode step for `seqs` (single layer). Returns (out, slots, pairs, host tables, lens).
+
+        With 16/32-bit pools the new rows are written inside the decode launch
+        (pa_decode_attention_write) unless fused=False; E4M3 pools write first."""
+        import torch
         slots, pairs, done = self.alloc.step_append(seqs)
         self.copy(pairs)
-        self.write(slots, k_new, v_new)
         bt, cl, t_host, lens = self.tables(seqs, max_blocks)
+        if fused and not self.fp8:
+            S, H, D = q.shape
+            mctx = int(lens.max())
+            out = torch.empty_like(q)
+            s = torch.as_tensor(np.asarray(slots, dtype=np.int64)).to(self.device)
+            L.pa_decode_attention_write(out, q, self.k[0], self.v[0], k_new, v_new, s, bt, cl,
+                                        mctx, self.workspace(S, H, mctx, partition_tokens),
+                                        partition_tokens=partition_tokens, scale=scale)
+            return out, slots, pairs, t_host, lens
+        self.write(slots, k_new, v_new)
         out = self.attend(q, bt, cl, int(lens.max()), partition_tokens=partition_tokens,
                           scale=scale)
         return out, slots, pairs, t_host, lens

@@ -256,9 +256,11 @@ __device__ __forceinline__ void load_chunk(Buf<KT, QT, D, GS>& b, const Cursor& 
       b.q[j][p] = *reinterpret_cast<const uint4*>(qrow + j * kQRowBytes + p * 16);
 }
 
-// Fused write in the vector kernel: when a writing run's last chunk is computed, the lanes
-// holding the new position's rows (just loaded from k_new / v_new) store them into their
-// place, if it is in the pool. The first run of each key/value head writes.
+// Fused write: when a writing run's last chunk is computed, the lanes holding the new
+// position's rows (just loaded from k_new / v_new) store them into their place, if it is
+// in the pool. The first run of each (text, key/value head) writes. The slot is read
+// through the scalar cache (a restrict kernel argument): a vector load there would make
+// the compiler wait for every load in flight, the next chunk's included.
 template <int B, int GS>
 __device__ __forceinline__ bool writes_new_row(const Cursor& c, const Ctx& x) {
   return c.L > 0 && c.u == c.U - 1 && (GS == 1 ? c.r % x.G : c.r % x.NG) == 0;
@@ -273,43 +275,6 @@ __device__ __forceinline__ void store_new_piece(const NewRows& nr, const Cursor&
   const int64_t row = ((slot / B) * x.Hkv + kvh) * B + slot % B;
   *reinterpret_cast<uint4*>(nr.kc + row * kRowBytes + col) = k;
   *reinterpret_cast<uint4*>(nr.vc + row * kRowBytes + col) = v;
-}
-
-// Fused write in the matrix-core kernel, after the segment's last chunk (stores inside
-// its streaming loop made the compiler's wait counts conservative): for every run whose last unit lies in
-// this segment, the first run of each key/value head copies the text's new key and value
-// rows from k_new / v_new into their place, when that place is in the pool. Each run's
-// last unit lies in exactly one segment, so each row is written once.
-template <int D, int ELT, int B, int GS>
-__device__ __forceinline__ void write_new_rows(const NewRows& nr, Cursor c, const Ctx& x,
-                                               int64_t seg_lo, int64_t seg_hi, int lane) {
-  constexpr int kRowBytes = D * ELT;
-  static_assert(kRowBytes <= 64 * 16, "one 16-byte piece per lane");
-  const int col = lane * 16;
-  while (c.s < x.S) {
-    const int64_t run_lo = c.excl + (int64_t)c.r * c.U;
-    if (run_lo >= seg_hi) break;
-    const int64_t run_last = run_lo + c.U - 1;
-    if (run_last >= seg_lo && run_last < seg_hi && c.L > 0 &&
-        (GS == 1 ? c.r % x.G : c.r % x.NG) == 0) {
-      const int64_t slot = nr.slots[c.s];
-      if (slot >= 0 && slot < (int64_t)x.num_blocks * B && col < kRowBytes) {
-        const int kvh = kv_head_of<GS>(c.r, x);
-        const int64_t src = ((int64_t)c.s * x.Hkv + kvh) * kRowBytes + col;
-        const int64_t dst = (((slot / B) * x.Hkv + kvh) * B + slot % B) * kRowBytes + col;
-        const uint4 k = *reinterpret_cast<const uint4*>(nr.k + src);
-        const uint4 v = *reinterpret_cast<const uint4*>(nr.v + src);
-        *reinterpret_cast<uint4*>(nr.kc + dst) = k;
-        *reinterpret_cast<uint4*>(nr.vc + dst) = v;
-      }
-    }
-    c.u = 0;
-    if (++c.r == x.R) {
-      c.r = 0;
-      c.excl += (int64_t)x.R * c.U;
-      set_text(c, x, c.s + 1);
-    }
-  }
 }
 
 template <int KT, int QT, int D, int GS>
@@ -574,7 +539,12 @@ __global__ __launch_bounds__(kThreads) void decode_partition(
     const char* __restrict__ vc, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ ctx, int S, int H, int Hkv, int maxb, int num_blocks, int W,
     int seg_fixed, float scale_log2, float v_scale, int64_t* __restrict__ hdr,
-    int64_t* __restrict__ excl_out, float* __restrict__ partials, NewRows nr) {
+    int64_t* __restrict__ excl_out, float* __restrict__ partials, NewRows nr_arg,
+    const int64_t* __restrict__ new_slots) {
+  // the slots as a restrict argument: the compiler may then read them through the scalar
+  // cache, which keeps the fused write's slot lookup out of the vector wait counts
+  NewRows nr = nr_arg;
+  nr.slots = new_slots;
   const int lane = threadIdx.x & 63;
   Segment sg;
   Ctx x;
@@ -948,8 +918,11 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mma(
     const char* __restrict__ vc, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ ctx, int S, int H, int Hkv, int maxb, int num_blocks, int W,
     int seg_fixed, float scale_log2, float v_scale, int64_t* __restrict__ hdr,
-    int64_t* __restrict__ excl_out, float* __restrict__ partials, NewRows nr) {
+    int64_t* __restrict__ excl_out, float* __restrict__ partials, NewRows nr_arg,
+    const int64_t* __restrict__ new_slots) {
   static_assert(GS == 4 || GS == 8, "4 or 8 query heads per wave");
+  NewRows nr = nr_arg;
+  nr.slots = new_slots;
   constexpr int VS = D + 16;
   using M = Mma16<QT>;
   typedef typename M::v8 v8;
@@ -986,7 +959,6 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mma(
   };
 
   Cursor ld = cur;
-  const Cursor seg_first = cur;
   MmaState<D> st;
   st.reset();
   MmaBuf<D> A, Bb;
@@ -996,6 +968,13 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mma(
   auto step = [&](const MmaBuf<D>& b, int i) {
     load_q(cur);
     compute_chunk_mma<QT, D>(b, cur, st, qv, vrow, scale_log2, lane);
+    if constexpr (FUSED) {
+      if (writes_new_row<B, GS>(cur, x) && cur.u * kChunk + col == cur.L - 1) {
+#pragma unroll
+        for (int cc = 0; cc < D / 32; ++cc)
+          store_new_piece<D, 2, B, GS>(nr, cur, x, (8 * grp + 32 * cc) * 2, b.k[cc], b.v[cc]);
+      }
+    }
     // last chunk of the run, or of the segment
     if (cur.u == cur.U - 1 || i == n - 1)
       flush_run_mma<QT, D, GS>(st, cur, x, seg_lo, seg_hi, w, out, partials, v_scale, lane);
@@ -1021,7 +1000,6 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mma(
   } else {
     step(A, i);
   }
-  if constexpr (FUSED) write_new_rows<D, 2, B, GS>(nr, seg_first, x, seg_lo, seg_hi, lane);
 }
 
 // ---- launch ------------------------------------------------------------------
@@ -1056,11 +1034,13 @@ void launch_partition(const Launch& a, int64_t* hdr, int64_t* excl, float* part)
   if constexpr ((GS == 4 || GS == 8) && KT == QT && (KT == PA_F16 || KT == PA_BF16))
     hipLaunchKernelGGL((decode_partition_mma<QT, D, B, GS, FUSED>), dim3(groups), dim3(kThreads),
                        0, a.st, a.out, a.q, a.kc, a.vc, a.tables, a.ctx, a.S, a.H, a.Hkv, a.maxb,
-                       a.nb, a.W, a.seg_fixed, a.sl, a.v_scale, hdr, excl, part, a.nr);
+                       a.nb, a.W, a.seg_fixed, a.sl, a.v_scale, hdr, excl, part, a.nr,
+                       a.nr.slots);
   else
     hipLaunchKernelGGL((decode_partition<KT, QT, D, B, GS, FUSED>), dim3(groups), dim3(kThreads),
                        0, a.st, a.out, a.q, a.kc, a.vc, a.tables, a.ctx, a.S, a.H, a.Hkv, a.maxb,
-                       a.nb, a.W, a.seg_fixed, a.sl, a.v_scale, hdr, excl, part, a.nr);
+                       a.nb, a.W, a.seg_fixed, a.sl, a.v_scale, hdr, excl, part, a.nr,
+                       a.nr.slots);
 }
 
 template <int KT, int QT, int D, int B, int GS>
