@@ -259,6 +259,172 @@ def cpu_baseline(w, d0, seconds: float, gpu_out0):
     }, err
 
 
+def unique_kv_bytes(tables, lens, B, Hkv, D, kv_elt) -> int:
+    """K and V bytes of the physical blocks a decode launch reads, each block once (blocks
+    shared by several texts counted once, with the most places any of them attends)."""
+    filled = {}
+    for t, L in zip(tables, lens):
+        for j in range((int(L) + B - 1) // B):
+            b = int(t[j])
+            filled[b] = max(filled.get(b, 0), min(B, int(L) - j * B))
+    return sum(filled.values()) * 2 * Hkv * D * kv_elt
+
+
+def bench_sharing(args, base) -> None:
+    """Parallel sampling / beam search: groups of texts share their prompt's blocks. Every
+    step each odd sample is replaced by a fork of its even partner (the pair then shares a
+    partly filled last block), one token is appended to every text (copy-on-write copies
+    for the first writer of a shared partial block) and every layer runs its block copies
+    and the fused write + decode. Reported on the unique physical bytes read (shared blocks
+    once) and, beside it, on the logical bytes (every text's tokens)."""
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from paged_kv_cache_320_amd import PagedKVCache, _lib as L, torch_dtype
+
+    K, W = args.steps, args.warmup
+    w = base.scaled(steps=K + W)
+    S, H, Hkv, D, B = w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size
+    NL = args.layers or 8
+    elt, kv_elt = ELT[w.dtype], ELT[w.pool_dtype]
+    log(f"setup: {w.name}, {NL} layers, drawing inputs on the GPU")
+    # one draw for every layer: the layers' pools are separate buffers; their values do
+    # not change what is read
+    d = wl.draw(w, device="cuda")
+    cache = PagedKVCache(w.num_blocks, B, Hkv, D, w.pool_dtype, layers=NL, device="cuda",
+                         free_order=d.free_order, fill=float("nan"))
+    ops = wl.script(w, d)
+    first_step = ops.index(("step", 0))
+    slot_of = {}
+
+    def host_op(op):
+        kind = op[0]
+        if kind == "add":
+            slot_of[op[1]] = cache.add()
+        elif kind == "fork":
+            slot_of[op[1]] = cache.fork(slot_of[op[2]])
+        elif kind == "free":
+            cache.free(slot_of.pop(op[1]))
+        elif kind in ("prefill", "suffix"):
+            ks = d.prefill_k if kind == "prefill" else d.suffix_k
+            vs = d.prefill_v if kind == "prefill" else d.suffix_v
+            if ks[op[2]].shape[0] == 0:
+                return
+            slots, pair = cache.alloc.append(slot_of[op[1]], int(ks[op[2]].shape[0]))
+            if pair[0] >= 0:
+                cache.copy([pair])
+            for li in range(NL):
+                cache.write(slots, ks[op[2]], vs[op[2]], layer=li)
+        else:
+            raise ValueError(kind)
+
+    for op in ops[:first_step]:
+        host_op(op)
+    step_ops, cur = [], []
+    for op in ops[first_step:]:
+        if op[0] == "step":
+            step_ops.append(cur)
+            cur = []
+        else:
+            cur.append(op)
+    torch.cuda.synchronize()
+
+    att0 = wl.attended_at_step0(w, d)
+    max_ctx_bound = max(att0) + K + W
+    max_blocks = (max_ctx_bound + B - 1) // B
+    ws = L.decode_workspace(S, H, D, max_ctx_bound, 0)
+    R = K + W
+    d_slots = torch.empty(S, dtype=torch.int64, device="cuda")
+    d_lens = torch.empty(S, dtype=torch.int32, device="cuda")
+    d_tables = torch.empty((S, max_blocks), dtype=torch.int32, device="cuda")
+    d_pairs = torch.empty((S, 2), dtype=torch.int32, device="cuda")
+    p_slots = [torch.empty(S, dtype=torch.int64, pin_memory=True) for _ in range(R)]
+    p_lens = [torch.empty(S, dtype=torch.int32, pin_memory=True) for _ in range(R)]
+    p_tables = [torch.empty((S, max_blocks), dtype=torch.int32, pin_memory=True) for _ in range(R)]
+    p_pairs = [torch.empty((S, 2), dtype=torch.int32, pin_memory=True) for _ in range(R)]
+    outs = [torch.empty((S, H, D), dtype=torch_dtype(w.dtype), device="cuda") for _ in range(NL)]
+    ev, logical, unique, copies = [], [], [], []
+
+    def step(i: int, timed: bool):
+        for op in step_ops[i]:
+            host_op(op)
+        seqs = [slot_of[s] for s in range(S)]
+        slots, pairs, done = cache.alloc.step_append(seqs)
+        p_slots[i].numpy()[:] = slots
+        L.pa_export_tables(cache.alloc.h, seqs, max_blocks, p_tables[i].numpy(),
+                           p_lens[i].numpy())
+        d_slots.copy_(p_slots[i], non_blocking=True)
+        d_lens.copy_(p_lens[i], non_blocking=True)
+        d_tables.copy_(p_tables[i], non_blocking=True)
+        if pairs:
+            p_pairs[i].numpy()[:len(pairs)] = np.asarray(pairs, dtype=np.int32)
+            d_pairs.copy_(p_pairs[i], non_blocking=True)
+            for li in range(NL):
+                L.pa_copy_blocks(cache.k[li], cache.v[li], d_pairs[:len(pairs)])
+        if timed:
+            lens = p_lens[i].numpy()
+            logical.append(decode_bytes(lens, H, D, B, elt, Hkv, kv_elt))
+            unique.append(unique_kv_bytes(p_tables[i].numpy(), lens, B, Hkv, D, kv_elt) +
+                          2 * S * H * D * elt + 4 * sum((int(x) + B - 1) // B for x in lens))
+            copies.append(len(pairs))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+        mctx = max_ctx_bound
+        for li in range(NL):
+            L.pa_decode_attention_write(outs[li], d.step_q[i], cache.k[li], cache.v[li],
+                                        d.step_k[i], d.step_v[i], d_slots, d_tables, d_lens,
+                                        mctx, ws)
+        if timed:
+            e1.record()
+            ev.append((e0, e1))
+
+    log(f"warmup {W} steps")
+    for i in range(W):
+        step(i, False)
+    torch.cuda.synchronize()
+    log(f"timing {K} steps")
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    quiet_gc()
+    t0.record()
+    for i in range(W, W + K):
+        step(i, True)
+    t1.record()
+    torch.cuda.synchronize()
+    gc.enable()
+    total_ms = t0.elapsed_time(t1)
+    launch_ms = [a.elapsed_time(b) / NL for a, b in ev]
+    avg = float(np.mean(launch_ms))
+    u_launch, l_launch = float(np.mean(unique)), float(np.mean(logical))
+    achieved = u_launch / (avg * 1e-3) / 1e9
+    value = sum(unique) * NL / (total_ms * 1e-3) / 1e9
+    log(f"step {total_ms / K * 1e3:.1f} us ({NL} layers, {np.mean(copies):.0f} block copies "
+        f"per layer), decode launch {avg * 1e3:.1f} us: unique {u_launch / 1e9:.2f} GB -> "
+        f"{achieved:.0f} GB/s = {achieved / HBM_PEAK_GBPS:.1%} of 8 TB/s; logical "
+        f"{l_launch / 1e9:.2f} GB -> {l_launch / (avg * 1e-3) / 1e9:.0f} GB/s")
+    line = {
+        "metric": "paged decode attention with shared prompt blocks: unique KV GB/s and % of HBM peak",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(total_ms / K, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded keys, values and queries; random block placement)",
+        "config": {"workload": w.name, "seqs": S, "groups": w.groups, "samples": w.samples,
+                   "prompt_len": w.prompt_len, "heads": H, "kv_heads": Hkv, "head_dim": D,
+                   "block_size": B, "pool_blocks": w.num_blocks, "layers_per_step": NL,
+                   "parallelism": "single GPU", "new_token_write": "fused into decode"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "pa_decode_attention_write = decode_partition (new-token write "
+                               "fused) + decode_merge",
+                     "avg_launch_us": round(avg * 1e3, 2), "bytes_per_launch": int(u_launch)},
+        "logical_gbps": round(l_launch / (avg * 1e-3) / 1e9, 1),
+        "logical_bytes_per_launch": int(l_launch),
+        "block_copies_per_layer_per_step": float(np.mean(copies)),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}   # dense fp16/bf16 matrix-core peak
 
 
@@ -505,6 +671,8 @@ def main():
     base = wl.BY_NAME[args.workload]
     if isinstance(base, wl.PromptWorkload):
         return bench_prompt(args, base)
+    if base.length_kind == "sharing":
+        return bench_sharing(args, base)
     assert base.length_kind in ("fixed", "uniform", "list"), \
         "bench.py times batches whose texts each decode one token per step (no forks)"
     kv_elt = ELT[base.pool_dtype]
