@@ -344,7 +344,7 @@ def bench_sharing(args, base) -> None:
     p_tables = [torch.empty((S, max_blocks), dtype=torch.int32, pin_memory=True) for _ in range(R)]
     p_pairs = [torch.empty((S, 2), dtype=torch.int32, pin_memory=True) for _ in range(R)]
     outs = [torch.empty((S, H, D), dtype=torch_dtype(w.dtype), device="cuda") for _ in range(NL)]
-    ev, logical, unique, copies = [], [], [], []
+    ev, logical, unique, copies, cev = [], [], [], [], []
 
     def step(i: int, timed: bool):
         for op in step_ops[i]:
@@ -360,8 +360,14 @@ def bench_sharing(args, base) -> None:
         if pairs:
             p_pairs[i].numpy()[:len(pairs)] = np.asarray(pairs, dtype=np.int32)
             d_pairs.copy_(p_pairs[i], non_blocking=True)
+            if timed:
+                c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                c0.record()
             for li in range(NL):
                 L.pa_copy_blocks(cache.k[li], cache.v[li], d_pairs[:len(pairs)])
+            if timed:
+                c1.record()
+                cev.append((c0, c1, len(pairs)))
         if timed:
             lens = p_lens[i].numpy()
             logical.append(decode_bytes(lens, H, D, B, elt, Hkv, kv_elt))
@@ -398,6 +404,12 @@ def bench_sharing(args, base) -> None:
     u_launch, l_launch = float(np.mean(unique)), float(np.mean(logical))
     achieved = u_launch / (avg * 1e-3) / 1e9
     value = sum(unique) * NL / (total_ms * 1e-3) / 1e9
+    copy_us = [a.elapsed_time(b) / NL * 1e3 for a, b, _ in cev]
+    copy_bytes = [2 * 2 * n * Hkv * B * D * kv_elt for _, _, n in cev]  # K and V, read + write
+    copy_gbps = (sum(copy_bytes) / (sum(copy_us) * 1e-6) / 1e9) if cev else None
+    if cev:
+        log(f"block copies: {np.mean(copy_us):.1f} us per layer ({np.mean(copy_bytes) / 1e6:.1f} MB "
+            f"read + written, {copy_gbps:.0f} GB/s)")
     log(f"step {total_ms / K * 1e3:.1f} us ({NL} layers, {np.mean(copies):.0f} block copies "
         f"per layer), decode launch {avg * 1e3:.1f} us: unique {u_launch / 1e9:.2f} GB -> "
         f"{achieved:.0f} GB/s = {achieved / HBM_PEAK_GBPS:.1%} of 8 TB/s; logical "
@@ -420,6 +432,8 @@ def bench_sharing(args, base) -> None:
         "logical_gbps": round(l_launch / (avg * 1e-3) / 1e9, 1),
         "logical_bytes_per_launch": int(l_launch),
         "block_copies_per_layer_per_step": float(np.mean(copies)),
+        "copy_blocks_us_per_layer": round(float(np.mean(copy_us)), 2) if cev else None,
+        "copy_blocks_gbps": round(copy_gbps, 1) if cev else None,
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
@@ -732,6 +746,7 @@ def main():
     qs = [[dl.step_q[i] for i in range(K + W)] for dl in draws]
     step_lens = []
     ev = []  # (start, end) events around every timed decode launch
+    wev = []  # the same around the separate new-token writes
     graphs = {}
 
     # 16- and 32-bit pools: each layer's new-token write runs inside its decode launch
@@ -799,12 +814,17 @@ def main():
         if pairs:
             for li in range(NL):
                 L.pa_copy_blocks(cache.k[li], cache.v[li], d_pairs[:len(pairs)])
-        if fused:
-            pass
-        elif i in graphs:
-            graphs[i][0].replay()
-        else:
-            write_all(i)
+        if not fused:
+            if timed:
+                w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                w0.record()
+            if i in graphs:
+                graphs[i][0].replay()
+            else:
+                write_all(i)
+            if timed:
+                w1.record()
+                wev.append((w0, w1))
         if timed:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
@@ -857,6 +877,9 @@ def main():
     achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
     traffic = measured_traffic(fused) if base.name == "opt13b_7x2048_f16_b16" else None
     log(f"host time per step (allocator, uploads, launches) {host_s / K * 1e6:.1f} us")
+    write_us = float(np.mean([a.elapsed_time(b) / NL * 1e3 for a, b in wev])) if wev else None
+    if wev:
+        log(f"separate new-token write: {write_us:.1f} us per layer")
     log(f"step {ms_per_step * 1e3:.1f} us ({NL} layers), decode launch {avg_launch_ms * 1e3:.1f} us "
         f"(min {min(launch_ms) * 1e3:.1f}), {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBPS:.1%} of 8 TB/s")
 
@@ -908,6 +931,7 @@ def main():
                                "pa_decode_attention = decode_partition + decode_merge",
                      "avg_launch_us": round(avg_launch_ms * 1e3, 2),
                      "bytes_per_launch": int(bytes_per_launch)},
+        "kv_write_us_per_layer": round(write_us, 2) if wev else None,
         "probe_read_gbps": round(probe, 1) if probe else None,
         "probe_same_pattern_gbps": round(tprobe, 1) if tprobe else None,
         "cpu_baseline": cpu,
