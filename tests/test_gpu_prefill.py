@@ -186,3 +186,46 @@ def test_scale_argument(native):
     assert_close(run_gpu(native, q, kc, vc, tables, L, qs, scale=0.3), want, "f16")
     with pytest.raises(native.PagedKVError):
         run_gpu(native, q, kc, vc, tables, L, qs, scale=-0.3)
+
+
+@pytest.mark.parametrize("w", __import__("workloads").PROMPT, ids=lambda w: w.name)
+def test_full_size_prompt_workload(native, w):
+    """The prompt-phase workloads at full size, in the launch configuration the bench times:
+    the prompts' keys and values (after the shared cached prefix, if any) in randomly placed
+    blocks, one pa_prefill_attention launch, and seeded sampled (row, head) outputs (every
+    text's first and last rows included) against the oracle computed row by row."""
+    import workloads as wl
+    say(f"prompt workload {w.name} (full size)")
+    d = wl.draw_prompt(w)
+    lens = list(d.prompt_lens)
+    S, H, Hkv, D, B = w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size
+    ctx = [w.prefix_len + n for n in lens]
+    nblk = [(L + B - 1) // B for L in ctx]
+    N = sum(nblk) + 3
+    rng = np.random.default_rng(w.seed)
+    perm = rng.permutation(N)
+    tables = np.full((S, max(nblk)), -1, dtype=np.int32)
+    kc = torch.full((N, Hkv, B, D), float("nan"), dtype=TD[w.dtype])
+    vc = torch.full((N, Hkv, B, D), float("nan"), dtype=TD[w.dtype])
+    off = 0
+    for s in range(S):
+        tables[s, :nblk[s]] = perm[off:off + nblk[s]]
+        off += nblk[s]
+        ks = torch.cat([d.prefix_k, d.prompt_k[s]])
+        vs = torch.cat([d.prefix_v, d.prompt_v[s]])
+        t = torch.arange(ks.shape[0])
+        blk = torch.from_numpy(tables[s].astype(np.int64))[t // B]
+        kc[blk, :, t % B] = ks
+        vc[blk, :, t % B] = vs
+    L = np.asarray(ctx, dtype=np.int32)
+    qs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    got = run_gpu(native, d.q, kc, vc, tables, L, qs, max_q=max(lens))
+    say("  GPU done")
+    sample = np.random.default_rng(w.seed + 1)
+    rows = [(int(sample.integers(qs[-1])), int(sample.integers(H))) for _ in range(48)]
+    rows += [(int(qs[s]), s % H) for s in range(S)] + [(int(qs[s + 1] - 1), (s + 1) % H)
+                                                        for s in range(S)]
+    want = prefill_attention(d.q, kc, vc, tables, L, qs, B, rows=rows)
+    g = got.to(torch.float64).numpy()
+    for r, h in rows:
+        assert_close(g[r, h], want[r, h], w.dtype, f"{w.name} row {r} head {h}")
