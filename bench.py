@@ -179,6 +179,32 @@ def run_probe(L, torch, gib=4):
     return gbps
 
 
+def run_volume_probe(L, torch, bytes_per_launch: int):
+    """A plain contiguous read of the decode's own volume per launch: each launch streams
+    the next disjoint range of a buffer of at least 4 GiB and 4 launches' worth, so the
+    launch's fixed costs (its ramp, the first loads' latency, the tail) weigh as they do in
+    the decode. Mean GB/s."""
+    per = (int(bytes_per_launch) + 4095) // 4096 * 4096
+    n = max(4 << 30, (4 * per + (1 << 30) - 1) >> 30 << 30)
+    buf = torch.empty(n // 2, dtype=torch.float16, device="cuda").normal_()
+    sink = torch.empty(L.pa_probe_sink_bytes(0), dtype=torch.uint8, device="cuda")
+    L.pa_stream_read_probe(buf[: per // 2], sink)  # checked call through the binding
+    torch.cuda.synchronize()
+    fn, stream = L.lib().pa_stream_read_probe, torch.cuda.current_stream().cuda_stream
+    calls = [(buf.data_ptr() + k * per, per, sink.data_ptr(), 0, stream) for k in range(n // per)]
+    for c in calls:  # first touch of every page outside the timed region
+        assert fn(*c) == 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for c in calls[1:]:
+        fn(*c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (len(calls) - 1)
+    del buf
+    return per / (ms * 1e-3) / 1e9
+
+
 def run_tile_probe(L, torch, tile_bytes: int, bytes_per_launch: int):
     """The decode's own read volume in randomly placed tiles of its (block, head) tile size:
     each launch reads a disjoint random set of tiles of a buffer of at least 4 GiB and 4
@@ -883,10 +909,13 @@ def main():
     log(f"step {ms_per_step * 1e3:.1f} us ({NL} layers), decode launch {avg_launch_ms * 1e3:.1f} us "
         f"(min {min(launch_ms) * 1e3:.1f}), {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBPS:.1%} of 8 TB/s")
 
-    probe = tprobe = None
+    probe = tprobe = vprobe = None
     if not args.no_probe:
         probe = run_probe(L, torch)
         log(f"stream-read probe: {probe:.0f} GB/s")
+        vprobe = run_volume_probe(L, torch, int(bytes_per_launch))
+        log(f"same-volume stream probe ({int(bytes_per_launch) >> 20} MiB per launch, "
+            f"contiguous): {vprobe:.0f} GB/s")
         tprobe = run_tile_probe(L, torch, B * D * kv_elt, int(bytes_per_launch))
         log(f"same-pattern probe ({int(bytes_per_launch) >> 20} MiB per launch in random "
             f"{B * D * kv_elt} B tiles): {tprobe:.0f} GB/s")
@@ -933,6 +962,7 @@ def main():
                      "bytes_per_launch": int(bytes_per_launch)},
         "kv_write_us_per_layer": round(write_us, 2) if wev else None,
         "probe_read_gbps": round(probe, 1) if probe else None,
+        "probe_same_volume_gbps": round(vprobe, 1) if vprobe else None,
         "probe_same_pattern_gbps": round(tprobe, 1) if tprobe else None,
         "cpu_baseline": cpu,
         "step0_max_abs_err_vs_oracle": err0,

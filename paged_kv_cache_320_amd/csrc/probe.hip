@@ -12,6 +12,8 @@ constexpr int kUnroll = 16;
 // Each workgroup reads its own contiguous range in 16-byte pieces, kUnroll non-temporal
 // loads in flight per lane (64 KiB per workgroup). Measured on this part: with 4 waves
 // per CU this pattern reads ~7.1 TB/s, plain loads or 4 loads in flight ~6.2-6.3 TB/s.
+// The range's last, partial group is issued at once too (lanes past the end re-read the
+// range's last piece, not counted), so a range of any length keeps its loads in flight.
 __global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __restrict__ buf,
                                                                int64_t pieces,
                                                                uint32_t* __restrict__ sink) {
@@ -29,9 +31,16 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __re
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) x ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
   }
-  for (; i < hi; i += kThreads) {
-    const u32x4 v = __builtin_nontemporal_load(p + i);
-    x ^= v.x ^ v.y ^ v.z ^ v.w;
+  if (lo < hi && i - threadIdx.x < hi) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const int64_t k = i + j * kThreads;
+      v[j] = __builtin_nontemporal_load(p + (k < hi ? k : hi - 1));
+    }
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j)
+      if (i + j * kThreads < hi) x ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
   }
   for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o);
   __shared__ uint32_t sh[kThreads / 64];

@@ -17,7 +17,8 @@ def sink_xor(sink) -> int:
     return xor_words(sink.cpu().numpy())
 
 
-@pytest.mark.parametrize("nbytes", [16, 4096 * 16 + 48, 3 << 20])
+@pytest.mark.parametrize("nbytes", [16, 4096 * 16 + 48, 3 << 20, (16 << 20) + 48,
+                                    (40 << 20) + 3 * 4096 + 16])
 def test_stream_read_probe_reads_every_word(native, nbytes):
     say(f"stream read probe {nbytes} B")
     g = torch.Generator().manual_seed(nbytes)
