@@ -241,6 +241,42 @@ int pa_decode_attention_write(void* out, const void* q, void* k_cache, void* v_c
                               int32_t partition_tokens, float scale, int32_t dtype,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* Decode over shared prompt blocks. Texts forked from one prompt (parallel sampling, beam
+ * search: "Shared, Copied on Write", the samples of one request hold the
+ * prompt's blocks in common) read those blocks once per group instead of once per text.
+ * Same result as pa_decode_attention (up to rounding: two softmax partials merged).
+ *   Group g: texts group_first[g] .. group_first[g] + group_count[g] - 1 (device int32
+ *   arrays [num_groups], like group_prefix), whose tables begin with the same
+ *   group_prefix[g] / block_size blocks (the caller's promise; the group's first member's
+ *   table row is read for them). group_prefix[g] is taken at most max_prefix_len and
+ *   every member's context length - 1 (each member keeps its newest token to itself),
+ *   rounded down to a block. At most 8 / (num_heads / num_kv_heads) members per group
+ *   (more are left out of the group; larger sharing sets: several groups over the same
+ *   blocks); group_first clamped into the batch. Groups must not overlap (a text in two
+ *   groups: result unspecified). Texts in no group decode as usual.
+ * Three passes on `stream`: group set-up, the groups' shared blocks (each key/value row
+ * read once for all members: the members' heads as one key/value head's 8 query heads),
+ * each text's own blocks with the shared part's softmax state folded in. No new-token
+ * write here (pa_kv_write first). dtype PA_F32, PA_F16 or PA_BF16; num_heads /
+ * num_kv_heads <= 8 (else PA_EUNSUPPORTED). num_groups 0: pa_decode_attention.
+ * workspace: pa_decode_prefix_workspace_bytes(...) bytes, 16-byte aligned, no
+ * initialization needed; overlapping calls on one workspace race. */
+size_t pa_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t block_size, int32_t max_context_len,
+                                        int32_t num_groups, int32_t max_prefix_len,
+                                        int32_t dtype);
+int pa_decode_attention_prefix(void* out, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, int32_t max_blocks_per_seq,
+                               int32_t max_context_len, int32_t num_groups,
+                               const int32_t* group_first, const int32_t* group_count,
+                               const int32_t* group_prefix, int32_t max_prefix_len, float scale,
+                               int32_t dtype, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 /* ---------------------------------------------------------------------------
  * Prefix caching ("What Came After": every full block gets a hash of its tokens and
  * of everything before them; a request that begins the same way reuses the blocks,

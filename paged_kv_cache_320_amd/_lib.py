@@ -55,6 +55,11 @@ SIGNATURES = {
     "pa_decode_attention_write": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                                  _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                                  _i32, ctypes.c_float, _i32, _vp, _sz, _vp]),
+    "pa_decode_prefix_workspace_bytes": (_sz, [_i32] * 9),
+    "pa_decode_attention_prefix": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                                  _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
+                                                  _vp, _i32, ctypes.c_float, _i32, _vp, _sz,
+                                                  _vp]),
     "pa_hash_blocks": (ctypes.c_int, [_vp, _i32, _i32, ctypes.c_uint64, _vp]),
     "pa_seq_add_cached": (ctypes.c_int, [_vp, _vp, _i32, _c_int32_p, _c_int32_p]),
     "pa_seq_cache_blocks": (ctypes.c_int, [_vp, _i32, _vp, _i32]),
@@ -362,6 +367,46 @@ def pa_decode_attention_write(out, q, k_cache, v_cache, k_new, v_new, slots, blo
         _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(slots, "slots"),
         _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), S, H, Hkv, D, B,
         N, int(block_tables.shape[1]), int(max_context_len), int(partition_tokens), float(scale),
+        dtype_code(q), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def pa_decode_prefix_workspace_bytes(num_seqs: int, num_heads: int, num_kv_heads: int,
+                                     head_dim: int, block_size: int, max_context_len: int,
+                                     num_groups: int, max_prefix_len: int, dtype: int) -> int:
+    n = lib().pa_decode_prefix_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+                                               block_size, max_context_len, num_groups,
+                                               max_prefix_len, dtype)
+    if n == 0:
+        raise PagedKVError(PA_EINVAL, pa_last_error())
+    return n
+
+
+def pa_decode_attention_prefix(out, q, k_cache, v_cache, block_tables, context_lens,
+                               max_context_len: int, group_first, group_count, group_prefix,
+                               max_prefix_len: int, workspace, scale: Optional[float] = None,
+                               stream=None) -> None:
+    """Decode where groups of texts share their tables' first blocks: group g is texts
+    group_first[g] .. + group_count[g] - 1 sharing group_prefix[g] tokens (int32 device
+    tensors [G]); the shared blocks are read once per group."""
+    S, H, D = q.shape
+    N, Hkv, B, Dk = k_cache.shape
+    assert Dk == D and tuple(out.shape) == (S, H, D) and out.dtype == q.dtype == k_cache.dtype
+    assert block_tables.shape[0] == S and context_lens.numel() == S
+    G = group_first.numel()
+    assert group_count.numel() == G and group_prefix.numel() == G
+    for t, name in ((group_first, "group_first"), (group_count, "group_count"),
+                    (group_prefix, "group_prefix")):
+        assert str(t.dtype) == "torch.int32", f"{name} must be int32"
+    if scale is None:
+        scale = D ** -0.5
+    _check(lib().pa_decode_attention_prefix(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), S, H, Hkv, D, B,
+        N, int(block_tables.shape[1]), int(max_context_len), G,
+        _dev(group_first, "group_first") if G else None,
+        _dev(group_count, "group_count") if G else None,
+        _dev(group_prefix, "group_prefix") if G else None, int(max_prefix_len), float(scale),
         dtype_code(q), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream)))
 

@@ -94,7 +94,8 @@ int decode_common(void* out, const void* q, const void* k_cache, const void* v_c
                   int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                   int32_t partition_tokens, float scale, float k_scale, float v_scale,
                   int32_t kv_dtype, int32_t q_dtype, void* workspace, size_t workspace_bytes,
-                  void* stream, const decode_impl::NewRows& nr = decode_impl::NewRows{}) {
+                  void* stream, const decode_impl::NewRows& nr = decode_impl::NewRows{},
+                  const decode_impl::Prefix& pf = decode_impl::Prefix{}) {
   if (head_dim != 64 && head_dim != 128)
     return fail(PA_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
   if (block_size != 4 && block_size != 8 && block_size != 16 && block_size != 32)
@@ -129,7 +130,7 @@ int decode_common(void* out, const void* q, const void* k_cache, const void* v_c
                  max_blocks_per_seq, num_blocks, (int)lay.W, partition_tokens / kChunk,
                  // scale * k_scale * log2(e): scores in the exp2 domain, key scale folded in
                  scale * k_scale * 1.4426950408889634f, v_scale,
-                 (char*)workspace, lay, (hipStream_t)stream, nr};
+                 (char*)workspace, lay, (hipStream_t)stream, nr, pf};
   const int GS = heads_per_wave(num_heads / num_kv_heads);
   bool done = false;
   const bool d64 = head_dim == 64;
@@ -205,4 +206,221 @@ extern "C" int pa_decode_attention_write(void* out, const void* q, void* k_cache
                        num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                        max_context_len, partition_tokens, scale, 1.0f, 1.0f, dtype, dtype,
                        workspace, workspace_bytes, stream, nr);
+}
+
+// ---- decode over shared prompt blocks --------------------------------------------
+//
+// Texts forked from one prompt (parallel sampling, beam search) hold the prompt's blocks
+// in common, and a plain decode reads those blocks once per text. Here the shared blocks
+// are read once per group: pass 1 attends every member's queries to the group's shared
+// blocks at once (the members' heads as the query heads of one key/value head, up to 8)
+// and keeps each member's (m, l, acc); pass 2 attends each text to its own blocks only
+// and folds that state in. Softmax over the union of the two token sets is the same
+// softmax, merged as the split-context partials are.
+
+namespace pagedkv {
+namespace {
+
+constexpr int kPrefixCols = 8;  // query heads per key/value head in pass 1
+
+struct PrefixLayout {
+  size_t decode_bytes, state_off, start_off, vfirst_off, vcount_off, vctx_off, vtab_off, vq_off,
+      bytes;
+  int maxbp;  // table entries per group (shared blocks at most)
+};
+
+int prefix_layout(int32_t S, int32_t H, int32_t Hkv, int32_t D, int32_t max_ctx, int32_t V,
+                  int32_t max_prefix, int32_t bsz, int32_t elt, PrefixLayout* pl) {
+  if (V < 1 || Hkv < 1 || H % Hkv != 0 || max_prefix < 0 || bsz < 1)
+    return fail(PA_EINVAL, "bad shared-prefix shape (num_groups %d, num_heads %d, num_kv_heads %d, "
+                "max_prefix_len %d, block_size %d)", V, H, Hkv, max_prefix, bsz);
+  Layout a, b;
+  int rc = layout(S, H, D, max_ctx, 0, &a);
+  if (rc != PA_OK) return rc;
+  rc = layout(V, Hkv * kPrefixCols, D, max_prefix, 0, &b);
+  if (rc != PA_OK) return rc;
+  pl->maxbp = max_prefix / bsz > 0 ? max_prefix / bsz : 1;
+  size_t off = align256(a.bytes > b.bytes ? a.bytes : b.bytes);
+  pl->decode_bytes = off;
+  pl->state_off = off;
+  off = align256(off + sizeof(float) * (size_t)S * H * (D + 4));
+  pl->start_off = off;
+  off = align256(off + sizeof(int32_t) * (size_t)S);
+  pl->vfirst_off = off;
+  off = align256(off + sizeof(int32_t) * (size_t)V);
+  pl->vcount_off = off;
+  off = align256(off + sizeof(int32_t) * (size_t)V);
+  pl->vctx_off = off;
+  off = align256(off + sizeof(int32_t) * (size_t)V);
+  pl->vtab_off = off;
+  off = align256(off + sizeof(int32_t) * (size_t)V * pl->maxbp);
+  pl->vq_off = off;
+  off = align256(off + (size_t)elt * V * Hkv * kPrefixCols * D);
+  pl->bytes = off;
+  return PA_OK;
+}
+
+// Every (text, head) state empty (m = -inf, l = 0, acc = 0); no text skips a start.
+__global__ void prefix_clear_kernel(float* __restrict__ state, int64_t n, int row,
+                                    int32_t* __restrict__ start, int S) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    state[i] = i % row == 0 ? -INFINITY : 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < S; i += stride)
+    start[i] = 0;
+}
+
+// One workgroup per group: its members (clamped into the batch, at most 8 / (H / Hkv)),
+// its shared length (at most every member's context less one token, so that each keeps
+// its newest token, at most max_prefix, rounded down to a block), the members' skipped
+// start, the group's table row (its first member's, past the shared blocks zero) and its
+// queries as a batch of Hkv * 8 query heads (column c of key/value head k: member
+// c / Gr's head k * Gr + c % Gr, Gr = H / Hkv; columns past the members zero).
+__global__ void prefix_prep_kernel(const int32_t* __restrict__ vfirst_in,
+                                   const int32_t* __restrict__ vcount_in,
+                                   const int32_t* __restrict__ vprefix_in,
+                                   const int32_t* __restrict__ ctx,
+                                   const int32_t* __restrict__ tables, const char* __restrict__ q,
+                                   int S, int H, int Hkv, int row_bytes, int maxb, int bsz,
+                                   int max_prefix, int maxbp, int32_t* __restrict__ vfirst,
+                                   int32_t* __restrict__ vcount, int32_t* __restrict__ vctx,
+                                   int32_t* __restrict__ vtables, char* __restrict__ vq,
+                                   int32_t* __restrict__ start) {
+  const int v = blockIdx.x;
+  const int Gr = H / Hkv;
+  __shared__ int sh[3];
+  if (threadIdx.x == 0) {
+    int f = vfirst_in[v];
+    f = f < 0 ? 0 : f >= S ? S - 1 : f;
+    int n = vcount_in[v];
+    const int most = kPrefixCols / Gr < S - f ? kPrefixCols / Gr : S - f;
+    n = n < 0 ? 0 : n > most ? most : n;
+    const int64_t capacity = (int64_t)maxb * bsz;
+    int64_t P = vprefix_in[v];
+    if (P > max_prefix) P = max_prefix;
+    for (int i = 0; i < n; ++i) {
+      int64_t L = ctx[f + i];
+      L = L < 0 ? 0 : L > capacity ? capacity : L;
+      if (P > L - 1) P = L - 1;
+    }
+    if (P < 0 || n == 0) P = 0;
+    P -= P % bsz;
+    sh[0] = f;
+    sh[1] = n;
+    sh[2] = (int)P;
+    vfirst[v] = f;
+    vcount[v] = n;
+    vctx[v] = (int)P;
+  }
+  __syncthreads();
+  const int f = sh[0], n = sh[1], P = sh[2];
+  for (int i = threadIdx.x; i < n; i += blockDim.x) start[f + i] = P;
+  const int nb = P / bsz;
+  for (int k = threadIdx.x; k < maxbp; k += blockDim.x)
+    vtables[(int64_t)v * maxbp + k] = k < nb ? tables[(int64_t)f * maxb + k] : 0;
+  const int pieces = row_bytes / 16;
+  const int total = Hkv * kPrefixCols * pieces;
+  for (int i = threadIdx.x; i < total; i += blockDim.x) {
+    const int hv = i / pieces, p = i - hv * pieces;
+    const int kvh = hv / kPrefixCols, c = hv - kvh * kPrefixCols, m = c / Gr;
+    uint4 val = make_uint4(0u, 0u, 0u, 0u);
+    if (m < n)
+      val = reinterpret_cast<const uint4*>(
+          q + ((int64_t)(f + m) * H + kvh * Gr + (c - m * Gr)) * row_bytes)[p];
+    reinterpret_cast<uint4*>(vq + ((int64_t)v * Hkv * kPrefixCols + hv) * row_bytes)[p] = val;
+  }
+}
+
+}  // namespace
+}  // namespace pagedkv
+
+extern "C" size_t pa_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                                   int32_t num_kv_heads, int32_t head_dim,
+                                                   int32_t block_size, int32_t max_context_len,
+                                                   int32_t num_groups, int32_t max_prefix_len,
+                                                   int32_t dtype) {
+  if (!dtype_ok(dtype)) return 0;
+  PrefixLayout pl;
+  if (prefix_layout(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, num_groups,
+                    max_prefix_len, block_size, elt_bytes(dtype), &pl) != PA_OK)
+    return 0;
+  return pl.bytes;
+}
+
+extern "C" int pa_decode_attention_prefix(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_groups,
+    const int32_t* group_first, const int32_t* group_count, const int32_t* group_prefix,
+    int32_t max_prefix_len, float scale, int32_t dtype, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  if (!dtype_ok(dtype)) return fail(PA_EINVAL, "dtype %d is not PA_F32/PA_F16/PA_BF16", dtype);
+  if (num_groups < 0) return fail(PA_EINVAL, "num_groups %d < 0", num_groups);
+  if (num_groups == 0)
+    return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                         num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                         max_blocks_per_seq, max_context_len, 0, scale, 1.0f, 1.0f, dtype, dtype,
+                         workspace, workspace_bytes, stream);
+  if (!group_first || !group_count || !group_prefix) return fail(PA_EINVAL, "null pointer");
+  if (((uintptr_t)group_first & 3u) || ((uintptr_t)group_count & 3u) ||
+      ((uintptr_t)group_prefix & 3u))
+    return fail(PA_EINVAL, "group arrays must be 4-byte aligned");
+  if (num_kv_heads < 1 || num_heads % num_kv_heads != 0)
+    return fail(PA_EINVAL, "num_heads %d is not a multiple of num_kv_heads %d", num_heads,
+                num_kv_heads);
+  if (num_heads / num_kv_heads > kPrefixCols)
+    return fail(PA_EUNSUPPORTED, "%d query heads per key/value head (at most %d share a read)",
+                num_heads / num_kv_heads, kPrefixCols);
+  // the plain decode's checks (shapes, pointers, alignment) before anything is launched
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
+  if (block_size != 4 && block_size != 8 && block_size != 16 && block_size != 32)
+    return fail(PA_EUNSUPPORTED, "block_size %d (supported: 4, 8, 16, 32)", block_size);
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !workspace)
+    return fail(PA_EINVAL, "null pointer");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(workspace))
+    return fail(PA_EINVAL, "out, q, pools and workspace must be 16-byte aligned");
+  if (num_seqs < 1 || max_blocks_per_seq < 1 || num_blocks < 1 || max_context_len < 0)
+    return fail(PA_EINVAL, "num_seqs, max_blocks_per_seq and num_blocks must be >= 1, "
+                "max_context_len >= 0");
+  PrefixLayout pl;
+  int rc = prefix_layout(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
+                         num_groups, max_prefix_len, block_size, elt_bytes(dtype), &pl);
+  if (rc != PA_OK) return rc;
+  if (workspace_bytes < pl.bytes)
+    return fail(PA_EINVAL, "workspace_bytes %zu < %zu required", workspace_bytes, pl.bytes);
+  char* ws = (char*)workspace;
+  float* state = (float*)(ws + pl.state_off);
+  int32_t* start = (int32_t*)(ws + pl.start_off);
+  int32_t* vfirst = (int32_t*)(ws + pl.vfirst_off);
+  int32_t* vcount = (int32_t*)(ws + pl.vcount_off);
+  int32_t* vctx = (int32_t*)(ws + pl.vctx_off);
+  int32_t* vtab = (int32_t*)(ws + pl.vtab_off);
+  char* vq = ws + pl.vq_off;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t nstate = (int64_t)num_seqs * num_heads * (head_dim + 4);
+  const int64_t want = (nstate + 255) / 256;
+  hipLaunchKernelGGL(prefix_clear_kernel, dim3((int)(want < 2048 ? want : 2048)), dim3(256), 0, st,
+                     state, nstate, head_dim + 4, start, num_seqs);
+  hipLaunchKernelGGL(prefix_prep_kernel, dim3(num_groups), dim3(256), 0, st, group_first,
+                     group_count, group_prefix, context_lens, block_tables, (const char*)q,
+                     num_seqs, num_heads, num_kv_heads, head_dim * elt_bytes(dtype),
+                     max_blocks_per_seq, block_size, max_prefix_len, pl.maxbp, vfirst, vcount,
+                     vctx, vtab, vq, start);
+  PA_HIP_CHECK(hipGetLastError());
+  // pass 1: the groups' shared blocks, states out
+  const decode_impl::Prefix p1{nullptr, state, vfirst, vcount, num_heads, 1};
+  rc = decode_common(out, vq, k_cache, v_cache, vtab, vctx, num_groups,
+                     num_kv_heads * kPrefixCols, num_kv_heads, head_dim, block_size, num_blocks,
+                     pl.maxbp, max_prefix_len, 0, scale, 1.0f, 1.0f, dtype, dtype, workspace,
+                     pl.decode_bytes, stream, decode_impl::NewRows{}, p1);
+  if (rc != PA_OK) return rc;
+  // pass 2: every text's own blocks, states folded in
+  const decode_impl::Prefix p2{start, state, nullptr, nullptr, num_heads, 2};
+  return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
+                       num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                       max_context_len, 0, scale, 1.0f, 1.0f, dtype, dtype, workspace,
+                       pl.decode_bytes, stream, decode_impl::NewRows{}, p2);
 }

@@ -92,8 +92,25 @@ struct Geo {
 struct Cursor {
   int s, r, u;      // text, run (head group) within the text, chunk within the run
   int U, L;         // chunks in the run, attended tokens (clamped to the table's capacity)
+  int toff;         // tokens skipped at the start of the text's table row (a block multiple)
   int over;         // context_lens[s] exceeded the table's capacity
   int64_t excl;     // number of the first unit of text s
+};
+
+// Shared-prefix decode (pa_decode_attention_prefix) runs the kernels twice. Mode 1 runs over
+// groups of texts whose tables begin with the same blocks: a group is one text of this
+// batch, its queries those of its members (query head c of key/value head k is member
+// c / Gr's head k * Gr + c % Gr, Gr = heads / Hkv), and each member's (m, l, acc) over
+// the shared blocks goes to its row of `state` [texts][heads][D + 4] instead of an
+// output. Mode 2 runs over every text's own blocks, from start[s] on, and folds the
+// text's state in before the output is formed. Mode 0: plain decode.
+struct Prefix {
+  const int32_t* __restrict__ start;   // mode 2: tokens skipped per text (block multiples)
+  float* state;                        // modes 1, 2
+  const int32_t* __restrict__ vfirst;  // mode 1: first member of each group
+  const int32_t* __restrict__ vcount;  // mode 1: members of each group
+  int heads;                           // mode 1: query heads per text of the real batch
+  int mode;
 };
 
 struct Ctx {
@@ -104,7 +121,36 @@ struct Ctx {
   int maxb, num_blocks;
   int64_t capacity;  // max_blocks_per_seq * block_size
   const int32_t* __restrict__ ctx;
+  Prefix pf;
 };
+
+// Tokens text s attends: its context length clamped into [0, capacity], less the tokens
+// its start skips (rounded down to a block, at most all of them). toff: the tokens
+// skipped, 0 when none is left to attend (so the row's first entry stays the one read).
+__device__ __forceinline__ int attended_len(const int32_t* __restrict__ ctx,
+                                            const int32_t* __restrict__ start, int s,
+                                            int64_t capacity, int bsz, int* toff, int* over) {
+  int L = ctx[s];
+  if (L < 0) L = 0;
+  *over = L > capacity;
+  if (L > capacity) L = (int)capacity;
+  int P = start ? start[s] : 0;
+  P = P < 0 ? 0 : P > L ? L : P;
+  P -= P % bsz;
+  *toff = L - P > 0 ? P : 0;
+  return L - P;
+}
+
+// Mode 1: the state row of group v's query head hv, or null for a column past its members.
+template <int D>
+__device__ __forceinline__ float* prefix_state_row(const Prefix& pf, int Hkv, int G, int v,
+                                                   int hv) {
+  const int kvh = hv / G, c = hv - kvh * G;
+  const int Gr = pf.heads / Hkv;
+  const int m = c / Gr;
+  if (m >= pf.vcount[v]) return nullptr;
+  return pf.state + ((int64_t)(pf.vfirst[v] + m) * pf.heads + kvh * Gr + (c - m * Gr)) * (D + 4);
+}
 
 // The step's new rows, for the fused write: k_new / v_new [S][Hkv][D] in the pools'
 // format, slots [S] (block * B + place), the pools to write.
@@ -118,12 +164,13 @@ struct NewRows {
 
 __device__ __forceinline__ void set_text(Cursor& c, const Ctx& x, int s) {
   c.s = s;
-  int L = s < x.S ? x.ctx[s] : 0;
-  if (L < 0) L = 0;
-  c.over = L > x.capacity;
-  if (c.over) L = (int)x.capacity;
-  c.L = L;
-  c.U = units_of(L);
+  if (s < x.S) {
+    c.L = attended_len(x.ctx, x.pf.start, s, x.capacity, (int)(x.capacity / x.maxb), &c.toff,
+                       &c.over);
+  } else {
+    c.L = c.toff = c.over = 0;
+  }
+  c.U = units_of(c.L);
 }
 
 __device__ __forceinline__ void advance(Cursor& c, const Ctx& x) {
@@ -189,7 +236,7 @@ __device__ __forceinline__ void load_chunk(Buf<KT, QT, D, GS>& b, const Cursor& 
   const int g = lane / G::LPR, lp = lane % G::LPR;
   const int kvh = kv_head_of<GS>(c.r, x);
   const int last = c.L > 0 ? c.L - 1 : 0;
-  const int32_t* trow = tables + (int64_t)c.s * x.maxb;
+  const int32_t* trow = tables + (int64_t)c.s * x.maxb + c.toff / B;
   const int t_first = c.u * kChunk;
   // fused write: the last position's rows come from k_new / v_new
   const int64_t new_row = ((int64_t)c.s * x.Hkv + kvh) * kRowBytes + lp * 16;
@@ -391,6 +438,33 @@ __device__ __forceinline__ void flush_run(State<KT, D, GS>& st, const Cursor& c,
       // the whole run is in this segment: finish it here
 #pragma unroll
       for (int j = 0; j < GS; ++j) {
+        if (x.pf.mode == 1) {
+          // shared blocks: the member's state, unnormalized
+          float* row = prefix_state_row<D>(x.pf, x.Hkv, x.G, c.s, h0 + j);
+          if (row) {
+            if (lane == 0) {
+              row[0] = st.m[j];
+              row[1] = st.l[j];
+            }
+            float4* a4 = reinterpret_cast<float4*>(row + 4 + lane * G::EPL);
+#pragma unroll
+            for (int e = 0; e < G::EPL; e += 4)
+              a4[e / 4] = make_float4(st.acc[j][e], st.acc[j][e + 1], st.acc[j][e + 2],
+                                      st.acc[j][e + 3]);
+          }
+          continue;
+        }
+        if (x.pf.mode == 2) {
+          // fold in the text's state over its shared blocks
+          const float* row = x.pf.state + ((int64_t)c.s * x.H + h0 + j) * (D + 4);
+          const float ms = row[0], M = fmaxf(st.m[j], ms);
+          const float mu = M == -INFINITY ? 0.f : M;
+          const float fa = fast_exp2(st.m[j] - mu), fb = fast_exp2(ms - mu);
+          st.l[j] = st.l[j] * fa + row[1] * fb;
+#pragma unroll
+          for (int e = 0; e < G::EPL; ++e)
+            st.acc[j][e] = st.acc[j][e] * fa + row[4 + lane * G::EPL + e] * fb;
+        }
         float o[G::EPL];
         const float inv = st.l[j] > 0.f ? v_scale / st.l[j] : 0.f;
         // 0 * acc: zeros when nothing was attended, NaN for a poisoned run
@@ -453,7 +527,8 @@ struct Segment {
 template <int B, int GS>
 __device__ __forceinline__ bool start_segment(const int32_t* __restrict__ ctx, int S, int H,
                                               int Hkv, int maxb, int num_blocks, int W,
-                                              int seg_fixed, int64_t* __restrict__ hdr,
+                                              int seg_fixed, const Prefix& pf,
+                                              int64_t* __restrict__ hdr,
                                               int64_t* __restrict__ excl_out, Segment& sg,
                                               Ctx& x, Cursor& cur) {
   __shared__ int64_t sh_red[kWavesPerGroup];
@@ -467,10 +542,8 @@ __device__ __forceinline__ bool start_segment(const int32_t* __restrict__ ctx, i
   const int Gq = H / Hkv;
   const int R = Hkv * (Gq / GS);
   auto units_at = [&](int i) -> int64_t {
-    int L = ctx[i];
-    if (L < 0) L = 0;
-    if (L > capacity) L = (int)capacity;
-    return (int64_t)R * units_of(L);
+    int toff, over;
+    return (int64_t)R * units_of(attended_len(ctx, pf.start, i, capacity, B, &toff, &over));
   };
 
   // ---- locate each wave's segment: total units, then an exclusive scan ----
@@ -523,7 +596,7 @@ __device__ __forceinline__ bool start_segment(const int32_t* __restrict__ ctx, i
   sg.seg_hi = sg.seg_lo + seg < total ? sg.seg_lo + seg : total;
   sg.n = (int)(sg.seg_hi - sg.seg_lo);
 
-  x = Ctx{S, H, Hkv, Gq, Gq / GS, R, maxb, num_blocks, capacity, ctx};
+  x = Ctx{S, H, Hkv, Gq, Gq / GS, R, maxb, num_blocks, capacity, ctx, pf};
   // values read from LDS are the same in every lane: keep them in scalar registers
   cur.excl = uniform64(sh_excl[wave]);
   set_text(cur, x, __builtin_amdgcn_readfirstlane(sh_seq[wave]));
@@ -540,7 +613,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition(
     const int32_t* __restrict__ ctx, int S, int H, int Hkv, int maxb, int num_blocks, int W,
     int seg_fixed, float scale_log2, float v_scale, int64_t* __restrict__ hdr,
     int64_t* __restrict__ excl_out, float* __restrict__ partials, NewRows nr_arg,
-    const int64_t* __restrict__ new_slots) {
+    const int64_t* __restrict__ new_slots, Prefix pf) {
   // the slots as a restrict argument: the compiler may then read them through the scalar
   // cache, which keeps the fused write's slot lookup out of the vector wait counts
   NewRows nr = nr_arg;
@@ -549,8 +622,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition(
   Segment sg;
   Ctx x;
   Cursor cur;
-  if (!start_segment<B, GS>(ctx, S, H, Hkv, maxb, num_blocks, W, seg_fixed, hdr, excl_out, sg,
-                            x, cur))
+  if (!start_segment<B, GS>(ctx, S, H, Hkv, maxb, num_blocks, W, seg_fixed, pf, hdr, excl_out,
+                            sg, x, cur))
     return;
   const int w = sg.w;
   const int64_t seg_lo = sg.seg_lo, seg_hi = sg.seg_hi;
@@ -619,15 +692,24 @@ __global__ __launch_bounds__(kThreads) void decode_partition(
 template <int QT, int D, int GS>
 __device__ __forceinline__ void merge_run(const float* __restrict__ partials, int64_t w0,
                                           int64_t w1, int64_t run_lo, int64_t seg, int j,
-                                          float v_scale, char* __restrict__ dst_row, int lane) {
+                                          float v_scale, char* __restrict__ dst_row, int lane,
+                                          const float* init = nullptr,
+                                          float* state_dst = nullptr) {
   constexpr int PER = D / 64;  // output elements per lane
   constexpr int UNROLL = 8;
   auto index_of = [&](int64_t w) -> int64_t {
     return partial_index<D, GS>(w, (w == w0 && run_lo != w0 * seg) ? 1 : 0, j);
   };
+  // init: a state (m, l, pad, pad, acc[D]) that comes first, before the partials
   float M = -INFINITY, den = 0.f, num[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) num[e] = 0.f;
+  if (init) {
+    M = init[0];
+    den = init[1];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) num[e] = init[4 + lane * PER + e];
+  }
   for (int64_t w = w0; w <= w1; w += UNROLL) {
     float m[UNROLL], l[UNROLL], a[UNROLL][PER];
 #pragma unroll
@@ -662,6 +744,16 @@ __device__ __forceinline__ void merge_run(const float* __restrict__ partials, in
     }
     M = mg;
   }
+  if (state_dst) {
+    // the merged state itself, unnormalized
+    if (lane == 0) {
+      state_dst[0] = M;
+      state_dst[1] = den;
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) state_dst[4 + lane * PER + e] = num[e];
+    return;
+  }
   float o[PER];
   const float inv = den > 0.f ? v_scale / den : 0.f;
   // 0 * num: NaN stays visible for a poisoned run
@@ -676,7 +768,7 @@ template <int QT, int D, int GS>
 __global__ __launch_bounds__(kThreads) void decode_merge(
     char* __restrict__ out, const int32_t* __restrict__ ctx, int S, int H, int Hkv, int maxb,
     int bsz, float v_scale, const int64_t* __restrict__ hdr, const int64_t* __restrict__ excl,
-    const float* __restrict__ partials) {
+    const float* __restrict__ partials, Prefix pf) {
   const int lane = threadIdx.x & 63;
   const int64_t pair =
       (int64_t)blockIdx.x * kWavesPerGroup + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -685,17 +777,21 @@ __global__ __launch_bounds__(kThreads) void decode_merge(
   const int Gq = H / Hkv, NG = Gq / GS;
   const int kvh = h / Gq, within = h - kvh * Gq;
   const int r = kvh * NG + within / GS, j = within % GS;
-  int L = ctx[s];
-  if (L < 0) L = 0;
-  const int64_t capacity = (int64_t)maxb * bsz;
-  if (L > capacity) L = (int)capacity;
+  int toff, over;
+  const int L = attended_len(ctx, pf.start, s, (int64_t)maxb * bsz, bsz, &toff, &over);
   const int U = units_of(L);
   const int64_t seg = hdr[1];
   const int64_t lo = excl[s] + (int64_t)r * U, hi = lo + U;
   const int64_t w0 = lo / seg, w1 = (hi - 1) / seg;
   if (w0 == w1) return;
+  if (pf.mode == 1) {
+    float* row = prefix_state_row<D>(pf, Hkv, Gq, s, h);
+    if (row) merge_run<QT, D, GS>(partials, w0, w1, lo, seg, j, v_scale, nullptr, lane, nullptr, row);
+    return;
+  }
+  const float* init = pf.mode == 2 ? pf.state + pair * (D + 4) : nullptr;
   merge_run<QT, D, GS>(partials, w0, w1, lo, seg, j, v_scale, out + pair * D * elt_size<QT>(),
-                       lane);
+                       lane, init);
 }
 
 // ---- shared key/value heads on the matrix cores --------------------------------
@@ -784,7 +880,7 @@ __device__ __forceinline__ void load_chunk_mma(MmaBuf<D>& b, const Cursor& c, co
   const int col = lane & 15, grp = lane >> 4;
   const int kvh = kv_head_of<GS>(c.r, x);
   const int last = c.L > 0 ? c.L - 1 : 0;
-  const int32_t* trow = tables + (int64_t)c.s * x.maxb;
+  const int32_t* trow = tables + (int64_t)c.s * x.maxb + c.toff / B;
   const int t = c.u * kChunk + col;
   const int tc = t < last ? t : last;
   int blk;
@@ -884,8 +980,34 @@ __device__ __forceinline__ void flush_run_mma(MmaState<D>& st, const Cursor& c, 
   const int64_t run_hi = run_lo + c.U;
   const int h0 = first_head_of<GS>(c.r, x);
   if (col < GS) {
-    if (run_lo >= seg_lo && run_hi <= seg_hi) {
+    if (run_lo >= seg_lo && run_hi <= seg_hi && x.pf.mode == 1) {
+      // shared blocks: the member's state, unnormalized
+      float* row = prefix_state_row<D>(x.pf, x.Hkv, x.G, c.s, h0 + col);
+      if (row) {
+        if (grp == 0) {
+          row[0] = st.m;
+          row[1] = l;
+        }
+#pragma unroll
+        for (int mt = 0; mt < D / 16; ++mt)
+          *reinterpret_cast<float4*>(row + 4 + 16 * mt + 4 * grp) =
+              make_float4(st.o[mt][0], st.o[mt][1], st.o[mt][2], st.o[mt][3]);
+      }
+    } else if (run_lo >= seg_lo && run_hi <= seg_hi) {
       // the whole run is in this segment: finish it here
+      if (x.pf.mode == 2) {
+        // fold in the text's state over its shared blocks
+        const float* row = x.pf.state + ((int64_t)c.s * x.H + h0 + col) * (D + 4);
+        const float ms = row[0], M = fmaxf(st.m, ms);
+        const float mu = M == -INFINITY ? 0.f : M;
+        const float fa = fast_exp2(st.m - mu), fb = fast_exp2(ms - mu);
+        l = l * fa + row[1] * fb;
+#pragma unroll
+        for (int mt = 0; mt < D / 16; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            st.o[mt][r] = st.o[mt][r] * fa + row[4 + 16 * mt + 4 * grp + r] * fb;
+      }
       const float inv = l > 0.f ? v_scale / l : 0.f;
       char* dst = out + ((int64_t)c.s * x.H + h0 + col) * D * elt_size<QT>();
 #pragma unroll
@@ -919,7 +1041,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mma(
     const int32_t* __restrict__ ctx, int S, int H, int Hkv, int maxb, int num_blocks, int W,
     int seg_fixed, float scale_log2, float v_scale, int64_t* __restrict__ hdr,
     int64_t* __restrict__ excl_out, float* __restrict__ partials, NewRows nr_arg,
-    const int64_t* __restrict__ new_slots) {
+    const int64_t* __restrict__ new_slots, Prefix pf) {
   static_assert(GS == 4 || GS == 8, "4 or 8 query heads per wave");
   NewRows nr = nr_arg;
   nr.slots = new_slots;
@@ -932,8 +1054,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mma(
   Segment sg;
   Ctx x;
   Cursor cur;
-  if (!start_segment<B, GS>(ctx, S, H, Hkv, maxb, num_blocks, W, seg_fixed, hdr, excl_out, sg,
-                            x, cur))
+  if (!start_segment<B, GS>(ctx, S, H, Hkv, maxb, num_blocks, W, seg_fixed, pf, hdr, excl_out,
+                            sg, x, cur))
     return;
   const int w = sg.w;
   const int64_t seg_lo = sg.seg_lo, seg_hi = sg.seg_hi;
@@ -1026,6 +1148,7 @@ struct Launch {
   Layout lay;
   hipStream_t st;
   NewRows nr;  // fused new-token write when nr.k != nullptr
+  Prefix pf;   // shared-prefix passes (mode 0: plain decode)
 };
 
 template <int KT, int QT, int D, int B, int GS, bool FUSED>
@@ -1035,12 +1158,12 @@ void launch_partition(const Launch& a, int64_t* hdr, int64_t* excl, float* part)
     hipLaunchKernelGGL((decode_partition_mma<QT, D, B, GS, FUSED>), dim3(groups), dim3(kThreads),
                        0, a.st, a.out, a.q, a.kc, a.vc, a.tables, a.ctx, a.S, a.H, a.Hkv, a.maxb,
                        a.nb, a.W, a.seg_fixed, a.sl, a.v_scale, hdr, excl, part, a.nr,
-                       a.nr.slots);
+                       a.nr.slots, a.pf);
   else
     hipLaunchKernelGGL((decode_partition<KT, QT, D, B, GS, FUSED>), dim3(groups), dim3(kThreads),
                        0, a.st, a.out, a.q, a.kc, a.vc, a.tables, a.ctx, a.S, a.H, a.Hkv, a.maxb,
                        a.nb, a.W, a.seg_fixed, a.sl, a.v_scale, hdr, excl, part, a.nr,
-                       a.nr.slots);
+                       a.nr.slots, a.pf);
 }
 
 template <int KT, int QT, int D, int B, int GS>
@@ -1059,7 +1182,7 @@ bool launch(const Launch& a) {
   const int64_t pairs = (int64_t)a.S * a.H;
   const int mgroups = (int)((pairs + kWavesPerGroup - 1) / kWavesPerGroup);
   hipLaunchKernelGGL((decode_merge<QT, D, GS>), dim3(mgroups), dim3(kThreads), 0, a.st, a.out,
-                     a.ctx, a.S, a.H, a.Hkv, a.maxb, B, a.v_scale, hdr, excl, part);
+                     a.ctx, a.S, a.H, a.Hkv, a.maxb, B, a.v_scale, hdr, excl, part, a.pf);
   return true;
 }
 
