@@ -371,6 +371,17 @@ def bench_sharing(args, base) -> None:
     p_pairs = [torch.empty((S, 2), dtype=torch.int32, pin_memory=True) for _ in range(R)]
     outs = [torch.empty((S, H, D), dtype=torch_dtype(w.dtype), device="cuda") for _ in range(NL)]
     ev, logical, unique, copies, cev = [], [], [], [], []
+    per_text = args.per_text_decode
+    if not per_text:
+        # texts are numbered group-major: group g is texts g*samples .. g*samples + samples - 1,
+        # whose tables begin with the prompt's blocks
+        G, J = w.groups, w.samples
+        g_first = torch.arange(0, S, J, dtype=torch.int32, device="cuda")
+        g_count = torch.full((G,), J, dtype=torch.int32, device="cuda")
+        g_prefix = torch.full((G,), w.prompt_len, dtype=torch.int32, device="cuda")
+        pws = torch.empty(L.pa_decode_prefix_workspace_bytes(
+            S, H, Hkv, D, B, max_ctx_bound, G, w.prompt_len, L.dtype_code(outs[0])),
+            dtype=torch.uint8, device="cuda")
 
     def step(i: int, timed: bool):
         for op in step_ops[i]:
@@ -403,10 +414,18 @@ def bench_sharing(args, base) -> None:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
         mctx = max_ctx_bound
-        for li in range(NL):
-            L.pa_decode_attention_write(outs[li], d.step_q[i], cache.k[li], cache.v[li],
-                                        d.step_k[i], d.step_v[i], d_slots, d_tables, d_lens,
-                                        mctx, ws)
+        if per_text:
+            for li in range(NL):
+                L.pa_decode_attention_write(outs[li], d.step_q[i], cache.k[li], cache.v[li],
+                                            d.step_k[i], d.step_v[i], d_slots, d_tables, d_lens,
+                                            mctx, ws)
+        else:
+            for li in range(NL):
+                L.pa_kv_write(cache.k[li], cache.v[li], d.step_k[i], d.step_v[i], d_slots)
+            for li in range(NL):
+                L.pa_decode_attention_prefix(outs[li], d.step_q[i], cache.k[li], cache.v[li],
+                                             d_tables, d_lens, mctx, g_first, g_count, g_prefix,
+                                             w.prompt_len, pws)
         if timed:
             e1.record()
             ev.append((e0, e1))
@@ -449,11 +468,15 @@ def bench_sharing(args, base) -> None:
         "config": {"workload": w.name, "seqs": S, "groups": w.groups, "samples": w.samples,
                    "prompt_len": w.prompt_len, "heads": H, "kv_heads": Hkv, "head_dim": D,
                    "block_size": B, "pool_blocks": w.num_blocks, "layers_per_step": NL,
-                   "parallelism": "single GPU", "new_token_write": "fused into decode"},
+                   "parallelism": "single GPU",
+                   "new_token_write": "fused into decode" if per_text else "pa_kv_write per layer",
+                   "shared_blocks": "read once per text" if per_text else "read once per group"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "pa_decode_attention_write = decode_partition (new-token write "
-                               "fused) + decode_merge",
+                     "kernel": ("pa_decode_attention_write = decode_partition (new-token "
+                                "write fused) + decode_merge") if per_text else
+                               ("pa_kv_write + pa_decode_attention_prefix (group set-up, shared "
+                                "blocks once per group, each text's own blocks, merge)"),
                      "avg_launch_us": round(avg * 1e3, 2), "bytes_per_launch": int(u_launch)},
         "logical_gbps": round(l_launch / (avg * 1e-3) / 1e9, 1),
         "logical_bytes_per_launch": int(l_launch),
@@ -680,6 +703,10 @@ def main():
     ap.add_argument("--separate-write", action="store_true",
                     help="write each layer's new token with pa_kv_write before its decode launch "
                          "instead of inside it (pa_decode_attention_write)")
+    ap.add_argument("--per-text-decode", action="store_true",
+                    help="shared-prompt workloads: every text streams its whole table "
+                         "(pa_decode_attention_write) instead of each group's shared blocks "
+                         "once (pa_kv_write, then pa_decode_attention_prefix)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each decode step's writes and decode launches from HIP graphs "
                          "captured for that step instead of launching them one by one")
