@@ -270,12 +270,14 @@ __global__ void prefix_clear_kernel(float* __restrict__ state, int64_t n, int ro
     start[i] = 0;
 }
 
-// One workgroup per group: its members (clamped into the batch, at most 8 / (H / Hkv)),
-// its shared length (at most every member's context less one token, so that each keeps
-// its newest token, at most max_prefix, rounded down to a block), the members' skipped
-// start, the group's table row (its first member's, past the shared blocks zero) and its
-// queries as a batch of Hkv * 8 query heads (column c of key/value head k: member
-// c / Gr's head k * Gr + c % Gr, Gr = H / Hkv; columns past the members zero).
+// One workgroup per (group, key/value head): its members (clamped into the batch, at most
+// 8 / (H / Hkv)), its shared length (at most every member's context less one token, so
+// that each keeps its newest token, at most max_prefix, rounded down to a block) and, from
+// the head-0 workgroup, the members' skipped start and the group's table row (its first
+// member's, past the shared blocks zero); every workgroup copies its key/value head's
+// queries into the group's batch of Hkv * 8 query heads (column c of key/value head k:
+// member c / Gr's head k * Gr + c % Gr, Gr = H / Hkv; columns past the members zero).
+// The members' lengths are read by one lane each and reduced across the wave.
 __global__ void prefix_prep_kernel(const int32_t* __restrict__ vfirst_in,
                                    const int32_t* __restrict__ vcount_in,
                                    const int32_t* __restrict__ vprefix_in,
@@ -286,10 +288,11 @@ __global__ void prefix_prep_kernel(const int32_t* __restrict__ vfirst_in,
                                    int32_t* __restrict__ vcount, int32_t* __restrict__ vctx,
                                    int32_t* __restrict__ vtables, char* __restrict__ vq,
                                    int32_t* __restrict__ start) {
-  const int v = blockIdx.x;
+  const int v = blockIdx.x, kvh = blockIdx.y;
   const int Gr = H / Hkv;
   __shared__ int sh[3];
-  if (threadIdx.x == 0) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
     int f = vfirst_in[v];
     f = f < 0 ? 0 : f >= S ? S - 1 : f;
     int n = vcount_in[v];
@@ -298,36 +301,48 @@ __global__ void prefix_prep_kernel(const int32_t* __restrict__ vfirst_in,
     const int64_t capacity = (int64_t)maxb * bsz;
     int64_t P = vprefix_in[v];
     if (P > max_prefix) P = max_prefix;
-    for (int i = 0; i < n; ++i) {
-      int64_t L = ctx[f + i];
+    int64_t keep = INT32_MAX;  // the members' lengths less one, smallest
+    if (lane < n) {
+      int64_t L = ctx[f + lane];
       L = L < 0 ? 0 : L > capacity ? capacity : L;
-      if (P > L - 1) P = L - 1;
+      keep = L - 1;
     }
+    for (int o = 32; o > 0; o >>= 1) {
+      const int64_t other = __shfl_xor(keep, o);
+      keep = other < keep ? other : keep;
+    }
+    if (P > keep) P = keep;
     if (P < 0 || n == 0) P = 0;
     P -= P % bsz;
-    sh[0] = f;
-    sh[1] = n;
-    sh[2] = (int)P;
-    vfirst[v] = f;
-    vcount[v] = n;
-    vctx[v] = (int)P;
+    if (lane == 0) {
+      sh[0] = f;
+      sh[1] = n;
+      sh[2] = (int)P;
+      if (kvh == 0) {
+        vfirst[v] = f;
+        vcount[v] = n;
+        vctx[v] = (int)P;
+      }
+    }
   }
   __syncthreads();
   const int f = sh[0], n = sh[1], P = sh[2];
-  for (int i = threadIdx.x; i < n; i += blockDim.x) start[f + i] = P;
-  const int nb = P / bsz;
-  for (int k = threadIdx.x; k < maxbp; k += blockDim.x)
-    vtables[(int64_t)v * maxbp + k] = k < nb ? tables[(int64_t)f * maxb + k] : 0;
+  if (kvh == 0) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) start[f + i] = P;
+    const int nb = P / bsz;
+    for (int k = threadIdx.x; k < maxbp; k += blockDim.x)
+      vtables[(int64_t)v * maxbp + k] = k < nb ? tables[(int64_t)f * maxb + k] : 0;
+  }
   const int pieces = row_bytes / 16;
-  const int total = Hkv * kPrefixCols * pieces;
+  const int total = kPrefixCols * pieces;
   for (int i = threadIdx.x; i < total; i += blockDim.x) {
-    const int hv = i / pieces, p = i - hv * pieces;
-    const int kvh = hv / kPrefixCols, c = hv - kvh * kPrefixCols, m = c / Gr;
+    const int c = i / pieces, p = i - c * pieces, m = c / Gr;
     uint4 val = make_uint4(0u, 0u, 0u, 0u);
     if (m < n)
       val = reinterpret_cast<const uint4*>(
           q + ((int64_t)(f + m) * H + kvh * Gr + (c - m * Gr)) * row_bytes)[p];
-    reinterpret_cast<uint4*>(vq + ((int64_t)v * Hkv * kPrefixCols + hv) * row_bytes)[p] = val;
+    reinterpret_cast<uint4*>(
+        vq + (((int64_t)v * Hkv + kvh) * kPrefixCols + c) * row_bytes)[p] = val;
   }
 }
 
@@ -404,8 +419,8 @@ extern "C" int pa_decode_attention_prefix(
   const int64_t want = (nstate + 255) / 256;
   hipLaunchKernelGGL(prefix_clear_kernel, dim3((int)(want < 2048 ? want : 2048)), dim3(256), 0, st,
                      state, nstate, head_dim + 4, start, num_seqs);
-  hipLaunchKernelGGL(prefix_prep_kernel, dim3(num_groups), dim3(256), 0, st, group_first,
-                     group_count, group_prefix, context_lens, block_tables, (const char*)q,
+  hipLaunchKernelGGL(prefix_prep_kernel, dim3(num_groups, num_kv_heads), dim3(256), 0, st,
+                     group_first, group_count, group_prefix, context_lens, block_tables, (const char*)q,
                      num_seqs, num_heads, num_kv_heads, head_dim * elt_bytes(dtype),
                      max_blocks_per_seq, block_size, max_prefix_len, pl.maxbp, vfirst, vcount,
                      vctx, vtab, vq, start);

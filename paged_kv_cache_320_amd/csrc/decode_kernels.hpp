@@ -210,6 +210,10 @@ template <int KT, int D, int GS>
 struct State {
   float m[GS], l[GS];
   float acc[GS][Geo<KT, D>::EPL];
+  // shared-prefix mode 2: the text's state over its shared blocks, loaded with the run's
+  // last chunk so that folding it in waits for no load issued later
+  float fm[GS], fl[GS];
+  float facc[GS][Geo<KT, D>::EPL];
   __device__ __forceinline__ void reset() {
 #pragma unroll
     for (int j = 0; j < GS; ++j) {
@@ -455,15 +459,14 @@ __device__ __forceinline__ void flush_run(State<KT, D, GS>& st, const Cursor& c,
           continue;
         }
         if (x.pf.mode == 2) {
-          // fold in the text's state over its shared blocks
-          const float* row = x.pf.state + ((int64_t)c.s * x.H + h0 + j) * (D + 4);
-          const float ms = row[0], M = fmaxf(st.m[j], ms);
+          // fold in the text's state over its shared blocks (prefetched by load_fold)
+          const float ms = st.fm[j], M = fmaxf(st.m[j], ms);
           const float mu = M == -INFINITY ? 0.f : M;
           const float fa = fast_exp2(st.m[j] - mu), fb = fast_exp2(ms - mu);
-          st.l[j] = st.l[j] * fa + row[1] * fb;
+          st.l[j] = st.l[j] * fa + st.fl[j] * fb;
 #pragma unroll
           for (int e = 0; e < G::EPL; ++e)
-            st.acc[j][e] = st.acc[j][e] * fa + row[4 + lane * G::EPL + e] * fb;
+            st.acc[j][e] = st.acc[j][e] * fa + st.facc[j][e] * fb;
         }
         float o[G::EPL];
         const float inv = st.l[j] > 0.f ? v_scale / st.l[j] : 0.f;
@@ -493,6 +496,47 @@ __device__ __forceinline__ void flush_run(State<KT, D, GS>& st, const Cursor& c,
     }
   }
   st.reset();
+}
+
+// Mode 2: the state row (of the run's first query head; the GS rows follow it) that
+// flush_run folds in when the run whose last chunk the cursor c points at is finished
+// within this segment, else null. 16- and 32-bit pools only (the shared-prefix call
+// takes no E4M3 pools).
+template <int KT, int QT, int D, int GS>
+__device__ __forceinline__ const float* fold_row(const Cursor& c, const Ctx& x, int64_t seg_lo,
+                                                 int64_t seg_hi) {
+  if constexpr (KT != QT) {
+    return nullptr;
+  } else {
+    if (x.pf.mode != 2 || c.u != c.U - 1) return nullptr;
+    const int64_t run_lo = c.excl + (int64_t)c.r * c.U;
+    if (run_lo < seg_lo || run_lo + c.U > seg_hi) return nullptr;
+    return x.pf.state + ((int64_t)c.s * x.H + first_head_of<GS>(c.r, x)) * (D + 4);
+  }
+}
+
+// Load a state row set into st.fm / st.fl / st.facc (lane l holds the lane l % LPR slice,
+// the slice the first row group's lanes fold in).
+template <int KT, int D, int GS>
+__device__ __forceinline__ void load_fold(State<KT, D, GS>& st, const float* __restrict__ row,
+                                          int lane) {
+  using G = Geo<KT, D>;
+  const int lp = lane % G::LPR;
+#pragma unroll
+  for (int j = 0; j < GS; ++j) {
+    const float* r = row + j * (D + 4);
+    const float2 ml = *reinterpret_cast<const float2*>(r);
+    st.fm[j] = ml.x;
+    st.fl[j] = ml.y;
+#pragma unroll
+    for (int e = 0; e < G::EPL; e += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(r + 4 + lp * G::EPL + e);
+      st.facc[j][e] = a.x;
+      st.facc[j][e + 1] = a.y;
+      st.facc[j][e + 2] = a.z;
+      st.facc[j][e + 3] = a.w;
+    }
+  }
 }
 
 __device__ __forceinline__ int64_t uniform64(int64_t v) {
@@ -635,6 +679,10 @@ __global__ __launch_bounds__(kThreads) void decode_partition(
   st.reset();
   Buf<KT, QT, D, GS> A, Bb;
   load_chunk<KT, QT, D, B, GS, FUSED>(A, ld, x, kc, vc, q, tables, nr, lane);
+  {
+    const float* fr = fold_row<KT, QT, D, GS>(ld, x, seg_lo, seg_hi);
+    if (fr) load_fold<KT, D, GS>(st, fr, lane);
+  }
   advance(ld, x);
 
   auto compute = [&](const Buf<KT, QT, D, GS>& b) {
@@ -659,22 +707,30 @@ __global__ __launch_bounds__(kThreads) void decode_partition(
 
   // steady state: both loads unconditional, so the next chunk's loads stay in
   // flight while the current one is computed
+  // (a chunk's fold row is loaded once the chunk before it has been finished, which
+  // is when that chunk's own fold, if any, has been used)
   int i = 0;
   while (i + 2 < n) {
     load_chunk<KT, QT, D, B, GS, FUSED>(Bb, ld, x, kc, vc, q, tables, nr, lane);
+    const float* fb = fold_row<KT, QT, D, GS>(ld, x, seg_lo, seg_hi);
     advance(ld, x);
     compute(A);
     finish(i);
+    if (fb) load_fold<KT, D, GS>(st, fb, lane);
     load_chunk<KT, QT, D, B, GS, FUSED>(A, ld, x, kc, vc, q, tables, nr, lane);
+    const float* fa = fold_row<KT, QT, D, GS>(ld, x, seg_lo, seg_hi);
     advance(ld, x);
     compute(Bb);
     finish(i + 1);
+    if (fa) load_fold<KT, D, GS>(st, fa, lane);
     i += 2;
   }
   if (i + 1 < n) {
     load_chunk<KT, QT, D, B, GS, FUSED>(Bb, ld, x, kc, vc, q, tables, nr, lane);
+    const float* fb = fold_row<KT, QT, D, GS>(ld, x, seg_lo, seg_hi);
     compute(A);
     finish(i);
+    if (fb) load_fold<KT, D, GS>(st, fb, lane);
     compute(Bb);
     finish(i + 1);
   } else {
