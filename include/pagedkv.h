@@ -130,6 +130,44 @@ int pa_num_free(const pa_alloc* a, int32_t* n_out);
 int pa_alloc_stats(const pa_alloc* a, int64_t* used_blocks, int64_t* filled_slots);
 
 /* ---------------------------------------------------------------------------
+ * Swapping to host memory («The KV Cache and PagedAttention», "When Memory Runs Out":
+ * when blocks run short, a text gives up all of its blocks at once; one answer is to
+ * move them to the CPU's memory and back when the text's turn comes).
+ *
+ * The allocator keeps a second pool of num_host_blocks blocks in host memory, a stack
+ * like the device free list (free_order[0] handed out first, else block 0). Swapping
+ * a list of texts moves every block they hold: each distinct block once (texts in list
+ * order, logical blocks in order, first occurrence), so blocks the listed texts share
+ * stay shared on the other side, with a count of the listed texts holding them. Blocks
+ * also held by texts not listed are copied and stay where they are for those texts.
+ * The caller moves the bytes with pa_swap_blocks, out before the device blocks are
+ * reused, in before the texts are next attended. A swapped-out text cannot be appended
+ * to, forked, exported or registered (PA_EINVAL); pa_seq_free releases its host blocks;
+ * pa_seq_info and pa_seq_block_table report its host blocks.
+ * ------------------------------------------------------------------------- */
+/* Set up the host pool once (PA_EINVAL if already set up). free_order: NULL or a
+ * permutation of 0..num_host_blocks-1. */
+int pa_alloc_host_pool(pa_alloc* a, int32_t num_host_blocks, const int32_t* free_order);
+/* Move texts seqs[0..n-1] (live, resident, each listed once) to host blocks. pairs_out
+ * [cap][2] receives (device block, host block) per distinct block; *num_pairs_out their
+ * number. Device blocks no text holds any more return to the free list in that order
+ * (as pa_seq_free releases them). All-or-nothing: PA_ENOBLOCKS if the host pool has too
+ * few free blocks, PA_EINVAL if cap is too small; nothing changes then. */
+int pa_swap_out(pa_alloc* a, const int32_t* seqs, int32_t n, int32_t* pairs_out, int32_t cap,
+                int32_t* num_pairs_out);
+/* Bring swapped-out texts back: pairs_out receives (host block, device block) per
+ * distinct host block, device blocks taken from the free list's top in that order;
+ * host blocks no text holds any more return to the host stack in that order.
+ * All-or-nothing as pa_swap_out (PA_ENOBLOCKS: too few free device blocks). */
+int pa_swap_in(pa_alloc* a, const int32_t* seqs, int32_t n, int32_t* pairs_out, int32_t cap,
+               int32_t* num_pairs_out);
+/* 1 if `seq` is swapped out, else 0. */
+int pa_seq_swapped(const pa_alloc* a, int32_t seq, int32_t* swapped_out);
+/* Count of a host block (0 = free), and the free host blocks. */
+int pa_host_block_ref(const pa_alloc* a, int32_t block, int32_t* ref_out);
+int pa_host_num_free(const pa_alloc* a, int32_t* n_out);
+
+/* ---------------------------------------------------------------------------
  * Device cache writes.
  * ------------------------------------------------------------------------- */
 
@@ -149,6 +187,22 @@ int pa_kv_write(void* k_cache, void* v_cache, const void* k_new, const void* v_n
  * A pair with an index outside [0, num_blocks) is skipped. dtype may be PA_FP8_E4M3. */
 int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
                    int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t block_size, int32_t dtype, void* stream);
+
+/* Move whole blocks between two pools of the same shape, for swapping ("When Memory Runs
+ * Out"): for each pair (src, dst) in order, block src of src_k / src_v is copied to block
+ * dst of dst_k / dst_v, bit for bit. One side is normally pinned host memory (hipHostMalloc;
+ * torch pin_memory), the other device memory; the kernel reads and writes host memory
+ * directly (one launch for all pairs). pairs: int32 [num_pairs][2] in device memory or
+ * pinned host memory. Every pointer is checked with hipPointerGetAttributes: device memory
+ * or pinned host memory, else PA_EINVAL (pageable host memory is refused before anything
+ * is launched). Pools: [num_src_blocks] / [num_dst_blocks] x [num_kv_heads][block_size]
+ * [head_dim], 16-byte aligned; the pools must not overlap. A pair with an index outside its
+ * pool is skipped. dtype may be PA_FP8_E4M3. Stream-ordered; host memory must stay
+ * allocated until the copy has finished. */
+int pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                   const int32_t* pairs, int32_t num_pairs, int32_t num_src_blocks,
+                   int32_t num_dst_blocks, int32_t num_kv_heads, int32_t head_dim,
                    int32_t block_size, int32_t dtype, void* stream);
 
 /* Like pa_kv_write into PA_FP8_E4M3 pools ("What Came After": the cache kept in 8-bit

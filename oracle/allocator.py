@@ -42,6 +42,23 @@ blocks). Readings where the page is silent:
     text's blocks the later ones first. Handing a registered block out again
     drops its registration (eviction).
 Without registered blocks every behaviour above is unchanged.
+
+Swapping (› "When Memory Runs Out": a text that gives way hands back all of
+its blocks; one of the paper's answers moves them to the CPU's memory and
+back when the text's turn comes). Readings where the page is silent:
+  * a second stack of host blocks, `free_order` as for the device pool;
+  * `swap_out(texts)` moves every block the listed texts hold, each distinct
+    block once (texts in list order, logical blocks in order, first
+    occurrence), so blocks they share stay shared on the host with the count
+    of listed holders; a block also held by a text not listed is copied and
+    stays on the device for it; device blocks nobody holds any more are
+    released as `free` releases them, in that order; `swap_in` is the mirror
+    image (device blocks from the top of the free stack, host blocks no text
+    holds any more back onto the host stack, in that order);
+  * both are all-or-nothing: too few free blocks on the receiving side
+    changes nothing;
+  * a swapped-out text cannot be appended to, forked, exported or
+    registered; freeing it releases its host blocks.
 """
 from __future__ import annotations
 
@@ -68,6 +85,10 @@ class BlockAllocator:
         self.next_id = 0
         self.hash_of: Dict[int, int] = {}    # registered block -> its hash
         self.block_of: Dict[int, int] = {}   # hash -> registered block
+        self.num_host_blocks = 0
+        self.host_free: List[int] = []       # top of stack = end of list
+        self.host_ref: List[int] = []
+        self.swapped: set = set()            # texts whose blocks are host blocks
 
     # -- texts --------------------------------------------------------------
     def add(self) -> int:
@@ -77,8 +98,13 @@ class BlockAllocator:
         self.filled[sid] = []
         return sid
 
+    def _resident(self, sid: int) -> None:
+        if sid in self.swapped:
+            raise ValueError(f"text {sid} is swapped out")
+
     def fork(self, parent: int) -> int:
         """A new text sharing every block of `parent`; each block's count + 1."""
+        self._resident(parent)
         child = self.add()
         self.blocks[child] = list(self.blocks[parent])
         self.filled[child] = list(self.filled[parent])
@@ -91,6 +117,7 @@ class BlockAllocator:
 
         (cow_src, cow_dst) is (-1, -1) when no block was copied.
         """
+        self._resident(sid)
         B = self.block_size
         blocks, filled = self.blocks[sid], self.filled[sid]
         if n == 0:
@@ -129,19 +156,99 @@ class BlockAllocator:
         self.ref[b] = 1
         return b
 
-    def free_seq(self, sid: int) -> None:
+    def _release(self, blocks: Sequence[int]) -> None:
+        """Device blocks whose count dropped to 0, in order, back onto the free stack."""
         cached = []
-        for b in self.blocks[sid]:
-            self.ref[b] -= 1
-            if self.ref[b] == 0:
-                if b in self.hash_of:
-                    cached.append(b)
-                else:
-                    self.free.append(b)
+        for b in blocks:
+            if b in self.hash_of:
+                cached.append(b)
+            else:
+                self.free.append(b)
         for b in reversed(cached):
             self.free.insert(0, b)  # bottom of the stack: handed out after all others
+
+    def free_seq(self, sid: int) -> None:
+        if sid in self.swapped:
+            for h in self.blocks[sid]:
+                self.host_ref[h] -= 1
+                if self.host_ref[h] == 0:
+                    self.host_free.append(h)
+            self.swapped.discard(sid)
+        else:
+            zero = []
+            for b in self.blocks[sid]:
+                self.ref[b] -= 1
+                if self.ref[b] == 0:
+                    zero.append(b)
+            self._release(zero)
         del self.blocks[sid]
         del self.filled[sid]
+
+    # -- swapping -----------------------------------------------------------
+    def host_pool(self, num_host_blocks: int, free_order: Optional[Sequence[int]] = None) -> None:
+        assert self.num_host_blocks == 0, "the host pool is set up once"
+        order = list(range(num_host_blocks)) if free_order is None else [int(b) for b in free_order]
+        assert sorted(order) == list(range(num_host_blocks))
+        self.num_host_blocks = num_host_blocks
+        self.host_free = list(reversed(order))
+        self.host_ref = [0] * num_host_blocks
+
+    def _holders(self, sids: Sequence[int], swapped: bool):
+        """Distinct blocks of the listed texts in first-seen order, and how many of the
+        listed texts hold each."""
+        assert self.num_host_blocks > 0, "no host pool"
+        assert len(set(sids)) == len(sids), "a text listed twice"
+        for sid in sids:
+            if (sid in self.swapped) != swapped:
+                raise ValueError(f"text {sid} is on the wrong side")
+        order, count = [], {}
+        for sid in sids:
+            for b in self.blocks[sid]:
+                if b not in count:
+                    count[b] = 0
+                    order.append(b)
+                count[b] += 1
+        return order, count
+
+    def swap_out(self, sids: Sequence[int]) -> List[Tuple[int, int]]:
+        """Move the texts to host blocks; returns (device block, host block) pairs."""
+        order, count = self._holders(sids, False)
+        if len(order) > len(self.host_free):
+            raise NoBlocks(f"need {len(order)} host blocks, {len(self.host_free)} free")
+        host_of, pairs, zero = {}, [], []
+        for b in order:
+            h = self.host_free.pop()
+            self.host_ref[h] = count[b]
+            host_of[b] = h
+            pairs.append((b, h))
+            self.ref[b] -= count[b]
+            if self.ref[b] == 0:
+                zero.append(b)
+        for sid in sids:
+            self.blocks[sid] = [host_of[b] for b in self.blocks[sid]]
+            self.swapped.add(sid)
+        self._release(zero)
+        return pairs
+
+    def swap_in(self, sids: Sequence[int]) -> List[Tuple[int, int]]:
+        """Bring the texts back to device blocks; returns (host block, device block) pairs."""
+        order, count = self._holders(sids, True)
+        if len(order) > len(self.free):
+            raise NoBlocks(f"need {len(order)} blocks, {len(self.free)} free")
+        dev_of, pairs = {}, []
+        for h in order:
+            b = self._take()
+            self.ref[b] = count[h]
+            dev_of[h] = b
+            pairs.append((h, b))
+        for sid in sids:
+            self.blocks[sid] = [dev_of[h] for h in self.blocks[sid]]
+            self.swapped.discard(sid)
+        for h in order:
+            self.host_ref[h] -= count[h]
+            if self.host_ref[h] == 0:
+                self.host_free.append(h)
+        return pairs
 
     # -- prefix caching -----------------------------------------------------
     def add_cached(self, hashes: Sequence[int]) -> Tuple[int, int]:
@@ -163,6 +270,7 @@ class BlockAllocator:
 
     def cache_blocks(self, sid: int, hashes: Sequence[int]) -> None:
         """Register the text's first len(hashes) blocks, which must be full."""
+        self._resident(sid)
         bl, fl = self.blocks[sid], self.filled[sid]
         if len(hashes) > len(bl) or any(f != self.block_size for f in fl[:len(hashes)]):
             raise ValueError("only full blocks of the text can be registered")
@@ -190,6 +298,7 @@ class BlockAllocator:
         tables = [[-1] * max_blocks for _ in sids]
         lens = []
         for i, sid in enumerate(sids):
+            self._resident(sid)
             bl = self.blocks[sid]
             assert len(bl) <= max_blocks
             tables[i][:len(bl)] = bl
@@ -203,6 +312,8 @@ class BlockAllocator:
         """(physical blocks in use, filled places over those blocks)."""
         seen = {}
         for sid, bl in self.blocks.items():
+            if sid in self.swapped:
+                continue
             for b, f in zip(bl, self.filled[sid]):
                 seen[b] = f
         return self.num_blocks - len(self.free), sum(seen.values())

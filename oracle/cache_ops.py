@@ -11,7 +11,11 @@ it shares, the block is copied and the write goes to the copy. The copy
 takes the whole block, keys and values, so the copy holds the same filled
 places as the original.
 
-Both are pure moves of stored numbers: the models copy element bit
+swap_blocks — › "When Memory Runs Out": a text that gives way can have its
+blocks moved to the CPU's memory and back; whole blocks move between two
+pools.
+
+All three are pure moves of stored numbers: the models copy element bit
 patterns and never convert them.
 """
 from __future__ import annotations
@@ -36,6 +40,19 @@ def copy_blocks(k_cache, v_cache, pairs) -> None:
     for src, dst in pairs:
         k_cache[int(dst)] = k_cache[int(src)].clone()
         v_cache[int(dst)] = v_cache[int(src)].clone()
+
+
+def swap_blocks(dst_k, dst_v, src_k, src_v, pairs) -> None:
+    """Whole blocks from one pool pair to another («The KV Cache and PagedAttention» ›
+    "When Memory Runs Out": a text's blocks moved to the CPU's memory and back): pairs
+    applied in order, dst[d] = src[s] for K and V; a pair naming a block outside its
+    pool moves nothing."""
+    for src, dst in pairs:
+        src, dst = int(src), int(dst)
+        if not (0 <= src < src_k.shape[0] and 0 <= dst < dst_k.shape[0]):
+            continue
+        dst_k[dst] = src_k[src].clone()
+        dst_v[dst] = src_v[src].clone()
 
 
 def quantize_rows(x, scale: float):

@@ -71,6 +71,14 @@ SIGNATURES = {
                                                _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float,
                                                ctypes.c_float, ctypes.c_float, _i32, _vp, _sz,
                                                _vp]),
+    "pa_alloc_host_pool": (ctypes.c_int, [_vp, _i32, _c_int32_p]),
+    "pa_swap_out": (ctypes.c_int, [_vp, _c_int32_p, _i32, _c_int32_p, _i32, _c_int32_p]),
+    "pa_swap_in": (ctypes.c_int, [_vp, _c_int32_p, _i32, _c_int32_p, _i32, _c_int32_p]),
+    "pa_seq_swapped": (ctypes.c_int, [_vp, _i32, _c_int32_p]),
+    "pa_host_block_ref": (ctypes.c_int, [_vp, _i32, _c_int32_p]),
+    "pa_host_num_free": (ctypes.c_int, [_vp, _c_int32_p]),
+    "pa_swap_blocks": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                      _i32, _vp]),
     "pa_probe_sink_bytes": (_sz, [_i32]),
     "pa_stream_read_probe": (ctypes.c_int, [_vp, _sz, _vp, _i32, _vp]),
     "pa_tile_read_probe": (ctypes.c_int, [_vp, _sz, _i32, _vp, ctypes.c_int64, _vp, _vp]),
@@ -246,6 +254,52 @@ def pa_cache_stats(h) -> Tuple[int, int]:
     return r.value, f.value
 
 
+# ---- swapping to host memory (host) ---------------------------------------------
+
+def pa_alloc_host_pool(h, num_host_blocks: int, free_order: Optional[Sequence[int]] = None) -> None:
+    arr = (ctypes.c_int32 * num_host_blocks)(*free_order) if free_order is not None else None
+    _check(lib().pa_alloc_host_pool(h, num_host_blocks, arr))
+
+
+def _swap(fn, h, seqs: Sequence[int], cap: Optional[int]) -> List[Tuple[int, int]]:
+    n = len(seqs)
+    if cap is None:
+        cap = sum(pa_seq_info(h, s)[1] for s in seqs)
+    arr = (ctypes.c_int32 * max(n, 1))(*seqs)
+    pairs = (ctypes.c_int32 * max(2 * cap, 2))()
+    k = ctypes.c_int32()
+    _check(fn(h, arr, n, pairs, cap, ctypes.byref(k)))
+    return [(pairs[2 * i], pairs[2 * i + 1]) for i in range(k.value)]
+
+
+def pa_swap_out(h, seqs: Sequence[int], cap: Optional[int] = None) -> List[Tuple[int, int]]:
+    """(device block, host block) pairs; cap defaults to the texts' block count."""
+    return _swap(lib().pa_swap_out, h, seqs, cap)
+
+
+def pa_swap_in(h, seqs: Sequence[int], cap: Optional[int] = None) -> List[Tuple[int, int]]:
+    """(host block, device block) pairs."""
+    return _swap(lib().pa_swap_in, h, seqs, cap)
+
+
+def pa_seq_swapped(h, seq: int) -> bool:
+    out = ctypes.c_int32()
+    _check(lib().pa_seq_swapped(h, seq, ctypes.byref(out)))
+    return bool(out.value)
+
+
+def pa_host_block_ref(h, block: int) -> int:
+    out = ctypes.c_int32()
+    _check(lib().pa_host_block_ref(h, block, ctypes.byref(out)))
+    return out.value
+
+
+def pa_host_num_free(h) -> int:
+    out = ctypes.c_int32()
+    _check(lib().pa_host_num_free(h, ctypes.byref(out)))
+    return out.value
+
+
 # ---- device operations ------------------------------------------------------
 
 def dtype_code(t) -> int:
@@ -303,6 +357,25 @@ def pa_copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
     _check(lib().pa_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                                 _dev(pairs, "pairs") if P else None, P, N, Hkv, D, B,
                                 dtype_code(k_cache), _stream(stream)))
+
+
+def pa_swap_blocks(dst_k, dst_v, src_k, src_v, pairs, stream=None) -> None:
+    """Pools [N, Hkv, B, D] of one shape but for N (one side pinned host memory, the other
+    on the device); pairs: int32 [P, 2] (source, destination) on the device or pinned.
+    The library itself refuses memory a kernel cannot reach."""
+    Ns, Hkv, B, D = src_k.shape
+    Nd = dst_k.shape[0]
+    assert tuple(dst_k.shape[1:]) == (Hkv, B, D) and dst_k.dtype == src_k.dtype
+    for t in (dst_k, dst_v, src_k, src_v):
+        if not t.is_contiguous():
+            raise ValueError("pools must be contiguous")
+    assert dst_v.shape == dst_k.shape and src_v.shape == src_k.shape
+    P = int(pairs.shape[0]) if pairs is not None else 0
+    if P and not pairs.is_contiguous():
+        raise ValueError("pairs must be contiguous")
+    _check(lib().pa_swap_blocks(dst_k.data_ptr(), dst_v.data_ptr(), src_k.data_ptr(),
+                                src_v.data_ptr(), pairs.data_ptr() if P else None, P, Ns, Nd,
+                                Hkv, D, B, dtype_code(src_k), _stream(stream)))
 
 
 def pa_decode_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,

@@ -92,6 +92,27 @@ class BlockAllocator:
     def cache_stats(self):
         return L.pa_cache_stats(self.h)
 
+    # swapping to host memory
+    def host_pool(self, num_host_blocks: int, free_order: Optional[Sequence[int]] = None) -> None:
+        L.pa_alloc_host_pool(self.h, num_host_blocks, free_order)
+
+    def swap_out(self, seqs: Sequence[int]):
+        """(device block, host block) pairs to move."""
+        return L.pa_swap_out(self.h, seqs)
+
+    def swap_in(self, seqs: Sequence[int]):
+        """(host block, device block) pairs to move."""
+        return L.pa_swap_in(self.h, seqs)
+
+    def swapped(self, seq: int) -> bool:
+        return L.pa_seq_swapped(self.h, seq)
+
+    def host_ref(self, block: int) -> int:
+        return L.pa_host_block_ref(self.h, block)
+
+    def host_num_free(self) -> int:
+        return L.pa_host_num_free(self.h)
+
 
 class PagedKVCache:
     """K/V pools [num_blocks, num_kv_heads, block_size, head_dim] per layer on one device.
@@ -146,6 +167,40 @@ class PagedKVCache:
         if n:
             self.write(slots, k, v, layer)
         return slots, pair
+
+    # ---- swapping to host memory ("When Memory Runs Out") -------------------
+    def host_pool(self, num_host_blocks: int, free_order: Optional[Sequence[int]] = None) -> None:
+        """Pinned host pools of num_host_blocks blocks per layer, for texts that give way."""
+        import torch
+        self.alloc.host_pool(num_host_blocks, free_order)
+        shape = (num_host_blocks, self.num_kv_heads, self.block_size, self.head_dim)
+        tdt = torch_dtype(self.dtype)
+        self.hk = [torch.empty(shape, dtype=tdt, pin_memory=True) for _ in self.k]
+        self.hv = [torch.empty(shape, dtype=tdt, pin_memory=True) for _ in self.k]
+
+    def swap_out(self, seqs: Sequence[int]):
+        """Move the texts' blocks (every layer) to the host pools; returns the pairs. The
+        freed device blocks may be handed out at once: the copies are stream-ordered before
+        any later write on this stream."""
+        pairs = self.alloc.swap_out(seqs)
+        self._move(pairs, to_host=True)
+        return pairs
+
+    def swap_in(self, seqs: Sequence[int]):
+        pairs = self.alloc.swap_in(seqs)
+        self._move(pairs, to_host=False)
+        return pairs
+
+    def _move(self, pairs, to_host: bool) -> None:
+        import torch
+        if not pairs:
+            return
+        p = torch.as_tensor(np.asarray(pairs, dtype=np.int32).reshape(-1, 2)).to(self.device)
+        for li in range(len(self.k)):
+            if to_host:
+                L.pa_swap_blocks(self.hk[li], self.hv[li], self.k[li], self.v[li], p)
+            else:
+                L.pa_swap_blocks(self.k[li], self.v[li], self.hk[li], self.hv[li], p)
 
     def write(self, slots, k, v, layer: int = 0) -> None:
         import torch

@@ -8,7 +8,8 @@
 //  "Shared, Copied on Write"   shared blocks carry reference counts; a sharer about to write
 //                              into a shared block gets a copy and the original's count drops.
 //  "When Memory Runs Out"      a text holds all of its blocks or none: an append that cannot
-//                              get every block it needs changes nothing.
+//                              get every block it needs changes nothing; texts that give way
+//                              move all their blocks to a pool in host memory and back.
 //  "What Came After"           prefix caching: full blocks registered under a chained hash of
 //                              their tokens are reused by texts that begin the same way;
 //                              registered blocks nobody holds are handed out last.
@@ -31,6 +32,7 @@ namespace {
 
 struct Seq {
   bool live = false;
+  bool swapped = false;         // blocks are host-pool blocks (pa_swap_out)
   std::vector<int32_t> blocks;  // physical block per logical block
   std::vector<int32_t> filled;  // places filled per logical block
   int64_t ctx = 0;              // tokens held
@@ -90,6 +92,10 @@ struct pa_alloc {
   std::unordered_map<uint64_t, int32_t> block_of;
   std::vector<uint64_t> hash_of;
   std::vector<char> registered;
+  // host pool for texts that give way (pa_swap_out / pa_swap_in)
+  int32_t num_host_blocks = 0;
+  FreeStack host_free;
+  std::vector<int32_t> host_ref;
 
   // Top of the free stack with count 1; a registered block loses its registration.
   int32_t take() {
@@ -100,6 +106,18 @@ struct pa_alloc {
     }
     ref[b] = 1;
     return b;
+  }
+
+  // Release device blocks whose count reached 0, in the order given: unregistered ones
+  // onto the top of the free stack, registered ones below every other free block (the
+  // later ones above the earlier), all above blocks freed before.
+  void release(const std::vector<int32_t>& zero) {
+    std::vector<int32_t> cached;
+    for (int32_t b : zero) {
+      if (registered[b]) cached.push_back(b);
+      else free_stack.push_top(b);
+    }
+    for (auto it = cached.rbegin(); it != cached.rend(); ++it) free_stack.push_bottom(*it);
   }
 
   Seq* find(int32_t id) {
@@ -205,6 +223,7 @@ int pa_seq_add(pa_alloc* a, int32_t* seq_out) {
 int pa_seq_fork(pa_alloc* a, int32_t parent, int32_t* child_out) {
   if (!a || !child_out) return fail(PA_EINVAL, "null argument");
   if (!a->find(parent)) return fail(PA_ENOSEQ, "unknown sequence %d", parent);
+  if (a->find(parent)->swapped) return fail(PA_EINVAL, "sequence %d is swapped out", parent);
   if (a->seqs.size() >= (size_t)INT32_MAX) return fail(PA_EINVAL, "sequence ids exhausted");
   Seq child = *a->find(parent);  // copy before emplace_back may reallocate
   for (int32_t b : child.blocks) a->ref[b] += 1;
@@ -220,6 +239,7 @@ int pa_seq_append(pa_alloc* a, int32_t seq, int32_t n_tokens, int64_t* slots_out
   if (n_tokens < 0) return fail(PA_EINVAL, "n_tokens %d < 0", n_tokens);
   Seq* s = a->find(seq);
   if (!s) return fail(PA_ENOSEQ, "unknown sequence %d", seq);
+  if (s->swapped) return fail(PA_EINVAL, "sequence %d is swapped out", seq);
   return a->append(*s, n_tokens, slots_out, cow_src, cow_dst);
 }
 
@@ -233,6 +253,7 @@ int pa_step_append(pa_alloc* a, const int32_t* seqs, int32_t n, int64_t* slots_o
   for (int32_t i = 0; i < n; ++i) {
     Seq* s = a->find(seqs[i]);
     if (!s) return fail(PA_ENOSEQ, "unknown sequence %d at batch index %d", seqs[i], i);
+    if (s->swapped) return fail(PA_EINVAL, "sequence %d is swapped out", seqs[i]);
     int32_t src, dst;
     int rc = a->append(*s, 1, &slots_out[i], &src, &dst);
     if (rc != PA_OK) return rc;
@@ -250,17 +271,15 @@ int pa_seq_free(pa_alloc* a, int32_t seq) {
   if (!a) return fail(PA_EINVAL, "null argument");
   Seq* s = a->find(seq);
   if (!s) return fail(PA_ENOSEQ, "unknown sequence %d", seq);
-  std::vector<int32_t> cached;
-  for (int32_t b : s->blocks) {
-    a->ref[b] -= 1;
-    if (a->ref[b] == 0) {
-      if (a->registered[b]) cached.push_back(b);
-      else a->free_stack.push_top(b);
-    }
+  if (s->swapped) {
+    for (int32_t b : s->blocks)
+      if (--a->host_ref[b] == 0) a->host_free.push_top(b);
+  } else {
+    std::vector<int32_t> zero;
+    for (int32_t b : s->blocks)
+      if (--a->ref[b] == 0) zero.push_back(b);
+    a->release(zero);
   }
-  // registered blocks go below every other free block: the text's later blocks above
-  // its earlier ones, all above blocks freed before
-  for (auto it = cached.rbegin(); it != cached.rend(); ++it) a->free_stack.push_bottom(*it);
   *s = Seq();  // live = false, storage released
   return ok();
 }
@@ -296,6 +315,7 @@ int pa_export_tables(const pa_alloc* a, const int32_t* seqs, int32_t n,
   for (int32_t i = 0; i < n; ++i) {
     const Seq* s = a->find(seqs[i]);
     if (!s) return fail(PA_ENOSEQ, "unknown sequence %d at batch index %d", seqs[i], i);
+    if (s->swapped) return fail(PA_EINVAL, "sequence %d is swapped out", seqs[i]);
     if ((int64_t)s->blocks.size() > max_blocks_per_seq)
       return fail(PA_EINVAL, "sequence %d has %zu blocks > max_blocks_per_seq %d", seqs[i],
                   s->blocks.size(), max_blocks_per_seq);
@@ -329,7 +349,7 @@ int pa_alloc_stats(const pa_alloc* a, int64_t* used_blocks, int64_t* filled_slot
   if (!a || !used_blocks || !filled_slots) return fail(PA_EINVAL, "null argument");
   std::vector<int32_t> filled(a->num_blocks, -1);
   for (const Seq& s : a->seqs) {
-    if (!s.live) continue;
+    if (!s.live || s.swapped) continue;
     for (size_t j = 0; j < s.blocks.size(); ++j) filled[s.blocks[j]] = s.filled[j];
   }
   int64_t f = 0;
@@ -401,6 +421,7 @@ int pa_seq_cache_blocks(pa_alloc* a, int32_t seq, const uint64_t* hashes, int32_
   if (!a || (n > 0 && !hashes)) return fail(PA_EINVAL, "null argument");
   Seq* s = a->find(seq);
   if (!s) return fail(PA_ENOSEQ, "unknown sequence %d", seq);
+  if (s->swapped) return fail(PA_EINVAL, "sequence %d is swapped out", seq);
   if (n < 0 || n > (int32_t)s->blocks.size())
     return fail(PA_EINVAL, "n %d outside [0, %zu]", n, s->blocks.size());
   for (int32_t j = 0; j < n; ++j)
@@ -426,6 +447,153 @@ int pa_cache_stats(const pa_alloc* a, int32_t* registered_out, int32_t* register
     }
   *registered_out = r;
   *registered_free_out = f;
+  return ok();
+}
+
+// ---- swapping to host memory ("When Memory Runs Out") ------------------------------
+
+int pa_alloc_host_pool(pa_alloc* a, int32_t num_host_blocks, const int32_t* free_order) {
+  if (!a) return fail(PA_EINVAL, "null argument");
+  if (a->num_host_blocks > 0) return fail(PA_EINVAL, "the host pool is already set up");
+  if (num_host_blocks < 1) return fail(PA_EINVAL, "num_host_blocks %d < 1", num_host_blocks);
+  if (free_order) {
+    std::vector<char> seen(num_host_blocks, 0);
+    for (int32_t i = 0; i < num_host_blocks; ++i) {
+      const int32_t b = free_order[i];
+      if (b < 0 || b >= num_host_blocks || seen[b])
+        return fail(PA_EINVAL, "free_order is not a permutation of 0..%d", num_host_blocks - 1);
+      seen[b] = 1;
+    }
+  }
+  a->num_host_blocks = num_host_blocks;
+  a->host_ref.assign(num_host_blocks, 0);
+  a->host_free.init(num_host_blocks);
+  for (int32_t i = 0; i < num_host_blocks; ++i)
+    a->host_free.push_bottom(free_order ? free_order[i] : i);
+  return ok();
+}
+
+// Checks shared by pa_swap_out and pa_swap_in: every listed text live, listed once, on the
+// side `swapped`; the blocks they hold in distinct first-seen order (texts in list order,
+// logical order within) with how many listed texts hold each.
+static int swap_plan(pa_alloc* a, const int32_t* seqs, int32_t n, bool swapped,
+                     std::vector<int32_t>* order, std::unordered_map<int32_t, int32_t>* holders) {
+  if (a->num_host_blocks < 1) return fail(PA_EINVAL, "no host pool (pa_alloc_host_pool)");
+  if (n < 0) return fail(PA_EINVAL, "n %d < 0", n);
+  if (n > 0 && !seqs) return fail(PA_EINVAL, "null argument");
+  std::unordered_map<int32_t, char> listed;
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq* s = a->find(seqs[i]);
+    if (!s) return fail(PA_ENOSEQ, "unknown sequence %d at list index %d", seqs[i], i);
+    if (s->swapped != swapped)
+      return fail(PA_EINVAL, "sequence %d is %s", seqs[i], swapped ? "not swapped out" :
+                  "already swapped out");
+    if (!listed.emplace(seqs[i], 1).second)
+      return fail(PA_EINVAL, "sequence %d is listed twice", seqs[i]);
+  }
+  for (int32_t i = 0; i < n; ++i)
+    for (int32_t b : a->find(seqs[i])->blocks) {
+      auto it = holders->find(b);
+      if (it == holders->end()) {
+        holders->emplace(b, 1);
+        order->push_back(b);
+      } else {
+        it->second += 1;
+      }
+    }
+  return ok();
+}
+
+int pa_swap_out(pa_alloc* a, const int32_t* seqs, int32_t n, int32_t* pairs_out, int32_t cap,
+                int32_t* num_pairs_out) {
+  if (!a || !num_pairs_out) return fail(PA_EINVAL, "null argument");
+  *num_pairs_out = 0;
+  std::vector<int32_t> order;
+  std::unordered_map<int32_t, int32_t> holders;
+  int rc = swap_plan(a, seqs, n, false, &order, &holders);
+  if (rc != PA_OK) return rc;
+  const int32_t need = (int32_t)order.size();
+  if (need > a->host_free.size)
+    return fail(PA_ENOBLOCKS, "swapping out needs %d host blocks, %d free", need,
+                a->host_free.size);
+  if (need > cap || (need > 0 && !pairs_out))
+    return fail(PA_EINVAL, "pairs capacity %d < %d blocks", cap, need);
+  std::unordered_map<int32_t, int32_t> host_of;
+  std::vector<int32_t> zero;
+  for (int32_t i = 0; i < need; ++i) {
+    const int32_t b = order[i], h = a->host_free.pop_top(), k = holders[b];
+    a->host_ref[h] = k;
+    host_of.emplace(b, h);
+    pairs_out[2 * i] = b;
+    pairs_out[2 * i + 1] = h;
+    a->ref[b] -= k;
+    if (a->ref[b] == 0) zero.push_back(b);
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    Seq* s = a->find(seqs[i]);
+    for (int32_t& b : s->blocks) b = host_of[b];
+    s->swapped = true;
+  }
+  a->release(zero);
+  *num_pairs_out = need;
+  return ok();
+}
+
+int pa_swap_in(pa_alloc* a, const int32_t* seqs, int32_t n, int32_t* pairs_out, int32_t cap,
+               int32_t* num_pairs_out) {
+  if (!a || !num_pairs_out) return fail(PA_EINVAL, "null argument");
+  *num_pairs_out = 0;
+  std::vector<int32_t> order;
+  std::unordered_map<int32_t, int32_t> holders;
+  int rc = swap_plan(a, seqs, n, true, &order, &holders);
+  if (rc != PA_OK) return rc;
+  const int32_t need = (int32_t)order.size();
+  if (need > a->free_stack.size)
+    return fail(PA_ENOBLOCKS, "swapping in needs %d blocks, %d free", need, a->free_stack.size);
+  if (need > cap || (need > 0 && !pairs_out))
+    return fail(PA_EINVAL, "pairs capacity %d < %d blocks", cap, need);
+  std::unordered_map<int32_t, int32_t> dev_of;
+  for (int32_t i = 0; i < need; ++i) {
+    const int32_t h = order[i], k = holders[h];
+    const int32_t b = a->take();
+    a->ref[b] = k;
+    dev_of.emplace(h, b);
+    pairs_out[2 * i] = h;
+    pairs_out[2 * i + 1] = b;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    Seq* s = a->find(seqs[i]);
+    for (int32_t& b : s->blocks) b = dev_of[b];
+    s->swapped = false;
+  }
+  for (int32_t i = 0; i < need; ++i) {
+    const int32_t h = order[i];
+    a->host_ref[h] -= holders[h];
+    if (a->host_ref[h] == 0) a->host_free.push_top(h);
+  }
+  *num_pairs_out = need;
+  return ok();
+}
+
+int pa_seq_swapped(const pa_alloc* a, int32_t seq, int32_t* swapped_out) {
+  if (!a || !swapped_out) return fail(PA_EINVAL, "null argument");
+  const Seq* s = a->find(seq);
+  if (!s) return fail(PA_ENOSEQ, "unknown sequence %d", seq);
+  *swapped_out = s->swapped ? 1 : 0;
+  return ok();
+}
+
+int pa_host_block_ref(const pa_alloc* a, int32_t block, int32_t* ref_out) {
+  if (!a || !ref_out) return fail(PA_EINVAL, "null argument");
+  if (block < 0 || block >= a->num_host_blocks)
+    return fail(PA_EINVAL, "host block %d outside [0, %d)", block, a->num_host_blocks);
+  *ref_out = a->host_ref[block];
+  return ok();
+}
+
+int pa_host_num_free(const pa_alloc* a, int32_t* n_out) {
+  if (!a || !n_out) return fail(PA_EINVAL, "null argument");
+  *n_out = a->host_free.size;
   return ok();
 }
 

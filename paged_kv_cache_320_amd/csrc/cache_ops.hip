@@ -3,7 +3,8 @@
 //
 // «The KV Cache and PagedAttention» › "One Token at a Time": each step adds only
 // the new token's key and value to the cache. › "Shared, Copied on Write": a
-// shared block is copied whole before a sharer writes into it.
+// shared block is copied whole before a sharer writes into it. › "When Memory Runs
+// Out": a text that gives way moves all its blocks to host memory and back (swap).
 #include "device.hpp"
 
 #include <cmath>
@@ -32,6 +33,25 @@ __global__ __launch_bounds__(kThreads) void kv_write_kernel(
     const int64_t dst = (((blk * hkv + head) * bsz + place) * lpr) + piece;
     kc[dst] = kn[i];
     vc[dst] = vn[i];
+  }
+}
+
+// Swap: one thread moves 16 bytes of one block for K and for V from the source pools to
+// the destination pools (one side pinned host memory, read or written across the bus).
+__global__ __launch_bounds__(kThreads) void swap_blocks_kernel(
+    uint4* __restrict__ dk, uint4* __restrict__ dv, const uint4* __restrict__ sk,
+    const uint4* __restrict__ sv, const int32_t* __restrict__ pairs, int64_t pieces_per_block,
+    int64_t total, int num_src, int num_dst) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * kThreads) {
+    const int64_t p = i / pieces_per_block;
+    const int64_t off = i - p * pieces_per_block;
+    const int src = pairs[2 * p], dst = pairs[2 * p + 1];
+    if (src < 0 || src >= num_src || dst < 0 || dst >= num_dst) continue;
+    const uint4 k = sk[(int64_t)src * pieces_per_block + off];
+    const uint4 v = sv[(int64_t)src * pieces_per_block + off];
+    dk[(int64_t)dst * pieces_per_block + off] = k;
+    dv[(int64_t)dst * pieces_per_block + off] = v;
   }
 }
 
@@ -194,6 +214,67 @@ extern "C" int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(grid_for(total)), dim3(kThreads), 0,
                      (hipStream_t)stream, (uint4*)k_cache, (uint4*)v_cache, pairs, ppb, total,
                      (int)num_blocks);
+  PA_HIP_CHECK(hipGetLastError());
+  return ok();
+}
+
+namespace {
+
+// The address a kernel on the current device uses for p: device memory of this device,
+// or pinned host memory (its device mapping). Anything else (pageable host memory,
+// another device's memory, managed memory) is refused.
+int device_view(const void* p, const char* name, const void** out) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return pagedkv::fail(PA_EINVAL, "%s is neither device memory nor pinned host memory", name);
+  }
+  int dev = 0;
+  PA_HIP_CHECK(hipGetDevice(&dev));
+  if (at.type == hipMemoryTypeDevice && !at.isManaged) {
+    if (at.device != dev)
+      return pagedkv::fail(PA_EINVAL, "%s is memory of device %d, not of the current device %d",
+                           name, at.device, dev);
+    *out = p;
+    return PA_OK;
+  }
+  if (at.type == hipMemoryTypeHost && at.devicePointer && !at.isManaged) {
+    // the mapping may be reported for the allocation's start or for p itself
+    const char* host = at.hostPointer ? (const char*)at.hostPointer : (const char*)p;
+    *out = (const char*)at.devicePointer + ((const char*)p - host);
+    return PA_OK;
+  }
+  return pagedkv::fail(PA_EINVAL, "%s is neither device memory nor pinned host memory", name);
+}
+
+}  // namespace
+
+extern "C" int pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                              const int32_t* pairs, int32_t num_pairs, int32_t num_src_blocks,
+                              int32_t num_dst_blocks, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int32_t dtype, void* stream) {
+  using namespace pagedkv;
+  int rc = check_shape(num_src_blocks, num_kv_heads, head_dim, block_size, dtype);
+  if (rc != PA_OK) return rc;
+  if (num_dst_blocks < 1) return fail(PA_EINVAL, "num_dst_blocks %d < 1", num_dst_blocks);
+  if (num_pairs < 0) return fail(PA_EINVAL, "num_pairs %d < 0", num_pairs);
+  if (num_pairs == 0) return ok();
+  if (!dst_k || !dst_v || !src_k || !src_v || !pairs) return fail(PA_EINVAL, "null pointer");
+  if (!aligned16(dst_k) || !aligned16(dst_v) || !aligned16(src_k) || !aligned16(src_v))
+    return fail(PA_EINVAL, "pools must be 16-byte aligned");
+  if (((uintptr_t)pairs & 3u) != 0) return fail(PA_EINVAL, "pairs must be 4-byte aligned");
+  const void *dk, *dv, *sk, *sv, *pp;
+  if ((rc = device_view(dst_k, "dst_k", &dk)) != PA_OK) return rc;
+  if ((rc = device_view(dst_v, "dst_v", &dv)) != PA_OK) return rc;
+  if ((rc = device_view(src_k, "src_k", &sk)) != PA_OK) return rc;
+  if ((rc = device_view(src_v, "src_v", &sv)) != PA_OK) return rc;
+  if ((rc = device_view(pairs, "pairs", &pp)) != PA_OK) return rc;
+  const int64_t ppb = (int64_t)num_kv_heads * block_size * head_dim * elt_bytes(dtype) / 16;
+  const int64_t total = ppb * num_pairs;
+  hipLaunchKernelGGL(swap_blocks_kernel, dim3(grid_for(total)), dim3(kThreads), 0,
+                     (hipStream_t)stream, (uint4*)dk, (uint4*)dv, (const uint4*)sk,
+                     (const uint4*)sv, (const int32_t*)pp, ppb, total, (int)num_src_blocks,
+                     (int)num_dst_blocks);
   PA_HIP_CHECK(hipGetLastError());
   return ok();
 }
