@@ -240,6 +240,32 @@ def run_tile_probe(L, torch, tile_bytes: int, bytes_per_launch: int):
     return per * tile_bytes / (ms * 1e-3) / 1e9
 
 
+def run_swap_probe(cache, seqs, torch, reps: int = 3):
+    """Texts given way and brought back («The KV Cache and PagedAttention», "When Memory
+    Runs Out"): every layer's blocks of two texts moved to pinned host pools by
+    pa_swap_blocks and back (the allocator's pairs). Returns (out GB/s, in GB/s, bytes
+    each way) over the host link, HIP events around each direction."""
+    chosen = list(seqs[:2])
+    nblk = sum(cache.alloc.info(s)[1] for s in chosen)
+    cache.host_pool(nblk)
+    per_block = 2 * cache.num_kv_heads * cache.block_size * cache.head_dim * \
+        cache.k[0].element_size() * len(cache.k)
+    t_out, t_in = [], []
+    for _ in range(reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record()
+        pairs = cache.swap_out(chosen)
+        e[1].record()
+        e[2].record()
+        cache.swap_in(chosen)
+        e[3].record()
+        torch.cuda.synchronize()
+        t_out.append(e[0].elapsed_time(e[1]))
+        t_in.append(e[2].elapsed_time(e[3]))
+    nbytes = len(pairs) * per_block
+    return (nbytes / (min(t_out) * 1e-3) / 1e9, nbytes / (min(t_in) * 1e-3) / 1e9, nbytes)
+
+
 def cpu_baseline(w, d0, seconds: float, gpu_out0):
     """The oracle as it stands, on one layer's step-0 batch, one thread, about `seconds` long."""
     import numpy as np
@@ -936,7 +962,7 @@ def main():
     log(f"step {ms_per_step * 1e3:.1f} us ({NL} layers), decode launch {avg_launch_ms * 1e3:.1f} us "
         f"(min {min(launch_ms) * 1e3:.1f}), {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBPS:.1%} of 8 TB/s")
 
-    probe = tprobe = vprobe = None
+    probe = tprobe = vprobe = swap = None
     if not args.no_probe:
         probe = run_probe(L, torch)
         log(f"stream-read probe: {probe:.0f} GB/s")
@@ -946,6 +972,9 @@ def main():
         tprobe = run_tile_probe(L, torch, B * D * kv_elt, int(bytes_per_launch))
         log(f"same-pattern probe ({int(bytes_per_launch) >> 20} MiB per launch in random "
             f"{B * D * kv_elt} B tiles): {tprobe:.0f} GB/s")
+        swap = run_swap_probe(cache, seqs, torch)
+        log(f"swap of two texts ({NL} layers, {swap[2] / 1e6:.0f} MB each way): out to pinned "
+            f"host memory {swap[0]:.1f} GB/s, back in {swap[1]:.1f} GB/s")
 
     cpu = None
     err0 = None
@@ -988,6 +1017,9 @@ def main():
                      "avg_launch_us": round(avg_launch_ms * 1e3, 2),
                      "bytes_per_launch": int(bytes_per_launch)},
         "kv_write_us_per_layer": round(write_us, 2) if wev else None,
+        "swap_out_gbps": round(swap[0], 2) if swap else None,
+        "swap_in_gbps": round(swap[1], 2) if swap else None,
+        "swap_bytes": int(swap[2]) if swap else None,
         "probe_read_gbps": round(probe, 1) if probe else None,
         "probe_same_volume_gbps": round(vprobe, 1) if vprobe else None,
         "probe_same_pattern_gbps": round(tprobe, 1) if tprobe else None,
