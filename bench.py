@@ -397,7 +397,8 @@ def bench_sharing(args, base) -> None:
     p_pairs = [torch.empty((S, 2), dtype=torch.int32, pin_memory=True) for _ in range(R)]
     outs = [torch.empty((S, H, D), dtype=torch_dtype(w.dtype), device="cuda") for _ in range(NL)]
     ev, logical, unique, copies, cev = [], [], [], [], []
-    per_text = args.per_text_decode
+    mode = args.sharing_decode
+    per_text = mode == "per-text"
     if not per_text:
         # texts are numbered group-major: group g is texts g*samples .. g*samples + samples - 1,
         # whose tables begin with the prompt's blocks
@@ -408,6 +409,16 @@ def bench_sharing(args, base) -> None:
         pws = torch.empty(L.pa_decode_prefix_workspace_bytes(
             S, H, Hkv, D, B, max_ctx_bound, G, w.prompt_len, L.dtype_code(outs[0])),
             dtype=torch.uint8, device="cuda")
+        # nested: each even sample and the odd sample forked from it share every block but
+        # the last one the step's copy-on-write split (the call clamps the shared length to
+        # each pair's shorter context less one token, rounded down to a block)
+        p_first = torch.arange(0, S, 2, dtype=torch.int32, device="cuda")
+        p_count = torch.full((S // 2,), 2, dtype=torch.int32, device="cuda")
+        p_prefix = torch.full((S // 2,), max_ctx_bound, dtype=torch.int32, device="cuda")
+        if mode == "nested":
+            pws = torch.empty(L.pa_decode_prefix2_workspace_bytes(
+                S, H, Hkv, D, B, max_ctx_bound, G, w.prompt_len, S // 2, max_ctx_bound, 2,
+                L.dtype_code(outs[0])), dtype=torch.uint8, device="cuda")
 
     def step(i: int, timed: bool):
         for op in step_ops[i]:
@@ -449,9 +460,15 @@ def bench_sharing(args, base) -> None:
             for li in range(NL):
                 L.pa_kv_write(cache.k[li], cache.v[li], d.step_k[i], d.step_v[i], d_slots)
             for li in range(NL):
-                L.pa_decode_attention_prefix(outs[li], d.step_q[i], cache.k[li], cache.v[li],
-                                             d_tables, d_lens, mctx, g_first, g_count, g_prefix,
-                                             w.prompt_len, pws)
+                if mode == "nested":
+                    L.pa_decode_attention_prefix2(outs[li], d.step_q[i], cache.k[li],
+                                                  cache.v[li], d_tables, d_lens, mctx, g_first,
+                                                  g_count, g_prefix, w.prompt_len, p_first,
+                                                  p_count, p_prefix, max_ctx_bound, 2, pws)
+                else:
+                    L.pa_decode_attention_prefix(outs[li], d.step_q[i], cache.k[li],
+                                                 cache.v[li], d_tables, d_lens, mctx, g_first,
+                                                 g_count, g_prefix, w.prompt_len, pws)
         if timed:
             e1.record()
             ev.append((e0, e1))
@@ -496,13 +513,17 @@ def bench_sharing(args, base) -> None:
                    "block_size": B, "pool_blocks": w.num_blocks, "layers_per_step": NL,
                    "parallelism": "single GPU",
                    "new_token_write": "fused into decode" if per_text else "pa_kv_write per layer",
-                   "shared_blocks": "read once per text" if per_text else "read once per group"},
+                   "shared_blocks": {"per-text": "read once per text",
+                                     "prefix": "prompt read once per group",
+                                     "nested": "prompt once per group, a pair's blocks once "
+                                               "per pair"}[mode]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": ("pa_decode_attention_write = decode_partition (new-token "
                                 "write fused) + decode_merge") if per_text else
-                               ("pa_kv_write + pa_decode_attention_prefix (group set-up, shared "
-                                "blocks once per group, each text's own blocks, merge)"),
+                               ("pa_kv_write + pa_decode_attention_prefix" +
+                                ("2" if mode == "nested" else "") + " (set-up, shared blocks "
+                                "once per group, each text's own blocks, merges)"),
                      "avg_launch_us": round(avg * 1e3, 2), "bytes_per_launch": int(u_launch)},
         "logical_gbps": round(l_launch / (avg * 1e-3) / 1e9, 1),
         "logical_bytes_per_launch": int(l_launch),
@@ -729,10 +750,12 @@ def main():
     ap.add_argument("--separate-write", action="store_true",
                     help="write each layer's new token with pa_kv_write before its decode launch "
                          "instead of inside it (pa_decode_attention_write)")
-    ap.add_argument("--per-text-decode", action="store_true",
-                    help="shared-prompt workloads: every text streams its whole table "
-                         "(pa_decode_attention_write) instead of each group's shared blocks "
-                         "once (pa_kv_write, then pa_decode_attention_prefix)")
+    ap.add_argument("--sharing-decode", choices=["nested", "prefix", "per-text"],
+                    default="nested",
+                    help="shared-prompt workloads: every shared block read once (the prompt per "
+                         "group, each forked pair's blocks per pair: pa_decode_attention_prefix2)"
+                         ", the prompt once per group (pa_decode_attention_prefix), or every "
+                         "text its whole table (pa_decode_attention_write)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each decode step's writes and decode launches from HIP graphs "
                          "captured for that step instead of launching them one by one")

@@ -331,6 +331,45 @@ int pa_decode_attention_prefix(void* out, const void* q, const void* k_cache,
                                int32_t dtype, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/* Decode over shared blocks at two nested levels, for sharing trees two deep (beam search:
+ * a request's samples share its prompt, and a pair of beams also shares the tokens written
+ * since they split; "Shared, Copied on Write"). Each shared block is read once for all the
+ * texts that hold it. The outer groups are pa_decode_attention_prefix's groups; each inner
+ * group's members lie in one outer group (or in none) and share the blocks from where
+ * that outer group's shared part ends (its first member's start) up to inner_prefix[g]
+ * (clamped as for the outer level: at most max_inner_prefix_len, every member's context
+ * less one token, a block multiple; an inner part no longer than the outer one is empty).
+ * The inner groups' table entries are read from their first member's row. Same result as
+ * pa_decode_attention up to rounding. At most 8 / (num_heads / num_kv_heads) members per
+ * outer group and inner_members per inner group (more are left out of the group);
+ * inner_members sets the width of the inner pass (its members' query heads per key/value
+ * head, rounded up to 1, 2, 4 or 8: pairs of texts with one query head per key/value head
+ * take the two-head vector kernel), PA_EUNSUPPORTED past 8. Passes on `stream`: set-up per level, the outer groups' shared
+ * blocks, the inner groups' shared blocks, a merge of the two levels' softmax states, every
+ * text's own blocks. dtype, limits and errors as pa_decode_attention_prefix; the group
+ * arrays are device int32 [num_groups] and [num_inner_groups], both counts >= 1.
+ * workspace: pa_decode_prefix2_workspace_bytes(...) bytes, 16-byte aligned, no
+ * initialization needed. */
+size_t pa_decode_prefix2_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t block_size, int32_t max_context_len,
+                                         int32_t num_groups, int32_t max_prefix_len,
+                                         int32_t num_inner_groups, int32_t max_inner_prefix_len,
+                                         int32_t inner_members, int32_t dtype);
+int pa_decode_attention_prefix2(void* out, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                int32_t num_blocks, int32_t max_blocks_per_seq,
+                                int32_t max_context_len, int32_t num_groups,
+                                const int32_t* group_first, const int32_t* group_count,
+                                const int32_t* group_prefix, int32_t max_prefix_len,
+                                int32_t num_inner_groups, const int32_t* inner_first,
+                                const int32_t* inner_count, const int32_t* inner_prefix,
+                                int32_t max_inner_prefix_len, int32_t inner_members,
+                                float scale, int32_t dtype, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Prefix caching ("What Came After": every full block gets a hash of its tokens and
  * of everything before them; a request that begins the same way reuses the blocks,

@@ -221,41 +221,62 @@ extern "C" int pa_decode_attention_write(void* out, const void* q, void* k_cache
 namespace pagedkv {
 namespace {
 
-constexpr int kPrefixCols = 8;  // query heads per key/value head in pass 1
+constexpr int kPrefixCols = 8;  // query heads per key/value head in a shared-blocks pass, at most
 
-struct PrefixLayout {
-  size_t decode_bytes, state_off, start_off, vfirst_off, vcount_off, vctx_off, vtab_off, vq_off,
-      bytes;
+// Workspace of the shared-prefix decode: the decode workspace (sized for the largest of the
+// passes), then per level the texts' states [S][H][D + 4] and starts [S], and the level's
+// group arrays, table rows and query batch.
+struct PrefixLevel {
+  size_t state_off, start_off, vfirst_off, vcount_off, vctx_off, vtab_off, vq_off;
   int maxbp;  // table entries per group (shared blocks at most)
 };
+struct PrefixLayout {
+  size_t decode_bytes, bytes;
+  int levels;
+  PrefixLevel lv[2];
+};
 
-int prefix_layout(int32_t S, int32_t H, int32_t Hkv, int32_t D, int32_t max_ctx, int32_t V,
-                  int32_t max_prefix, int32_t bsz, int32_t elt, PrefixLayout* pl) {
-  if (V < 1 || Hkv < 1 || H % Hkv != 0 || max_prefix < 0 || bsz < 1)
-    return fail(PA_EINVAL, "bad shared-prefix shape (num_groups %d, num_heads %d, num_kv_heads %d, "
-                "max_prefix_len %d, block_size %d)", V, H, Hkv, max_prefix, bsz);
-  Layout a, b;
+int prefix_layout(int32_t S, int32_t H, int32_t Hkv, int32_t D, int32_t max_ctx, int32_t levels,
+                  const int32_t* V, const int32_t* max_prefix, const int32_t* cols, int32_t bsz,
+                  int32_t elt, PrefixLayout* pl) {
+  if (Hkv < 1 || H % Hkv != 0 || bsz < 1 || levels < 1 || levels > 2)
+    return fail(PA_EINVAL, "bad shared-prefix shape (num_heads %d, num_kv_heads %d, "
+                "block_size %d)", H, Hkv, bsz);
+  for (int l = 0; l < levels; ++l)
+    if (V[l] < 1 || max_prefix[l] < 0)
+      return fail(PA_EINVAL, "bad shared-prefix groups (level %d: num_groups %d, "
+                  "max_prefix_len %d)", l + 1, V[l], max_prefix[l]);
+  Layout a;
   int rc = layout(S, H, D, max_ctx, 0, &a);
   if (rc != PA_OK) return rc;
-  rc = layout(V, Hkv * kPrefixCols, D, max_prefix, 0, &b);
-  if (rc != PA_OK) return rc;
-  pl->maxbp = max_prefix / bsz > 0 ? max_prefix / bsz : 1;
-  size_t off = align256(a.bytes > b.bytes ? a.bytes : b.bytes);
+  size_t need = a.bytes;
+  for (int l = 0; l < levels; ++l) {
+    Layout b;
+    rc = layout(V[l], Hkv * cols[l], D, max_prefix[l], 0, &b);
+    if (rc != PA_OK) return rc;
+    if (b.bytes > need) need = b.bytes;
+  }
+  size_t off = align256(need);
   pl->decode_bytes = off;
-  pl->state_off = off;
-  off = align256(off + sizeof(float) * (size_t)S * H * (D + 4));
-  pl->start_off = off;
-  off = align256(off + sizeof(int32_t) * (size_t)S);
-  pl->vfirst_off = off;
-  off = align256(off + sizeof(int32_t) * (size_t)V);
-  pl->vcount_off = off;
-  off = align256(off + sizeof(int32_t) * (size_t)V);
-  pl->vctx_off = off;
-  off = align256(off + sizeof(int32_t) * (size_t)V);
-  pl->vtab_off = off;
-  off = align256(off + sizeof(int32_t) * (size_t)V * pl->maxbp);
-  pl->vq_off = off;
-  off = align256(off + (size_t)elt * V * Hkv * kPrefixCols * D);
+  pl->levels = levels;
+  for (int l = 0; l < levels; ++l) {
+    PrefixLevel& v = pl->lv[l];
+    v.maxbp = max_prefix[l] / bsz > 0 ? max_prefix[l] / bsz : 1;
+    v.state_off = off;
+    off = align256(off + sizeof(float) * (size_t)S * H * (D + 4));
+    v.start_off = off;
+    off = align256(off + sizeof(int32_t) * (size_t)S);
+    v.vfirst_off = off;
+    off = align256(off + sizeof(int32_t) * (size_t)V[l]);
+    v.vcount_off = off;
+    off = align256(off + sizeof(int32_t) * (size_t)V[l]);
+    v.vctx_off = off;
+    off = align256(off + sizeof(int32_t) * (size_t)V[l]);
+    v.vtab_off = off;
+    off = align256(off + sizeof(int32_t) * (size_t)V[l] * v.maxbp);
+    v.vq_off = off;
+    off = align256(off + (size_t)elt * V[l] * Hkv * cols[l] * D);
+  }
   pl->bytes = off;
   return PA_OK;
 }
@@ -268,6 +289,27 @@ __global__ void prefix_clear_kernel(float* __restrict__ state, int64_t n, int ro
     state[i] = i % row == 0 ? -INFINITY : 0.f;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < S; i += stride)
     start[i] = 0;
+}
+
+// Two levels: each (text, head) state of the inner level becomes the merge of both levels'
+// states (the softmax over the union of the two token ranges, as split-context partials
+// merge). One wave per row; every lane reads the row's m and l before lane 0 writes them.
+__global__ void prefix_combine_kernel(const float* __restrict__ outer, float* __restrict__ inner,
+                                      int64_t rows, int D) {
+  const int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const float* a = outer + row * (D + 4);
+  float* b = inner + row * (D + 4);
+  const float ma = a[0], la = a[1], mb = b[0], lb = b[1];
+  const float M = fmaxf(ma, mb);
+  const float mu = M == -INFINITY ? 0.f : M;
+  const float fa = __builtin_amdgcn_exp2f(ma - mu), fb = __builtin_amdgcn_exp2f(mb - mu);
+  for (int e = lane; e < D; e += 64) b[4 + e] = a[4 + e] * fa + b[4 + e] * fb;
+  if (lane == 0) {
+    b[0] = M;
+    b[1] = la * fa + lb * fb;
+  }
 }
 
 // One workgroup per (group, key/value head): its members (clamped into the batch, at most
@@ -287,16 +329,18 @@ __global__ void prefix_prep_kernel(const int32_t* __restrict__ vfirst_in,
                                    int max_prefix, int maxbp, int32_t* __restrict__ vfirst,
                                    int32_t* __restrict__ vcount, int32_t* __restrict__ vctx,
                                    int32_t* __restrict__ vtables, char* __restrict__ vq,
-                                   int32_t* __restrict__ start) {
+                                   int32_t* __restrict__ start,
+                                   const int32_t* __restrict__ base_start,
+                                   int32_t* __restrict__ start_also, int cols) {
   const int v = blockIdx.x, kvh = blockIdx.y;
   const int Gr = H / Hkv;
-  __shared__ int sh[3];
+  __shared__ int sh[4];
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     int f = vfirst_in[v];
     f = f < 0 ? 0 : f >= S ? S - 1 : f;
     int n = vcount_in[v];
-    const int most = kPrefixCols / Gr < S - f ? kPrefixCols / Gr : S - f;
+    const int most = cols / Gr < S - f ? cols / Gr : S - f;
     n = n < 0 ? 0 : n > most ? most : n;
     const int64_t capacity = (int64_t)maxb * bsz;
     int64_t P = vprefix_in[v];
@@ -314,27 +358,34 @@ __global__ void prefix_prep_kernel(const int32_t* __restrict__ vfirst_in,
     if (P > keep) P = keep;
     if (P < 0 || n == 0) P = 0;
     P -= P % bsz;
+    // an inner level starts where the first member's outer level ended
+    const int P0 = base_start && n > 0 ? base_start[f] : 0;
+    if (P < P0) P = P0;
     if (lane == 0) {
       sh[0] = f;
       sh[1] = n;
       sh[2] = (int)P;
+      sh[3] = P0;
       if (kvh == 0) {
         vfirst[v] = f;
         vcount[v] = n;
-        vctx[v] = (int)P;
+        vctx[v] = (int)P - P0;
       }
     }
   }
   __syncthreads();
-  const int f = sh[0], n = sh[1], P = sh[2];
+  const int f = sh[0], n = sh[1], P = sh[2], P0 = sh[3];
   if (kvh == 0) {
-    for (int i = threadIdx.x; i < n; i += blockDim.x) start[f + i] = P;
-    const int nb = P / bsz;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      start[f + i] = P;
+      if (start_also) start_also[f + i] = P;
+    }
+    const int nb = (P - P0) / bsz, b0 = P0 / bsz;
     for (int k = threadIdx.x; k < maxbp; k += blockDim.x)
-      vtables[(int64_t)v * maxbp + k] = k < nb ? tables[(int64_t)f * maxb + k] : 0;
+      vtables[(int64_t)v * maxbp + k] = k < nb ? tables[(int64_t)f * maxb + b0 + k] : 0;
   }
   const int pieces = row_bytes / 16;
-  const int total = kPrefixCols * pieces;
+  const int total = cols * pieces;
   for (int i = threadIdx.x; i < total; i += blockDim.x) {
     const int c = i / pieces, p = i - c * pieces, m = c / Gr;
     uint4 val = make_uint4(0u, 0u, 0u, 0u);
@@ -342,45 +393,62 @@ __global__ void prefix_prep_kernel(const int32_t* __restrict__ vfirst_in,
       val = reinterpret_cast<const uint4*>(
           q + ((int64_t)(f + m) * H + kvh * Gr + (c - m * Gr)) * row_bytes)[p];
     reinterpret_cast<uint4*>(
-        vq + (((int64_t)v * Hkv + kvh) * kPrefixCols + c) * row_bytes)[p] = val;
+        vq + (((int64_t)v * Hkv + kvh) * cols + c) * row_bytes)[p] = val;
   }
 }
 
 }  // namespace
 }  // namespace pagedkv
 
-extern "C" size_t pa_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads,
-                                                   int32_t num_kv_heads, int32_t head_dim,
-                                                   int32_t block_size, int32_t max_context_len,
-                                                   int32_t num_groups, int32_t max_prefix_len,
-                                                   int32_t dtype) {
+namespace pagedkv {
+namespace {
+
+// One level of shared-prefix groups as the caller gives it.
+struct GroupsIn {
+  int32_t n;
+  const int32_t *first, *count, *prefix;
+  int32_t max_prefix;
+  int32_t cols;  // query columns per key/value head in the level's pass (members x H / Hkv)
+};
+
+size_t prefix_bytes(int32_t S, int32_t H, int32_t Hkv, int32_t D, int32_t bsz, int32_t max_ctx,
+                    int levels, const int32_t* V, const int32_t* maxp, const int32_t* cols,
+                    int32_t dtype) {
   if (!dtype_ok(dtype)) return 0;
   PrefixLayout pl;
-  if (prefix_layout(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, num_groups,
-                    max_prefix_len, block_size, elt_bytes(dtype), &pl) != PA_OK)
+  if (prefix_layout(S, H, Hkv, D, max_ctx, levels, V, maxp, cols, bsz, elt_bytes(dtype), &pl) !=
+      PA_OK)
     return 0;
   return pl.bytes;
 }
 
-extern "C" int pa_decode_attention_prefix(
-    void* out, const void* q, const void* k_cache, const void* v_cache,
-    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
-    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-    int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_groups,
-    const int32_t* group_first, const int32_t* group_count, const int32_t* group_prefix,
-    int32_t max_prefix_len, float scale, int32_t dtype, void* workspace, size_t workspace_bytes,
-    void* stream) {
+// Query columns per key/value head for groups of up to `members` texts: the members' heads,
+// rounded up to a head-group width the decode kernels take (1, 2, 4, 8); 0 if too many.
+int32_t prefix_cols(int32_t members, int32_t H, int32_t Hkv) {
+  if (Hkv < 1 || H % Hkv != 0 || members < 1) return 0;
+  const int32_t need = members * (H / Hkv);
+  for (int32_t c = 1; c <= kPrefixCols; c *= 2)
+    if (c >= need) return c;
+  return 0;
+}
+
+// The shared-prefix decode over one level of groups or two nested ones: set-up, one pass
+// per level over the groups' shared blocks (states out; with two levels the inner level's
+// states are merged with the outer's), then every text's own blocks with its state folded in.
+int prefix_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                  int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                  int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                  int levels, const GroupsIn* g, float scale, int32_t dtype, void* workspace,
+                  size_t workspace_bytes, void* stream) {
   if (!dtype_ok(dtype)) return fail(PA_EINVAL, "dtype %d is not PA_F32/PA_F16/PA_BF16", dtype);
-  if (num_groups < 0) return fail(PA_EINVAL, "num_groups %d < 0", num_groups);
-  if (num_groups == 0)
-    return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
-                         num_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                         max_blocks_per_seq, max_context_len, 0, scale, 1.0f, 1.0f, dtype, dtype,
-                         workspace, workspace_bytes, stream);
-  if (!group_first || !group_count || !group_prefix) return fail(PA_EINVAL, "null pointer");
-  if (((uintptr_t)group_first & 3u) || ((uintptr_t)group_count & 3u) ||
-      ((uintptr_t)group_prefix & 3u))
-    return fail(PA_EINVAL, "group arrays must be 4-byte aligned");
+  for (int l = 0; l < levels; ++l) {
+    if (g[l].n < 1) return fail(PA_EINVAL, "num_groups %d < 1 (level %d)", g[l].n, l + 1);
+    if (!g[l].first || !g[l].count || !g[l].prefix) return fail(PA_EINVAL, "null pointer");
+    if (((uintptr_t)g[l].first & 3u) || ((uintptr_t)g[l].count & 3u) ||
+        ((uintptr_t)g[l].prefix & 3u))
+      return fail(PA_EINVAL, "group arrays must be 4-byte aligned");
+  }
   if (num_kv_heads < 1 || num_heads % num_kv_heads != 0)
     return fail(PA_EINVAL, "num_heads %d is not a multiple of num_kv_heads %d", num_heads,
                 num_kv_heads);
@@ -400,42 +468,146 @@ extern "C" int pa_decode_attention_prefix(
   if (num_seqs < 1 || max_blocks_per_seq < 1 || num_blocks < 1 || max_context_len < 0)
     return fail(PA_EINVAL, "num_seqs, max_blocks_per_seq and num_blocks must be >= 1, "
                 "max_context_len >= 0");
+  const int32_t V[2] = {g[0].n, levels > 1 ? g[1].n : 0};
+  const int32_t maxp[2] = {g[0].max_prefix, levels > 1 ? g[1].max_prefix : 0};
+  const int32_t cols[2] = {g[0].cols, levels > 1 ? g[1].cols : 1};
+  for (int l = 0; l < levels; ++l)
+    if (cols[l] < num_heads / num_kv_heads || cols[l] > kPrefixCols)
+      return fail(PA_EINVAL, "bad group width at level %d", l + 1);
   PrefixLayout pl;
-  int rc = prefix_layout(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
-                         num_groups, max_prefix_len, block_size, elt_bytes(dtype), &pl);
+  int rc = prefix_layout(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, levels, V,
+                         maxp, cols, block_size, elt_bytes(dtype), &pl);
   if (rc != PA_OK) return rc;
   if (workspace_bytes < pl.bytes)
     return fail(PA_EINVAL, "workspace_bytes %zu < %zu required", workspace_bytes, pl.bytes);
   char* ws = (char*)workspace;
-  float* state = (float*)(ws + pl.state_off);
-  int32_t* start = (int32_t*)(ws + pl.start_off);
-  int32_t* vfirst = (int32_t*)(ws + pl.vfirst_off);
-  int32_t* vcount = (int32_t*)(ws + pl.vcount_off);
-  int32_t* vctx = (int32_t*)(ws + pl.vctx_off);
-  int32_t* vtab = (int32_t*)(ws + pl.vtab_off);
-  char* vq = ws + pl.vq_off;
   hipStream_t st = (hipStream_t)stream;
-  const int64_t nstate = (int64_t)num_seqs * num_heads * (head_dim + 4);
+  const int64_t rows = (int64_t)num_seqs * num_heads;
+  const int64_t nstate = rows * (head_dim + 4);
   const int64_t want = (nstate + 255) / 256;
-  hipLaunchKernelGGL(prefix_clear_kernel, dim3((int)(want < 2048 ? want : 2048)), dim3(256), 0, st,
-                     state, nstate, head_dim + 4, start, num_seqs);
-  hipLaunchKernelGGL(prefix_prep_kernel, dim3(num_groups, num_kv_heads), dim3(256), 0, st,
-                     group_first, group_count, group_prefix, context_lens, block_tables, (const char*)q,
-                     num_seqs, num_heads, num_kv_heads, head_dim * elt_bytes(dtype),
-                     max_blocks_per_seq, block_size, max_prefix_len, pl.maxbp, vfirst, vcount,
-                     vctx, vtab, vq, start);
-  PA_HIP_CHECK(hipGetLastError());
-  // pass 1: the groups' shared blocks, states out
-  const decode_impl::Prefix p1{nullptr, state, vfirst, vcount, num_heads, 1};
-  rc = decode_common(out, vq, k_cache, v_cache, vtab, vctx, num_groups,
-                     num_kv_heads * kPrefixCols, num_kv_heads, head_dim, block_size, num_blocks,
-                     pl.maxbp, max_prefix_len, 0, scale, 1.0f, 1.0f, dtype, dtype, workspace,
-                     pl.decode_bytes, stream, decode_impl::NewRows{}, p1);
-  if (rc != PA_OK) return rc;
-  // pass 2: every text's own blocks, states folded in
-  const decode_impl::Prefix p2{start, state, nullptr, nullptr, num_heads, 2};
+  float* state[2];
+  int32_t* start[2];
+  for (int l = 0; l < levels; ++l) {
+    state[l] = (float*)(ws + pl.lv[l].state_off);
+    start[l] = (int32_t*)(ws + pl.lv[l].start_off);
+    hipLaunchKernelGGL(prefix_clear_kernel, dim3((int)(want < 2048 ? want : 2048)), dim3(256), 0,
+                       st, state[l], nstate, head_dim + 4, start[l], num_seqs);
+  }
+  for (int l = 0; l < levels; ++l) {
+    const PrefixLevel& v = pl.lv[l];
+    hipLaunchKernelGGL(prefix_prep_kernel, dim3(g[l].n, num_kv_heads), dim3(256), 0, st,
+                       g[l].first, g[l].count, g[l].prefix, context_lens, block_tables,
+                       (const char*)q, num_seqs, num_heads, num_kv_heads,
+                       head_dim * elt_bytes(dtype), max_blocks_per_seq, block_size,
+                       g[l].max_prefix, v.maxbp, (int32_t*)(ws + v.vfirst_off),
+                       (int32_t*)(ws + v.vcount_off), (int32_t*)(ws + v.vctx_off),
+                       (int32_t*)(ws + v.vtab_off), ws + v.vq_off, start[l],
+                       l > 0 ? start[l - 1] : (const int32_t*)nullptr,
+                       l + 1 < levels ? start[l + 1] : (int32_t*)nullptr, (int)cols[l]);
+    PA_HIP_CHECK(hipGetLastError());
+  }
+  // a pass per level over the groups' shared blocks, states out
+  for (int l = 0; l < levels; ++l) {
+    const PrefixLevel& v = pl.lv[l];
+    const decode_impl::Prefix p1{nullptr, state[l], (const int32_t*)(ws + v.vfirst_off),
+                                 (const int32_t*)(ws + v.vcount_off), num_heads, 1};
+    rc = decode_common(out, ws + v.vq_off, k_cache, v_cache, (const int32_t*)(ws + v.vtab_off),
+                       (const int32_t*)(ws + v.vctx_off), g[l].n, num_kv_heads * cols[l],
+                       num_kv_heads, head_dim, block_size, num_blocks, v.maxbp, g[l].max_prefix,
+                       0, scale, 1.0f, 1.0f, dtype, dtype, workspace, pl.decode_bytes, stream,
+                       decode_impl::NewRows{}, p1);
+    if (rc != PA_OK) return rc;
+  }
+  if (levels > 1) {
+    const int64_t threads = rows * 64;
+    hipLaunchKernelGGL(prefix_combine_kernel, dim3((int)((threads + 255) / 256)), dim3(256), 0,
+                       st, state[0], state[1], rows, (int)head_dim);
+    PA_HIP_CHECK(hipGetLastError());
+  }
+  // every text's own blocks, its state folded in
+  const decode_impl::Prefix p2{start[levels - 1], state[levels - 1], nullptr, nullptr, num_heads,
+                               2};
   return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
                        num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                        max_context_len, 0, scale, 1.0f, 1.0f, dtype, dtype, workspace,
                        pl.decode_bytes, stream, decode_impl::NewRows{}, p2);
+}
+
+}  // namespace
+}  // namespace pagedkv
+
+extern "C" size_t pa_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                                   int32_t num_kv_heads, int32_t head_dim,
+                                                   int32_t block_size, int32_t max_context_len,
+                                                   int32_t num_groups, int32_t max_prefix_len,
+                                                   int32_t dtype) {
+  const int32_t V[1] = {num_groups}, maxp[1] = {max_prefix_len}, cols[1] = {kPrefixCols};
+  return prefix_bytes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len, 1,
+                      V, maxp, cols, dtype);
+}
+
+extern "C" size_t pa_decode_prefix2_workspace_bytes(
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t max_context_len, int32_t num_groups, int32_t max_prefix_len,
+    int32_t num_inner_groups, int32_t max_inner_prefix_len, int32_t inner_members,
+    int32_t dtype) {
+  const int32_t V[2] = {num_groups, num_inner_groups};
+  const int32_t maxp[2] = {max_prefix_len, max_inner_prefix_len};
+  const int32_t cols[2] = {kPrefixCols, prefix_cols(inner_members, num_heads, num_kv_heads)};
+  if (cols[1] == 0) return 0;
+  return prefix_bytes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len, 2,
+                      V, maxp, cols, dtype);
+}
+
+extern "C" int pa_decode_attention_prefix(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_groups,
+    const int32_t* group_first, const int32_t* group_count, const int32_t* group_prefix,
+    int32_t max_prefix_len, float scale, int32_t dtype, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  if (!dtype_ok(dtype)) return fail(PA_EINVAL, "dtype %d is not PA_F32/PA_F16/PA_BF16", dtype);
+  if (num_groups < 0) return fail(PA_EINVAL, "num_groups %d < 0", num_groups);
+  if (num_groups == 0)
+    return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                         num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                         max_blocks_per_seq, max_context_len, 0, scale, 1.0f, 1.0f, dtype, dtype,
+                         workspace, workspace_bytes, stream);
+  const GroupsIn g[1] = {{num_groups, group_first, group_count, group_prefix, max_prefix_len,
+                          kPrefixCols}};
+  return prefix_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
+                       num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                       max_context_len, 1, g, scale, dtype, workspace, workspace_bytes, stream);
+}
+
+extern "C" int pa_decode_attention_prefix2(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_groups,
+    const int32_t* group_first, const int32_t* group_count, const int32_t* group_prefix,
+    int32_t max_prefix_len, int32_t num_inner_groups, const int32_t* inner_first,
+    const int32_t* inner_count, const int32_t* inner_prefix, int32_t max_inner_prefix_len,
+    int32_t inner_members, float scale, int32_t dtype, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  if (num_groups < 1 || num_inner_groups < 1)
+    return fail(PA_EINVAL, "num_groups %d and num_inner_groups %d must be >= 1", num_groups,
+                num_inner_groups);
+  if (num_kv_heads < 1 || num_heads % num_kv_heads != 0)
+    return fail(PA_EINVAL, "num_heads %d is not a multiple of num_kv_heads %d", num_heads,
+                num_kv_heads);
+  const int32_t icols = prefix_cols(inner_members, num_heads, num_kv_heads);
+  if (icols == 0)
+    return fail(inner_members < 1 ? PA_EINVAL : PA_EUNSUPPORTED,
+                "inner_members %d: 1 .. %d with %d query heads per key/value head",
+                inner_members, kPrefixCols / (num_heads / num_kv_heads),
+                num_heads / num_kv_heads);
+  const GroupsIn g[2] = {{num_groups, group_first, group_count, group_prefix, max_prefix_len,
+                          kPrefixCols},
+                         {num_inner_groups, inner_first, inner_count, inner_prefix,
+                          max_inner_prefix_len, icols}};
+  return prefix_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
+                       num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                       max_context_len, 2, g, scale, dtype, workspace, workspace_bytes, stream);
 }

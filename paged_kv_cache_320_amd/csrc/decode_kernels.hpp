@@ -95,6 +95,7 @@ struct Cursor {
   int toff;         // tokens skipped at the start of the text's table row (a block multiple)
   int over;         // context_lens[s] exceeded the table's capacity
   int64_t excl;     // number of the first unit of text s
+  int vfirst, vcount;  // shared-prefix mode 1: text s is a group; its first member and count
 };
 
 // Shared-prefix decode (pa_decode_attention_prefix) runs the kernels twice. Mode 1 runs over
@@ -141,15 +142,16 @@ __device__ __forceinline__ int attended_len(const int32_t* __restrict__ ctx,
   return L - P;
 }
 
-// Mode 1: the state row of group v's query head hv, or null for a column past its members.
+// Mode 1: the state row of query head hv of a group whose members are texts vfirst ..
+// vfirst + vcount - 1, or null for a column past its members.
 template <int D>
-__device__ __forceinline__ float* prefix_state_row(const Prefix& pf, int Hkv, int G, int v,
-                                                   int hv) {
+__device__ __forceinline__ float* prefix_state_row(const Prefix& pf, int Hkv, int G, int vfirst,
+                                                   int vcount, int hv) {
   const int kvh = hv / G, c = hv - kvh * G;
   const int Gr = pf.heads / Hkv;
   const int m = c / Gr;
-  if (m >= pf.vcount[v]) return nullptr;
-  return pf.state + ((int64_t)(pf.vfirst[v] + m) * pf.heads + kvh * Gr + (c - m * Gr)) * (D + 4);
+  if (m >= vcount) return nullptr;
+  return pf.state + ((int64_t)(vfirst + m) * pf.heads + kvh * Gr + (c - m * Gr)) * (D + 4);
 }
 
 // The step's new rows, for the fused write: k_new / v_new [S][Hkv][D] in the pools'
@@ -162,11 +164,18 @@ struct NewRows {
   char* vc;
 };
 
+// (In shared-prefix mode 1 the group's members are read here, once per group, with its
+// length: read where a run is finished they made the wave wait for every load in flight.)
 __device__ __forceinline__ void set_text(Cursor& c, const Ctx& x, int s) {
   c.s = s;
+  c.vfirst = c.vcount = 0;
   if (s < x.S) {
     c.L = attended_len(x.ctx, x.pf.start, s, x.capacity, (int)(x.capacity / x.maxb), &c.toff,
                        &c.over);
+    if (x.pf.mode == 1) {
+      c.vfirst = __builtin_amdgcn_readfirstlane(x.pf.vfirst[s]);
+      c.vcount = __builtin_amdgcn_readfirstlane(x.pf.vcount[s]);
+    }
   } else {
     c.L = c.toff = c.over = 0;
   }
@@ -444,7 +453,7 @@ __device__ __forceinline__ void flush_run(State<KT, D, GS>& st, const Cursor& c,
       for (int j = 0; j < GS; ++j) {
         if (x.pf.mode == 1) {
           // shared blocks: the member's state, unnormalized
-          float* row = prefix_state_row<D>(x.pf, x.Hkv, x.G, c.s, h0 + j);
+          float* row = prefix_state_row<D>(x.pf, x.Hkv, x.G, c.vfirst, c.vcount, h0 + j);
           if (row) {
             if (lane == 0) {
               row[0] = st.m[j];
@@ -841,7 +850,7 @@ __global__ __launch_bounds__(kThreads) void decode_merge(
   const int64_t w0 = lo / seg, w1 = (hi - 1) / seg;
   if (w0 == w1) return;
   if (pf.mode == 1) {
-    float* row = prefix_state_row<D>(pf, Hkv, Gq, s, h);
+    float* row = prefix_state_row<D>(pf, Hkv, Gq, pf.vfirst[s], pf.vcount[s], h);
     if (row) merge_run<QT, D, GS>(partials, w0, w1, lo, seg, j, v_scale, nullptr, lane, nullptr, row);
     return;
   }
@@ -1038,7 +1047,7 @@ __device__ __forceinline__ void flush_run_mma(MmaState<D>& st, const Cursor& c, 
   if (col < GS) {
     if (run_lo >= seg_lo && run_hi <= seg_hi && x.pf.mode == 1) {
       // shared blocks: the member's state, unnormalized
-      float* row = prefix_state_row<D>(x.pf, x.Hkv, x.G, c.s, h0 + col);
+      float* row = prefix_state_row<D>(x.pf, x.Hkv, x.G, c.vfirst, c.vcount, h0 + col);
       if (row) {
         if (grp == 0) {
           row[0] = st.m;

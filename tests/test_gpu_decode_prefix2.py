@@ -1,0 +1,150 @@
+"""pa_decode_attention_prefix2 (shared blocks at two nested levels, each read once for all
+the texts that hold it) on the GPU: the same attention as over every text's whole table,
+within the decode tolerance of the fp64 oracle (attention.decode_attention over the full
+tables)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_common import assert_close, say
+from oracle.attention import decode_attention
+
+pytestmark = pytest.mark.gpu
+
+TD = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+
+def make_nested(seed, outer, H, Hkv, D, B, dtype, q_std=1.0, extra=5):
+    """outer: list of (P1, inner) with P1 a block multiple (0: no outer group) and inner a
+    list of (P2, [own tokens of each member]): the members of an inner entry share P2 more
+    tokens (a block multiple, 0: none) after the outer group's P1. Returns q, pools, tables,
+    lengths, and the outer and inner groups as (first, count, shared length) lists."""
+    g = torch.Generator().manual_seed(seed)
+    rng = np.random.default_rng(seed)
+    n_blocks = extra
+    for P1, inner in outer:
+        n_blocks += P1 // B
+        for P2, own in inner:
+            n_blocks += P2 // B + sum((n + B - 1) // B for n in own)
+    perm = list(rng.permutation(n_blocks))
+    kc = torch.full((n_blocks, Hkv, B, D), float("nan"), dtype=TD[dtype])
+    vc = torch.full((n_blocks, Hkv, B, D), float("nan"), dtype=TD[dtype])
+    std = 1.0 if dtype == "f32" else 1.0 / math.sqrt(D)
+
+    def fill(blocks, ntok):
+        k = (torch.randn((ntok, Hkv, D), generator=g) * std).to(TD[dtype])
+        v = (torch.randn((ntok, Hkv, D), generator=g) * std).to(TD[dtype])
+        for t in range(ntok):
+            kc[blocks[t // B], :, t % B] = k[t]
+            vc[blocks[t // B], :, t % B] = v[t]
+
+    rows, lens, og, ig = [], [], [], []
+    for P1, inner in outer:
+        b1 = [perm.pop() for _ in range(P1 // B)]
+        fill(b1, P1)
+        first1 = len(rows)
+        for P2, own in inner:
+            b2 = [perm.pop() for _ in range(P2 // B)]
+            fill(b2, P2)
+            first2 = len(rows)
+            for n in own:
+                mine = [perm.pop() for _ in range((n + B - 1) // B)]
+                fill(mine, n)
+                rows.append(b1 + b2 + mine)
+                lens.append(P1 + P2 + n)
+            ig.append((first2, len(own), P1 + P2))
+        og.append((first1, len(rows) - first1, P1))
+    tables = np.full((len(rows), max(len(r) for r in rows)), -1, dtype=np.int32)
+    for s, r in enumerate(rows):
+        tables[s, :len(r)] = r
+    q = (torch.randn((len(rows), H, D), generator=g) * q_std).to(TD[dtype])
+    return q, kc, vc, tables, np.asarray(lens, dtype=np.int32), og, ig
+
+
+def run_nested(native, q, kc, vc, tables, lens, og, ig, shift=0, inner_members=None):
+    S, H, D = q.shape
+    Hkv, B = kc.shape[1], kc.shape[2]
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    arr = lambda gs, i: np.array([x[i] for x in gs], dtype=np.int32)
+    max_ctx = int(lens.max())
+    p1, p2 = arr(og, 2), arr(ig, 2) + shift
+    m1, m2 = int(p1.max()), int(p2.max())
+    im = inner_members or max(x[1] for x in ig)
+    n = native.pa_decode_prefix2_workspace_bytes(S, H, Hkv, D, B, max_ctx, len(og), m1, len(ig),
+                                                 m2, im, CODE[q.dtype])
+    ws = torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda")
+    out = torch.full(q.shape, 7.0, dtype=q.dtype, device="cuda")
+    native.pa_decode_attention_prefix2(out, q.cuda(), kc.cuda(), vc.cuda(), dev(tables), dev(lens),
+                                       max_ctx, dev(arr(og, 0)), dev(arr(og, 1)), dev(p1), m1,
+                                       dev(arr(ig, 0)), dev(arr(ig, 1)), dev(p2), m2, im, ws)
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+def check(native, dtype, case, what, shift=0, inner_members=None):
+    q, kc, vc, tables, lens, og, ig = case
+    got = run_nested(native, q, kc, vc, tables, lens, og, ig, shift, inner_members)
+    want = decode_attention(q, kc, vc, tables, lens, kc.shape[2])
+    assert np.isfinite(got.double().numpy()).all(), f"{what}: non-finite output"
+    return assert_close(got, want, dtype, what)
+
+
+SHAPES = [(dt, D, B) for dt in ("f32", "f16", "bf16") for D, B in ((64, 4), (128, 16), (128, 32))]
+
+
+@pytest.mark.parametrize("dtype,D,B", SHAPES)
+def test_nested_matches_whole_table_attention(native, dtype, D, B):
+    """Beam-style pairs inside sampled groups: pairs sharing several blocks after the prompt,
+    an inner part of zero, members with own parts of 0, 1, B - 1, B + 1 and more tokens, an
+    inner group of one, texts in no group, and a group whose inner level is the only one."""
+    outer = [(0, [(0, [37])]),
+             (4 * 32, [(3 * 32, [5, 1]), (2 * 32, [B - 1, B + 1]), (0, [9, 70]), (32, [0, 3])]),
+             (0, [(64, [11, 4])]),
+             (8 * 32, [(5 * 32, [2, 40, 1]), (32, [17])]),
+             (0, [(0, [128, 3])])]
+    say(f"nested shared-prefix decode dtype={dtype} D={D} B={B}")
+    case = make_nested(D * 10 + B, outer, 4, 4, D, B, dtype)
+    check(native, dtype, case, f"{dtype} D={D} B={B}")
+
+
+@pytest.mark.parametrize("H,Hkv", [(8, 4), (16, 4), (16, 2)])
+def test_nested_with_shared_kv_heads(native, H, Hkv):
+    """2, 4 and 8 query heads per key/value head (4, 2 and 1 members share a read)."""
+    outer = [(64, [(48, [3, 17]), (16, [1, 40])]), (0, [(32, [20, 2])])]
+    say(f"nested shared-prefix decode GQA H={H} Hkv={Hkv}")
+    case = make_nested(H * 7 + Hkv, outer, H, Hkv, 128, 16, "f16")
+    check(native, "f16", case, f"H={H} Hkv={Hkv}", inner_members=min(2, 8 * Hkv // H))
+
+
+def test_nested_rounds_and_clamps(native):
+    """Inner shared lengths off a block boundary round down; an inner length at or below the
+    outer one leaves an empty inner part."""
+    outer = [(64, [(32, [5, 6]), (16, [7, 8])]), (96, [(0, [1, 30])])]
+    case = make_nested(5, outer, 4, 4, 128, 16, "bf16")
+    check(native, "bf16", case, "inner + 7", shift=7)
+    check(native, "bf16", case, "inner - 40", shift=-40)
+
+
+def test_nested_sharp_scores(native):
+    """Queries x32: a lost or doubled block at either level would show."""
+    outer = [(256, [(128, [4, 40]), (64, [1, 100]), (32, [17, 3]), (0, [9, 60])])]
+    case = make_nested(11, outer, 8, 8, 128, 16, "bf16", q_std=32.0)
+    check(native, "bf16", case, "sharp")
+
+
+@pytest.mark.parametrize("members", [1, 2, 3, 8])
+def test_nested_inner_width(native, members):
+    """The inner pass's width follows inner_members (1, 2, 4 and 8 query columns per
+    key/value head); inner groups larger than it keep only their first members."""
+    outer = [(64, [(32, [5, 6, 1]), (48, [2]), (16, [9, 3, 4, 30])])]
+    case = make_nested(members, outer, 4, 4, 128, 16, "f16")
+    check(native, "f16", case, f"inner_members={members}", inner_members=members)
+
+
+def test_nested_rejects_too_wide_inner_groups(native):
+    q, kc, vc, tables, lens, og, ig = make_nested(3, [(32, [(16, [3, 4])])], 8, 2, 64, 16, "f16")
+    with pytest.raises(native.PagedKVError):
+        run_nested(native, q, kc, vc, tables, lens, og, ig, inner_members=3)
