@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import workloads as wl
-from gpu_common import NativeReplay, assert_close, sample_pairs, say
+from gpu_common import NativeReplay, StepOut, assert_close, sample_pairs, say
 from oracle import cache_ops
 from oracle.replay import Replay
 
@@ -144,3 +144,72 @@ def test_full_size_workload(native, w):
     if w.length_kind == "sharing":
         assert sum(len(s.pairs) for s in ns) > 0
     say(f"  max abs error {err:.3e}")
+
+
+class SharedDecodes(NativeReplay):
+    """The native replay, plus after every step the decode over shared blocks on the same
+    pools, tables, lengths and queries, in the bench's launch configuration: prompt groups
+    once per group (pa_decode_attention_prefix), and prompt groups with each forked pair's
+    blocks once per pair (pa_decode_attention_prefix2)."""
+
+    def run(self, ops, max_blocks=None):
+        self.shared = {"prefix": [], "nested": []}
+        for op in ops:
+            super().run([op], max_blocks)
+            if op[0] == "step":
+                self._shared_decode(op[1])
+        return self.steps
+
+    def _shared_decode(self, t):
+        from paged_kv_cache_320_amd import _lib as L
+        w, st = self.w, self.steps[-1]
+        S, H, Hkv, D, B = w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size
+        bt = torch.from_numpy(np.ascontiguousarray(st.tables, dtype=np.int32)).cuda()
+        cl = torch.from_numpy(np.asarray(st.lens, dtype=np.int32)).cuda()
+        q = self._dev(self.d.step_q[t])
+        kc, vc = self.cache.k[0], self.cache.v[0]
+        mx = int(max(st.lens))
+        G, J, P = w.groups, w.samples, w.prompt_len
+        i32 = dict(dtype=torch.int32, device="cuda")
+        gf, gc, gp = torch.arange(0, S, J, **i32), torch.full((G,), J, **i32), \
+            torch.full((G,), P, **i32)
+        pf, pc, pp = torch.arange(0, S, 2, **i32), torch.full((S // 2,), 2, **i32), \
+            torch.full((S // 2,), mx, **i32)
+        code = L.dtype_code(q)
+        ws1 = torch.empty(L.pa_decode_prefix_workspace_bytes(S, H, Hkv, D, B, mx, G, P, code),
+                          dtype=torch.uint8, device="cuda")
+        out1 = torch.empty_like(q)
+        L.pa_decode_attention_prefix(out1, q, kc, vc, bt, cl, mx, gf, gc, gp, P, ws1)
+        ws2 = torch.empty(L.pa_decode_prefix2_workspace_bytes(S, H, Hkv, D, B, mx, G, P, S // 2,
+                                                              mx, 2, code),
+                          dtype=torch.uint8, device="cuda")
+        out2 = torch.empty_like(q)
+        L.pa_decode_attention_prefix2(out2, q, kc, vc, bt, cl, mx, gf, gc, gp, P, pf, pc, pp, mx,
+                                      2, ws2)
+        self.shared["prefix"].append(out1)
+        self.shared["nested"].append(out2)
+
+
+def test_full_size_sharing_shared_block_decodes(native):
+    """The sharing workload at full size (32 groups x 8 samples, 1,024-token prompts, pair
+    forks with copy-on-write every step): both shared-block decodes against the oracle on
+    sampled (text, head) pairs, every step, within the plain 2e-3 gate."""
+    w = wl.SHARING_32x8
+    say(f"workload {w.name} (full size), shared-block decodes")
+    d = wl.draw(w, device="cuda")
+    ops = wl.script(w, d)
+    nat = SharedDecodes(w, d)
+    ns = nat.run(ops)
+    torch.cuda.synchronize()
+    lens0 = wl.attended_at_step0(w, d)
+
+    def pairs_for(t):
+        return sample_pairs(lens0, w.num_heads, 48, seed=100 + t)
+
+    ora = Replay(w, d, pool=False)
+    os_ = ora.run(ops, decode_pairs=pairs_for)
+    for kind in ("prefix", "nested"):
+        steps = [StepOut(o, s.slots, s.pairs, s.tables, s.lens, s.seq_ids)
+                 for o, s in zip(nat.shared[kind], ns)]
+        err = compare_steps(w, steps, os_, pairs_for=pairs_for, strict_gate=True)
+        say(f"  {kind}: max abs error {err:.3e}")
