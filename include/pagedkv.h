@@ -334,9 +334,11 @@ int pa_decode_attention_prefix(void* out, const void* q, const void* k_cache,
 /* Decode over shared blocks at two nested levels, for sharing trees two deep (beam search:
  * a request's samples share its prompt, and a pair of beams also shares the tokens written
  * since they split; "Shared, Copied on Write"). Each shared block is read once for all the
- * texts that hold it. The outer groups are pa_decode_attention_prefix's groups; each inner
- * group's members lie in one outer group (or in none) and share the blocks from where
- * that outer group's shared part ends (its first member's start) up to inner_prefix[g]
+ * texts that hold it. The outer groups are pa_decode_attention_prefix's groups; an inner
+ * group's members share the blocks from where their outer group's shared part ends up to
+ * inner_prefix[g] (an inner group keeps its members up to the first whose outer shared
+ * part differs from its first member's: members of different outer groups, or of none,
+ * are not grouped together)
  * (clamped as for the outer level: at most max_inner_prefix_len, every member's context
  * less one token, a block multiple; an inner part no longer than the outer one is empty).
  * The inner groups' table entries are read from their first member's row. Same result as

@@ -345,6 +345,13 @@ __global__ void prefix_prep_kernel(const int32_t* __restrict__ vfirst_in,
     const int64_t capacity = (int64_t)maxb * bsz;
     int64_t P = vprefix_in[v];
     if (P > max_prefix) P = max_prefix;
+    // an inner level keeps its members up to the first whose outer part differs from the
+    // first member's (members of different outer groups cannot share this level's blocks)
+    if (base_start && n > 1) {
+      const bool other = lane < n && base_start[f + lane] != base_start[f];
+      const uint64_t mask = __ballot(other);
+      if (mask) n = __ffsll((unsigned long long)mask) - 1;
+    }
     int64_t keep = INT32_MAX;  // the members' lengths less one, smallest
     if (lane < n) {
       int64_t L = ctx[f + lane];

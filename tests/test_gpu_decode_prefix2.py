@@ -148,3 +148,16 @@ def test_nested_rejects_too_wide_inner_groups(native):
     q, kc, vc, tables, lens, og, ig = make_nested(3, [(32, [(16, [3, 4])])], 8, 2, 64, 16, "f16")
     with pytest.raises(native.PagedKVError):
         run_nested(native, q, kc, vc, tables, lens, og, ig, inner_members=3)
+
+
+def test_nested_inner_group_across_outer_groups(native):
+    """An inner group whose members straddle two outer groups (and one text in none) keeps
+    only the members whose outer part matches its first member's; the result is still the
+    whole-table attention."""
+    outer = [(64, [(32, [5, 6])]), (32, [(16, [7, 8])]), (0, [(0, [40])])]
+    q, kc, vc, tables, lens, og, ig = make_nested(17, outer, 4, 4, 128, 16, "f16")
+    # one inner group over texts 1 .. 4: text 1 in the first outer group, 2 and 3 in the
+    # second, 4 in none (their tables agree on nothing beyond what the outer level covers)
+    ig = [(0, 1, 64 + 32), (1, 4, 200)]
+    check(native, "f16", (q, kc, vc, tables, lens, og, ig), "straddling inner group",
+          inner_members=4)
