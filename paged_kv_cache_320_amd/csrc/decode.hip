@@ -291,21 +291,39 @@ __global__ void prefix_clear_kernel(float* __restrict__ state, int64_t n, int ro
     start[i] = 0;
 }
 
+// Two levels: no text skips a start at either level (the states are not cleared: a
+// level's state row is used only where that level's start moved past the level before).
+__global__ void prefix_clear_starts_kernel(int32_t* __restrict__ a, int32_t* __restrict__ b,
+                                           int S) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < S; i += gridDim.x * blockDim.x) {
+    a[i] = 0;
+    b[i] = 0;
+  }
+}
+
 // Two levels: each (text, head) state of the inner level becomes the merge of both levels'
 // states (the softmax over the union of the two token ranges, as split-context partials
-// merge). One wave per row; every lane reads the row's m and l before lane 0 writes them.
+// merge). A level's state counts only where its start moved past the level before (outer:
+// start > 0; inner: start beyond the outer start); otherwise it is empty. One wave per row;
+// every lane reads the row's m and l before lane 0 writes them.
 __global__ void prefix_combine_kernel(const float* __restrict__ outer, float* __restrict__ inner,
+                                      const int32_t* __restrict__ start_outer,
+                                      const int32_t* __restrict__ start_inner, int H,
                                       int64_t rows, int D) {
   const int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
+  const int64_t s = row / H;
+  const bool use_a = start_outer[s] > 0, use_b = start_inner[s] > start_outer[s];
   const float* a = outer + row * (D + 4);
   float* b = inner + row * (D + 4);
-  const float ma = a[0], la = a[1], mb = b[0], lb = b[1];
+  const float ma = use_a ? a[0] : -INFINITY, la = use_a ? a[1] : 0.f;
+  const float mb = use_b ? b[0] : -INFINITY, lb = use_b ? b[1] : 0.f;
   const float M = fmaxf(ma, mb);
   const float mu = M == -INFINITY ? 0.f : M;
   const float fa = __builtin_amdgcn_exp2f(ma - mu), fb = __builtin_amdgcn_exp2f(mb - mu);
-  for (int e = lane; e < D; e += 64) b[4 + e] = a[4 + e] * fa + b[4 + e] * fb;
+  for (int e = lane; e < D; e += 64)
+    b[4 + e] = (use_a ? a[4 + e] * fa : 0.f) + (use_b ? b[4 + e] * fb : 0.f);
   if (lane == 0) {
     b[0] = M;
     b[1] = la * fa + lb * fb;
@@ -497,8 +515,14 @@ int prefix_decode(void* out, const void* q, const void* k_cache, const void* v_c
   for (int l = 0; l < levels; ++l) {
     state[l] = (float*)(ws + pl.lv[l].state_off);
     start[l] = (int32_t*)(ws + pl.lv[l].start_off);
+  }
+  if (levels == 1) {
     hipLaunchKernelGGL(prefix_clear_kernel, dim3((int)(want < 2048 ? want : 2048)), dim3(256), 0,
-                       st, state[l], nstate, head_dim + 4, start[l], num_seqs);
+                       st, state[0], nstate, head_dim + 4, start[0], num_seqs);
+  } else {
+    const int blocks = (num_seqs + 255) / 256;
+    hipLaunchKernelGGL(prefix_clear_starts_kernel, dim3(blocks < 1024 ? blocks : 1024), dim3(256),
+                       0, st, start[0], start[1], num_seqs);
   }
   for (int l = 0; l < levels; ++l) {
     const PrefixLevel& v = pl.lv[l];
@@ -528,7 +552,8 @@ int prefix_decode(void* out, const void* q, const void* k_cache, const void* v_c
   if (levels > 1) {
     const int64_t threads = rows * 64;
     hipLaunchKernelGGL(prefix_combine_kernel, dim3((int)((threads + 255) / 256)), dim3(256), 0,
-                       st, state[0], state[1], rows, (int)head_dim);
+                       st, state[0], state[1], start[0], start[1], (int)num_heads, rows,
+                       (int)head_dim);
     PA_HIP_CHECK(hipGetLastError());
   }
   // every text's own blocks, its state folded in
