@@ -21,19 +21,17 @@ int layout(int32_t S, int32_t H, int32_t D, int32_t max_ctx, int32_t T, Layout* 
   if (S < 1 || H < 1 || (D != 64 && D != 128) || max_ctx < 0 || T < 0 || T % kChunk != 0)
     return fail(PA_EINVAL, "bad workspace shape (num_seqs %d, num_heads %d, head_dim %d, "
                 "max_context_len %d, partition_tokens %d)", S, H, D, max_ctx, T);
-  // runs per text are at most H (one query head per wave), so this bounds every GS
+  // runs per text are at most H (one query head per wave), so this bounds every GS; a
+  // device-side length beyond max_ctx lengthens the segments (seg::segment_units)
   const int64_t units_bound = (int64_t)S * H * units_of(max_ctx);
-  int64_t W;
+  int64_t slots = 0;
   if (T == 0) {
     int cus = 0;
     int rc = device_cus(&cus);
     if (rc != PA_OK) return rc;
-    W = (int64_t)cus * kWavesPerCU;
-    if (W > units_bound) W = units_bound;
-  } else {
-    const int64_t seg = T / kChunk;
-    W = (units_bound + seg - 1) / seg;
+    slots = (int64_t)cus * kWavesPerCU;
   }
+  const int64_t W = pagedkv::seg::grid_segments(units_bound, slots, T / kChunk);
   if (W > 0x7fffffff / 2) return fail(PA_EINVAL, "too many segments");
   lay->W = W;
   lay->excl_off = kHdrBytes;
@@ -232,6 +230,7 @@ struct PrefixLevel {
 };
 struct PrefixLayout {
   size_t decode_bytes, bytes;
+  size_t gid_off;  // two levels: each text's outer group (-1: none) [S]
   int levels;
   PrefixLevel lv[2];
 };
@@ -277,6 +276,8 @@ int prefix_layout(int32_t S, int32_t H, int32_t Hkv, int32_t D, int32_t max_ctx,
     v.vq_off = off;
     off = align256(off + (size_t)elt * V[l] * Hkv * cols[l] * D);
   }
+  pl->gid_off = off;
+  if (levels > 1) off = align256(off + sizeof(int32_t) * (size_t)S);
   pl->bytes = off;
   return PA_OK;
 }
@@ -291,13 +292,15 @@ __global__ void prefix_clear_kernel(float* __restrict__ state, int64_t n, int ro
     start[i] = 0;
 }
 
-// Two levels: no text skips a start at either level (the states are not cleared: a
-// level's state row is used only where that level's start moved past the level before).
+// Two levels: no text skips a start at either level and none is in an outer group (the
+// states are not cleared: a level's state row is used only where that level's start moved
+// past the level before).
 __global__ void prefix_clear_starts_kernel(int32_t* __restrict__ a, int32_t* __restrict__ b,
-                                           int S) {
+                                           int32_t* __restrict__ gid, int S) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < S; i += gridDim.x * blockDim.x) {
     a[i] = 0;
     b[i] = 0;
+    gid[i] = -1;
   }
 }
 
@@ -338,6 +341,8 @@ __global__ void prefix_combine_kernel(const float* __restrict__ outer, float* __
 // queries into the group's batch of Hkv * 8 query heads (column c of key/value head k:
 // member c / Gr's head k * Gr + c % Gr, Gr = H / Hkv; columns past the members zero).
 // The members' lengths are read by one lane each and reduced across the wave.
+// Two levels: the outer level records each member's group (gid_out); the inner level keeps
+// its members up to the first whose outer group (base_gid) differs from its first member's.
 __global__ void prefix_prep_kernel(const int32_t* __restrict__ vfirst_in,
                                    const int32_t* __restrict__ vcount_in,
                                    const int32_t* __restrict__ vprefix_in,
@@ -349,7 +354,9 @@ __global__ void prefix_prep_kernel(const int32_t* __restrict__ vfirst_in,
                                    int32_t* __restrict__ vtables, char* __restrict__ vq,
                                    int32_t* __restrict__ start,
                                    const int32_t* __restrict__ base_start,
-                                   int32_t* __restrict__ start_also, int cols) {
+                                   int32_t* __restrict__ start_also, int cols,
+                                   int32_t* __restrict__ gid_out,
+                                   const int32_t* __restrict__ base_gid) {
   const int v = blockIdx.x, kvh = blockIdx.y;
   const int Gr = H / Hkv;
   __shared__ int sh[4];
@@ -363,10 +370,10 @@ __global__ void prefix_prep_kernel(const int32_t* __restrict__ vfirst_in,
     const int64_t capacity = (int64_t)maxb * bsz;
     int64_t P = vprefix_in[v];
     if (P > max_prefix) P = max_prefix;
-    // an inner level keeps its members up to the first whose outer part differs from the
+    // an inner level keeps its members up to the first whose outer group differs from the
     // first member's (members of different outer groups cannot share this level's blocks)
-    if (base_start && n > 1) {
-      const bool other = lane < n && base_start[f + lane] != base_start[f];
+    if (base_gid && n > 1) {
+      const bool other = lane < n && base_gid[f + lane] != base_gid[f];
       const uint64_t mask = __ballot(other);
       if (mask) n = __ffsll((unsigned long long)mask) - 1;
     }
@@ -404,6 +411,7 @@ __global__ void prefix_prep_kernel(const int32_t* __restrict__ vfirst_in,
     for (int i = threadIdx.x; i < n; i += blockDim.x) {
       start[f + i] = P;
       if (start_also) start_also[f + i] = P;
+      if (gid_out) gid_out[f + i] = v;
     }
     const int nb = (P - P0) / bsz, b0 = P0 / bsz;
     for (int k = threadIdx.x; k < maxbp; k += blockDim.x)
@@ -522,7 +530,7 @@ int prefix_decode(void* out, const void* q, const void* k_cache, const void* v_c
   } else {
     const int blocks = (num_seqs + 255) / 256;
     hipLaunchKernelGGL(prefix_clear_starts_kernel, dim3(blocks < 1024 ? blocks : 1024), dim3(256),
-                       0, st, start[0], start[1], num_seqs);
+                       0, st, start[0], start[1], (int32_t*)(ws + pl.gid_off), num_seqs);
   }
   for (int l = 0; l < levels; ++l) {
     const PrefixLevel& v = pl.lv[l];
@@ -534,7 +542,9 @@ int prefix_decode(void* out, const void* q, const void* k_cache, const void* v_c
                        (int32_t*)(ws + v.vcount_off), (int32_t*)(ws + v.vctx_off),
                        (int32_t*)(ws + v.vtab_off), ws + v.vq_off, start[l],
                        l > 0 ? start[l - 1] : (const int32_t*)nullptr,
-                       l + 1 < levels ? start[l + 1] : (int32_t*)nullptr, (int)cols[l]);
+                       l + 1 < levels ? start[l + 1] : (int32_t*)nullptr, (int)cols[l],
+                       l == 0 && levels > 1 ? (int32_t*)(ws + pl.gid_off) : (int32_t*)nullptr,
+                       l > 0 ? (const int32_t*)(ws + pl.gid_off) : (const int32_t*)nullptr);
     PA_HIP_CHECK(hipGetLastError());
   }
   // a pass per level over the groups' shared blocks, states out

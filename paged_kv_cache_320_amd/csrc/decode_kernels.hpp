@@ -47,6 +47,7 @@
 #pragma once
 
 #include "device.hpp"
+#include "segments.hpp"
 
 #include <cmath>
 
@@ -54,7 +55,8 @@ namespace pagedkv {
 namespace decode_impl {
 
 
-constexpr int kChunk = 16;         // tokens per work unit
+using seg::kChunk;                 // tokens per work unit
+using seg::units_of;
 constexpr int kWavesPerGroup = 4;  // wavefronts per workgroup
 constexpr int kThreads = 64 * kWavesPerGroup;
 constexpr int kWavesPerCU = 4;     // auto grid: segments per CU (measured best of 4, 6, 8, 12, 16)
@@ -70,10 +72,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load_stream(const char* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-__host__ __device__ __forceinline__ int units_of(int L) {
-  return L <= 0 ? 1 : (L + kChunk - 1) / kChunk;
 }
 
 // KT: storage format of keys and values; QT: format of queries and outputs (the same
@@ -432,7 +430,7 @@ __device__ __forceinline__ void store_out(char* __restrict__ dst, const float* o
 // 1: its last run).
 template <int D, int GS>
 __device__ __forceinline__ int64_t partial_index(int64_t w, int slot, int j) {
-  return ((w * 2 + slot) * GS + j) * (int64_t)(D + 4);
+  return seg::partial_offset(w, slot, j, GS, D + 4);
 }
 
 template <int KT, int QT, int D, int GS>
@@ -489,7 +487,7 @@ __device__ __forceinline__ void flush_run(State<KT, D, GS>& st, const Cursor& c,
           reinterpret_cast<uint4*>(dst)[p] = narrow16<QT>(o + p * (G::EPL / QP));
       }
     } else {
-      const int slot = run_lo <= seg_lo ? 0 : 1;
+      const int slot = seg::partial_slot(run_lo, seg_lo);
 #pragma unroll
       for (int j = 0; j < GS; ++j) {
         float* p = partials + partial_index<D, GS>(w, slot, j);
@@ -554,29 +552,22 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Sum over the workgroup (every thread gets it).
-__device__ __forceinline__ int64_t block_sum(int64_t x, int64_t* sh) {
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  const int wave = threadIdx.x / 64;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh[wave] = x;
-  __syncthreads();
-  int64_t t = 0;
-#pragma unroll
-  for (int j = 0; j < kWavesPerGroup; ++j) t += sh[j];
-  return t;
-}
-
-// This wave's segment of the unit numbering: every workgroup sums the texts' units and
-// scans them to find where its waves' segments start. Returns false when the wave has
-// no units; otherwise sets the segment [seg_lo, seg_hi), the context and the cursor at
-// the segment's first unit (all wave-uniform).
+// This wave's segment of the unit numbering. Returns false when the wave has no units;
+// otherwise sets the segment [seg_lo, seg_hi), the context and the cursor at the segment's
+// first unit (all wave-uniform).
 struct Segment {
   int w;
   int64_t seg_lo, seg_hi;
   int n;
 };
 
+// Every workgroup finds where its waves' segments start with one pass over the texts'
+// lengths: thread t takes a contiguous range of about S / 256 texts and sums their units
+// (independent loads, all in flight), one workgroup-wide exclusive scan of the 256 range
+// sums gives each range's first unit and the total, and the (at most 4) threads whose
+// range holds one of the workgroup's segment starts walk their range again to find the
+// text and the unit within it. Two barriers whatever S is. Workgroup 0 also writes every
+// text's first unit (excl_out) and the header (total units, segment length) for the merge.
 template <int B, int GS>
 __device__ __forceinline__ bool start_segment(const int32_t* __restrict__ ctx, int S, int H,
                                               int Hkv, int maxb, int num_blocks, int W,
@@ -584,7 +575,7 @@ __device__ __forceinline__ bool start_segment(const int32_t* __restrict__ ctx, i
                                               int64_t* __restrict__ hdr,
                                               int64_t* __restrict__ excl_out, Segment& sg,
                                               Ctx& x, Cursor& cur) {
-  __shared__ int64_t sh_red[kWavesPerGroup];
+  __shared__ int64_t sh_wave[kWavesPerGroup];
   __shared__ int sh_seq[kWavesPerGroup];
   __shared__ int64_t sh_off[kWavesPerGroup];
   __shared__ int64_t sh_excl[kWavesPerGroup];
@@ -599,47 +590,59 @@ __device__ __forceinline__ bool start_segment(const int32_t* __restrict__ ctx, i
     return (int64_t)R * units_of(attended_len(ctx, pf.start, i, capacity, B, &toff, &over));
   };
 
-  // ---- locate each wave's segment: total units, then an exclusive scan ----
-  int64_t local = 0;
-  for (int i = tid; i < S; i += kThreads) local += units_at(i);
-  const int64_t total = uniform64(block_sum(local, sh_red));
-  const int64_t seg = seg_fixed > 0 ? seg_fixed : (total + W - 1) / W;
-  if (blockIdx.x == 0 && tid == 0) {
-    hdr[0] = total;
-    hdr[1] = seg;
+  // ---- this thread's range of texts and its units ----
+  const int per = (S + kThreads - 1) / kThreads;
+  const int r_lo = tid * per < S ? tid * per : S;
+  const int r_hi = r_lo + per < S ? r_lo + per : S;
+  int64_t mine = 0;
+  for (int i = r_lo; i < r_hi; ++i) mine += units_at(i);
+
+  // ---- exclusive scan of the range sums over the workgroup; the total ----
+  int64_t incl = mine;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
   }
-  int64_t carry = 0;
-  for (int base = 0; base < S; base += kThreads) {
-    const int i = base + tid;
-    const int64_t n = i < S ? units_at(i) : 0;
-    int64_t incl = n;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int64_t y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    __syncthreads();
-    if (lane == 63) sh_red[wave] = incl;
-    __syncthreads();
-    int64_t before = 0, all = 0;
+  if (lane == 63) sh_wave[wave] = incl;
+  __syncthreads();
+  int64_t before = 0, total = 0;
 #pragma unroll
-    for (int j = 0; j < kWavesPerGroup; ++j) {
-      before += j < wave ? sh_red[j] : 0;
-      all += sh_red[j];
+  for (int j = 0; j < kWavesPerGroup; ++j) {
+    before += j < wave ? sh_wave[j] : 0;
+    total += sh_wave[j];
+  }
+  total = uniform64(total);
+  const int64_t ex = before + incl - mine;  // first unit of this thread's range
+  const int64_t seg = seg::segment_units(total, W, seg_fixed);
+  if (blockIdx.x == 0) {
+    if (tid == 0) {
+      hdr[0] = total;
+      hdr[1] = seg;
     }
-    const int64_t ex = carry + before + incl - n;
-    if (i < S) {
-      if (blockIdx.x == 0) excl_out[i] = ex;
+    int64_t e = ex;
+    for (int i = r_lo; i < r_hi; ++i) {
+      excl_out[i] = e;
+      e += units_at(i);
+    }
+  }
+
+  // ---- the texts holding this workgroup's segment starts ----
 #pragma unroll
-      for (int j = 0; j < kWavesPerGroup; ++j) {
-        const int64_t c0 = ((int64_t)blockIdx.x * kWavesPerGroup + j) * seg;
-        if (c0 >= ex && c0 < ex + n) {
+  for (int j = 0; j < kWavesPerGroup; ++j) {
+    const int64_t c0 = ((int64_t)blockIdx.x * kWavesPerGroup + j) * seg;
+    if (c0 >= ex && c0 < ex + mine) {
+      int64_t e = ex;
+      for (int i = r_lo; i < r_hi; ++i) {
+        const int64_t n = units_at(i);
+        if (c0 < e + n) {
           sh_seq[j] = i;
-          sh_off[j] = c0 - ex;
-          sh_excl[j] = ex;
+          sh_off[j] = c0 - e;
+          sh_excl[j] = e;
+          break;
         }
+        e += n;
       }
     }
-    carry += all;
   }
   __syncthreads();
 
@@ -763,7 +766,7 @@ __device__ __forceinline__ void merge_run(const float* __restrict__ partials, in
   constexpr int PER = D / 64;  // output elements per lane
   constexpr int UNROLL = 8;
   auto index_of = [&](int64_t w) -> int64_t {
-    return partial_index<D, GS>(w, (w == w0 && run_lo != w0 * seg) ? 1 : 0, j);
+    return partial_index<D, GS>(w, seg::partial_slot(run_lo, w * seg), j);
   };
   // init: a state (m, l, pad, pad, acc[D]) that comes first, before the partials
   float M = -INFINITY, den = 0.f, num[PER];
@@ -828,12 +831,12 @@ __device__ __forceinline__ void merge_run(const float* __restrict__ partials, in
 }
 
 // Merge pass: one wave per (text, query head); runs finished inside one segment
-// return at once.
+// return at once. W: segments of the partition launch (the merge range is clamped to it).
 template <int QT, int D, int GS>
 __global__ __launch_bounds__(kThreads) void decode_merge(
     char* __restrict__ out, const int32_t* __restrict__ ctx, int S, int H, int Hkv, int maxb,
-    int bsz, float v_scale, const int64_t* __restrict__ hdr, const int64_t* __restrict__ excl,
-    const float* __restrict__ partials, Prefix pf) {
+    int bsz, int W, float v_scale, const int64_t* __restrict__ hdr,
+    const int64_t* __restrict__ excl, const float* __restrict__ partials, Prefix pf) {
   const int lane = threadIdx.x & 63;
   const int64_t pair =
       (int64_t)blockIdx.x * kWavesPerGroup + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -847,7 +850,8 @@ __global__ __launch_bounds__(kThreads) void decode_merge(
   const int U = units_of(L);
   const int64_t seg = hdr[1];
   const int64_t lo = excl[s] + (int64_t)r * U, hi = lo + U;
-  const int64_t w0 = lo / seg, w1 = (hi - 1) / seg;
+  int64_t w0, w1;
+  seg::run_segments(lo, hi, seg, W, &w0, &w1);
   if (w0 == w1) return;
   if (pf.mode == 1) {
     float* row = prefix_state_row<D>(pf, Hkv, Gq, pf.vfirst[s], pf.vcount[s], h);
@@ -1084,7 +1088,7 @@ __device__ __forceinline__ void flush_run_mma(MmaState<D>& st, const Cursor& c, 
         store_out<QT, 4>(dst + (16 * mt + 4 * grp) * elt_size<QT>(), o);
       }
     } else {
-      const int slot = run_lo <= seg_lo ? 0 : 1;
+      const int slot = seg::partial_slot(run_lo, seg_lo);
       float* p = partials + partial_index<D, GS>(w, slot, col);
       if (grp == 0) {
         p[0] = st.m;
@@ -1247,7 +1251,7 @@ bool launch(const Launch& a) {
   const int64_t pairs = (int64_t)a.S * a.H;
   const int mgroups = (int)((pairs + kWavesPerGroup - 1) / kWavesPerGroup);
   hipLaunchKernelGGL((decode_merge<QT, D, GS>), dim3(mgroups), dim3(kThreads), 0, a.st, a.out,
-                     a.ctx, a.S, a.H, a.Hkv, a.maxb, B, a.v_scale, hdr, excl, part, a.pf);
+                     a.ctx, a.S, a.H, a.Hkv, a.maxb, B, a.W, a.v_scale, hdr, excl, part, a.pf);
   return true;
 }
 

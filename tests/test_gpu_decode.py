@@ -246,3 +246,21 @@ def test_repeated_launches_are_bit_identical(native):
         assert_close(first, want, "f16", f"T={T}")
         for o in outs[1:]:
             assert torch.equal(o.cpu().view(torch.int16), first.view(torch.int16))
+
+
+@pytest.mark.parametrize("H,Hkv", [(8, 8), (16, 2)])
+def test_context_beyond_the_host_bound(native, H, Hkv):
+    """context_lens above max_context_len (still within the tables) with 16-token
+    partitions: the grid is sized for the smaller bound, so the segments lengthen to cover
+    every unit and the merge stays inside the grid. Sharp scores (q x 32, V ~ N(0,1)):
+    an output left stale (7.0) or a partial read from the wrong place would show."""
+    lens = [300, 1000, 64, 777, 1]
+    say(f"context beyond host bound H={H} Hkv={Hkv}")
+    q, kc, vc, tables, L = make_case(31 + H, lens, H, Hkv, 128, 16, "f16",
+                                     kv_std=1.0 / math.sqrt(128), q_std=32.0)
+    vc = torch.where(torch.isnan(vc), vc, vc * math.sqrt(128))
+    want = decode_attention(q, kc, vc, tables, L, 16)
+    for T in (16, 48):
+        got = run_gpu(native, q, kc, vc, tables, L, partition_tokens=T, max_ctx=100)
+        assert torch.isfinite(got.float()).all()
+        assert_close(got, want, "f16", f"T={T} max_context_len=100")

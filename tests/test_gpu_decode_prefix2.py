@@ -161,3 +161,18 @@ def test_nested_inner_group_across_outer_groups(native):
     ig = [(0, 1, 64 + 32), (1, 4, 200)]
     check(native, "f16", (q, kc, vc, tables, lens, og, ig), "straddling inner group",
           inner_members=4)
+
+
+def test_nested_inner_group_across_equal_outer_groups(native):
+    """Two outer groups with the same shared length (the usual case: prompts of equal
+    length) and an inner group straddling them: the members from the second outer group
+    are left out of it (their outer group differs from the first member's, though their
+    outer shared length is the same), so the result is still the whole-table attention.
+    Sharp scores, so reading the first member's blocks for the others would show."""
+    outer = [(64, [(32, [5, 6])]), (64, [(32, [7, 8])])]
+    q, kc, vc, tables, lens, og, ig = make_nested(19, outer, 4, 4, 128, 16, "f16", q_std=32.0)
+    # inner groups: text 0 alone, then texts 1 .. 3 (text 1 in the first outer group, texts
+    # 2 and 3 in the second; all three have 64 outer tokens)
+    ig = [(0, 1, 64 + 32), (1, 3, 64 + 32)]
+    check(native, "f16", (q, kc, vc, tables, lens, og, ig), "inner group across equal outer groups",
+          inner_members=4)

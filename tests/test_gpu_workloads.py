@@ -25,6 +25,33 @@ def bits(t):
     return t.view(torch.int32) if t.element_size() == 4 else t.view(torch.int16)
 
 
+# Relative bound on max |error| / max |out| over the checked outputs: half an ulp of the
+# output format (its rounding) plus 1e-3 of fp32 accumulation room; fp32 outputs 1e-5.
+REL_GATE = {"f32": 1e-5, "f16": 2.0 ** -11 + 1e-3, "bf16": 2.0 ** -8 + 1e-3}
+
+
+def relative_error(nat_steps, ora_steps, pairs_for):
+    """max |got - want| / max |want| over every step's checked outputs."""
+    num = den = 0.0
+    for t, (n, o) in enumerate(zip(nat_steps, ora_steps)):
+        got = n.out.cpu().to(torch.float64).numpy()
+        want = o.out
+        for s, h in pairs_for(t):
+            num = max(num, float(np.abs(got[s, h] - want[s, h]).max()))
+            den = max(den, float(np.abs(want[s, h]).max()))
+    return num / den, num, den
+
+
+def log_parity(record: dict):
+    """Append one JSON line to $PA_PARITY_LOG (if set): the full-size parity figures."""
+    import json
+    import os
+    path = os.environ.get("PA_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(record) + "\n")
+
+
 def compare_steps(w, nat_steps, ora_steps, pairs_for=None, strict_gate=False):
     assert len(nat_steps) == len(ora_steps) == w.steps
     worst = 0.0
@@ -119,9 +146,11 @@ FULL = [wl.OPT13B_7x2048, wl.OPT13B_MIXED256, wl.SHARING_32x8, wl.LONG_16x32K,
         wl.LLAMA70B_32x4096, wl.OPT13B_7x2048_FP8]
 
 
-@pytest.mark.parametrize("w", FULL, ids=lambda w: w.name)
-def test_full_size_workload(native, w):
-    say(f"workload {w.name} (full size)")
+def run_full_size(w, nsample=48, strict_gate=True):
+    """The workload's script through the native path (the bench's launch configuration:
+    random placement, NaN in every place never written) and through the oracle in logical
+    mode; every (text, head) output compared when there are at most 280, else a seeded
+    sample. Returns (worst abs error, relative error, pairs checked per step)."""
     d = wl.draw(w, device="cuda")
     ops = wl.script(w, d)
     nat = NativeReplay(w, d)
@@ -134,16 +163,51 @@ def test_full_size_workload(native, w):
     def pairs_for(t):
         if every:
             return [(s, h) for s in range(w.num_seqs) for h in range(w.num_heads)]
-        return sample_pairs(lens0, w.num_heads, 48, seed=t)
+        return sample_pairs(lens0, w.num_heads, nsample, seed=t)
 
     ora = Replay(w, d, pool=False)
     os_ = ora.run(ops, decode_pairs=pairs_for)
     say("  oracle done")
-    err = compare_steps(w, ns, os_, pairs_for=pairs_for, strict_gate=True)
+    err = compare_steps(w, ns, os_, pairs_for=pairs_for, strict_gate=strict_gate)
     check_sampled_slots(nat, ora, w, d)
     if w.length_kind == "sharing":
         assert sum(len(s.pairs) for s in ns) > 0
-    say(f"  max abs error {err:.3e}")
+    rel, num, den = relative_error(ns, os_, pairs_for)
+    return err, rel, den, len(pairs_for(0))
+
+
+@pytest.mark.parametrize("w", FULL, ids=lambda w: w.name)
+def test_full_size_workload(native, w):
+    say(f"workload {w.name} (full size)")
+    err, rel, den, npairs = run_full_size(w)
+    say(f"  max abs error {err:.3e}; relative {rel:.3e} (max |out| {den:.3e})")
+    log_parity({"workload": w.name, "variant": "plain", "steps": w.steps,
+                "pairs_per_step": npairs, "max_abs_err": err, "max_abs_out": den,
+                "rel_err": rel})
+
+
+SHARP = [wl.OPT13B_7x2048, wl.OPT13B_MIXED256, wl.LONG_16x32K, wl.LLAMA70B_32x4096,
+         wl.OPT13B_7x2048_FP8]
+
+
+@pytest.mark.parametrize("base", SHARP, ids=lambda w: w.name)
+def test_full_size_sharp(native, base):
+    """Each full-size workload with a peaked softmax (queries x 32, values N(0, 1): scores
+    of standard deviation ~2.8, outputs of order 1 made of few tokens), at its shapes and
+    pool size (the 6.4 and 5.4 GB pools of the mixed and long workloads put blocks past
+    4 GiB), random placement and NaN in every unwritten place. Gated on the absolute bound
+    and on max |error| / max |out|: an output that attended a wrong, dropped or doubled
+    block moves by far more than either."""
+    w = wl.sharp(base)
+    say(f"workload {w.name} (full size, sharp)")
+    err, rel, den, npairs = run_full_size(w, nsample=64, strict_gate=False)
+    gate = REL_GATE[w.dtype]
+    say(f"  max abs error {err:.3e}; relative {rel:.3e} (max |out| {den:.3e}, gate {gate:.2e})")
+    log_parity({"workload": w.name, "variant": "sharp", "steps": w.steps,
+                "pairs_per_step": npairs, "max_abs_err": err, "max_abs_out": den,
+                "rel_err": rel, "rel_gate": gate})
+    assert den > 0.5, "the sharp variant must give outputs of order 1"
+    assert rel <= gate, f"{w.name}: relative error {rel:.3e} > {gate:.2e}"
 
 
 class SharedDecodes(NativeReplay):
@@ -190,11 +254,14 @@ class SharedDecodes(NativeReplay):
         self.shared["nested"].append(out2)
 
 
-def test_full_size_sharing_shared_block_decodes(native):
+@pytest.mark.parametrize("variant", ["plain", "sharp"])
+def test_full_size_sharing_shared_block_decodes(native, variant):
     """The sharing workload at full size (32 groups x 8 samples, 1,024-token prompts, pair
     forks with copy-on-write every step): both shared-block decodes against the oracle on
-    sampled (text, head) pairs, every step, within the plain 2e-3 gate."""
-    w = wl.SHARING_32x8
+    sampled (text, head) pairs, every step, within the plain 2e-3 gate (plain variant) or
+    the per-element bound and the relative bound (sharp variant: queries x 32, values
+    N(0, 1))."""
+    w = wl.SHARING_32x8 if variant == "plain" else wl.sharp(wl.SHARING_32x8)
     say(f"workload {w.name} (full size), shared-block decodes")
     d = wl.draw(w, device="cuda")
     ops = wl.script(w, d)
@@ -208,8 +275,17 @@ def test_full_size_sharing_shared_block_decodes(native):
 
     ora = Replay(w, d, pool=False)
     os_ = ora.run(ops, decode_pairs=pairs_for)
-    for kind in ("prefix", "nested"):
-        steps = [StepOut(o, s.slots, s.pairs, s.tables, s.lens, s.seq_ids)
-                 for o, s in zip(nat.shared[kind], ns)]
-        err = compare_steps(w, steps, os_, pairs_for=pairs_for, strict_gate=True)
-        say(f"  {kind}: max abs error {err:.3e}")
+    for kind in ("plain", "prefix", "nested"):
+        if kind == "plain":
+            steps = ns
+        else:
+            steps = [StepOut(o, s.slots, s.pairs, s.tables, s.lens, s.seq_ids)
+                     for o, s in zip(nat.shared[kind], ns)]
+        err = compare_steps(w, steps, os_, pairs_for=pairs_for, strict_gate=variant == "plain")
+        rel, num, den = relative_error(steps, os_, pairs_for)
+        say(f"  {kind}: max abs error {err:.3e}; relative {rel:.3e} (max |out| {den:.3e})")
+        log_parity({"workload": w.name, "variant": variant, "decode": kind, "steps": w.steps,
+                    "pairs_per_step": len(pairs_for(0)), "max_abs_err": err,
+                    "max_abs_out": den, "rel_err": rel})
+        if variant == "sharp":
+            assert den > 0.5 and rel <= REL_GATE[w.dtype], (kind, rel)

@@ -43,6 +43,8 @@ class Workload:
     kv_std: float
     q_std: float
     steps: int = 1
+    # standard deviation of the values when it differs from the keys' (0: kv_std)
+    v_std: float = 0.0
     # "fixed": every sequence attends `ctx_fixed` tokens at step 0.
     # "list": attended lengths at step 0 are `ctx_list`.
     # "uniform": attended lengths ~ U{ctx_lo..ctx_hi} (inclusive).
@@ -67,6 +69,10 @@ class Workload:
     @property
     def pool_dtype(self) -> str:
         return self.cache_dtype or self.dtype
+
+    @property
+    def value_std(self) -> float:
+        return self.v_std or self.kv_std
 
     def scaled(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -120,22 +126,34 @@ LLAMA70B_32x4096 = Workload(
     description="Llama-2-70B-shaped layer: 64 query heads sharing 8 key/value heads of 128, "
                 "fp16, block 16, 32 x 4,096 tokens")
 
-# The cache kept in 8-bit floating point (P1 "What Came After": one byte a number, about
-# twice the tokens in the same memory): the OPT-13B 7 x 2,048 step with E4M3 pools. The
-# scales 1/256 (exact reciprocals) map the drawn keys/values (std 0.088) well inside E4M3's
-# range (448 * 1/256 = 1.75, about 20 standard deviations).
 GQA4_32x4096 = Workload(
     name="gqa4_32x4096_f16_b16", seed=7, num_seqs=32, num_heads=32, num_kv_heads=8,
     head_dim=128, block_size=16, num_blocks=32 * 257 + 64, dtype="f16",
     kv_std=1 / math.sqrt(128), q_std=1.0, steps=4, length_kind="fixed", ctx_fixed=4096,
     description="shared K/V heads, 4 query heads per K/V head: 32 query heads over 8 K/V "
                 "heads x 128, fp16, block 16, 32 texts x 4096 tokens")
+# The cache kept in 8-bit floating point (P1 "What Came After": one byte a number, about
+# twice the tokens in the same memory): the OPT-13B 7 x 2,048 step with E4M3 pools. The
+# scales 1/256 (exact reciprocals) map the drawn keys/values (std 0.088) well inside E4M3's
+# range (448 * 1/256 = 1.75, about 20 standard deviations).
 OPT13B_7x2048_FP8 = OPT13B_7x2048.scaled(
     name="opt13b_7x2048_fp8_b16", cache_dtype="fp8", k_scale=1 / 256, v_scale=1 / 256,
     description="OPT-13B one layer with an E4M3 cache: 40 heads x 128, fp16 queries, "
                 "block 16, 7 x 2048 tokens, pool scales 1/256")
 
 ALL = (TINY, OPT13B_7x2048, OPT13B_MIXED256, SHARING_32x8, LONG_16x32K)
+
+
+def sharp(w: Workload) -> Workload:
+    """The workload with a peaked softmax: queries x 32 (scores of standard deviation about
+    2.8 instead of 0.088) and values N(0, 1), so that a dropped, doubled or misplaced block
+    moves the output by far more than the accuracy bound. E4M3 pools keep the values inside
+    the format's range with a value scale of 1/32 (largest code 448 / 32 = 14)."""
+    kw = dict(name=w.name + "_sharp", q_std=32.0 * w.q_std, v_std=1.0,
+              description=w.description + "; sharp: queries x 32, values N(0, 1)")
+    if w.pool_dtype == "fp8":
+        kw["v_scale"] = 1 / 32
+    return w.scaled(**kw)
 
 
 # --- Prompt-phase workloads ----------------------------------------------------
@@ -290,15 +308,15 @@ def draw(w: Workload, device: Optional[str] = None) -> Draws:
     pk, pv = [], []
     for n in prefill_lens:
         pk.append(st.normal((n, Hk, D), w.kv_std, w.dtype))
-        pv.append(st.normal((n, Hk, D), w.kv_std, w.dtype))
+        pv.append(st.normal((n, Hk, D), w.value_std, w.dtype))
     sk, sv = [], []
     for n in suffix_lens:
         sk.append(st.normal((n, Hk, D), w.kv_std, w.dtype))
-        sv.append(st.normal((n, Hk, D), w.kv_std, w.dtype))
+        sv.append(st.normal((n, Hk, D), w.value_std, w.dtype))
     step_k, step_v, step_q = [], [], []
     for _ in range(w.steps):
         step_k.append(st.normal((w.num_seqs, Hk, D), w.kv_std, w.dtype))
-        step_v.append(st.normal((w.num_seqs, Hk, D), w.kv_std, w.dtype))
+        step_v.append(st.normal((w.num_seqs, Hk, D), w.value_std, w.dtype))
         step_q.append(st.normal((w.num_seqs, w.num_heads, D), w.q_std, w.dtype))
     return Draws(free_order=free_order, prefill_lens=prefill_lens, prefill_k=pk, prefill_v=pv,
                  step_k=step_k, step_v=step_v, step_q=step_q, suffix_lens=suffix_lens,
