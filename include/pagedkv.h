@@ -255,6 +255,27 @@ int pa_decode_attention(void* out, const void* q, const void* k_cache, const voi
                         int32_t partition_tokens, float scale, int32_t dtype,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* pa_decode_attention without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). The workspace is the library's own: a device array of
+ * pa_decode_noalloc_max_bytes() = 16 MiB, one copy per GPU (devices 0..63), set up on the
+ * first call on each device and held until the process ends. This call allocates nothing.
+ * A launch whose workspace (pa_decode_workspace_bytes for the same arguments) would exceed
+ * it is refused with PA_EINVAL before anything is launched: with partition_tokens 0 a
+ * head_dim-128 launch needs 8.7 MB plus 8 bytes per text on 256 compute units. Every call
+ * on one GPU uses the same array: calls that may overlap on one GPU (two streams, two
+ * threads) race and give wrong results; order them on one stream. The array needs no
+ * clearing (each launch writes what it reads). Otherwise as pa_decode_attention. */
+size_t pa_decode_noalloc_max_bytes(void);
+int pa_decode_attention_noalloc(void* out, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, int32_t num_seqs,
+                                int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, int32_t num_blocks,
+                                int32_t max_blocks_per_seq, int32_t max_context_len,
+                                int32_t partition_tokens, float scale, int32_t dtype,
+                                void* stream);
+
 /* Decode attention over PA_FP8_E4M3 pools: every stored key is decode(code) * k_scale,
  * every value decode(code) * v_scale; q and out are q_dtype (PA_F16 or PA_BF16).
  * Otherwise as pa_decode_attention (same workspace sizing). */

@@ -52,6 +52,10 @@ SIGNATURES = {
     "pa_decode_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                            _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32,
                                            _vp, _sz, _vp]),
+    "pa_decode_noalloc_max_bytes": (_sz, []),
+    "pa_decode_attention_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                                   _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                   ctypes.c_float, _i32, _vp]),
     "pa_decode_attention_write": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                                  _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                                  _i32, ctypes.c_float, _i32, _vp, _sz, _vp]),
@@ -424,6 +428,27 @@ def pa_decode_attention(out, q, k_cache, v_cache, block_tables, context_lens, ma
         N, int(block_tables.shape[1]), int(max_context_len), int(partition_tokens), float(scale),
         dtype_code(q), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+
+
+def pa_decode_noalloc_max_bytes() -> int:
+    return int(lib().pa_decode_noalloc_max_bytes())
+
+
+def pa_decode_attention_noalloc(out, q, k_cache, v_cache, block_tables, context_lens,
+                                max_context_len: int, partition_tokens: int = 0,
+                                scale: Optional[float] = None, stream=None) -> None:
+    """pa_decode_attention with the library's own workspace (no allocation)."""
+    S, H, D = q.shape
+    N, Hkv, B, Dk = k_cache.shape
+    assert Dk == D and tuple(out.shape) == (S, H, D)
+    assert block_tables.shape[0] == S and context_lens.numel() == S
+    if scale is None:
+        scale = D ** -0.5
+    _check(lib().pa_decode_attention_noalloc(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), S, H, Hkv, D, B,
+        N, int(block_tables.shape[1]), int(max_context_len), int(partition_tokens), float(scale),
+        dtype_code(q), _stream(stream)))
 
 
 def pa_decode_attention_write(out, q, k_cache, v_cache, k_new, v_new, slots, block_tables,

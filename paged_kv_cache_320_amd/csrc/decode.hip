@@ -3,6 +3,7 @@
 #include "decode_kernels.hpp"
 
 #include <cmath>
+#include <mutex>
 
 namespace pagedkv {
 namespace {
@@ -204,6 +205,77 @@ extern "C" int pa_decode_attention_write(void* out, const void* q, void* k_cache
                        num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                        max_context_len, partition_tokens, scale, 1.0f, 1.0f, dtype, dtype,
                        workspace, workspace_bytes, stream, nr);
+}
+
+// ---- decode with the library's own workspace ---------------------------------------
+//
+// For callers that cannot allocate device memory (code under graph capture, tight serving
+// loops, harnesses that forbid hipMalloc): the workspace is a file-scope device array, one
+// copy per GPU, held until the process ends. Calls on one GPU share it.
+
+namespace pagedkv {
+
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+constexpr int kScratchDevices = 64;
+
+// Workspace of pa_decode_attention_noalloc. Host code must not pass this name to a kernel
+// (on the host it is only a stand-in for the symbol): scratch_address() gives the device
+// address of the current GPU's copy.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+std::mutex scratch_mu;
+void* scratch_ptr[kScratchDevices];
+
+// The current GPU's copy of `scratch`, looked up once per device with that device current.
+int scratch_address(void** out) {
+  int dev = 0;
+  PA_HIP_CHECK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(PA_EUNSUPPORTED, "device %d: the built-in workspace serves devices 0..%d", dev,
+                kScratchDevices - 1);
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    PA_HIP_CHECK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(PA_EHIP, "hipGetSymbolAddress gave a null address for the workspace");
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return PA_OK;
+}
+
+}  // namespace
+}  // namespace pagedkv
+
+extern "C" size_t pa_decode_noalloc_max_bytes(void) { return kScratchBytes; }
+
+extern "C" int pa_decode_attention_noalloc(void* out, const void* q, const void* k_cache,
+                                           const void* v_cache, const int32_t* block_tables,
+                                           const int32_t* context_lens, int32_t num_seqs,
+                                           int32_t num_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size,
+                                           int32_t num_blocks, int32_t max_blocks_per_seq,
+                                           int32_t max_context_len, int32_t partition_tokens,
+                                           float scale, int32_t dtype, void* stream) {
+  if (!dtype_ok(dtype)) return fail(PA_EINVAL, "dtype %d is not PA_F32/PA_F16/PA_BF16", dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
+  Layout lay;
+  int rc = layout(num_seqs, num_heads, head_dim, max_context_len, partition_tokens, &lay);
+  if (rc != PA_OK) return rc;
+  if (lay.bytes > kScratchBytes)
+    return fail(PA_EINVAL, "this launch needs %zu bytes of workspace, more than the %zu of the "
+                "built-in one (fewer texts, partition_tokens 0, or pa_decode_attention with a "
+                "workspace)", lay.bytes, kScratchBytes);
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc != PA_OK) return rc;
+  return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
+                       num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                       max_context_len, partition_tokens, scale, 1.0f, 1.0f, dtype, dtype, ws,
+                       kScratchBytes, stream);
 }
 
 // ---- decode over shared prompt blocks --------------------------------------------

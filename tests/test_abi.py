@@ -69,3 +69,19 @@ def test_device_entry_points_validate_before_any_hip_call(native):
     rc = L.pa_decode_attention(None, None, None, None, None, None, 1, 8, 8, 128, 16, 10, 4, 64, 0,
                                0.1, 1, None, 0, None)
     assert rc == native.PA_EINVAL and "null" in native.pa_last_error()
+
+
+def test_noalloc_refuses_past_its_workspace_before_any_hip_call(native):
+    """The allocation-free decode refuses a launch whose workspace would exceed its built-in
+    array (16 MiB), and bad shapes, before touching the device."""
+    L = native.lib()
+    assert native.pa_decode_noalloc_max_bytes() == 16 << 20
+    rc = L.pa_decode_attention_noalloc(None, None, None, None, None, None, 64, 40, 40, 128, 16, 4,
+                                       2048, 32768, 16, 0.1, 1, None)
+    assert rc == native.PA_EINVAL and "built-in" in native.pa_last_error()
+    rc = L.pa_decode_attention_noalloc(None, None, None, None, None, None, 1, 8, 8, 80, 16, 4, 4,
+                                       64, 16, 0.1, 1, None)
+    assert rc == native.PA_EUNSUPPORTED
+    rc = L.pa_decode_attention_noalloc(None, None, None, None, None, None, 1, 8, 8, 128, 16, 4, 4,
+                                       64, 16, 0.1, 9, None)
+    assert rc == native.PA_EINVAL
