@@ -82,15 +82,30 @@ def src_hash() -> str:
 
 
 def measured_traffic(fused: bool):
-    """HBM bytes per decode launch from the committed counter runs, if the kernel is unchanged
-    (same sources, and the same variant: with or without the fused new-token write)."""
+    """The committed counter record of the decode launch (HBM bytes per launch and the run they
+    come from), if the kernel is unchanged (same sources, and the same variant: with or
+    without the fused new-token write); else None."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
     if rec.get("decode_src_sha256_16") != src_hash() or rec.get("fused_write", False) != fused:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
+
+
+def traffic_note(rec):
+    """Where roofline.traffic comes from: the counter runs' steps and their own algorithmic
+    bytes per launch (the ratio is taken within those runs)."""
+    if not rec:
+        return None
+    alg = rec.get("algorithmic_bytes_per_launch")
+    note = (f"rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE of `bench.py --steps "
+            f"{rec.get('steps')} --warmup {rec.get('warmup')}`, copy-calibrated")
+    if alg:
+        note += (f"; that run's algorithmic bytes per launch {alg}, HBM / algorithmic "
+                 f"{rec['hbm_bytes_per_launch'] / alg:.4f}")
+    return note
 
 
 COPY_CAL_BYTES = 512 << 20
@@ -142,9 +157,23 @@ def traffic_from_counters(fetch_dir: str, write_dir: str) -> None:
                                          (float(np.median(merge)) if merge else 0.0)) * 1024 * scale}
     if len(fused) != 1:
         raise SystemExit("counter runs mix the decode kernel with and without the fused write")
-    rec = {"decode_src_sha256_16": src_hash(), "workload": "opt13b_7x2048_f16_b16",
+    # the profiled runs' own JSON lines (--line-out DIR/line.json): their algorithmic bytes
+    lines = []
+    for d in (fetch_dir, write_dir):
+        try:
+            lines.append(json.load(open(os.path.join(d, "line.json"))))
+        except (OSError, ValueError):
+            raise SystemExit(f"{d}/line.json missing: profile `bench.py --copy-calibration "
+                             f"--line-out {d}/line.json`")
+    alg = float(np.mean([ln["roofline"]["bytes_per_launch"] for ln in lines]))
+    hbm = int(res["fetch"]["bytes_per_launch"] + res["write"]["bytes_per_launch"])
+    rec = {"decode_src_sha256_16": src_hash(), "workload": lines[0]["config"]["workload"],
            "fused_write": fused.pop(),
-           "hbm_bytes_per_launch": int(res["fetch"]["bytes_per_launch"] + res["write"]["bytes_per_launch"]),
+           "steps": lines[0]["steps"], "warmup": lines[0]["warmup"],
+           "layers": lines[0]["config"]["layers_per_step"],
+           "hbm_bytes_per_launch": hbm,
+           "algorithmic_bytes_per_launch": int(alg),
+           "hbm_over_algorithmic": round(hbm / alg, 5),
            "fetch": res["fetch"], "write": res["write"],
            "calibration": f"pa_copy_probe reading and writing {COPY_CAL_BYTES} bytes"}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
@@ -266,6 +295,18 @@ def run_swap_probe(cache, seqs, torch, reps: int = 3):
     return (nbytes / (min(t_out) * 1e-3) / 1e9, nbytes / (min(t_in) * 1e-3) / 1e9, nbytes)
 
 
+def host_cores() -> dict:
+    """The host the CPU baseline ran on: logical CPUs, the ones this process may use, and the
+    BLAS threads numpy would use by default (the baseline itself is limited to one)."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((p.get("num_threads", 0) for p in threadpool_info()), default=None)
+    except Exception:
+        blas = None
+    return {"nproc": os.cpu_count(), "affinity_cores": len(os.sched_getaffinity(0)),
+            "blas_threads_default": blas, "baseline_threads": 1}
+
+
 def cpu_baseline(w, d0, seconds: float, gpu_out0):
     """The oracle as it stands, on one layer's step-0 batch, one thread, about `seconds` long."""
     import numpy as np
@@ -305,6 +346,7 @@ def cpu_baseline(w, d0, seconds: float, gpu_out0):
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
+        "host": host_cores(),
         "sample": f"{w.name} one layer, step 0: all {w.num_seqs * w.num_heads} (text, head) pairs "
                   f"x {reps} repetitions in {dt:.1f} s (fp64 numpy, BLAS limited to 1 thread)",
         "seq_layers_per_s": round(w.num_seqs * reps / dt, 3),
@@ -322,7 +364,7 @@ def unique_kv_bytes(tables, lens, B, Hkv, D, kv_elt) -> int:
     return sum(filled.values()) * 2 * Hkv * D * kv_elt
 
 
-def bench_sharing(args, base) -> None:
+def bench_sharing(args, base, K: int, W: int) -> dict:
     """Parallel sampling / beam search: groups of texts share their prompt's blocks. Every
     step each odd sample is replaced by a fork of its even partner (the pair then shares a
     partly filled last block), one token is appended to every text (copy-on-write copies
@@ -335,7 +377,6 @@ def bench_sharing(args, base) -> None:
     import workloads as wl
     from paged_kv_cache_320_amd import PagedKVCache, _lib as L, torch_dtype
 
-    K, W = args.steps, args.warmup
     w = base.scaled(steps=K + W)
     S, H, Hkv, D, B = w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size
     NL = args.layers or 8
@@ -498,6 +539,8 @@ def bench_sharing(args, base) -> None:
     if cev:
         log(f"block copies: {np.mean(copy_us):.1f} us per layer ({np.mean(copy_bytes) / 1e6:.1f} MB "
             f"read + written, {copy_gbps:.0f} GB/s)")
+    used_blocks, filled = cache.alloc.stats()
+    util = filled / (used_blocks * B) if used_blocks else None
     log(f"step {total_ms / K * 1e3:.1f} us ({NL} layers, {np.mean(copies):.0f} block copies "
         f"per layer), decode launch {avg * 1e3:.1f} us: unique {u_launch / 1e9:.2f} GB -> "
         f"{achieved:.0f} GB/s = {achieved / HBM_PEAK_GBPS:.1%} of 8 TB/s; logical "
@@ -524,7 +567,12 @@ def bench_sharing(args, base) -> None:
                                ("pa_kv_write + pa_decode_attention_prefix" +
                                 ("2" if mode == "nested" else "") + " (set-up, shared blocks "
                                 "once per group, each text's own blocks, merges)"),
-                     "avg_launch_us": round(avg * 1e3, 2), "bytes_per_launch": int(u_launch)},
+                     "avg_launch_us": round(avg * 1e3, 2),
+                     "median_launch_us": round(float(np.median(launch_ms)) * 1e3, 2),
+                     "min_launch_us": round(float(min(launch_ms)) * 1e3, 2),
+                     "bytes_per_launch": int(u_launch)},
+        "seq_layers_per_s": round(S * NL * K / (total_ms * 1e-3), 1),
+        "cache_holding_tokens": round(util, 4) if util is not None else None,
         "logical_gbps": round(l_launch / (avg * 1e-3) / 1e9, 1),
         "logical_bytes_per_launch": int(l_launch),
         "block_copies_per_layer_per_step": float(np.mean(copies)),
@@ -532,7 +580,7 @@ def bench_sharing(args, base) -> None:
         "copy_blocks_gbps": round(copy_gbps, 1) if cev else None,
         "cpu_baseline": None,
     }
-    print(json.dumps(line), flush=True)
+    return line
 
 
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}   # dense fp16/bf16 matrix-core peak
@@ -545,7 +593,7 @@ def prompt_flops(prompt_lens, prefix_len, H, D) -> int:
     return 4 * D * H * keys
 
 
-def bench_prompt(args, w) -> None:
+def bench_prompt(args, w) -> dict:
     """The prompt phase: per step, every text is added (after the shared cached prefix,
     if any), its prompt's keys and values are written, and pa_prefill_attention runs."""
     import numpy as np
@@ -679,7 +727,7 @@ def bench_prompt(args, w) -> None:
         "sampled_max_abs_err_vs_oracle": err0,
         "wall_s_timed": round(wall, 4),
     }
-    print(json.dumps(line), flush=True)
+    return line
 
 
 def cpu_baseline_prompt(w, d, tables0, seconds: float, gpu_out0):
@@ -730,67 +778,24 @@ def cpu_baseline_prompt(w, d, tables0, seconds: float, gpu_out0):
     flops = 4 * D * keys
     err = float(max(np.abs(gpu_out0[r, h].astype(np.float64) - got[(r, h)]).max() for r, h in done))
     return {"value": round(flops / dt / 1e9, 4), "unit": "GFLOP/s", "cores": 1, "kind": "oracle",
+            "host": host_cores(),
             "sample": f"{w.name} one layer, step 0: {len(done)} seeded (query row, head) pairs "
                       f"in {dt:.1f} s (fp64 numpy, BLAS limited to 1 thread)"}, err
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="opt13b_7x2048_f16_b16",
-                    help="fixed-length workload from workloads.BY_NAME")
-    ap.add_argument("--layers", type=int, default=0,
-                    help="pools (model layers) per step; 0 = enough for >= 2 GB of pools")
-    ap.add_argument("--partition-tokens", type=int, default=0)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-probe", action="store_true")
-    ap.add_argument("--separate-write", action="store_true",
-                    help="write each layer's new token with pa_kv_write before its decode launch "
-                         "instead of inside it (pa_decode_attention_write)")
-    ap.add_argument("--sharing-decode", choices=["nested", "prefix", "per-text"],
-                    default="nested",
-                    help="shared-prompt workloads: every shared block read once (the prompt per "
-                         "group, each forked pair's blocks per pair: pa_decode_attention_prefix2)"
-                         ", the prompt once per group (pa_decode_attention_prefix), or every "
-                         "text its whole table (pa_decode_attention_write)")
-    ap.add_argument("--graph", action="store_true",
-                    help="replay each decode step's writes and decode launches from HIP graphs "
-                         "captured for that step instead of launching them one by one")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run pa_copy_probe over 512 MiB (reference for memory counters)")
-    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
-                         "`bench.py --copy-calibration` into " + os.path.relpath(TRAFFIC_FILE, ROOT))
-    args = ap.parse_args()
-    if args.traffic_from:
-        traffic_from_counters(*args.traffic_from)
-        return
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the decode path shards by sequence with no exchange; see the design notes). "
-              f"Got --gpus {args.gpus}, WORLD_SIZE {world}.", file=sys.stderr)
-        sys.exit(2)
+def bench_decode(args, base, K: int, W: int, layers: int = 0, placement: str = "random",
+                 probes: bool = True, cpu: bool = True) -> dict:
+    """Decode steps of a workload whose texts each decode one token per step: the JSON line.
 
+    layers: pools per step (0: --layers, else enough for >= 2 GB of pools); placement
+    "random" (the workload's seeded free-list permutation) or "identity" (blocks handed out
+    in id order); probes / cpu: also run the read probes and swap probe / the CPU oracle."""
     import numpy as np
     import torch
 
     import workloads as wl
     from paged_kv_cache_320_amd import PagedKVCache, _lib as L, torch_dtype
 
-    L.lib()  # fails loudly when libpagedkv.so has not been built
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    K, W = args.steps, args.warmup
-    base = wl.BY_NAME[args.workload]
-    if isinstance(base, wl.PromptWorkload):
-        return bench_prompt(args, base)
-    if base.length_kind == "sharing":
-        return bench_sharing(args, base)
-    assert base.length_kind in ("fixed", "uniform", "list"), \
-        "bench.py times batches whose texts each decode one token per step (no forks)"
     kv_elt = ELT[base.pool_dtype]
     fp8 = base.pool_dtype == "fp8"
     w = base.scaled(steps=K + W)
@@ -800,7 +805,7 @@ def main():
     draws = [wl.draw(w, device="cuda")]
     lens0 = [n + 1 for n in draws[0].prefill_lens]  # attended at step 0
     per_layer = sum(lens0) * 2 * Hkv * D * kv_elt
-    NL = args.layers or min(16, max(8, -(-2_000_000_000 // per_layer)))
+    NL = layers or args.layers or min(16, max(8, -(-2_000_000_000 // per_layer)))
     need = sum((n + K + W + B - 1) // B for n in draws[0].prefill_lens)
     assert need <= w.num_blocks, f"the pool holds {w.num_blocks} blocks; {K + W} steps need {need}"
     log(f"{NL} layers")
@@ -808,8 +813,12 @@ def main():
         # every layer holds the same texts (lengths), with its own keys, values and queries
         draws.append(wl.draw(w.scaled(seed=w.seed * 1000 + li, length_kind="list",
                                       ctx_list=tuple(lens0)), device="cuda"))
+    # random placement: the workload's seeded permutation of the free list; identity: the
+    # free list in block order, so that every text's blocks are consecutive ids
+    free_order = draws[0].free_order if placement == "random" else \
+        np.arange(w.num_blocks, dtype=np.int32)
     cache = PagedKVCache(w.num_blocks, B, Hkv, D, w.pool_dtype, layers=NL, device="cuda",
-                         free_order=draws[0].free_order, fill=float("nan"),
+                         free_order=free_order, fill=float("nan"),
                          k_scale=w.k_scale, v_scale=w.v_scale)
     seqs = []
     for s in range(S):
@@ -938,7 +947,7 @@ def main():
             e1.record()
             ev.append((e0, e1))
 
-    if args.copy_calibration:
+    if args.copy_calibration and probes:
         run_copy_calibration(L, torch)
 
     log(f"warmup {W} steps")
@@ -977,16 +986,21 @@ def main():
     bytes_per_launch = float(np.mean([decode_bytes(l, H, D, B, elt, Hkv, kv_elt)
                                       for l in timed_lens]))
     achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
-    traffic = measured_traffic(fused) if base.name == "opt13b_7x2048_f16_b16" else None
+    traffic = measured_traffic(fused) if (base.name == "opt13b_7x2048_f16_b16" and
+                                          placement == "random") else None
     log(f"host time per step (allocator, uploads, launches) {host_s / K * 1e6:.1f} us")
     write_us = float(np.mean([a.elapsed_time(b) / NL * 1e3 for a, b in wev])) if wev else None
     if wev:
         log(f"separate new-token write: {write_us:.1f} us per layer")
+    used_blocks, filled = cache.alloc.stats()
+    util = filled / (used_blocks * B) if used_blocks else None
     log(f"step {ms_per_step * 1e3:.1f} us ({NL} layers), decode launch {avg_launch_ms * 1e3:.1f} us "
-        f"(min {min(launch_ms) * 1e3:.1f}), {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBPS:.1%} of 8 TB/s")
+        f"(median {np.median(launch_ms) * 1e3:.1f}, min {min(launch_ms) * 1e3:.1f}), "
+        f"{achieved:.0f} GB/s = {achieved / HBM_PEAK_GBPS:.1%} of 8 TB/s; {placement} placement; "
+        f"cache holding tokens {util:.2%}")
 
     probe = tprobe = vprobe = swap = None
-    if not args.no_probe:
+    if probes and not args.no_probe:
         probe = run_probe(L, torch)
         log(f"stream-read probe: {probe:.0f} GB/s")
         vprobe = run_volume_probe(L, torch, int(bytes_per_launch))
@@ -1001,7 +1015,7 @@ def main():
 
     cpu = None
     err0 = None
-    if not args.no_cpu_baseline:
+    if cpu and not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle, one layer, one thread")
         cpu, err0 = cpu_baseline(base, draws[0], args.cpu_seconds, out0)
         log(f"cpu baseline {cpu['value']} GB/s; step-0 max abs error vs oracle {err0:.3e}")
@@ -1019,7 +1033,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": f"synthetic (seeded N(0,1)*{w.kv_std:.4g} keys/values, N(0,{w.q_std:g}) queries; "
-                "random block placement)",
+                f"{placement} block placement)",
         "config": {"workload": base.name, "seqs": S,
                    "context_at_step0": (lens0[0] if len(set(lens0)) == 1 else
                                         f"{min(lens0)}..{max(lens0)}, mean {np.mean(lens0):.0f}"),
@@ -1033,12 +1047,17 @@ def main():
         "seq_layers_per_s": round(S * NL * K / (total_ms * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic,
+                     "traffic": traffic["hbm_bytes_per_launch"] if traffic else None,
+                     "traffic_source": traffic_note(traffic),
                      "kernel": ("pa_decode_attention_write = decode_partition (new-token write "
                                 "fused) + decode_merge") if fused else
                                "pa_decode_attention = decode_partition + decode_merge",
                      "avg_launch_us": round(avg_launch_ms * 1e3, 2),
+                     "median_launch_us": round(float(np.median(launch_ms)) * 1e3, 2),
+                     "min_launch_us": round(float(min(launch_ms)) * 1e3, 2),
                      "bytes_per_launch": int(bytes_per_launch)},
+        "cache_holding_tokens": round(util, 4) if util is not None else None,
+        "placement": placement,
         "kv_write_us_per_layer": round(write_us, 2) if wev else None,
         "swap_out_gbps": round(swap[0], 2) if swap else None,
         "swap_in_gbps": round(swap[1], 2) if swap else None,
@@ -1051,6 +1070,137 @@ def main():
         "wall_s_timed": round(wall, 4),
         "decode_src_sha256_16": src_hash(),
     }
+    return line
+
+
+CONFIG_RUNS = (
+    # (workload, steps, warmup, layers): the other decode configurations, each far beyond the
+    # 256 MB Infinity Cache per launch, timed after the headline one and reported beside it
+    ("opt13b_mixed256_f16_b16", 10, 3, 2),
+    ("long_16x32k_f16_b16", 6, 2, 2),
+    ("sharing_32x8_bf16_b16", 8, 2, 8),
+)
+
+
+def config_summary(line: dict) -> dict:
+    """The figures of one configuration's JSON line that go into the headline line."""
+    r = line["roofline"]
+    out = {"op_us_mean": r["avg_launch_us"], "op_us_median": r.get("median_launch_us"),
+           "op_us_min": r.get("min_launch_us"), "bytes_per_op": r["bytes_per_launch"],
+           "gbps": r["achieved"], "frac_of_hbm_peak": r["frac"],
+           "ms_per_step": line["ms_per_step"], "layers_per_step": line["config"]["layers_per_step"],
+           "steps": line["steps"], "kernel": r["kernel"]}
+    for k in ("seq_layers_per_s", "cache_holding_tokens", "logical_gbps",
+              "logical_bytes_per_launch", "copy_blocks_us_per_layer", "copy_blocks_gbps",
+              "placement"):
+        if k in line:
+            out[k] = line[k]
+    if "logical_gbps" in line:
+        out["bytes"] = "unique physical blocks (shared blocks once); logical beside it"
+    return out
+
+
+def free_gpu():
+    import torch
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="opt13b_7x2048_f16_b16",
+                    help="workload from workloads.BY_NAME")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="pools (model layers) per step; 0 = enough for >= 2 GB of pools")
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--placement", choices=["random", "identity"], default="random",
+                    help="block placement of the decode workloads: the seeded random free list, "
+                         "or blocks handed out in id order")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time only the headline workload (not the other configurations, nor "
+                         "the identity-placement run)")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="write each layer's new token with pa_kv_write before its decode launch "
+                         "instead of inside it (pa_decode_attention_write)")
+    ap.add_argument("--sharing-decode", choices=["nested", "prefix", "per-text"],
+                    default="nested",
+                    help="shared-prompt workloads: every shared block read once (the prompt per "
+                         "group, each forked pair's blocks per pair: pa_decode_attention_prefix2)"
+                         ", the prompt once per group (pa_decode_attention_prefix), or every "
+                         "text its whole table (pa_decode_attention_write)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each decode step's writes and decode launches from HIP graphs "
+                         "captured for that step instead of launching them one by one")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run pa_copy_probe over 512 MiB (reference for memory counters)")
+    ap.add_argument("--line-out", metavar="PATH",
+                    help="also write the JSON line to PATH (for the counter runs)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "`bench.py --copy-calibration --line-out DIR/line.json` into " +
+                         os.path.relpath(TRAFFIC_FILE, ROOT))
+    args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from_counters(*args.traffic_from)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (the decode "
+              "path would shard by text, with no exchange between GPUs). "
+              f"Got --gpus {args.gpus}, WORLD_SIZE {world}.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads as wl
+    from paged_kv_cache_320_amd import _lib as L
+
+    L.lib()  # fails loudly when libpagedkv.so has not been built
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    base = wl.BY_NAME[args.workload]
+    if isinstance(base, wl.PromptWorkload):
+        line = bench_prompt(args, base)
+    elif base.length_kind == "sharing":
+        line = bench_sharing(args, base, args.steps, args.warmup)
+    else:
+        assert base.length_kind in ("fixed", "uniform", "list"), \
+            "bench.py times batches whose texts each decode one token per step (no forks)"
+        line = bench_decode(args, base, args.steps, args.warmup, placement=args.placement)
+        if args.workload == "opt13b_7x2048_f16_b16" and not args.no_configs:
+            free_gpu()
+            # the paging cost: the same step with every text's blocks in id order
+            log("identity placement run")
+            ident = bench_decode(args, base, args.steps, args.warmup, placement="identity",
+                                 probes=False, cpu=False)
+            r_op, i_op = line["roofline"]["avg_launch_us"], ident["roofline"]["avg_launch_us"]
+            line["placement_cost"] = {
+                "random_op_us": r_op, "identity_op_us": i_op,
+                "random_over_identity": round(r_op / i_op, 4),
+                "identity_op_us_median": ident["roofline"]["median_launch_us"],
+                "random_op_us_median": line["roofline"]["median_launch_us"]}
+            del ident
+            configs = {}
+            for name, k, w_, nl in CONFIG_RUNS:
+                free_gpu()
+                cw = wl.BY_NAME[name]
+                log(f"configuration {name}: {k} steps, {w_} warmup, {nl} layers")
+                sub = argparse.Namespace(**{**vars(args), "layers": nl, "partition_tokens": 0})
+                if cw.length_kind == "sharing":
+                    c = bench_sharing(sub, cw, k, w_)
+                else:
+                    c = bench_decode(sub, cw, k, w_, layers=nl, probes=False, cpu=False)
+                configs[name] = config_summary(c)
+            line["configs"] = configs
+    if args.line_out:
+        with open(args.line_out, "w") as f:
+            f.write(json.dumps(line) + "\n")
     print(json.dumps(line), flush=True)
 
 

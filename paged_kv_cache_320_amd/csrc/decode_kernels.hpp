@@ -832,6 +832,9 @@ __device__ __forceinline__ void merge_run(const float* __restrict__ partials, in
 
 // Merge pass: one wave per (text, query head); runs finished inside one segment
 // return at once. W: segments of the partition launch (the merge range is clamped to it).
+// (Taking the first unit and the segment length from the lengths themselves for small
+// batches, instead of the header and offsets the partition kernel wrote, measured 0.6 us
+// slower per op on the 7 x 2,048 OPT-13B step.)
 template <int QT, int D, int GS>
 __global__ __launch_bounds__(kThreads) void decode_merge(
     char* __restrict__ out, const int32_t* __restrict__ ctx, int S, int H, int Hkv, int maxb,

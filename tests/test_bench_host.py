@@ -28,3 +28,22 @@ def test_unique_bytes_count_a_shared_block_once():
 def test_unique_bytes_take_the_most_filled_view_of_a_block():
     tables = np.array([[4], [4]])
     assert bench.unique_kv_bytes(tables, [1, 3], 4, 1, 2, 1) == 3 * 2 * 1 * 2 * 1
+
+
+def test_config_summary_keeps_the_figures_of_a_configuration():
+    line = {"roofline": {"avg_launch_us": 931.3, "median_launch_us": 930.7, "min_launch_us": 922.9,
+                         "bytes_per_launch": 5737112369, "achieved": 6160.5, "frac": 0.7701,
+                         "kernel": "k"},
+            "ms_per_step": 1.9, "steps": 10, "config": {"layers_per_step": 2},
+            "seq_layers_per_s": 268588.9, "cache_holding_tokens": 0.9933, "placement": "random"}
+    s = bench.config_summary(line)
+    assert s["op_us_mean"] == 931.3 and s["frac_of_hbm_peak"] == 0.7701
+    assert s["cache_holding_tokens"] == 0.9933 and s["layers_per_step"] == 2
+
+
+def test_more_than_one_gpu_is_refused():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
+                       text=True)
+    assert r.returncode == 2 and "one GPU" in r.stderr

@@ -141,6 +141,16 @@ OPT13B_7x2048_FP8 = OPT13B_7x2048.scaled(
     description="OPT-13B one layer with an E4M3 cache: 40 heads x 128, fp16 queries, "
                 "block 16, 7 x 2048 tokens, pool scales 1/256")
 
+# Many short texts (a serving batch of fresh requests): 4,096 texts of 16..64 tokens, where
+# the per-text costs of the decode launch (finding each wave's first text, finishing runs)
+# weigh most.
+SHORT_4096 = Workload(
+    name="short4096_f16_b16", seed=8, num_seqs=4096, num_heads=40, num_kv_heads=40,
+    head_dim=128, block_size=16, num_blocks=4096 * 7 + 64, dtype="f16",
+    kv_std=1 / math.sqrt(128), q_std=1.0, length_kind="uniform", ctx_lo=16, ctx_hi=64,
+    description="4,096 texts of U{16..64} attended tokens, OPT-13B shapes (40 x 128), fp16, "
+                "block 16")
+
 ALL = (TINY, OPT13B_7x2048, OPT13B_MIXED256, SHARING_32x8, LONG_16x32K)
 
 
@@ -208,7 +218,7 @@ OPT13B_PREFIX_32x1024 = PromptWorkload(
                 "(64 blocks held by all 32 texts), OPT-13B shapes, fp16, block 16")
 PROMPT = (OPT13B_PROMPT_7x2048, OPT13B_PROMPT_MIXED64, LLAMA70B_PROMPT_8x4096,
           OPT13B_PREFIX_32x1024)
-EXTRA = (LLAMA70B_32x4096, OPT13B_7x2048_FP8, GQA4_32x4096)
+EXTRA = (LLAMA70B_32x4096, OPT13B_7x2048_FP8, GQA4_32x4096, SHORT_4096)
 BY_NAME = {w.name: w for w in ALL + EXTRA + PROMPT}
 
 
