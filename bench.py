@@ -441,25 +441,23 @@ def bench_sharing(args, base, K: int, W: int) -> dict:
     mode = args.sharing_decode
     per_text = mode == "per-text"
     if not per_text:
-        # texts are numbered group-major: group g is texts g*samples .. g*samples + samples - 1,
-        # whose tables begin with the prompt's blocks
-        G, J = w.groups, w.samples
-        g_first = torch.arange(0, S, J, dtype=torch.int32, device="cuda")
-        g_count = torch.full((G,), J, dtype=torch.int32, device="cuda")
-        g_prefix = torch.full((G,), w.prompt_len, dtype=torch.int32, device="cuda")
-        pws = torch.empty(L.pa_decode_prefix_workspace_bytes(
-            S, H, Hkv, D, B, max_ctx_bound, G, w.prompt_len, L.dtype_code(outs[0])),
-            dtype=torch.uint8, device="cuda")
-        # nested: each even sample and the odd sample forked from it share every block but
-        # the last one the step's copy-on-write split (the call clamps the shared length to
-        # each pair's shorter context less one token, rounded down to a block)
-        p_first = torch.arange(0, S, 2, dtype=torch.int32, device="cuda")
-        p_count = torch.full((S // 2,), 2, dtype=torch.int32, device="cuda")
-        p_prefix = torch.full((S // 2,), max_ctx_bound, dtype=torch.int32, device="cuda")
+        # the share groups are read off the block tables every step (pa_share_groups): a
+        # request's samples hold its prompt's blocks in common; each forked pair of beams
+        # also holds the blocks written before the pair split (up to the last block the
+        # step's copy-on-write split), so the groups' promise holds by construction
+        J = w.samples
+        GMAX = S // 2
+        d_groups = torch.empty((6, GMAX), dtype=torch.int32, device="cuda")
+        p_groups = [torch.empty((6, GMAX), dtype=torch.int32, pin_memory=True) for _ in range(R)]
         if mode == "nested":
             pws = torch.empty(L.pa_decode_prefix2_workspace_bytes(
-                S, H, Hkv, D, B, max_ctx_bound, G, w.prompt_len, S // 2, max_ctx_bound, 2,
+                S, H, Hkv, D, B, max_ctx_bound, GMAX, max_ctx_bound, GMAX, max_ctx_bound, 2,
                 L.dtype_code(outs[0])), dtype=torch.uint8, device="cuda")
+        else:
+            pws = torch.empty(L.pa_decode_prefix_workspace_bytes(
+                S, H, Hkv, D, B, max_ctx_bound, GMAX, max_ctx_bound, L.dtype_code(outs[0])),
+                dtype=torch.uint8, device="cuda")
+    ngroups = [0, 0]
 
     def step(i: int, timed: bool):
         for op in step_ops[i]:
@@ -472,6 +470,14 @@ def bench_sharing(args, base, K: int, W: int) -> dict:
         d_slots.copy_(p_slots[i], non_blocking=True)
         d_lens.copy_(p_lens[i], non_blocking=True)
         d_tables.copy_(p_tables[i], non_blocking=True)
+        if not per_text:
+            outer, inner = cache.alloc.share_groups(seqs, J, inner_members=2)
+            pg = p_groups[i].numpy()
+            for k, a in enumerate(outer + inner):
+                pg[k, :len(a)] = a
+            ngroups[0], ngroups[1] = len(outer[0]), len(inner[0])
+            assert ngroups[0] > 0, "every request's samples share its prompt"
+            d_groups.copy_(p_groups[i], non_blocking=True)
         if pairs:
             p_pairs[i].numpy()[:len(pairs)] = np.asarray(pairs, dtype=np.int32)
             d_pairs.copy_(p_pairs[i], non_blocking=True)
@@ -500,16 +506,18 @@ def bench_sharing(args, base, K: int, W: int) -> dict:
         else:
             for li in range(NL):
                 L.pa_kv_write(cache.k[li], cache.v[li], d.step_k[i], d.step_v[i], d_slots)
+            no, ni = ngroups
+            og = [d_groups[k, :no] for k in range(3)]
+            ig = [d_groups[3 + k, :ni] for k in range(3)]
             for li in range(NL):
-                if mode == "nested":
+                if mode == "nested" and ni > 0:
                     L.pa_decode_attention_prefix2(outs[li], d.step_q[i], cache.k[li],
-                                                  cache.v[li], d_tables, d_lens, mctx, g_first,
-                                                  g_count, g_prefix, w.prompt_len, p_first,
-                                                  p_count, p_prefix, max_ctx_bound, 2, pws)
+                                                  cache.v[li], d_tables, d_lens, mctx, *og,
+                                                  max_ctx_bound, *ig, max_ctx_bound, 2, pws)
                 else:
                     L.pa_decode_attention_prefix(outs[li], d.step_q[i], cache.k[li],
-                                                 cache.v[li], d_tables, d_lens, mctx, g_first,
-                                                 g_count, g_prefix, w.prompt_len, pws)
+                                                 cache.v[li], d_tables, d_lens, mctx, *og,
+                                                 max_ctx_bound, pws)
         if timed:
             e1.record()
             ev.append((e0, e1))
@@ -1199,6 +1207,7 @@ def main():
                 configs[name] = config_summary(c)
             line["configs"] = configs
     if args.line_out:
+        os.makedirs(os.path.dirname(os.path.abspath(args.line_out)), exist_ok=True)
         with open(args.line_out, "w") as f:
             f.write(json.dumps(line) + "\n")
     print(json.dumps(line), flush=True)

@@ -27,7 +27,8 @@
  *    pointers the caller owns, enqueue work on `stream` (a hipStream_t; NULL
  *    is the null stream) and return without waiting. Host-side checks cover
  *    null pointers, sizes, dtype and 16-byte alignment; indices stored in
- *    device memory are bounds-guarded inside the kernels as stated per call.
+ *    device memory are bounds-guarded inside the kernels as stated per call, and the
+ *    promises the calls take on trust can be re-checked (pa_set_debug_checks).
  *  - Layouts (row-major, contiguous):
  *      k_cache, v_cache  [num_blocks][num_kv_heads][block_size][head_dim]
  *      q, out            [num_seqs][num_heads][head_dim]
@@ -129,6 +130,30 @@ int pa_num_free(const pa_alloc* a, int32_t* n_out);
  * filled / (used * block_size) is the share of the cache holding tokens ("What It Does"). */
 int pa_alloc_stats(const pa_alloc* a, int64_t* used_blocks, int64_t* filled_slots);
 
+/* Share groups of a batch for pa_decode_attention_prefix / _prefix2, read off the block
+ * tables ("Shared, Copied on Write": texts forked from one another hold their common
+ * blocks in common, with counts), so that the groups' promise (members' tables begin with
+ * the same blocks) holds by construction.
+ * pa_share_groups: maximal runs of consecutive batch texts seqs[i], seqs[i+1], ... (at most
+ * max_members, >= 2) that all hold the run's first text's first block; each run of two or
+ * more texts is a group: first_out = its first batch index, count_out = its texts,
+ * prefix_out = the leading blocks all its members hold in common, times block_size (the
+ * decode clamps that to each member's context less one token). Texts in no run are in no
+ * group. Outputs [cap]; *num_groups_out groups (PA_EINVAL if more than cap).
+ * pa_share_groups_inner: inside each given group (first, count, prefix as above), maximal
+ * runs of at most inner_members (>= 2) consecutive members that hold more leading blocks in
+ * common than prefix / block_size: the inner level of pa_decode_attention_prefix2 (a pair
+ * of beams also shares the tokens written since the two split).
+ * Swapped-out texts: PA_EINVAL; unknown ids: PA_ENOSEQ. */
+int pa_share_groups(const pa_alloc* a, const int32_t* seqs, int32_t n, int32_t max_members,
+                    int32_t cap, int32_t* first_out, int32_t* count_out, int32_t* prefix_out,
+                    int32_t* num_groups_out);
+int pa_share_groups_inner(const pa_alloc* a, const int32_t* seqs, int32_t n, int32_t num_groups,
+                          const int32_t* group_first, const int32_t* group_count,
+                          const int32_t* group_prefix, int32_t inner_members, int32_t cap,
+                          int32_t* first_out, int32_t* count_out, int32_t* prefix_out,
+                          int32_t* num_inner_out);
+
 /* ---------------------------------------------------------------------------
  * Swapping to host memory («The KV Cache and PagedAttention», "When Memory Runs Out":
  * when blocks run short, a text gives up all of its blocks at once; one answer is to
@@ -166,6 +191,23 @@ int pa_seq_swapped(const pa_alloc* a, int32_t seq, int32_t* swapped_out);
 /* Count of a host block (0 = free), and the free host blocks. */
 int pa_host_block_ref(const pa_alloc* a, int32_t block, int32_t* ref_out);
 int pa_host_num_free(const pa_alloc* a, int32_t* n_out);
+
+/* ---------------------------------------------------------------------------
+ * Debug re-checks of what the device calls take on trust (on the host, before launch):
+ *  - pa_kv_write, pa_kv_write_fp8: the slots inside the pool are distinct;
+ *  - pa_decode_attention_write: also, each text's slot is the place of its last attended
+ *    position in its table;
+ *  - pa_copy_blocks: destinations distinct, no block both a source and a destination;
+ *  - pa_decode_attention_prefix / _prefix2: no text in two groups of one level, and every
+ *    member's table holds its group's first member's blocks over the blocks the level
+ *    reads once for the group (with the decode's own clamps).
+ * A failed check returns PA_EINVAL naming the offender, and nothing is launched. Each check
+ * copies the device arrays it needs to the host and waits for `stream`: for testing, not
+ * for the timed path. Off by default; on when PA_DEBUG_CHECKS is set to a value other than
+ * "0" in the environment when first consulted, or after pa_set_debug_checks(1).
+ * pa_debug_checks() returns 1 when on. */
+int pa_set_debug_checks(int32_t on);
+int pa_debug_checks(void);
 
 /* ---------------------------------------------------------------------------
  * Device cache writes.

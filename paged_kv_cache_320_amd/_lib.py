@@ -42,6 +42,13 @@ SIGNATURES = {
     "pa_block_ref": (ctypes.c_int, [_vp, _i32, _c_int32_p]),
     "pa_num_free": (ctypes.c_int, [_vp, _c_int32_p]),
     "pa_alloc_stats": (ctypes.c_int, [_vp, _c_int64_p, _c_int64_p]),
+    "pa_share_groups": (ctypes.c_int, [_vp, _c_int32_p, _i32, _i32, _i32, _c_int32_p, _c_int32_p,
+                                       _c_int32_p, _c_int32_p]),
+    "pa_share_groups_inner": (ctypes.c_int, [_vp, _c_int32_p, _i32, _i32, _c_int32_p, _c_int32_p,
+                                             _c_int32_p, _i32, _i32, _c_int32_p, _c_int32_p,
+                                             _c_int32_p, _c_int32_p]),
+    "pa_set_debug_checks": (ctypes.c_int, [_i32]),
+    "pa_debug_checks": (ctypes.c_int, []),
     "pa_kv_write": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                    _vp]),
     "pa_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
@@ -209,6 +216,49 @@ def pa_export_tables(h, seqs: Sequence[int], max_blocks: int, tables_out=None, l
                                   tables.ctypes.data_as(_c_int32_p),
                                   lens.ctypes.data_as(_c_int32_p)))
     return tables, lens
+
+
+def pa_share_groups(h, seqs: Sequence[int], max_members: int):
+    """Share groups of the batch read off the block tables: (first, count, prefix) int32
+    numpy arrays, one entry per group."""
+    import numpy as np
+    n = len(seqs)
+    arr = np.ascontiguousarray(np.asarray(seqs, dtype=np.int32))
+    cap = max(1, n // 2)
+    f, c, p = (np.empty(cap, np.int32) for _ in range(3))
+    num = ctypes.c_int32()
+    _check(lib().pa_share_groups(h, arr.ctypes.data_as(_c_int32_p), n, max_members, cap,
+                                 f.ctypes.data_as(_c_int32_p), c.ctypes.data_as(_c_int32_p),
+                                 p.ctypes.data_as(_c_int32_p), ctypes.byref(num)))
+    k = num.value
+    return f[:k].copy(), c[:k].copy(), p[:k].copy()
+
+
+def pa_share_groups_inner(h, seqs: Sequence[int], groups, inner_members: int):
+    """Inner share groups inside `groups` = (first, count, prefix) arrays."""
+    import numpy as np
+    n = len(seqs)
+    arr = np.ascontiguousarray(np.asarray(seqs, dtype=np.int32))
+    gf, gc, gp = (np.ascontiguousarray(np.asarray(x, dtype=np.int32)) for x in groups)
+    cap = max(1, n // 2)
+    f, c, p = (np.empty(cap, np.int32) for _ in range(3))
+    num = ctypes.c_int32()
+    _check(lib().pa_share_groups_inner(h, arr.ctypes.data_as(_c_int32_p), n, len(gf),
+                                       gf.ctypes.data_as(_c_int32_p),
+                                       gc.ctypes.data_as(_c_int32_p),
+                                       gp.ctypes.data_as(_c_int32_p), inner_members, cap,
+                                       f.ctypes.data_as(_c_int32_p), c.ctypes.data_as(_c_int32_p),
+                                       p.ctypes.data_as(_c_int32_p), ctypes.byref(num)))
+    k = num.value
+    return f[:k].copy(), c[:k].copy(), p[:k].copy()
+
+
+def pa_set_debug_checks(on: bool) -> None:
+    _check(lib().pa_set_debug_checks(1 if on else 0))
+
+
+def pa_debug_checks() -> bool:
+    return bool(lib().pa_debug_checks())
 
 
 def pa_block_ref(h, block: int) -> int:

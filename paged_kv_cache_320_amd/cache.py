@@ -81,6 +81,14 @@ class BlockAllocator:
     def stats(self):
         return L.pa_alloc_stats(self.h)
 
+    def share_groups(self, seqs: Sequence[int], max_members: int, inner_members: int = 0):
+        """Share groups of the batch for the shared-block decodes, read off the tables:
+        (first, count, prefix) arrays, and with inner_members >= 2 the inner level too."""
+        outer = L.pa_share_groups(self.h, seqs, max_members)
+        if inner_members < 2:
+            return outer
+        return outer, L.pa_share_groups_inner(self.h, seqs, outer, inner_members)
+
     # prefix caching
     def add_cached(self, hashes: Sequence[int]):
         """New text on the registered blocks matching its leading hashes: (id, blocks reused)."""

@@ -360,6 +360,106 @@ int pa_alloc_stats(const pa_alloc* a, int64_t* used_blocks, int64_t* filled_slot
   return ok();
 }
 
+// ---- share groups for the shared-block decode ("Shared, Copied on Write") ------
+
+// Leading physical blocks two texts hold in common.
+static int64_t common_blocks(const Seq& x, const Seq& y) {
+  const size_t m = std::min(x.blocks.size(), y.blocks.size());
+  size_t j = 0;
+  while (j < m && x.blocks[j] == y.blocks[j]) ++j;
+  return (int64_t)j;
+}
+
+// Runs of consecutive batch texts [lo, hi) whose leading blocks agree beyond `above` blocks,
+// at most `members` texts each; emit (first, count, shared tokens) for runs of 2 or more.
+static int emit_runs(const pa_alloc* a, const std::vector<const Seq*>& s, int32_t lo, int32_t hi,
+                     int64_t above, int32_t members, int32_t cap, int32_t* first_out,
+                     int32_t* count_out, int32_t* prefix_out, int32_t* num) {
+  int32_t i = lo;
+  while (i < hi) {
+    int64_t c = INT64_MAX;
+    int32_t j = i + 1;
+    while (j < hi && j - i < members) {
+      const int64_t cb = common_blocks(*s[i], *s[j]);
+      if (cb <= above) break;
+      c = std::min(c, cb);
+      ++j;
+    }
+    if (j - i >= 2) {
+      if (*num >= cap) return fail(PA_EINVAL, "more than %d share groups", cap);
+      const int64_t tokens = c * a->block_size;
+      first_out[*num] = i;
+      count_out[*num] = j - i;
+      prefix_out[*num] = (int32_t)std::min<int64_t>(tokens, INT32_MAX);
+      ++*num;
+      i = j;
+    } else {
+      ++i;
+    }
+  }
+  return PA_OK;
+}
+
+static int batch_seqs(const pa_alloc* a, const int32_t* seqs, int32_t n,
+                      std::vector<const Seq*>* out) {
+  out->resize(n);
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq* s = a->find(seqs[i]);
+    if (!s) return fail(PA_ENOSEQ, "unknown sequence %d at batch index %d", seqs[i], i);
+    if (s->swapped) return fail(PA_EINVAL, "sequence %d is swapped out", seqs[i]);
+    (*out)[i] = s;
+  }
+  return PA_OK;
+}
+
+int pa_share_groups(const pa_alloc* a, const int32_t* seqs, int32_t n, int32_t max_members,
+                    int32_t cap, int32_t* first_out, int32_t* count_out, int32_t* prefix_out,
+                    int32_t* num_groups_out) {
+  if (!a || !num_groups_out || (n > 0 && !seqs) ||
+      (cap > 0 && (!first_out || !count_out || !prefix_out)))
+    return fail(PA_EINVAL, "null argument");
+  if (n < 0 || cap < 0 || max_members < 2)
+    return fail(PA_EINVAL, "n %d and cap %d must be >= 0, max_members %d >= 2", n, cap,
+                max_members);
+  std::vector<const Seq*> s;
+  int rc = batch_seqs(a, seqs, n, &s);
+  if (rc != PA_OK) return rc;
+  int32_t num = 0;
+  rc = emit_runs(a, s, 0, n, 0, max_members, cap, first_out, count_out, prefix_out, &num);
+  if (rc != PA_OK) return rc;
+  *num_groups_out = num;
+  return ok();
+}
+
+int pa_share_groups_inner(const pa_alloc* a, const int32_t* seqs, int32_t n, int32_t num_groups,
+                          const int32_t* group_first, const int32_t* group_count,
+                          const int32_t* group_prefix, int32_t inner_members, int32_t cap,
+                          int32_t* first_out, int32_t* count_out, int32_t* prefix_out,
+                          int32_t* num_inner_out) {
+  if (!a || !num_inner_out || (n > 0 && !seqs) ||
+      (num_groups > 0 && (!group_first || !group_count || !group_prefix)) ||
+      (cap > 0 && (!first_out || !count_out || !prefix_out)))
+    return fail(PA_EINVAL, "null argument");
+  if (n < 0 || num_groups < 0 || cap < 0 || inner_members < 2)
+    return fail(PA_EINVAL, "n %d, num_groups %d and cap %d must be >= 0, inner_members %d >= 2",
+                n, num_groups, cap, inner_members);
+  std::vector<const Seq*> s;
+  int rc = batch_seqs(a, seqs, n, &s);
+  if (rc != PA_OK) return rc;
+  int32_t num = 0;
+  for (int32_t g = 0; g < num_groups; ++g) {
+    const int32_t f = group_first[g], k = group_count[g];
+    if (f < 0 || k < 0 || (int64_t)f + k > n || group_prefix[g] < 0)
+      return fail(PA_EINVAL, "group %d (first %d, count %d, shared %d) outside the batch", g, f,
+                  k, group_prefix[g]);
+    rc = emit_runs(a, s, f, f + k, group_prefix[g] / a->block_size, inner_members, cap,
+                   first_out, count_out, prefix_out, &num);
+    if (rc != PA_OK) return rc;
+  }
+  *num_inner_out = num;
+  return ok();
+}
+
 // ---- prefix caching ("What Came After") ---------------------------------------
 
 // 64-bit FNV-1a (offset basis 0xcbf29ce484222325, prime 0x100000001b3) over `n` bytes,

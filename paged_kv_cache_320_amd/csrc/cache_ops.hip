@@ -151,6 +151,10 @@ extern "C" int pa_kv_write_fp8(void* k_cache, void* v_cache, const void* k_new,
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
     return fail(PA_EINVAL, "pools and new rows must be 16-byte aligned");
   if (((uintptr_t)slots & 7u) != 0) return fail(PA_EINVAL, "slots must be 8-byte aligned");
+  if (debug_checks()) {
+    rc = check_slots(slots, num_tokens, (int64_t)num_blocks * block_size, (hipStream_t)stream);
+    if (rc != PA_OK) return rc;
+  }
   const int lpr = head_dim / 16;  // 16 codes per piece
   const int64_t pieces = (int64_t)num_tokens * num_kv_heads * lpr;
   // the rounding of x / scale is decided as fp32(x) * fp32(1 / scale)
@@ -188,6 +192,10 @@ extern "C" int pa_kv_write(void* k_cache, void* v_cache, const void* k_new, cons
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
     return fail(PA_EINVAL, "pools and new rows must be 16-byte aligned");
   if (((uintptr_t)slots & 7u) != 0) return fail(PA_EINVAL, "slots must be 8-byte aligned");
+  if (debug_checks()) {
+    rc = check_slots(slots, num_tokens, (int64_t)num_blocks * block_size, (hipStream_t)stream);
+    if (rc != PA_OK) return rc;
+  }
   const int lpr = head_dim * elt_bytes(dtype) / 16;
   const int64_t pieces = (int64_t)num_tokens * num_kv_heads * lpr;
   hipLaunchKernelGGL(kv_write_kernel, dim3(grid_for(pieces)), dim3(kThreads), 0,
@@ -209,6 +217,10 @@ extern "C" int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs
   if (!k_cache || !v_cache || !pairs) return fail(PA_EINVAL, "null pointer");
   if (!aligned16(k_cache) || !aligned16(v_cache)) return fail(PA_EINVAL, "pools must be 16-byte aligned");
   if (((uintptr_t)pairs & 3u) != 0) return fail(PA_EINVAL, "pairs must be 4-byte aligned");
+  if (debug_checks()) {
+    rc = check_pairs(pairs, num_pairs, num_blocks, (hipStream_t)stream);
+    if (rc != PA_OK) return rc;
+  }
   const int64_t ppb = (int64_t)num_kv_heads * block_size * head_dim * elt_bytes(dtype) / 16;
   const int64_t total = ppb * num_pairs;
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(grid_for(total)), dim3(kThreads), 0,

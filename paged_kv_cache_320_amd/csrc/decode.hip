@@ -2,8 +2,10 @@
 // the choice of kernel instance. The kernels are in decode_kernels.hpp.
 #include "decode_kernels.hpp"
 
+#include <algorithm>
 #include <cmath>
 #include <mutex>
+#include <vector>
 
 namespace pagedkv {
 namespace {
@@ -186,6 +188,36 @@ extern "C" int pa_decode_attention_fp8(void* out, const void* q, const void* k_c
                        q_dtype, workspace, workspace_bytes, stream);
 }
 
+namespace pagedkv {
+namespace {
+
+// Debug re-check of the fused write's promise: each text's slot (when inside the pool) is
+// the place of its last attended position in its table, and no two texts share a slot.
+int check_new_slots(const int64_t* slots, const int32_t* tables, const int32_t* ctx, int32_t S,
+                    int32_t maxb, int32_t B, int32_t num_blocks, hipStream_t st) {
+  int rc = check_slots(slots, S, (int64_t)num_blocks * B, st);
+  if (rc != PA_OK) return rc;
+  std::vector<int64_t> sl;
+  std::vector<int32_t> tab, len;
+  if ((rc = fetch(sl, slots, (size_t)S, st)) != PA_OK) return rc;
+  if ((rc = fetch(tab, tables, (size_t)S * maxb, st)) != PA_OK) return rc;
+  if ((rc = fetch(len, ctx, (size_t)S, st)) != PA_OK) return rc;
+  for (int32_t s = 0; s < S; ++s) {
+    if (sl[s] < 0 || sl[s] >= (int64_t)num_blocks * B || len[s] < 1) continue;
+    const int64_t p = len[s] - 1;
+    if (p / B >= maxb) continue;  // the decode poisons such a text
+    const int64_t want = (int64_t)tab[(int64_t)s * maxb + p / B] * B + p % B;
+    if (sl[s] != want)
+      return fail(PA_EINVAL, "debug check: text %d writes slot %lld, but its last position "
+                  "%lld sits at slot %lld of its table", s, (long long)sl[s], (long long)p,
+                  (long long)want);
+  }
+  return PA_OK;
+}
+
+}  // namespace
+}  // namespace pagedkv
+
 extern "C" int pa_decode_attention_write(void* out, const void* q, void* k_cache, void* v_cache,
                                          const void* k_new, const void* v_new,
                                          const int64_t* slots, const int32_t* block_tables,
@@ -199,6 +231,13 @@ extern "C" int pa_decode_attention_write(void* out, const void* q, void* k_cache
   if (!k_new || !v_new || !slots) return fail(PA_EINVAL, "null pointer");
   if (!aligned16(k_new) || !aligned16(v_new) || ((uintptr_t)slots & 7u))
     return fail(PA_EINVAL, "k_new and v_new must be 16-byte aligned, slots 8-byte aligned");
+  if (debug_checks() && block_tables && context_lens && num_seqs > 0 && max_blocks_per_seq > 0 &&
+      num_blocks > 0 && block_size > 0) {
+    const int rc = check_new_slots(slots, block_tables, context_lens, num_seqs,
+                                   max_blocks_per_seq, block_size, num_blocks,
+                                   (hipStream_t)stream);
+    if (rc != PA_OK) return rc;
+  }
   const decode_impl::NewRows nr{(const char*)k_new, (const char*)v_new, slots, (char*)k_cache,
                                 (char*)v_cache};
   return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
@@ -537,6 +576,64 @@ int32_t prefix_cols(int32_t members, int32_t H, int32_t Hkv) {
   return 0;
 }
 
+// Debug re-check of the share groups' promise, with the set-up kernel's own clamps: at
+// each level no text is in two groups, and every member's table holds the same blocks as
+// its group's first member's over the blocks the level reads once for the group.
+int check_groups(int levels, const GroupsIn* g, const int32_t* ctx_d, const int32_t* tables_d,
+                 int32_t S, int32_t H, int32_t Hkv, int32_t maxb, int32_t B, hipStream_t st) {
+  std::vector<int32_t> ctx, tab;
+  int rc;
+  if ((rc = fetch(ctx, ctx_d, (size_t)S, st)) != PA_OK) return rc;
+  if ((rc = fetch(tab, tables_d, (size_t)S * maxb, st)) != PA_OK) return rc;
+  const int Gr = H / Hkv;
+  const int64_t capacity = (int64_t)maxb * B;
+  std::vector<int32_t> start_prev(S, 0), gid_prev(S, -1);
+  for (int l = 0; l < levels; ++l) {
+    std::vector<int32_t> first, count, prefix;
+    if ((rc = fetch(first, g[l].first, (size_t)g[l].n, st)) != PA_OK) return rc;
+    if ((rc = fetch(count, g[l].count, (size_t)g[l].n, st)) != PA_OK) return rc;
+    if ((rc = fetch(prefix, g[l].prefix, (size_t)g[l].n, st)) != PA_OK) return rc;
+    std::vector<int32_t> owner(S, -1), start(start_prev), gid(S, -1);
+    for (int32_t v = 0; v < g[l].n; ++v) {
+      const int32_t f = first[v] < 0 ? 0 : first[v] >= S ? S - 1 : first[v];
+      const int32_t most = std::min(g[l].cols / Gr, S - f);
+      int32_t n = count[v] < 0 ? 0 : count[v] > most ? most : count[v];
+      if (l > 0)
+        for (int32_t m = 1; m < n; ++m)
+          if (gid_prev[f + m] != gid_prev[f]) {
+            n = m;
+            break;
+          }
+      int64_t P = std::min(prefix[v], g[l].max_prefix);
+      int64_t keep = INT32_MAX;
+      for (int32_t m = 0; m < n; ++m)
+        keep = std::min(keep, std::min<int64_t>(std::max(ctx[f + m], 0), capacity) - 1);
+      if (P > keep) P = keep;
+      if (P < 0 || n == 0) P = 0;
+      P -= P % B;
+      const int64_t P0 = l > 0 && n > 0 ? start_prev[f] : 0;
+      if (P < P0) P = P0;
+      for (int32_t m = 0; m < n; ++m) {
+        if (owner[f + m] >= 0)
+          return fail(PA_EINVAL, "debug check: text %d is in groups %d and %d (level %d)", f + m,
+                      owner[f + m], v, l + 1);
+        owner[f + m] = v;
+        start[f + m] = (int32_t)P;
+        gid[f + m] = v;
+        for (int64_t j = P0 / B; j < P / B; ++j)
+          if (tab[(int64_t)(f + m) * maxb + j] != tab[(int64_t)f * maxb + j])
+            return fail(PA_EINVAL, "debug check: group %d (level %d): text %d holds block %d "
+                        "at logical block %lld, its first member %d holds block %d", v, l + 1,
+                        f + m, tab[(int64_t)(f + m) * maxb + j], (long long)j, f,
+                        tab[(int64_t)f * maxb + j]);
+      }
+    }
+    start_prev.swap(start);
+    gid_prev.swap(gid);
+  }
+  return PA_OK;
+}
+
 // The shared-prefix decode over one level of groups or two nested ones: set-up, one pass
 // per level over the groups' shared blocks (states out; with two levels the inner level's
 // states are merged with the outer's), then every text's own blocks with its state folded in.
@@ -587,6 +684,11 @@ int prefix_decode(void* out, const void* q, const void* k_cache, const void* v_c
     return fail(PA_EINVAL, "workspace_bytes %zu < %zu required", workspace_bytes, pl.bytes);
   char* ws = (char*)workspace;
   hipStream_t st = (hipStream_t)stream;
+  if (debug_checks()) {
+    rc = check_groups(levels, g, context_lens, block_tables, num_seqs, num_heads, num_kv_heads,
+                      max_blocks_per_seq, block_size, st);
+    if (rc != PA_OK) return rc;
+  }
   const int64_t rows = (int64_t)num_seqs * num_heads;
   const int64_t nstate = rows * (head_dim + 4);
   const int64_t want = (nstate + 255) / 256;

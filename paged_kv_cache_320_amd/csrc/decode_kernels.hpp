@@ -717,6 +717,53 @@ __global__ __launch_bounds__(kThreads) void decode_partition(
     advance(cur, x);
   };
 
+  if constexpr (KT == PA_FP8_E4M3) {
+    // 8-bit pools: a chunk is half the bytes of a 16-bit one, so two chunks stay in flight
+    // (three buffers) to keep as many bytes in flight per wave. (No fold rows and no fused
+    // write here: neither takes 8-bit pools.)
+    Buf<KT, QT, D, GS> C;
+    if (n > 1) {
+      load_chunk<KT, QT, D, B, GS, FUSED>(Bb, ld, x, kc, vc, q, tables, nr, lane);
+      advance(ld, x);
+    }
+    int i = 0;
+    while (i + 4 < n) {  // A: chunk i, Bb: chunk i + 1, both issued
+      load_chunk<KT, QT, D, B, GS, FUSED>(C, ld, x, kc, vc, q, tables, nr, lane);
+      advance(ld, x);
+      compute(A);
+      finish(i);
+      load_chunk<KT, QT, D, B, GS, FUSED>(A, ld, x, kc, vc, q, tables, nr, lane);
+      advance(ld, x);
+      compute(Bb);
+      finish(i + 1);
+      load_chunk<KT, QT, D, B, GS, FUSED>(Bb, ld, x, kc, vc, q, tables, nr, lane);
+      advance(ld, x);
+      compute(C);
+      finish(i + 2);
+      i += 3;
+    }
+    const int r = n - i;  // 1 .. 4 chunks left; A holds chunk i, Bb chunk i + 1 (r >= 2)
+    if (r >= 3) {
+      load_chunk<KT, QT, D, B, GS, FUSED>(C, ld, x, kc, vc, q, tables, nr, lane);
+      advance(ld, x);
+    }
+    compute(A);
+    finish(i);
+    if (r == 4) load_chunk<KT, QT, D, B, GS, FUSED>(A, ld, x, kc, vc, q, tables, nr, lane);
+    if (r >= 2) {
+      compute(Bb);
+      finish(i + 1);
+    }
+    if (r >= 3) {
+      compute(C);
+      finish(i + 2);
+    }
+    if (r == 4) {
+      compute(A);
+      finish(i + 3);
+    }
+    return;
+  }
   // steady state: both loads unconditional, so the next chunk's loads stay in
   // flight while the current one is computed
   // (a chunk's fold row is loaded once the chunk before it has been finished, which

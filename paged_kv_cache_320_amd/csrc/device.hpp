@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <vector>
 
 #include "status.hpp"
 
@@ -27,6 +28,23 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Compute units of the current device (cached per device id).
 int device_cus(int* cus);
+
+// Host copy of n elements of device (or pinned host) memory, once the work already ordered
+// on `stream` is done (for the debug re-checks only).
+template <typename T>
+int fetch(std::vector<T>& out, const T* src, size_t n, hipStream_t stream) {
+  out.resize(n);
+  if (n == 0) return PA_OK;
+  PA_HIP_CHECK(hipMemcpyAsync(out.data(), src, n * sizeof(T), hipMemcpyDeviceToHost, stream));
+  PA_HIP_CHECK(hipStreamSynchronize(stream));
+  return PA_OK;
+}
+
+// Debug re-checks (see debug_checks()): the slots inside [0, num_slots) are distinct; the
+// copy pairs inside [0, num_blocks) have distinct destinations and no block is both a
+// source and a destination. PA_EINVAL names the first offender.
+int check_slots(const int64_t* slots, int32_t n, int64_t num_slots, hipStream_t stream);
+int check_pairs(const int32_t* pairs, int32_t n, int32_t num_blocks, hipStream_t stream);
 
 // ---- element formats -------------------------------------------------------
 

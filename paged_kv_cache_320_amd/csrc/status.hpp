@@ -28,3 +28,14 @@ inline int ok() {
 }
 
 }  // namespace pagedkv
+
+namespace pagedkv {
+
+// Host re-checks of the promises the device entry points rely on (distinct slots, copy
+// pairs disjoint from their sources, share groups whose members' tables agree): on when
+// the environment variable PA_DEBUG_CHECKS is set to a value other than 0 when the library
+// first checks, or after pa_set_debug_checks(1). Each check copies the device arrays it
+// needs to the host (ordered on the call's stream, which it waits for).
+bool debug_checks();
+
+}  // namespace pagedkv

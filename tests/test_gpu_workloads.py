@@ -217,7 +217,7 @@ class SharedDecodes(NativeReplay):
     blocks once per pair (pa_decode_attention_prefix2)."""
 
     def run(self, ops, max_blocks=None):
-        self.shared = {"prefix": [], "nested": []}
+        self.shared = {"prefix": [], "nested": [], "derived": []}
         for op in ops:
             super().run([op], max_blocks)
             if op[0] == "step":
@@ -252,6 +252,17 @@ class SharedDecodes(NativeReplay):
                                       2, ws2)
         self.shared["prefix"].append(out1)
         self.shared["nested"].append(out2)
+        # the groups read off the block tables by the allocator (pa_share_groups)
+        outer, inner = self.cache.alloc.share_groups(st.seq_ids, J, inner_members=2)
+        dv = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+        assert len(outer[0]) == G and len(inner[0]) >= 1
+        ws3 = torch.empty(L.pa_decode_prefix2_workspace_bytes(S, H, Hkv, D, B, mx, len(outer[0]),
+                                                              mx, len(inner[0]), mx, 2, code),
+                          dtype=torch.uint8, device="cuda")
+        out3 = torch.empty_like(q)
+        L.pa_decode_attention_prefix2(out3, q, kc, vc, bt, cl, mx, *map(dv, outer), mx,
+                                      *map(dv, inner), mx, 2, ws3)
+        self.shared["derived"].append(out3)
 
 
 @pytest.mark.parametrize("variant", ["plain", "sharp"])
@@ -275,7 +286,7 @@ def test_full_size_sharing_shared_block_decodes(native, variant):
 
     ora = Replay(w, d, pool=False)
     os_ = ora.run(ops, decode_pairs=pairs_for)
-    for kind in ("plain", "prefix", "nested"):
+    for kind in ("plain", "prefix", "nested", "derived"):
         if kind == "plain":
             steps = ns
         else:
