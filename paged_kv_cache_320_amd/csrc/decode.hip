@@ -20,7 +20,9 @@ using decode_impl::units_of;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-int layout(int32_t S, int32_t H, int32_t D, int32_t max_ctx, int32_t T, Layout* lay) {
+// wpc: segments per compute unit of an auto grid (partition_tokens 0).
+int layout(int32_t S, int32_t H, int32_t D, int32_t max_ctx, int32_t T, Layout* lay,
+           int wpc = kWavesPerCU) {
   if (S < 1 || H < 1 || (D != 64 && D != 128) || max_ctx < 0 || T < 0 || T % kChunk != 0)
     return fail(PA_EINVAL, "bad workspace shape (num_seqs %d, num_heads %d, head_dim %d, "
                 "max_context_len %d, partition_tokens %d)", S, H, D, max_ctx, T);
@@ -32,7 +34,7 @@ int layout(int32_t S, int32_t H, int32_t D, int32_t max_ctx, int32_t T, Layout* 
     int cus = 0;
     int rc = device_cus(&cus);
     if (rc != PA_OK) return rc;
-    slots = (int64_t)cus * kWavesPerCU;
+    slots = (int64_t)cus * wpc;
   }
   const int64_t W = pagedkv::seg::grid_segments(units_bound, slots, T / kChunk);
   if (W > 0x7fffffff / 2) return fail(PA_EINVAL, "too many segments");
@@ -96,7 +98,8 @@ int decode_common(void* out, const void* q, const void* k_cache, const void* v_c
                   int32_t partition_tokens, float scale, float k_scale, float v_scale,
                   int32_t kv_dtype, int32_t q_dtype, void* workspace, size_t workspace_bytes,
                   void* stream, const decode_impl::NewRows& nr = decode_impl::NewRows{},
-                  const decode_impl::Prefix& pf = decode_impl::Prefix{}) {
+                  const decode_impl::Prefix& pf = decode_impl::Prefix{},
+                  int wpc = kWavesPerCU) {
   if (head_dim != 64 && head_dim != 128)
     return fail(PA_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
   if (block_size != 4 && block_size != 8 && block_size != 16 && block_size != 32)
@@ -122,7 +125,7 @@ int decode_common(void* out, const void* q, const void* k_cache, const void* v_c
   if (((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u))
     return fail(PA_EINVAL, "tables and context_lens must be 4-byte aligned");
   Layout lay;
-  int rc = layout(num_seqs, num_heads, head_dim, max_context_len, partition_tokens, &lay);
+  int rc = layout(num_seqs, num_heads, head_dim, max_context_len, partition_tokens, &lay, wpc);
   if (rc != PA_OK) return rc;
   if (workspace_bytes < lay.bytes)
     return fail(PA_EINVAL, "workspace_bytes %zu < %zu required", workspace_bytes, lay.bytes);
@@ -346,6 +349,17 @@ struct PrefixLayout {
   PrefixLevel lv[2];
 };
 
+// Segments per compute unit of one pass of the shared-block decode, whose key/value heads
+// each serve G query heads: the matrix-core kernel (4 or 8 query heads per wave, 16-bit
+// formats) keeps 4; the vector kernel takes 8, which on the 32 x 8 sharing workload (bf16)
+// took the forked pairs' pass from 162 to 142 us and the texts' own pass from 24 to 20 us
+// (the matrix-core prompts pass went from 128 to 136 us with 8; the plain decode of 256
+// mixed-length texts was unchanged).
+int pass_waves(int G, int32_t elt) {
+  const int gs = heads_per_wave(G);
+  return gs >= 4 && elt == 2 ? kWavesPerCU : 2 * kWavesPerCU;
+}
+
 int prefix_layout(int32_t S, int32_t H, int32_t Hkv, int32_t D, int32_t max_ctx, int32_t levels,
                   const int32_t* V, const int32_t* max_prefix, const int32_t* cols, int32_t bsz,
                   int32_t elt, PrefixLayout* pl) {
@@ -357,12 +371,12 @@ int prefix_layout(int32_t S, int32_t H, int32_t Hkv, int32_t D, int32_t max_ctx,
       return fail(PA_EINVAL, "bad shared-prefix groups (level %d: num_groups %d, "
                   "max_prefix_len %d)", l + 1, V[l], max_prefix[l]);
   Layout a;
-  int rc = layout(S, H, D, max_ctx, 0, &a);
+  int rc = layout(S, H, D, max_ctx, 0, &a, pass_waves(H / Hkv, elt));
   if (rc != PA_OK) return rc;
   size_t need = a.bytes;
   for (int l = 0; l < levels; ++l) {
     Layout b;
-    rc = layout(V[l], Hkv * cols[l], D, max_prefix[l], 0, &b);
+    rc = layout(V[l], Hkv * cols[l], D, max_prefix[l], 0, &b, pass_waves(cols[l], elt));
     if (rc != PA_OK) return rc;
     if (b.bytes > need) need = b.bytes;
   }
@@ -730,7 +744,7 @@ int prefix_decode(void* out, const void* q, const void* k_cache, const void* v_c
                        (const int32_t*)(ws + v.vctx_off), g[l].n, num_kv_heads * cols[l],
                        num_kv_heads, head_dim, block_size, num_blocks, v.maxbp, g[l].max_prefix,
                        0, scale, 1.0f, 1.0f, dtype, dtype, workspace, pl.decode_bytes, stream,
-                       decode_impl::NewRows{}, p1);
+                       decode_impl::NewRows{}, p1, pass_waves(cols[l], elt_bytes(dtype)));
     if (rc != PA_OK) return rc;
   }
   if (levels > 1) {
@@ -746,7 +760,8 @@ int prefix_decode(void* out, const void* q, const void* k_cache, const void* v_c
   return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
                        num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                        max_context_len, 0, scale, 1.0f, 1.0f, dtype, dtype, workspace,
-                       pl.decode_bytes, stream, decode_impl::NewRows{}, p2);
+                       pl.decode_bytes, stream, decode_impl::NewRows{}, p2,
+                       pass_waves(num_heads / num_kv_heads, elt_bytes(dtype)));
 }
 
 }  // namespace
