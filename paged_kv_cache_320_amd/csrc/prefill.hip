@@ -109,25 +109,29 @@ __device__ __forceinline__ int swz_v(int r) { return CPR == 16 ? 4 * (r & 3) : 4
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+// Element offset, within a value tile, of the piece lane `lane` addresses for 32-row tile mt
+// of subtile 0, k-step 0: the lane's key there is 4 (grp / 2) + j / 4, whose swizzle
+// (depending on key mod 4, or (key / 2) mod 2 for D = 64) is the same for every subtile,
+// k-step and the +8 key of the second read, which therefore only add (32 st + 16 kk [+ 8]) D
+// elements. Computed once per lane (the per-read address then costs no arithmetic).
 template <int D>
-__device__ __forceinline__ const uint16_t* v_piece(const uint16_t* vs, int key, int dim) {
+__device__ __forceinline__ int v_offset(int mt, int lane) {
   constexpr int CPR = D / 8;
-  return vs + key * D + (((dim >> 3) ^ swz_v<CPR>(key)) << 3) + (dim & 7);
-}
-
-template <int D>
-__device__ __forceinline__ u32x4 vt_operand(const uint16_t* vs, int st, int mt, int kk, int lane) {
   const int grp = lane >> 4, j = lane & 15;
   const int dim = 32 * mt + 16 * (grp & 1) + 4 * (j & 3);
-  const int key = 32 * st + 16 * kk + 4 * (grp >> 1) + (j >> 2);
-  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)v_piece<D>(vs, key, dim));
-  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)v_piece<D>(vs, key + 8, dim));
-  u32x4 w;
-  w[0] = (uint16_t)a[0] | ((uint32_t)(uint16_t)a[1] << 16);
-  w[1] = (uint16_t)a[2] | ((uint32_t)(uint16_t)a[3] << 16);
-  w[2] = (uint16_t)b[0] | ((uint32_t)(uint16_t)b[1] << 16);
-  w[3] = (uint16_t)b[2] | ((uint32_t)(uint16_t)b[3] << 16);
-  return w;
+  const int key = 4 * (grp >> 1) + (j >> 2);
+  return key * D + (((dim >> 3) ^ swz_v<CPR>(key)) << 3) + (dim & 7);
+}
+
+// The two transposing reads of one A operand: keys `key0` and key0 + 8 relative to the
+// lane's offset; the two 64-bit results are the operand's four words as they come.
+template <int D>
+__device__ __forceinline__ u32x4 vt_operand(const uint16_t* vs, int voff, int key0) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + voff + key0 * D));
+  const s16x4 b =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + voff + (key0 + 8) * D));
+  const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+  return u32x4{ua.x, ua.y, ub.x, ub.y};
 }
 
 // gfx950 LDS DMA: each lane's 16 bytes from `src` land at lds + 16 * lane (lds must be
@@ -196,6 +200,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int row = wrow0 + col;
     const bool row_ok = row < row_hi;
     const int pos = row_ok ? first + row : -1;   // -1 attends nothing
+
+    // LDS element offsets of this lane's operand reads (fixed for the whole loop): key
+    // operand of k-step c (subtile 1 adds 32 D), value operand of 32-row tile mt
+    int koff[NQ], voff[NM];
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) koff[c] = col * D + (((2 * c + half) ^ swz_k<CPR>(col)) * 8);
+#pragma unroll
+    for (int mt = 0; mt < NM; ++mt) voff[mt] = v_offset<D>(mt, lane);
 
     // queries: lane holds q[row][16c + 8 half .. +7] for k-step c
     v8 qv[NQ];
@@ -283,22 +295,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       if (wave_on && kt * kKeys <= wave_last) {  // causal skip (wave-uniform)
         // S^T = K Q^T per 32-key subtile: A = 32 keys x 16 dims from LDS, B = the wave's
         // queries; the subtiles' products are independent, so they overlap
+        // (the swizzle of row 32 st + col equals that of row col, so subtile st's pieces
+        // sit 32 D elements after subtile 0's; the first product starts from zero)
+        // The key operands of k-step c + 1 are read while the products of step c run, so
+        // the LDS latency is not paid before every pair of products.
         f32x16 sacc[kSub];
+        u32x4 ka[2][kSub];
 #pragma unroll
-        for (int st = 0; st < kSub; ++st) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[st][r] = 0.f;
-        }
+        for (int st = 0; st < kSub; ++st) ka[0][st] = *(const u32x4*)(kb + koff[0] + 32 * st * D);
 #pragma unroll
         for (int c = 0; c < NQ; ++c) {
+          if (c + 1 < NQ) {
 #pragma unroll
-          for (int st = 0; st < kSub; ++st) {
-            const int row = 32 * st + col;
-            const v8 a = __builtin_bit_cast(
-                v8, *(const u32x4*)(kb + row * D + (((2 * c + half) ^ swz_k<CPR>(row)) * 8)));
-            sacc[st] = M::mfma(a, qv[c], sacc[st]);
+            for (int st = 0; st < kSub; ++st)
+              ka[(c + 1) & 1][st] = *(const u32x4*)(kb + koff[c + 1] + 32 * st * D);
           }
+#pragma unroll
+          for (int st = 0; st < kSub; ++st)
+            sacc[st] = M::mfma(__builtin_bit_cast(v8, ka[c & 1][st]), qv[c],
+                               c == 0 ? f32x16{} : sacc[st]);
         }
+        // keep that order (the scheduler would otherwise sink each read next to its use):
+        // the reads of steps 0 and 1, then per step its two products and the next reads
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kSub, 0);
+#pragma unroll
+        for (int c = 0; c + 2 < NQ; ++c) {
+          __builtin_amdgcn_sched_group_barrier(0x008, kSub, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, kSub, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * kSub, 0);
         // raw scores (scale_log2 > 0 keeps their order); on a diagonal tile, keys after
         // a query's own position get no weight
         if (kt * kKeys + kKeys - 1 > wave_first) {
@@ -335,6 +360,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         float psum = 0.f;
 #pragma unroll
         for (int st = 0; st < kSub; ++st) {
+          // V^T operands of this subtile first (rows d = 32 mt + col over its keys, through
+          // the transposing LDS read), held back by a scheduling barrier so that they
+          // arrive while the weights below are formed, instead of each read being sunk next
+          // to its product
+          u32x4 va[NM][2];
+#pragma unroll
+          for (int mt = 0; mt < NM; ++mt)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+              va[mt][kk] = vt_operand<D>(vb, voff[mt], 32 * st + 16 * kk);
+          __builtin_amdgcn_sched_barrier(0);
           // P^T operand of k-step kk: the lane's scores r = 8kk .. 8kk+7 (keys
           // 32 st + key_of(r, half))
           v8 pb[2];
@@ -351,15 +387,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             for (int j = 0; j < 4; ++j) w[j] = M::pack2(z[2 * j], z[2 * j + 1]);
             pb[kk] = __builtin_bit_cast(v8, w);
           }
-          // O^T += V^T P^T: A = V^T rows d = 32 mt + col over the same 8 keys per k-step,
-          // read from the row-major value tile by the transposing LDS read
+          // O^T += V^T P^T: A = V^T rows d = 32 mt + col over the same 8 keys per k-step
 #pragma unroll
           for (int mt = 0; mt < NM; ++mt) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
-              o[mt] = M::mfma(
-                  __builtin_bit_cast(v8, vt_operand<D>(vb, st, mt, kk, lane)),
-                  pb[kk], o[mt]);
+              o[mt] = M::mfma(__builtin_bit_cast(v8, va[mt][kk]), pb[kk], o[mt]);
           }
         }
         l += psum;
