@@ -411,8 +411,9 @@ int pa_decode_attention_prefix(void* out, const void* q, const void* k_cache,
  * head, rounded up to 1, 2, 4 or 8: pairs of texts with one query head per key/value head
  * take the two-head vector kernel), PA_EUNSUPPORTED past 8. Passes on `stream`: the texts'
  * starts cleared, set-up per level, the outer groups' shared blocks, the inner groups'
- * shared blocks, a merge of the two levels' softmax states (each level's state used only
- * where its start moved past the level before), every text's own blocks. dtype, limits and errors as pa_decode_attention_prefix; the group
+ * shared blocks, every text's own blocks with both levels' softmax states folded in (each
+ * level's state used only where its start moved past the level before). dtype, limits
+ * and errors as pa_decode_attention_prefix; the group
  * arrays are device int32 [num_groups] and [num_inner_groups], both counts >= 1.
  * workspace: pa_decode_prefix2_workspace_bytes(...) bytes, 16-byte aligned, no
  * initialization needed. */

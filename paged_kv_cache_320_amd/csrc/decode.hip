@@ -407,54 +407,15 @@ int prefix_layout(int32_t S, int32_t H, int32_t Hkv, int32_t D, int32_t max_ctx,
   return PA_OK;
 }
 
-// Every (text, head) state empty (m = -inf, l = 0, acc = 0); no text skips a start.
-__global__ void prefix_clear_kernel(float* __restrict__ state, int64_t n, int row,
-                                    int32_t* __restrict__ start, int S) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
-    state[i] = i % row == 0 ? -INFINITY : 0.f;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < S; i += stride)
-    start[i] = 0;
-}
-
-// Two levels: no text skips a start at either level and none is in an outer group (the
-// states are not cleared: a level's state row is used only where that level's start moved
-// past the level before).
+// No text skips a start at any level and none is in an outer group (b and gid: two levels
+// only). The states are not cleared: a level's state row is read only where that level's
+// start moved past the level before.
 __global__ void prefix_clear_starts_kernel(int32_t* __restrict__ a, int32_t* __restrict__ b,
                                            int32_t* __restrict__ gid, int S) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < S; i += gridDim.x * blockDim.x) {
     a[i] = 0;
-    b[i] = 0;
-    gid[i] = -1;
-  }
-}
-
-// Two levels: each (text, head) state of the inner level becomes the merge of both levels'
-// states (the softmax over the union of the two token ranges, as split-context partials
-// merge). A level's state counts only where its start moved past the level before (outer:
-// start > 0; inner: start beyond the outer start); otherwise it is empty. One wave per row;
-// every lane reads the row's m and l before lane 0 writes them.
-__global__ void prefix_combine_kernel(const float* __restrict__ outer, float* __restrict__ inner,
-                                      const int32_t* __restrict__ start_outer,
-                                      const int32_t* __restrict__ start_inner, int H,
-                                      int64_t rows, int D) {
-  const int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  const int64_t s = row / H;
-  const bool use_a = start_outer[s] > 0, use_b = start_inner[s] > start_outer[s];
-  const float* a = outer + row * (D + 4);
-  float* b = inner + row * (D + 4);
-  const float ma = use_a ? a[0] : -INFINITY, la = use_a ? a[1] : 0.f;
-  const float mb = use_b ? b[0] : -INFINITY, lb = use_b ? b[1] : 0.f;
-  const float M = fmaxf(ma, mb);
-  const float mu = M == -INFINITY ? 0.f : M;
-  const float fa = __builtin_amdgcn_exp2f(ma - mu), fb = __builtin_amdgcn_exp2f(mb - mu);
-  for (int e = lane; e < D; e += 64)
-    b[4 + e] = (use_a ? a[4 + e] * fa : 0.f) + (use_b ? b[4 + e] * fb : 0.f);
-  if (lane == 0) {
-    b[0] = M;
-    b[1] = la * fa + lb * fb;
+    if (b) b[i] = 0;
+    if (gid) gid[i] = -1;
   }
 }
 
@@ -703,22 +664,17 @@ int prefix_decode(void* out, const void* q, const void* k_cache, const void* v_c
                       max_blocks_per_seq, block_size, st);
     if (rc != PA_OK) return rc;
   }
-  const int64_t rows = (int64_t)num_seqs * num_heads;
-  const int64_t nstate = rows * (head_dim + 4);
-  const int64_t want = (nstate + 255) / 256;
   float* state[2];
   int32_t* start[2];
   for (int l = 0; l < levels; ++l) {
     state[l] = (float*)(ws + pl.lv[l].state_off);
     start[l] = (int32_t*)(ws + pl.lv[l].start_off);
   }
-  if (levels == 1) {
-    hipLaunchKernelGGL(prefix_clear_kernel, dim3((int)(want < 2048 ? want : 2048)), dim3(256), 0,
-                       st, state[0], nstate, head_dim + 4, start[0], num_seqs);
-  } else {
+  {
     const int blocks = (num_seqs + 255) / 256;
     hipLaunchKernelGGL(prefix_clear_starts_kernel, dim3(blocks < 1024 ? blocks : 1024), dim3(256),
-                       0, st, start[0], start[1], (int32_t*)(ws + pl.gid_off), num_seqs);
+                       0, st, start[0], levels > 1 ? start[1] : (int32_t*)nullptr,
+                       levels > 1 ? (int32_t*)(ws + pl.gid_off) : (int32_t*)nullptr, num_seqs);
   }
   for (int l = 0; l < levels; ++l) {
     const PrefixLevel& v = pl.lv[l];
@@ -739,7 +695,8 @@ int prefix_decode(void* out, const void* q, const void* k_cache, const void* v_c
   for (int l = 0; l < levels; ++l) {
     const PrefixLevel& v = pl.lv[l];
     const decode_impl::Prefix p1{nullptr, state[l], (const int32_t*)(ws + v.vfirst_off),
-                                 (const int32_t*)(ws + v.vcount_off), num_heads, 1};
+                                 (const int32_t*)(ws + v.vcount_off), num_heads, 1, nullptr,
+                                 nullptr};
     rc = decode_common(out, ws + v.vq_off, k_cache, v_cache, (const int32_t*)(ws + v.vtab_off),
                        (const int32_t*)(ws + v.vctx_off), g[l].n, num_kv_heads * cols[l],
                        num_kv_heads, head_dim, block_size, num_blocks, v.maxbp, g[l].max_prefix,
@@ -747,16 +704,10 @@ int prefix_decode(void* out, const void* q, const void* k_cache, const void* v_c
                        decode_impl::NewRows{}, p1, pass_waves(cols[l], elt_bytes(dtype)));
     if (rc != PA_OK) return rc;
   }
-  if (levels > 1) {
-    const int64_t threads = rows * 64;
-    hipLaunchKernelGGL(prefix_combine_kernel, dim3((int)((threads + 255) / 256)), dim3(256), 0,
-                       st, state[0], state[1], start[0], start[1], (int)num_heads, rows,
-                       (int)head_dim);
-    PA_HIP_CHECK(hipGetLastError());
-  }
-  // every text's own blocks, its state folded in
+  // every text's own blocks, its states folded in (each level's where it applies)
   const decode_impl::Prefix p2{start[levels - 1], state[levels - 1], nullptr, nullptr, num_heads,
-                               2};
+                               2, levels > 1 ? start[0] : (const int32_t*)nullptr,
+                               levels > 1 ? state[0] : (const float*)nullptr};
   return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
                        num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                        max_context_len, 0, scale, 1.0f, 1.0f, dtype, dtype, workspace,

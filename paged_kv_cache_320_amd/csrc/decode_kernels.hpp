@@ -94,6 +94,7 @@ struct Cursor {
   int over;         // context_lens[s] exceeded the table's capacity
   int64_t excl;     // number of the first unit of text s
   int vfirst, vcount;  // shared-prefix mode 1: text s is a group; its first member and count
+  int fold;            // shared-prefix mode 2: fold_mask of text s
 };
 
 // Shared-prefix decode (pa_decode_attention_prefix) runs the kernels twice. Mode 1 runs over
@@ -110,7 +111,20 @@ struct Prefix {
   const int32_t* __restrict__ vcount;  // mode 1: members of each group
   int heads;                           // mode 1: query heads per text of the real batch
   int mode;
+  // mode 2 over two nested levels: the outer level's starts and states. A text folds in
+  // the outer state where its outer start is past 0 and the `state` row (the inner level's,
+  // or with one level the only one) where `start` is past the outer start (past 0 with one
+  // level); rows that do not apply are never read, so neither array needs clearing.
+  const int32_t* __restrict__ start0;
+  const float* state0;
 };
+
+// Mode 2: which state rows text s folds in (bit 0: the outer level's, bit 1: `state`'s).
+__device__ __forceinline__ int fold_mask(const Prefix& pf, int s) {
+  const int p1 = pf.start[s];
+  const int p0 = pf.start0 ? pf.start0[s] : 0;
+  return (p0 > 0 ? 1 : 0) | (p1 > p0 ? 2 : 0);
+}
 
 struct Ctx {
   int S, H, Hkv;
@@ -167,12 +181,15 @@ struct NewRows {
 __device__ __forceinline__ void set_text(Cursor& c, const Ctx& x, int s) {
   c.s = s;
   c.vfirst = c.vcount = 0;
+  c.fold = 0;
   if (s < x.S) {
     c.L = attended_len(x.ctx, x.pf.start, s, x.capacity, (int)(x.capacity / x.maxb), &c.toff,
                        &c.over);
     if (x.pf.mode == 1) {
       c.vfirst = __builtin_amdgcn_readfirstlane(x.pf.vfirst[s]);
       c.vcount = __builtin_amdgcn_readfirstlane(x.pf.vcount[s]);
+    } else if (x.pf.mode == 2) {
+      c.fold = __builtin_amdgcn_readfirstlane(fold_mask(x.pf, s));
     }
   } else {
     c.L = c.toff = c.over = 0;
@@ -217,10 +234,11 @@ template <int KT, int D, int GS>
 struct State {
   float m[GS], l[GS];
   float acc[GS][Geo<KT, D>::EPL];
-  // shared-prefix mode 2: the text's state over its shared blocks, loaded with the run's
-  // last chunk so that folding it in waits for no load issued later
-  float fm[GS], fl[GS];
-  float facc[GS][Geo<KT, D>::EPL];
+  // shared-prefix mode 2: the text's states over its shared blocks (the outer level's,
+  // then the inner or only level's), loaded with the run's last chunk so that folding
+  // them in waits for no load issued later; empty where a level does not apply
+  float fm[2][GS], fl[2][GS];
+  float facc[2][GS][Geo<KT, D>::EPL];
   __device__ __forceinline__ void reset() {
 #pragma unroll
     for (int j = 0; j < GS; ++j) {
@@ -229,6 +247,17 @@ struct State {
 #pragma unroll
       for (int e = 0; e < Geo<KT, D>::EPL; ++e) acc[j][e] = 0.f;
     }
+  }
+  __device__ __forceinline__ void reset_fold() {
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int j = 0; j < GS; ++j) {
+        fm[k][j] = -INFINITY;
+        fl[k][j] = 0.f;
+#pragma unroll
+        for (int e = 0; e < Geo<KT, D>::EPL; ++e) facc[k][j][e] = 0.f;
+      }
   }
 };
 
@@ -466,14 +495,16 @@ __device__ __forceinline__ void flush_run(State<KT, D, GS>& st, const Cursor& c,
           continue;
         }
         if (x.pf.mode == 2) {
-          // fold in the text's state over its shared blocks (prefetched by load_fold)
-          const float ms = st.fm[j], M = fmaxf(st.m[j], ms);
+          // fold in the text's states over its shared blocks (prefetched by load_fold;
+          // a level that does not apply is empty and weighs 0)
+          const float M = fmaxf(st.m[j], fmaxf(st.fm[0][j], st.fm[1][j]));
           const float mu = M == -INFINITY ? 0.f : M;
-          const float fa = fast_exp2(st.m[j] - mu), fb = fast_exp2(ms - mu);
-          st.l[j] = st.l[j] * fa + st.fl[j] * fb;
+          const float f = fast_exp2(st.m[j] - mu);
+          const float fa = fast_exp2(st.fm[0][j] - mu), fb = fast_exp2(st.fm[1][j] - mu);
+          st.l[j] = st.l[j] * f + st.fl[0][j] * fa + st.fl[1][j] * fb;
 #pragma unroll
           for (int e = 0; e < G::EPL; ++e)
-            st.acc[j][e] = st.acc[j][e] * fa + st.facc[j][e] * fb;
+            st.acc[j][e] = st.acc[j][e] * f + st.facc[0][j][e] * fa + st.facc[1][j][e] * fb;
         }
         float o[G::EPL];
         const float inv = st.l[j] > 0.f ? v_scale / st.l[j] : 0.f;
@@ -503,45 +534,52 @@ __device__ __forceinline__ void flush_run(State<KT, D, GS>& st, const Cursor& c,
     }
   }
   st.reset();
+  if (x.pf.mode == 2) st.reset_fold();
 }
 
-// Mode 2: the state row (of the run's first query head; the GS rows follow it) that
-// flush_run folds in when the run whose last chunk the cursor c points at is finished
-// within this segment, else null. 16- and 32-bit pools only (the shared-prefix call
-// takes no E4M3 pools).
+// Mode 2: the offset (in floats, of the run's first query head; the GS rows follow it) of
+// the state rows that flush_run folds in when the run whose last chunk the cursor c points
+// at is finished within this segment and the text has a level to fold, else -1. 16- and
+// 32-bit pools only (the shared-prefix call takes no E4M3 pools).
 template <int KT, int QT, int D, int GS>
-__device__ __forceinline__ const float* fold_row(const Cursor& c, const Ctx& x, int64_t seg_lo,
-                                                 int64_t seg_hi) {
+__device__ __forceinline__ int64_t fold_row(const Cursor& c, const Ctx& x, int64_t seg_lo,
+                                            int64_t seg_hi) {
   if constexpr (KT != QT) {
-    return nullptr;
+    return -1;
   } else {
-    if (x.pf.mode != 2 || c.u != c.U - 1) return nullptr;
+    if (x.pf.mode != 2 || c.fold == 0 || c.u != c.U - 1) return -1;
     const int64_t run_lo = c.excl + (int64_t)c.r * c.U;
-    if (run_lo < seg_lo || run_lo + c.U > seg_hi) return nullptr;
-    return x.pf.state + ((int64_t)c.s * x.H + first_head_of<GS>(c.r, x)) * (D + 4);
+    if (run_lo < seg_lo || run_lo + c.U > seg_hi) return -1;
+    return ((int64_t)c.s * x.H + first_head_of<GS>(c.r, x)) * (D + 4);
   }
 }
 
-// Load a state row set into st.fm / st.fl / st.facc (lane l holds the lane l % LPR slice,
-// the slice the first row group's lanes fold in).
+// Load the state rows the text folds (its fold mask) into st.fm / st.fl / st.facc (lane l
+// holds the lane l % LPR slice, the slice the first row group's lanes fold in); the other
+// set stays empty.
 template <int KT, int D, int GS>
-__device__ __forceinline__ void load_fold(State<KT, D, GS>& st, const float* __restrict__ row,
-                                          int lane) {
+__device__ __forceinline__ void load_fold(State<KT, D, GS>& st, const Prefix& pf, int fold,
+                                          int64_t off, int lane) {
   using G = Geo<KT, D>;
   const int lp = lane % G::LPR;
 #pragma unroll
-  for (int j = 0; j < GS; ++j) {
-    const float* r = row + j * (D + 4);
-    const float2 ml = *reinterpret_cast<const float2*>(r);
-    st.fm[j] = ml.x;
-    st.fl[j] = ml.y;
+  for (int k = 0; k < 2; ++k) {
+    if (!(fold >> k & 1)) continue;
+    const float* row = (k == 0 ? pf.state0 : pf.state) + off;
 #pragma unroll
-    for (int e = 0; e < G::EPL; e += 4) {
-      const float4 a = *reinterpret_cast<const float4*>(r + 4 + lp * G::EPL + e);
-      st.facc[j][e] = a.x;
-      st.facc[j][e + 1] = a.y;
-      st.facc[j][e + 2] = a.z;
-      st.facc[j][e + 3] = a.w;
+    for (int j = 0; j < GS; ++j) {
+      const float* r = row + j * (D + 4);
+      const float2 ml = *reinterpret_cast<const float2*>(r);
+      st.fm[k][j] = ml.x;
+      st.fl[k][j] = ml.y;
+#pragma unroll
+      for (int e = 0; e < G::EPL; e += 4) {
+        const float4 a = *reinterpret_cast<const float4*>(r + 4 + lp * G::EPL + e);
+        st.facc[k][j][e] = a.x;
+        st.facc[k][j][e + 1] = a.y;
+        st.facc[k][j][e + 2] = a.z;
+        st.facc[k][j][e + 3] = a.w;
+      }
     }
   }
 }
@@ -689,11 +727,12 @@ __global__ __launch_bounds__(kThreads) void decode_partition(
 
   State<KT, D, GS> st;
   st.reset();
+  st.reset_fold();
   Buf<KT, QT, D, GS> A, Bb;
   load_chunk<KT, QT, D, B, GS, FUSED>(A, ld, x, kc, vc, q, tables, nr, lane);
   {
-    const float* fr = fold_row<KT, QT, D, GS>(ld, x, seg_lo, seg_hi);
-    if (fr) load_fold<KT, D, GS>(st, fr, lane);
+    const int64_t fr = fold_row<KT, QT, D, GS>(ld, x, seg_lo, seg_hi);
+    if (fr >= 0) load_fold<KT, D, GS>(st, x.pf, ld.fold, fr, lane);
   }
   advance(ld, x);
 
@@ -771,25 +810,28 @@ __global__ __launch_bounds__(kThreads) void decode_partition(
   int i = 0;
   while (i + 2 < n) {
     load_chunk<KT, QT, D, B, GS, FUSED>(Bb, ld, x, kc, vc, q, tables, nr, lane);
-    const float* fb = fold_row<KT, QT, D, GS>(ld, x, seg_lo, seg_hi);
+    const int64_t fb = fold_row<KT, QT, D, GS>(ld, x, seg_lo, seg_hi);
+    const int fbm = ld.fold;
     advance(ld, x);
     compute(A);
     finish(i);
-    if (fb) load_fold<KT, D, GS>(st, fb, lane);
+    if (fb >= 0) load_fold<KT, D, GS>(st, x.pf, fbm, fb, lane);
     load_chunk<KT, QT, D, B, GS, FUSED>(A, ld, x, kc, vc, q, tables, nr, lane);
-    const float* fa = fold_row<KT, QT, D, GS>(ld, x, seg_lo, seg_hi);
+    const int64_t fa = fold_row<KT, QT, D, GS>(ld, x, seg_lo, seg_hi);
+    const int fam = ld.fold;
     advance(ld, x);
     compute(Bb);
     finish(i + 1);
-    if (fa) load_fold<KT, D, GS>(st, fa, lane);
+    if (fa >= 0) load_fold<KT, D, GS>(st, x.pf, fam, fa, lane);
     i += 2;
   }
   if (i + 1 < n) {
     load_chunk<KT, QT, D, B, GS, FUSED>(Bb, ld, x, kc, vc, q, tables, nr, lane);
-    const float* fb = fold_row<KT, QT, D, GS>(ld, x, seg_lo, seg_hi);
+    const int64_t fb = fold_row<KT, QT, D, GS>(ld, x, seg_lo, seg_hi);
+    const int fbm = ld.fold;
     compute(A);
     finish(i);
-    if (fb) load_fold<KT, D, GS>(st, fb, lane);
+    if (fb >= 0) load_fold<KT, D, GS>(st, x.pf, fbm, fb, lane);
     compute(Bb);
     finish(i + 1);
   } else {
@@ -798,48 +840,62 @@ __global__ __launch_bounds__(kThreads) void decode_partition(
   }
 }
 
-// Combine the partials of one run for query head j (of the run's GS), left by
-// segments w0..w1, in segment order. Segment w0 holds the run in its slot 1 unless
-// the run starts exactly at w0's first unit (then it is w0's first run, slot 0);
-// every later segment starts inside the run, so the run is its first run (slot 0).
-// The partials are read UNROLL at a time with all loads in flight and combined
-// with a running maximum (the rescaling of the online softmax), in one pass.
+// Combine the partials of one run, left by segments w0..w1, in segment order, for all GS
+// query heads of the run at once: the wave's lanes form GS groups of CL = 64 / GS lanes,
+// group j taking head j's D values, PE = D / CL per lane. Segment w0 holds the run in its
+// slot 1 unless the run starts exactly at w0's first unit (then it is w0's first run, slot
+// 0); every later segment starts inside the run, so the run is its first run (slot 0).
+// The partials are read UNROLL at a time with all loads in flight and combined with a
+// running maximum (the rescaling of the online softmax), in one pass. init / init2: states
+// (m, l, pad, pad, acc[D]) of the lane's head that come first (null: none); state_dst: the
+// merged state itself is written there instead of an output row (null: the lane's head
+// writes nothing).
 template <int QT, int D, int GS>
 __device__ __forceinline__ void merge_run(const float* __restrict__ partials, int64_t w0,
-                                          int64_t w1, int64_t run_lo, int64_t seg, int j,
+                                          int64_t w1, int64_t run_lo, int64_t seg,
                                           float v_scale, char* __restrict__ dst_row, int lane,
-                                          const float* init = nullptr,
-                                          float* state_dst = nullptr) {
-  constexpr int PER = D / 64;  // output elements per lane
-  constexpr int UNROLL = 8;
+                                          const float* init, float* state_dst,
+                                          const float* init2) {
+  constexpr int CL = 64 / GS;  // lanes per head
+  constexpr int PE = D / CL;   // values per lane
+  constexpr int UNROLL = PE >= 16 ? 4 : 8;
+  const int j = lane / CL, c = lane % CL;
   auto index_of = [&](int64_t w) -> int64_t {
     return partial_index<D, GS>(w, seg::partial_slot(run_lo, w * seg), j);
   };
-  // init: a state (m, l, pad, pad, acc[D]) that comes first, before the partials
-  float M = -INFINITY, den = 0.f, num[PER];
+  float M = -INFINITY, den = 0.f, num[PE];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) num[e] = 0.f;
+  for (int e = 0; e < PE; ++e) num[e] = 0.f;
   if (init) {
     M = init[0];
     den = init[1];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) num[e] = init[4 + lane * PER + e];
+    for (int e = 0; e < PE; ++e) num[e] = init[4 + c * PE + e];
+  }
+  if (init2) {  // a second state (the inner level's), folded in as a partial would be
+    const float m2 = init2[0], mg = fmaxf(M, m2);
+    const float mu = mg == -INFINITY ? 0.f : mg;
+    const float r = fast_exp2(M - mu), f = fast_exp2(m2 - mu);
+    den = den * r + init2[1] * f;
+#pragma unroll
+    for (int e = 0; e < PE; ++e) num[e] = num[e] * r + init2[4 + c * PE + e] * f;
+    M = mg;
   }
   for (int64_t w = w0; w <= w1; w += UNROLL) {
-    float m[UNROLL], l[UNROLL], a[UNROLL][PER];
+    float m[UNROLL], l[UNROLL], a[UNROLL][PE];
 #pragma unroll
     for (int k = 0; k < UNROLL; ++k) {
       // past w1: an empty partial (weight 0) instead of a load
       m[k] = -INFINITY;
       l[k] = 0.f;
 #pragma unroll
-      for (int e = 0; e < PER; ++e) a[k][e] = 0.f;
+      for (int e = 0; e < PE; ++e) a[k][e] = 0.f;
       if (w + k <= w1) {
         const float* p = partials + index_of(w + k);
         m[k] = p[0];
         l[k] = p[1];
 #pragma unroll
-        for (int e = 0; e < PER; ++e) a[k][e] = p[4 + lane * PER + e];
+        for (int e = 0; e < PE; ++e) a[k][e] = p[4 + c * PE + e];
       }
     }
     float mg = M;
@@ -849,52 +905,52 @@ __device__ __forceinline__ void merge_run(const float* __restrict__ partials, in
     const float r = fast_exp2(M - mu);
     den *= r;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) num[e] *= r;
+    for (int e = 0; e < PE; ++e) num[e] *= r;
 #pragma unroll
     for (int k = 0; k < UNROLL; ++k) {  // segment order
       const float f = fast_exp2(m[k] - mu);
       den += f * l[k];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) num[e] += f * a[k][e];
+      for (int e = 0; e < PE; ++e) num[e] += f * a[k][e];
     }
     M = mg;
   }
-  if (state_dst) {
+  if (state_dst || !dst_row) {
+    if (!state_dst) return;
     // the merged state itself, unnormalized
-    if (lane == 0) {
+    if (c == 0) {
       state_dst[0] = M;
       state_dst[1] = den;
     }
 #pragma unroll
-    for (int e = 0; e < PER; ++e) state_dst[4 + lane * PER + e] = num[e];
+    for (int e = 0; e < PE; ++e) state_dst[4 + c * PE + e] = num[e];
     return;
   }
-  float o[PER];
+  float o[PE];
   const float inv = den > 0.f ? v_scale / den : 0.f;
   // 0 * num: NaN stays visible for a poisoned run
 #pragma unroll
-  for (int e = 0; e < PER; ++e) o[e] = den > 0.f ? num[e] * inv : 0.f * num[e];
-  store_out<QT, PER>(dst_row + lane * PER * elt_size<QT>(), o);
+  for (int e = 0; e < PE; ++e) o[e] = den > 0.f ? num[e] * inv : 0.f * num[e];
+  store_out<QT, PE>(dst_row + c * PE * elt_size<QT>(), o);
 }
 
-// Merge pass: one wave per (text, query head); runs finished inside one segment
-// return at once. W: segments of the partition launch (the merge range is clamped to it).
-// (Taking the first unit and the segment length from the lengths themselves for small
-// batches, instead of the header and offsets the partition kernel wrote, measured 0.6 us
-// slower per op on the 7 x 2,048 OPT-13B step.)
+// Merge pass: one wave per run (a text's head group of GS query heads), all GS heads at
+// once; runs finished inside one segment return at once. W: segments of the partition
+// launch (the merge range is clamped to it). (One wave per query head instead launched GS
+// times the waves for the same partials. Taking the first unit and the segment length from
+// the lengths themselves for small batches, instead of the header and offsets the partition
+// kernel wrote, measured 0.6 us slower per op on the 7 x 2,048 OPT-13B step.)
 template <int QT, int D, int GS>
 __global__ __launch_bounds__(kThreads) void decode_merge(
     char* __restrict__ out, const int32_t* __restrict__ ctx, int S, int H, int Hkv, int maxb,
     int bsz, int W, float v_scale, const int64_t* __restrict__ hdr,
     const int64_t* __restrict__ excl, const float* __restrict__ partials, Prefix pf) {
   const int lane = threadIdx.x & 63;
-  const int64_t pair =
+  const int Gq = H / Hkv, NG = Gq / GS, R = Hkv * NG;
+  const int64_t run =
       (int64_t)blockIdx.x * kWavesPerGroup + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (pair >= (int64_t)S * H) return;
-  const int s = (int)(pair / H), h = (int)(pair - (int64_t)s * H);
-  const int Gq = H / Hkv, NG = Gq / GS;
-  const int kvh = h / Gq, within = h - kvh * Gq;
-  const int r = kvh * NG + within / GS, j = within % GS;
+  if (run >= (int64_t)S * R) return;
+  const int s = (int)(run / R), r = (int)(run - (int64_t)s * R);
   int toff, over;
   const int L = attended_len(ctx, pf.start, s, (int64_t)maxb * bsz, bsz, &toff, &over);
   const int U = units_of(L);
@@ -903,14 +959,20 @@ __global__ __launch_bounds__(kThreads) void decode_merge(
   int64_t w0, w1;
   seg::run_segments(lo, hi, seg, W, &w0, &w1);
   if (w0 == w1) return;
+  const int h = (r / NG) * Gq + (r % NG) * GS + lane / (64 / GS);  // the lane's query head
+  const int64_t pair = (int64_t)s * H + h;
   if (pf.mode == 1) {
     float* row = prefix_state_row<D>(pf, Hkv, Gq, pf.vfirst[s], pf.vcount[s], h);
-    if (row) merge_run<QT, D, GS>(partials, w0, w1, lo, seg, j, v_scale, nullptr, lane, nullptr, row);
+    merge_run<QT, D, GS>(partials, w0, w1, lo, seg, v_scale, nullptr, lane, nullptr, row,
+                         nullptr);
     return;
   }
-  const float* init = pf.mode == 2 ? pf.state + pair * (D + 4) : nullptr;
-  merge_run<QT, D, GS>(partials, w0, w1, lo, seg, j, v_scale, out + pair * D * elt_size<QT>(),
-                       lane, init);
+  // mode 2: the text's states over its shared blocks come first (the levels that apply)
+  const int fold = pf.mode == 2 ? fold_mask(pf, s) : 0;
+  const float* init = fold & 1 ? pf.state0 + pair * (D + 4) : nullptr;
+  const float* init2 = fold & 2 ? pf.state + pair * (D + 4) : nullptr;
+  merge_run<QT, D, GS>(partials, w0, w1, lo, seg, v_scale, out + pair * D * elt_size<QT>(),
+                       lane, init, nullptr, init2);
 }
 
 // ---- shared key/value heads on the matrix cores --------------------------------
@@ -1115,17 +1177,23 @@ __device__ __forceinline__ void flush_run_mma(MmaState<D>& st, const Cursor& c, 
     } else if (run_lo >= seg_lo && run_hi <= seg_hi) {
       // the whole run is in this segment: finish it here
       if (x.pf.mode == 2) {
-        // fold in the text's state over its shared blocks
-        const float* row = x.pf.state + ((int64_t)c.s * x.H + h0 + col) * (D + 4);
-        const float ms = row[0], M = fmaxf(st.m, ms);
-        const float mu = M == -INFINITY ? 0.f : M;
-        const float fa = fast_exp2(st.m - mu), fb = fast_exp2(ms - mu);
-        l = l * fa + row[1] * fb;
+        // fold in the text's states over its shared blocks (the levels that apply)
+        const int64_t off = ((int64_t)c.s * x.H + h0 + col) * (D + 4);
 #pragma unroll
-        for (int mt = 0; mt < D / 16; ++mt)
+        for (int k = 0; k < 2; ++k) {
+          if (!(c.fold >> k & 1)) continue;
+          const float* row = (k == 0 ? x.pf.state0 : x.pf.state) + off;
+          const float ms = row[0], M = fmaxf(st.m, ms);
+          const float mu = M == -INFINITY ? 0.f : M;
+          const float fa = fast_exp2(st.m - mu), fb = fast_exp2(ms - mu);
+          l = l * fa + row[1] * fb;
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            st.o[mt][r] = st.o[mt][r] * fa + row[4 + 16 * mt + 4 * grp + r] * fb;
+          for (int mt = 0; mt < D / 16; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              st.o[mt][r] = st.o[mt][r] * fa + row[4 + 16 * mt + 4 * grp + r] * fb;
+          st.m = M;
+        }
       }
       const float inv = l > 0.f ? v_scale / l : 0.f;
       char* dst = out + ((int64_t)c.s * x.H + h0 + col) * D * elt_size<QT>();
@@ -1298,8 +1366,8 @@ bool launch(const Launch& a) {
   } else {
     launch_partition<KT, QT, D, B, GS, false>(a, hdr, excl, part);
   }
-  const int64_t pairs = (int64_t)a.S * a.H;
-  const int mgroups = (int)((pairs + kWavesPerGroup - 1) / kWavesPerGroup);
+  const int64_t runs = (int64_t)a.S * (a.H / GS);  // merge waves: one per run
+  const int mgroups = (int)((runs + kWavesPerGroup - 1) / kWavesPerGroup);
   hipLaunchKernelGGL((decode_merge<QT, D, GS>), dim3(mgroups), dim3(kThreads), 0, a.st, a.out,
                      a.ctx, a.S, a.H, a.Hkv, a.maxb, B, a.W, a.v_scale, hdr, excl, part, a.pf);
   return true;
