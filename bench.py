@@ -1021,12 +1021,12 @@ def bench_decode(args, base, K: int, W: int, layers: int = 0, placement: str = "
         log(f"swap of two texts ({NL} layers, {swap[2] / 1e6:.0f} MB each way): out to pinned "
             f"host memory {swap[0]:.1f} GB/s, back in {swap[1]:.1f} GB/s")
 
-    cpu = None
+    cpu_line = None
     err0 = None
     if cpu and not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle, one layer, one thread")
-        cpu, err0 = cpu_baseline(base, draws[0], args.cpu_seconds, out0)
-        log(f"cpu baseline {cpu['value']} GB/s; step-0 max abs error vs oracle {err0:.3e}")
+        cpu_line, err0 = cpu_baseline(base, draws[0], args.cpu_seconds, out0)
+        log(f"cpu baseline {cpu_line['value']} GB/s; step-0 max abs error vs oracle {err0:.3e}")
 
     line = {
         "metric": "paged decode attention: KV GB/s and % of HBM peak; sequences·layers/sec",
@@ -1073,7 +1073,7 @@ def bench_decode(args, base, K: int, W: int, layers: int = 0, placement: str = "
         "probe_read_gbps": round(probe, 1) if probe else None,
         "probe_same_volume_gbps": round(vprobe, 1) if vprobe else None,
         "probe_same_pattern_gbps": round(tprobe, 1) if tprobe else None,
-        "cpu_baseline": cpu,
+        "cpu_baseline": cpu_line,
         "step0_max_abs_err_vs_oracle": err0,
         "wall_s_timed": round(wall, 4),
         "decode_src_sha256_16": src_hash(),
