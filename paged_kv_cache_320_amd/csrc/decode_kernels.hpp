@@ -584,12 +584,6 @@ __device__ __forceinline__ void load_fold(State<KT, D, GS>& st, const Prefix& pf
   }
 }
 
-__device__ __forceinline__ int64_t uniform64(int64_t v) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
 // This wave's segment of the unit numbering. Returns false when the wave has no units;
 // otherwise sets the segment [seg_lo, seg_hi), the context and the cursor at the segment's
 // first unit (all wave-uniform).
@@ -599,13 +593,22 @@ struct Segment {
   int n;
 };
 
-// Every workgroup finds where its waves' segments start with one pass over the texts'
-// lengths: thread t takes a contiguous range of about S / 256 texts and sums their units
-// (independent loads, all in flight), one workgroup-wide exclusive scan of the 256 range
-// sums gives each range's first unit and the total, and the (at most 4) threads whose
-// range holds one of the workgroup's segment starts walk their range again to find the
-// text and the unit within it. Two barriers whatever S is. Workgroup 0 also writes every
-// text's first unit (excl_out) and the header (total units, segment length) for the merge.
+__device__ __forceinline__ int64_t readlane64(int64_t v, int src) {
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, src);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), src);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Every wave finds where its own segment starts from the texts' lengths: lane l takes a
+// contiguous range of about S / 64 texts and sums their units (independent loads, all in
+// flight), a wave-wide scan of the 64 range sums gives each range's first unit and the
+// total, and a ballot names the lane whose range holds the wave's first unit. While that
+// range holds more than one text, the wave splits it over its lanes the same way (a second
+// round for S > 64, a third past 4,096). No barrier and no LDS: a wave starts loading keys
+// and values as soon as its own lengths arrive (a workgroup-wide search with two barriers
+// took 3.0 us from the first instruction to the first load on the 7 x 2,048 OPT-13B step,
+// this one 2.2 us). Wave 0 of workgroup 0 also writes every text's first unit (excl_out)
+// and the header (total units, segment length) for the merge.
 template <int B, int GS>
 __device__ __forceinline__ bool start_segment(const int32_t* __restrict__ ctx, int S, int H,
                                               int Hkv, int maxb, int num_blocks, int W,
@@ -613,13 +616,8 @@ __device__ __forceinline__ bool start_segment(const int32_t* __restrict__ ctx, i
                                               int64_t* __restrict__ hdr,
                                               int64_t* __restrict__ excl_out, Segment& sg,
                                               Ctx& x, Cursor& cur) {
-  __shared__ int64_t sh_wave[kWavesPerGroup];
-  __shared__ int sh_seq[kWavesPerGroup];
-  __shared__ int64_t sh_off[kWavesPerGroup];
-  __shared__ int64_t sh_excl[kWavesPerGroup];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t capacity = (int64_t)maxb * B;
   const int Gq = H / Hkv;
   const int R = Hkv * (Gq / GS);
@@ -627,62 +625,41 @@ __device__ __forceinline__ bool start_segment(const int32_t* __restrict__ ctx, i
     int toff, over;
     return (int64_t)R * units_of(attended_len(ctx, pf.start, i, capacity, B, &toff, &over));
   };
+  // lane's range of texts [r_lo, r_hi) of the n texts from lo, its units, and its first unit
+  // (base + the units of the lower lanes' ranges)
+  auto split = [&](int lo, int n, int64_t base, int& r_lo, int& r_hi, int64_t& mine,
+                   int64_t& incl) {
+    const int per = (n + 63) / 64;
+    r_lo = lo + (lane * per < n ? lane * per : n);
+    r_hi = lo + (lane * per + per < n ? lane * per + per : n);
+    mine = 0;
+    for (int i = r_lo; i < r_hi; ++i) mine += units_at(i);
+    incl = mine;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    incl += base;
+    return per;
+  };
 
-  // ---- this thread's range of texts and its units ----
-  const int per = (S + kThreads - 1) / kThreads;
-  const int r_lo = tid * per < S ? tid * per : S;
-  const int r_hi = r_lo + per < S ? r_lo + per : S;
-  int64_t mine = 0;
-  for (int i = r_lo; i < r_hi; ++i) mine += units_at(i);
-
-  // ---- exclusive scan of the range sums over the workgroup; the total ----
-  int64_t incl = mine;
-  for (int o = 1; o < 64; o <<= 1) {
-    const int64_t y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
-  if (lane == 63) sh_wave[wave] = incl;
-  __syncthreads();
-  int64_t before = 0, total = 0;
-#pragma unroll
-  for (int j = 0; j < kWavesPerGroup; ++j) {
-    before += j < wave ? sh_wave[j] : 0;
-    total += sh_wave[j];
-  }
-  total = uniform64(total);
-  const int64_t ex = before + incl - mine;  // first unit of this thread's range
+  // ---- every text: the total, the segment length, the header ----
+  int r_lo, r_hi;
+  int64_t mine, incl;
+  int per = split(0, S, 0, r_lo, r_hi, mine, incl);
+  const int64_t total = readlane64(incl, 63);
   const int64_t seg = seg::segment_units(total, W, seg_fixed);
-  if (blockIdx.x == 0) {
-    if (tid == 0) {
+  if (blockIdx.x == 0 && wave == 0) {
+    if (lane == 0) {
       hdr[0] = total;
       hdr[1] = seg;
     }
-    int64_t e = ex;
+    int64_t e = incl - mine;
     for (int i = r_lo; i < r_hi; ++i) {
       excl_out[i] = e;
       e += units_at(i);
     }
   }
-
-  // ---- the texts holding this workgroup's segment starts ----
-#pragma unroll
-  for (int j = 0; j < kWavesPerGroup; ++j) {
-    const int64_t c0 = ((int64_t)blockIdx.x * kWavesPerGroup + j) * seg;
-    if (c0 >= ex && c0 < ex + mine) {
-      int64_t e = ex;
-      for (int i = r_lo; i < r_hi; ++i) {
-        const int64_t n = units_at(i);
-        if (c0 < e + n) {
-          sh_seq[j] = i;
-          sh_off[j] = c0 - e;
-          sh_excl[j] = e;
-          break;
-        }
-        e += n;
-      }
-    }
-  }
-  __syncthreads();
 
   sg.w = blockIdx.x * kWavesPerGroup + wave;
   sg.seg_lo = (int64_t)sg.w * seg;
@@ -690,11 +667,28 @@ __device__ __forceinline__ bool start_segment(const int32_t* __restrict__ ctx, i
   sg.seg_hi = sg.seg_lo + seg < total ? sg.seg_lo + seg : total;
   sg.n = (int)(sg.seg_hi - sg.seg_lo);
 
+  // ---- the text holding this wave's first unit: exactly one lane's range holds it ----
+  const int64_t c0 = sg.seg_lo;
+  int found;
+  int64_t f_excl;
+  for (;;) {
+    const uint64_t hit = __ballot(c0 >= incl - mine && c0 < incl);
+    const int src = __builtin_amdgcn_readfirstlane(__builtin_ffsll((long long)hit) - 1);
+    const int lo = __builtin_amdgcn_readlane(r_lo, src);
+    const int hi = __builtin_amdgcn_readlane(r_hi, src);
+    const int64_t base = readlane64(incl - mine, src);
+    if (per == 1 || hi - lo <= 1) {  // (each round's n is below the last's: it ends)
+      found = lo < S ? lo : S - 1;
+      f_excl = base;
+      break;
+    }
+    per = split(lo, hi - lo, base, r_lo, r_hi, mine, incl);
+  }
+
   x = Ctx{S, H, Hkv, Gq, Gq / GS, R, maxb, num_blocks, capacity, ctx, pf};
-  // values read from LDS are the same in every lane: keep them in scalar registers
-  cur.excl = uniform64(sh_excl[wave]);
-  set_text(cur, x, __builtin_amdgcn_readfirstlane(sh_seq[wave]));
-  const int64_t off = uniform64(sh_off[wave]);
+  cur.excl = f_excl;
+  set_text(cur, x, found);
+  const int64_t off = c0 - f_excl;
   cur.r = (int)(off / cur.U);
   cur.u = (int)(off - (int64_t)cur.r * cur.U);
   return true;

@@ -12,7 +12,6 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
-#include <algorithm>
 #include <random>
 #include <vector>
 
@@ -22,7 +21,7 @@ using namespace pagedkv::seg;
 
 namespace {
 
-constexpr int kThreads = 256;   // threads per workgroup of the partition kernel
+constexpr int kLanes = 64;      // lanes of the wave that searches for its segment's start
 constexpr int kWavesPerGroup = 4;
 constexpr int kMaxGS = 8;
 
@@ -61,49 +60,57 @@ bool check(const Case& c, bool old, char* why, size_t n) {
              (long long)total, (long long)W, (long long)seg);
     return false;
   }
-  // the workgroups' search for their waves' first units: thread ranges of ceil(S / 256)
-  // texts, an exclusive scan of the range sums, a walk of the range holding each start
-  const int per = (c.S + kThreads - 1) / kThreads;
-  std::vector<int64_t> range_first(kThreads), range_units(kThreads);
-  int64_t run = 0;
-  for (int t = 0; t < kThreads; ++t) {
-    const int lo = t * per < c.S ? t * per : c.S, hi = lo + per < c.S ? lo + per : c.S;
-    range_first[t] = run;
-    int64_t m = 0;
-    for (int i = lo; i < hi; ++i) m += (int64_t)R * U[i];
-    range_units[t] = m;
-    run += m;
-  }
-  if (run != total) {
-    snprintf(why, n, "range sums %lld != total %lld", (long long)run, (long long)total);
-    return false;
+  // each wave's search for its first unit: lane ranges of ceil(n / 64) of the n texts in
+  // question, a scan of the range sums, the range holding the start; repeated inside that
+  // range while it holds more than one text
+  std::vector<int64_t> cum(c.S + 1, 0);  // units of the texts before each
+  for (int s = 0; s < c.S; ++s) cum[s + 1] = cum[s] + (int64_t)R * U[s];
+  {
+    const int64_t run = cum[c.S];
+    if (run != total) {
+      snprintf(why, n, "range sums %lld != total %lld", (long long)run, (long long)total);
+      return false;
+    }
   }
   for (int64_t w = 0; w < W; ++w) {
     const int64_t c0 = w * seg;
     if (c0 >= total) continue;
-    int hits = 0, text = -1;
-    int64_t off = -1;
-    // the ranges holding c0: the last range starting at or before it, and any empty ranges
-    // sharing that start (which hold nothing)
-    const int last = (int)(std::upper_bound(range_first.begin(), range_first.end(), c0) -
-                           range_first.begin()) - 1;
-    for (int t = last; t >= 0 && range_first[t] == range_first[last]; --t) {
-      if (!(c0 >= range_first[t] && c0 < range_first[t] + range_units[t])) continue;
-      ++hits;
-      int64_t e = range_first[t];
-      const int lo = t * per, hi = lo + per < c.S ? lo + per : c.S;
-      for (int i = lo; i < hi; ++i) {
-        if (c0 < e + (int64_t)R * U[i]) {
-          text = i;
-          off = c0 - e;
-          break;
+    int lo = 0, cnt = c.S, text = -1, rounds = 0;
+    int64_t base = 0, off = -1;
+    for (;;) {
+      ++rounds;
+      const int per = (cnt + kLanes - 1) / kLanes;
+      int hits = 0, hlo = -1, hhi = -1;
+      int64_t hbase = 0, first = base;
+      for (int t = 0; t < kLanes; ++t) {
+        const int a = lo + (t * per < cnt ? t * per : cnt);
+        const int b = lo + (t * per + per < cnt ? t * per + per : cnt);
+        const int64_t m = cum[b] - cum[a];
+        if (c0 >= first && c0 < first + m) {
+          ++hits;
+          hlo = a;
+          hhi = b;
+          hbase = first;
         }
-        e += (int64_t)R * U[i];
+        first += m;
       }
+      if (hits != 1 || rounds > 8) {
+        snprintf(why, n, "segment %lld: start unit %lld in %d ranges at round %d", (long long)w,
+                 (long long)c0, hits, rounds);
+        return false;
+      }
+      if (per == 1 || hhi - hlo <= 1) {
+        text = hlo;
+        off = c0 - hbase;
+        break;
+      }
+      lo = hlo;
+      cnt = hhi - hlo;
+      base = hbase;
     }
-    if (hits != 1 || text < 0 || excl[text] + off != c0 || off >= (int64_t)R * U[text]) {
-      snprintf(why, n, "segment %lld: start unit %lld found %d times (text %d, offset %lld)",
-               (long long)w, (long long)c0, hits, text, (long long)off);
+    if (text < 0 || text >= c.S || excl[text] + off != c0 || off >= (int64_t)R * U[text]) {
+      snprintf(why, n, "segment %lld: start unit %lld found in text %d at offset %lld",
+               (long long)w, (long long)c0, text, (long long)off);
       return false;
     }
   }
@@ -163,9 +170,9 @@ int main(int argc, char** argv) {
   char why[512];
   for (int k = 0; k < cases; ++k) {
     Case c;
-    const int shape = pick(0, 3);
+    const int shape = pick(0, 4);
     c.S = shape == 0 ? pick(1, 8) : shape == 1 ? pick(1, 300) : shape == 2 ? pick(250, 3000)
-                                                                          : pick(1, 40);
+          : shape == 3 ? pick(1, 40) : pick(4000, 20000);  // shape 4: three search rounds
     const int gs_opts[4] = {1, 2, 4, 8};
     c.GS = gs_opts[pick(0, 3)];
     const int G = c.GS * pick(1, 2);
@@ -174,7 +181,7 @@ int main(int argc, char** argv) {
     c.D = pick(0, 1) ? 64 : 128;
     const int bs[4] = {4, 8, 16, 32};
     c.B = bs[pick(0, 3)];
-    const int longest = shape == 3 ? pick(1, 40000) : pick(0, 2100);
+    const int longest = shape == 3 ? pick(1, 40000) : shape == 4 ? pick(0, 300) : pick(0, 2100);
     c.maxb = (longest + c.B - 1) / c.B + pick(0, 3);
     if (c.maxb < 1) c.maxb = 1;
     c.lens.resize(c.S);

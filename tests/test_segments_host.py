@@ -5,7 +5,7 @@ csrc/segments.hpp; tests/native/segments_driver.cpp compiles that header for the
 checks, for random lengths, head groupings, partition sizes and grid sizes (with the
 host's bound on the lengths sometimes below the longest length on the device):
   * every work unit lies in exactly one segment below the grid size W;
-  * each workgroup's search finds the text and unit where its waves' segments start;
+  * each wave's search finds the text and unit where its segment starts;
   * each run's merge range is exactly the segments it touches, never past W - 1;
   * no two runs write the same partial record and every record lies in the workspace.
 The same driver with the segment length fixed to the partition length (the arithmetic
