@@ -132,6 +132,7 @@ int decode_common(void* out, const void* q, const void* k_cache, const void* v_c
   const Launch a{(char*)out, (const char*)q, (const char*)k_cache, (const char*)v_cache,
                  block_tables, context_lens, num_seqs, num_heads, num_kv_heads,
                  max_blocks_per_seq, num_blocks, (int)lay.W, partition_tokens / kChunk,
+                 max_context_len,
                  // scale * k_scale * log2(e): scores in the exp2 domain, key scale folded in
                  scale * k_scale * 1.4426950408889634f, v_scale,
                  (char*)workspace, lay, (hipStream_t)stream, nr, pf};

@@ -131,7 +131,7 @@ struct Ctx {
   int G;            // query heads per key/value head
   int NG;           // head groups per key/value head (G / GS)
   int R;            // runs per text (Hkv * NG)
-  int maxb, num_blocks;
+  int maxb, num_blocks, bsz;
   int64_t capacity;  // max_blocks_per_seq * block_size
   const int32_t* __restrict__ ctx;
   Prefix pf;
@@ -140,10 +140,8 @@ struct Ctx {
 // Tokens text s attends: its context length clamped into [0, capacity], less the tokens
 // its start skips (rounded down to a block, at most all of them). toff: the tokens
 // skipped, 0 when none is left to attend (so the row's first entry stays the one read).
-__device__ __forceinline__ int attended_len(const int32_t* __restrict__ ctx,
-                                            const int32_t* __restrict__ start, int s,
-                                            int64_t capacity, int bsz, int* toff, int* over) {
-  int L = ctx[s];
+__device__ __forceinline__ int attended_from(int L, const int32_t* __restrict__ start, int s,
+                                             int64_t capacity, int bsz, int* toff, int* over) {
   if (L < 0) L = 0;
   *over = L > capacity;
   if (L > capacity) L = (int)capacity;
@@ -152,6 +150,13 @@ __device__ __forceinline__ int attended_len(const int32_t* __restrict__ ctx,
   P -= P % bsz;
   *toff = L - P > 0 ? P : 0;
   return L - P;
+}
+
+// The same for context length ctx[s].
+__device__ __forceinline__ int attended_len(const int32_t* __restrict__ ctx,
+                                            const int32_t* __restrict__ start, int s,
+                                            int64_t capacity, int bsz, int* toff, int* over) {
+  return attended_from(ctx[s], start, s, capacity, bsz, toff, over);
 }
 
 // Mode 1: the state row of query head hv of a group whose members are texts vfirst ..
@@ -178,13 +183,13 @@ struct NewRows {
 
 // (In shared-prefix mode 1 the group's members are read here, once per group, with its
 // length: read where a run is finished they made the wave wait for every load in flight.)
-__device__ __forceinline__ void set_text(Cursor& c, const Ctx& x, int s) {
+// The cursor at text s, whose context length is raw (ctx[s], already read).
+__device__ __forceinline__ void set_text_raw(Cursor& c, const Ctx& x, int s, int raw) {
   c.s = s;
   c.vfirst = c.vcount = 0;
   c.fold = 0;
   if (s < x.S) {
-    c.L = attended_len(x.ctx, x.pf.start, s, x.capacity, (int)(x.capacity / x.maxb), &c.toff,
-                       &c.over);
+    c.L = attended_from(raw, x.pf.start, s, x.capacity, x.bsz, &c.toff, &c.over);
     if (x.pf.mode == 1) {
       c.vfirst = __builtin_amdgcn_readfirstlane(x.pf.vfirst[s]);
       c.vcount = __builtin_amdgcn_readfirstlane(x.pf.vcount[s]);
@@ -195,6 +200,10 @@ __device__ __forceinline__ void set_text(Cursor& c, const Ctx& x, int s) {
     c.L = c.toff = c.over = 0;
   }
   c.U = units_of(c.L);
+}
+
+__device__ __forceinline__ void set_text(Cursor& c, const Ctx& x, int s) {
+  set_text_raw(c, x, s, s < x.S ? x.ctx[s] : 0);
 }
 
 __device__ __forceinline__ void advance(Cursor& c, const Ctx& x) {
@@ -593,6 +602,31 @@ struct Segment {
   int n;
 };
 
+// One step of a wave scan: add the value that DPP control CTRL moves into each lane of the
+// rows in ROWS (lanes without a source add 0), 64 bits as two halves with the carry.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void scan_step(uint32_t& lo, uint32_t& hi) {
+  const uint32_t l2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, CTRL, ROWS, 0xf, false);
+  const uint32_t h2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, CTRL, ROWS, 0xf, false);
+  const uint32_t nl = lo + l2;
+  hi = hi + h2 + (nl < lo ? 1u : 0u);
+  lo = nl;
+}
+
+// Inclusive sum over lanes 0..lane of a wave, by DPP moves (no LDS): row shifts by 1, 2,
+// 4, 8 within each row of 16 lanes, then lane 15 of each row into the next row, and lane 31
+// into the upper two rows.
+__device__ __forceinline__ int64_t wave_scan64(int64_t v) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)((uint64_t)v >> 32);
+  scan_step<0x111, 0xf>(lo, hi);  // row_shr:1
+  scan_step<0x112, 0xf>(lo, hi);  // row_shr:2
+  scan_step<0x114, 0xf>(lo, hi);  // row_shr:4
+  scan_step<0x118, 0xf>(lo, hi);  // row_shr:8
+  scan_step<0x142, 0xa>(lo, hi);  // row_bcast:15 into rows 1 and 3
+  scan_step<0x143, 0xc>(lo, hi);  // row_bcast:31 into rows 2 and 3
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ int64_t readlane64(int64_t v, int src) {
   const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, src);
   const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), src);
@@ -628,25 +662,21 @@ __device__ __forceinline__ bool start_segment(const int32_t* __restrict__ ctx, i
   // lane's range of texts [r_lo, r_hi) of the n texts from lo, its units, and its first unit
   // (base + the units of the lower lanes' ranges)
   auto split = [&](int lo, int n, int64_t base, int& r_lo, int& r_hi, int64_t& mine,
-                   int64_t& incl) {
+                   int64_t& incl, int& first_raw) {
     const int per = (n + 63) / 64;
     r_lo = lo + (lane * per < n ? lane * per : n);
     r_hi = lo + (lane * per + per < n ? lane * per + per : n);
+    first_raw = r_lo < r_hi ? ctx[r_lo] : 0;
     mine = 0;
     for (int i = r_lo; i < r_hi; ++i) mine += units_at(i);
-    incl = mine;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int64_t y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    incl += base;
+    incl = wave_scan64(mine) + base;
     return per;
   };
 
   // ---- every text: the total, the segment length, the header ----
-  int r_lo, r_hi;
+  int r_lo, r_hi, first_raw;
   int64_t mine, incl;
-  int per = split(0, S, 0, r_lo, r_hi, mine, incl);
+  int per = split(0, S, 0, r_lo, r_hi, mine, incl, first_raw);
   const int64_t total = readlane64(incl, 63);
   const int64_t seg = seg::segment_units(total, W, seg_fixed);
   if (blockIdx.x == 0 && wave == 0) {
@@ -669,7 +699,7 @@ __device__ __forceinline__ bool start_segment(const int32_t* __restrict__ ctx, i
 
   // ---- the text holding this wave's first unit: exactly one lane's range holds it ----
   const int64_t c0 = sg.seg_lo;
-  int found;
+  int found, f_raw;
   int64_t f_excl;
   for (;;) {
     const uint64_t hit = __ballot(c0 >= incl - mine && c0 < incl);
@@ -679,17 +709,18 @@ __device__ __forceinline__ bool start_segment(const int32_t* __restrict__ ctx, i
     const int64_t base = readlane64(incl - mine, src);
     if (per == 1 || hi - lo <= 1) {  // (each round's n is below the last's: it ends)
       found = lo < S ? lo : S - 1;
+      f_raw = __builtin_amdgcn_readlane(first_raw, src);
       f_excl = base;
       break;
     }
-    per = split(lo, hi - lo, base, r_lo, r_hi, mine, incl);
+    per = split(lo, hi - lo, base, r_lo, r_hi, mine, incl, first_raw);
   }
 
-  x = Ctx{S, H, Hkv, Gq, Gq / GS, R, maxb, num_blocks, capacity, ctx, pf};
+  x = Ctx{S, H, Hkv, Gq, Gq / GS, R, maxb, num_blocks, B, capacity, ctx, pf};
   cur.excl = f_excl;
-  set_text(cur, x, found);
-  const int64_t off = c0 - f_excl;
-  cur.r = (int)(off / cur.U);
+  set_text_raw(cur, x, found, f_raw);
+  const int64_t off = c0 - f_excl;  // below R * U
+  cur.r = off <= 0x7fffffff ? (int)off / cur.U : (int)(off / cur.U);
   cur.u = (int)(off - (int64_t)cur.r * cur.U);
   return true;
 }
@@ -834,12 +865,97 @@ __global__ __launch_bounds__(kThreads) void decode_partition(
   }
 }
 
-// Combine the partials of one run, left by segments w0..w1, in segment order, for all GS
+// Combining the partials of one run, left by segments w0..w1, in segment order, for all GS
 // query heads of the run at once: the wave's lanes form GS groups of CL = 64 / GS lanes,
 // group j taking head j's D values, PE = D / CL per lane. Segment w0 holds the run in its
 // slot 1 unless the run starts exactly at w0's first unit (then it is w0's first run, slot
 // 0); every later segment starts inside the run, so the run is its first run (slot 0).
-// The partials are read UNROLL at a time with all loads in flight and combined with a
+// The partials are read UNROLL at a time with all loads in flight.
+//
+// The records a merge step reads: UNROLL partials of one lane's head (m, l, its acc values).
+template <int D, int GS>
+struct MergeBatch {
+  static constexpr int CL = 64 / GS;  // lanes per head
+  static constexpr int PE = D / CL;   // values per lane
+  static constexpr int UNROLL = PE >= 16 ? 4 : 8;
+  float m[UNROLL], l[UNROLL], a[UNROLL][PE];
+};
+
+// Loads the partials of segments w .. min(w + UNROLL - 1, w1) of the run starting at run_lo
+// (past w1: empty partials of weight 0).
+template <int D, int GS>
+__device__ __forceinline__ void load_batch(MergeBatch<D, GS>& b, const float* __restrict__ partials,
+                                           int64_t w, int64_t w1, int64_t run_lo, int64_t seg,
+                                           int lane) {
+  using MB = MergeBatch<D, GS>;
+  const int j = lane / MB::CL, c = lane % MB::CL;
+#pragma unroll
+  for (int k = 0; k < MB::UNROLL; ++k) {
+    b.m[k] = -INFINITY;
+    b.l[k] = 0.f;
+#pragma unroll
+    for (int e = 0; e < MB::PE; ++e) b.a[k][e] = 0.f;
+    if (w + k <= w1) {
+      const float* p =
+          partials + partial_index<D, GS>(w + k, seg::partial_slot(run_lo, (w + k) * seg), j);
+      b.m[k] = p[0];
+      b.l[k] = p[1];
+#pragma unroll
+      for (int e = 0; e < MB::PE; ++e) b.a[k][e] = p[4 + c * MB::PE + e];
+    }
+  }
+}
+
+template <int D, int GS>
+__device__ __forceinline__ void fold_batch(const MergeBatch<D, GS>& b, float& M, float& den,
+                                           float* num) {
+  using MB = MergeBatch<D, GS>;
+  float mg = M;
+#pragma unroll
+  for (int k = 0; k < MB::UNROLL; ++k) mg = fmaxf(mg, b.m[k]);
+  const float mu = mg == -INFINITY ? 0.f : mg;
+  const float r = fast_exp2(M - mu);
+  den *= r;
+#pragma unroll
+  for (int e = 0; e < MB::PE; ++e) num[e] *= r;
+#pragma unroll
+  for (int k = 0; k < MB::UNROLL; ++k) {  // segment order
+    const float f = fast_exp2(b.m[k] - mu);
+    den += f * b.l[k];
+#pragma unroll
+    for (int e = 0; e < MB::PE; ++e) num[e] += f * b.a[k][e];
+  }
+  M = mg;
+}
+
+// Writes a merged run: the state itself (state_dst, unnormalized) or the output row
+// (dst_row; null with no state_dst: the lane's head writes nothing).
+template <int QT, int D, int GS>
+__device__ __forceinline__ void merge_finish(float M, float den, const float* num,
+                                             float v_scale, char* __restrict__ dst_row,
+                                             float* state_dst, int lane) {
+  using MB = MergeBatch<D, GS>;
+  constexpr int PE = MB::PE;
+  const int c = lane % MB::CL;
+  if (state_dst || !dst_row) {
+    if (!state_dst) return;
+    if (c == 0) {
+      state_dst[0] = M;
+      state_dst[1] = den;
+    }
+#pragma unroll
+    for (int e = 0; e < PE; ++e) state_dst[4 + c * PE + e] = num[e];
+    return;
+  }
+  float o[PE];
+  const float inv = den > 0.f ? v_scale / den : 0.f;
+  // 0 * num: NaN stays visible for a poisoned run
+#pragma unroll
+  for (int e = 0; e < PE; ++e) o[e] = den > 0.f ? num[e] * inv : 0.f * num[e];
+  store_out<QT, PE>(dst_row + c * PE * elt_size<QT>(), o);
+}
+
+// Merges a run's partials w0 .. w1 (in segment order) into its output row, with one
 // running maximum (the rescaling of the online softmax), in one pass. init / init2: states
 // (m, l, pad, pad, acc[D]) of the lane's head that come first (null: none); state_dst: the
 // merged state itself is written there instead of an output row (null: the lane's head
@@ -850,13 +966,9 @@ __device__ __forceinline__ void merge_run(const float* __restrict__ partials, in
                                           float v_scale, char* __restrict__ dst_row, int lane,
                                           const float* init, float* state_dst,
                                           const float* init2) {
-  constexpr int CL = 64 / GS;  // lanes per head
-  constexpr int PE = D / CL;   // values per lane
-  constexpr int UNROLL = PE >= 16 ? 4 : 8;
-  const int j = lane / CL, c = lane % CL;
-  auto index_of = [&](int64_t w) -> int64_t {
-    return partial_index<D, GS>(w, seg::partial_slot(run_lo, w * seg), j);
-  };
+  using MB = MergeBatch<D, GS>;
+  constexpr int PE = MB::PE;
+  const int c = lane % MB::CL;
   float M = -INFINITY, den = 0.f, num[PE];
 #pragma unroll
   for (int e = 0; e < PE; ++e) num[e] = 0.f;
@@ -875,57 +987,12 @@ __device__ __forceinline__ void merge_run(const float* __restrict__ partials, in
     for (int e = 0; e < PE; ++e) num[e] = num[e] * r + init2[4 + c * PE + e] * f;
     M = mg;
   }
-  for (int64_t w = w0; w <= w1; w += UNROLL) {
-    float m[UNROLL], l[UNROLL], a[UNROLL][PE];
-#pragma unroll
-    for (int k = 0; k < UNROLL; ++k) {
-      // past w1: an empty partial (weight 0) instead of a load
-      m[k] = -INFINITY;
-      l[k] = 0.f;
-#pragma unroll
-      for (int e = 0; e < PE; ++e) a[k][e] = 0.f;
-      if (w + k <= w1) {
-        const float* p = partials + index_of(w + k);
-        m[k] = p[0];
-        l[k] = p[1];
-#pragma unroll
-        for (int e = 0; e < PE; ++e) a[k][e] = p[4 + c * PE + e];
-      }
-    }
-    float mg = M;
-#pragma unroll
-    for (int k = 0; k < UNROLL; ++k) mg = fmaxf(mg, m[k]);
-    const float mu = mg == -INFINITY ? 0.f : mg;
-    const float r = fast_exp2(M - mu);
-    den *= r;
-#pragma unroll
-    for (int e = 0; e < PE; ++e) num[e] *= r;
-#pragma unroll
-    for (int k = 0; k < UNROLL; ++k) {  // segment order
-      const float f = fast_exp2(m[k] - mu);
-      den += f * l[k];
-#pragma unroll
-      for (int e = 0; e < PE; ++e) num[e] += f * a[k][e];
-    }
-    M = mg;
+  for (int64_t w = w0; w <= w1; w += MB::UNROLL) {
+    MB b;
+    load_batch<D, GS>(b, partials, w, w1, run_lo, seg, lane);
+    fold_batch<D, GS>(b, M, den, num);
   }
-  if (state_dst || !dst_row) {
-    if (!state_dst) return;
-    // the merged state itself, unnormalized
-    if (c == 0) {
-      state_dst[0] = M;
-      state_dst[1] = den;
-    }
-#pragma unroll
-    for (int e = 0; e < PE; ++e) state_dst[4 + c * PE + e] = num[e];
-    return;
-  }
-  float o[PE];
-  const float inv = den > 0.f ? v_scale / den : 0.f;
-  // 0 * num: NaN stays visible for a poisoned run
-#pragma unroll
-  for (int e = 0; e < PE; ++e) o[e] = den > 0.f ? num[e] * inv : 0.f * num[e];
-  store_out<QT, PE>(dst_row + c * PE * elt_size<QT>(), o);
+  merge_finish<QT, D, GS>(M, den, num, v_scale, dst_row, state_dst, lane);
 }
 
 // Merge pass: one wave per run (a text's head group of GS query heads), all GS heads at
@@ -933,20 +1000,58 @@ __device__ __forceinline__ void merge_run(const float* __restrict__ partials, in
 // launch (the merge range is clamped to it). (One wave per query head instead launched GS
 // times the waves for the same partials. Taking the first unit and the segment length from
 // the lengths themselves for small batches, instead of the header and offsets the partition
-// kernel wrote, measured 0.6 us slower per op on the 7 x 2,048 OPT-13B step.)
+// kernel wrote, measured 0.6 us slower per op on the 7 x 2,048 OPT-13B step: loading the
+// partials on a guess beside them, checked against them, is what saves the round trip.)
 template <int QT, int D, int GS>
 __global__ __launch_bounds__(kThreads) void decode_merge(
     char* __restrict__ out, const int32_t* __restrict__ ctx, int S, int H, int Hkv, int maxb,
     int bsz, int W, float v_scale, const int64_t* __restrict__ hdr,
-    const int64_t* __restrict__ excl, const float* __restrict__ partials, Prefix pf) {
+    const int64_t* __restrict__ excl, const float* __restrict__ partials, Prefix pf,
+    int max_ctx, int seg_fixed) {
   const int lane = threadIdx.x & 63;
   const int Gq = H / Hkv, NG = Gq / GS, R = Hkv * NG;
   const int64_t run =
       (int64_t)blockIdx.x * kWavesPerGroup + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (run >= (int64_t)S * R) return;
   const int s = (int)(run / R), r = (int)(run - (int64_t)s * R);
+  const int64_t capacity = (int64_t)maxb * bsz;
+  if (pf.mode == 0) {
+    // The geometry if every text attends max_context_len tokens (a batch of equal lengths):
+    // this run's partials are loaded on that guess at once, beside the lengths, header and
+    // offsets that decide it, instead of after them (one memory round trip fewer), and
+    // used only where the guess holds.
+    const int Lg = max_ctx < 0 ? 0 : max_ctx > capacity ? (int)capacity : max_ctx;
+    const int Ug = units_of(Lg);
+    const int64_t segg = seg::segment_units((int64_t)S * R * Ug, W, seg_fixed);
+    const int64_t log = ((int64_t)s * R + r) * Ug;
+    int64_t gw0, gw1;
+    seg::run_segments(log, log + Ug, segg, W, &gw0, &gw1);
+    using MB = MergeBatch<D, GS>;
+    MB b;
+    load_batch<D, GS>(b, partials, gw0, gw1, log, segg, lane);
+    int toff, over;
+    const int L = attended_len(ctx, pf.start, s, capacity, bsz, &toff, &over);
+    const int64_t seg = hdr[1];
+    const int64_t lo = excl[s] + (int64_t)r * units_of(L);
+    if (units_of(L) == Ug && seg == segg && lo == log) {
+      if (gw0 == gw1) return;
+      const int h = (r / NG) * Gq + (r % NG) * GS + lane / (64 / GS);
+      float M = -INFINITY, den = 0.f, num[MB::PE];
+#pragma unroll
+      for (int e = 0; e < MB::PE; ++e) num[e] = 0.f;
+      fold_batch<D, GS>(b, M, den, num);  // the same batches, in the same order, as merge_run
+      for (int64_t w = gw0 + MB::UNROLL; w <= gw1; w += MB::UNROLL) {
+        MB b2;
+        load_batch<D, GS>(b2, partials, w, gw1, lo, seg, lane);
+        fold_batch<D, GS>(b2, M, den, num);
+      }
+      merge_finish<QT, D, GS>(M, den, num, v_scale,
+                              out + ((int64_t)s * H + h) * D * elt_size<QT>(), nullptr, lane);
+      return;
+    }
+  }
   int toff, over;
-  const int L = attended_len(ctx, pf.start, s, (int64_t)maxb * bsz, bsz, &toff, &over);
+  const int L = attended_len(ctx, pf.start, s, capacity, bsz, &toff, &over);
   const int U = units_of(L);
   const int64_t seg = hdr[1];
   const int64_t lo = excl[s] + (int64_t)r * U, hi = lo + U;
@@ -1323,6 +1428,7 @@ struct Launch {
   const int32_t* tables;
   const int32_t* ctx;
   int S, H, Hkv, maxb, nb, W, seg_fixed;
+  int max_ctx;    // the caller's bound on the context lengths (the merge's guess)
   float sl;       // scale * k_scale * log2(e)
   float v_scale;
   char* ws;
@@ -1363,7 +1469,8 @@ bool launch(const Launch& a) {
   const int64_t runs = (int64_t)a.S * (a.H / GS);  // merge waves: one per run
   const int mgroups = (int)((runs + kWavesPerGroup - 1) / kWavesPerGroup);
   hipLaunchKernelGGL((decode_merge<QT, D, GS>), dim3(mgroups), dim3(kThreads), 0, a.st, a.out,
-                     a.ctx, a.S, a.H, a.Hkv, a.maxb, B, a.W, a.v_scale, hdr, excl, part, a.pf);
+                     a.ctx, a.S, a.H, a.Hkv, a.maxb, B, a.W, a.v_scale, hdr, excl, part, a.pf,
+                     a.max_ctx, a.seg_fixed);
   return true;
 }
 
