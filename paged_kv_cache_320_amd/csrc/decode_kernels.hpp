@@ -361,6 +361,18 @@ template <int B, int GS>
 __device__ __forceinline__ bool writes_new_row(const Cursor& c, const Ctx& x) {
   return c.L > 0 && c.u == c.U - 1 && (GS == 1 ? c.r % x.G : c.r % x.NG) == 0;
 }
+// One 16-byte piece of the new row of one pool (kv: nr.kc or nr.vc) at byte col.
+template <int D, int ELT, int B, int GS>
+__device__ __forceinline__ void store_new_piece_of(const NewRows& nr, char* __restrict__ kv,
+                                                   const Cursor& c, const Ctx& x, int col,
+                                                   const uint4& piece) {
+  constexpr int kRowBytes = D * ELT;
+  const int64_t slot = nr.slots[c.s];
+  if (slot < 0 || slot >= (int64_t)x.num_blocks * B) return;
+  const int kvh = kv_head_of<GS>(c.r, x);
+  const int64_t row = ((slot / B) * x.Hkv + kvh) * B + slot % B;
+  *reinterpret_cast<uint4*>(kv + row * kRowBytes + col) = piece;
+}
 template <int D, int ELT, int B, int GS>
 __device__ __forceinline__ void store_new_piece(const NewRows& nr, const Cursor& c, const Ctx& x,
                                                 int col, const uint4& k, const uint4& v) {
@@ -1177,11 +1189,31 @@ __device__ __forceinline__ void load_chunk_mma(MmaBuf<D>& b, const Cursor& c, co
   // fused write: the last position's rows come from k_new / v_new
   const bool fresh = FUSED && tc == last;
   const char* ksrc = fresh ? nr.k + ((int64_t)c.s * x.Hkv + kvh) * kRowBytes : kc + row;
-  const char* vsrc = fresh ? nr.v + ((int64_t)c.s * x.Hkv + kvh) * kRowBytes : vc + row;
+#pragma unroll
+  for (int cc = 0; cc < D / 32; ++cc) b.k[cc] = load_stream(ksrc + (8 * grp + 32 * cc) * 2);
+  // values go through LDS anyway (for the transposing read), so they are loaded whole rows
+  // at a time: load cc takes rows kVRows cc + lane / kVLanes, 16 bytes each (the keys' MFMA
+  // layout reads half of each 128-byte line per load)
+  constexpr int kVLanes = kRowBytes / 16, kVRows = 64 / kVLanes;
+  const int vr = lane / kVLanes, vp = lane % kVLanes;
+  const char* vnew = nr.v + ((int64_t)c.s * x.Hkv + kvh) * kRowBytes + vp * 16;
 #pragma unroll
   for (int cc = 0; cc < D / 32; ++cc) {
-    b.k[cc] = load_stream(ksrc + (8 * grp + 32 * cc) * 2);
-    b.v[cc] = load_stream(vsrc + (8 * grp + 32 * cc) * 2);
+    const int tv = c.u * kChunk + kVRows * cc + vr;
+    const int tvc = tv < last ? tv : last;
+    int vblk = blk;
+    if constexpr (B < kChunk) {
+      vblk = trow[tvc / B];
+      if ((unsigned)vblk >= (unsigned)x.num_blocks) {
+        b.bad = true;
+        vblk = 0;
+      }
+    }
+    const char* vsrc = FUSED && tvc == last
+                           ? vnew
+                           : vc + ((int64_t)vblk * x.Hkv + kvh) * kTileBytes +
+                                 (int64_t)(tvc % B) * kRowBytes + vp * 16;
+    b.v[cc] = load_stream(vsrc);
   }
 }
 
@@ -1198,10 +1230,13 @@ __device__ __forceinline__ void compute_chunk_mma(const MmaBuf<D>& b, const Curs
   constexpr int VS = D + 16;  // LDS row: 8-bank shift per row for the transposing read
   if (c.L == 0) return;  // nothing attended: the run's result is zeros
   const int col = lane & 15, grp = lane >> 4;
-  // values into this wave's LDS rows (token col), read back transposed below
+  // values into this wave's LDS rows, read back transposed below (load cc holds rows
+  // kVRows cc + lane / kVLanes, piece lane % kVLanes)
+  constexpr int kVLanes = D * 2 / 16, kVRows = 64 / kVLanes;
 #pragma unroll
   for (int cc = 0; cc < D / 32; ++cc)
-    *reinterpret_cast<uint4*>(vrow + col * VS + 8 * grp + 32 * cc) = b.v[cc];
+    *reinterpret_cast<uint4*>(vrow + (kVRows * cc + lane / kVLanes) * VS +
+                              8 * (lane % kVLanes)) = b.v[cc];
   f4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int cc = 0; cc < D / 32; ++cc) s = M::qk(__builtin_bit_cast(v8, b.k[cc]), qv[cc], s);
@@ -1377,10 +1412,18 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mma(
     load_q(cur);
     compute_chunk_mma<QT, D>(b, cur, st, qv, vrow, scale_log2, lane);
     if constexpr (FUSED) {
-      if (writes_new_row<B, GS>(cur, x) && cur.u * kChunk + col == cur.L - 1) {
+      if (writes_new_row<B, GS>(cur, x)) {
+        const int at = cur.L - 1 - cur.u * kChunk;  // the new row's place in the chunk
+        if (col == at) {
+#pragma unroll
+          for (int cc = 0; cc < D / 32; ++cc)
+            store_new_piece_of<D, 2, B, GS>(nr, nr.kc, cur, x, (8 * grp + 32 * cc) * 2, b.k[cc]);
+        }
+        constexpr int kVLanes = D * 2 / 16, kVRows = 64 / kVLanes;
 #pragma unroll
         for (int cc = 0; cc < D / 32; ++cc)
-          store_new_piece<D, 2, B, GS>(nr, cur, x, (8 * grp + 32 * cc) * 2, b.k[cc], b.v[cc]);
+          if (kVRows * cc + lane / kVLanes == at)
+            store_new_piece_of<D, 2, B, GS>(nr, nr.vc, cur, x, (lane % kVLanes) * 16, b.v[cc]);
       }
     }
     // last chunk of the run, or of the segment
