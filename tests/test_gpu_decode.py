@@ -264,3 +264,36 @@ def test_context_beyond_the_host_bound(native, H, Hkv):
         got = run_gpu(native, q, kc, vc, tables, L, partition_tokens=T, max_ctx=100)
         assert torch.isfinite(got.float()).all()
         assert_close(got, want, "f16", f"T={T} max_context_len=100")
+
+
+@pytest.mark.parametrize("H,Hkv", [(8, 8), (16, 2), (32, 4)])
+def test_merge_guess_and_general_path_agree_bit_for_bit(native, H, Hkv):
+    """The merge loads a run's partials on the guess that every text attends
+    max_context_len tokens. With max_context_len exact (the guess holds) and with a looser
+    bound of the same grid (the guess fails: the general path), the outputs must be the
+    same bits: both fold the same partials in the same order. Unequal lengths (the guess
+    fails everywhere but the longest texts) must agree with the oracle as well."""
+    D, B = 128, 16
+    for lens in ([300] * 9, [300, 17, 300, 1, 288, 300, 0, 299, 300]):
+        q, kc, vc, tables, L = make_case(11, lens, H, Hkv, D, B, "f16", kv_std=0.125)
+        say(f"merge guess H={H} Hkv={Hkv} lens={lens}")
+        exact = run_gpu(native, q, kc, vc, tables, L, max_ctx=300)
+        loose = run_gpu(native, q, kc, vc, tables, L, max_ctx=300 + 3 * B)
+        assert torch.equal(exact.view(torch.int16), loose.view(torch.int16))
+        want = decode_attention(q, kc, vc, tables, L, B)
+        assert_close(exact, want, "f16", f"lens {lens}")
+
+
+def test_segment_search_past_4096_texts(native):
+    """More than 4,096 texts: each wave's segment search takes three rounds (64 lane
+    ranges of 66 texts, then their sub-ranges, then single texts). Short random lengths,
+    empty texts included; every output against the oracle."""
+    rng = np.random.default_rng(5)
+    lens = [int(x) for x in rng.integers(0, 25, 4200)]
+    lens[::97] = [0] * len(lens[::97])
+    H, Hkv, D, B = 2, 2, 64, 4
+    q, kc, vc, tables, L = make_case(12, lens, H, Hkv, D, B, "f16", kv_std=0.125, extra=3)
+    say(f"segment search, {len(lens)} texts")
+    got = run_gpu(native, q, kc, vc, tables, L)
+    want = decode_attention(q, kc, vc, tables, L, B)
+    assert_close(got, want, "f16", "4,200 texts")
