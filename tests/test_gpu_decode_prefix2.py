@@ -176,3 +176,46 @@ def test_nested_inner_group_across_equal_outer_groups(native):
     ig = [(0, 1, 64 + 32), (1, 3, 64 + 32)]
     check(native, "f16", (q, kc, vc, tables, lens, og, ig), "inner group across equal outer groups",
           inner_members=4)
+
+
+def test_nested_graph_replays_match_eager(native):
+    """The whole call (start clear, both levels' set-ups and passes with their merges, the
+    texts' own pass) captured into a HIP graph: every replay equals the eager call bit for
+    bit, with eager work on the same buffers between replays."""
+    case = make_nested(61, [(64, [(32, [5, 9]), (16, [3, 20])]), (32, [(48, [1, 4])])],
+                       8, 4, 128, 16, "bf16")
+    q, kc, vc, tables, lens, og, ig = case
+    S, H, D = q.shape
+    Hkv, B = kc.shape[1], kc.shape[2]
+    say(f"prefix2 graph replay S={S} H={H}")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    arr = lambda gs, i: np.array([x[i] for x in gs], dtype=np.int32)
+    max_ctx = int(lens.max())
+    p1, p2 = arr(og, 2), arr(ig, 2)
+    m1, m2, im = int(p1.max()), int(p2.max()), max(x[1] for x in ig)
+    n = native.pa_decode_prefix2_workspace_bytes(S, H, Hkv, D, B, max_ctx, len(og), m1, len(ig),
+                                                 m2, im, CODE[q.dtype])
+    ins = (q.cuda(), kc.cuda(), vc.cuda(), dev(tables), dev(lens), max_ctx, dev(arr(og, 0)),
+           dev(arr(og, 1)), dev(p1), m1, dev(arr(ig, 0)), dev(arr(ig, 1)), dev(p2), m2, im)
+    ws_e = torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda")
+    ws_g = torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda")
+    out_e = torch.full(q.shape, 7.0, dtype=q.dtype, device="cuda")
+    out_g = torch.full(q.shape, 7.0, dtype=q.dtype, device="cuda")
+    native.pa_decode_attention_prefix2(out_e, *ins, ws_e)
+    native.pa_decode_attention_prefix2(out_g, *ins, ws_g)  # eager first: properties cached
+    torch.cuda.synchronize()
+    want = out_e.cpu()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        native.pa_decode_attention_prefix2(out_g, *ins, ws_g)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out_g.fill_(float("nan"))
+        ws_g.fill_(0x5A)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out_g.cpu()
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"replay {rep}"
+    ref = decode_attention(q, kc, vc, tables, lens, B)
+    assert_close(want, ref, "bf16", "prefix2 eager (graph test)")
