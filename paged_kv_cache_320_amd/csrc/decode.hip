@@ -352,13 +352,14 @@ struct PrefixLayout {
 
 // Segments per compute unit of one pass of the shared-block decode, whose key/value heads
 // each serve G query heads: the matrix-core kernel (4 or 8 query heads per wave, 16-bit
-// formats) keeps 4; the vector kernel takes 8, which on the 32 x 8 sharing workload (bf16)
-// took the forked pairs' pass from 162 to 142 us and the texts' own pass from 24 to 20 us
-// (the matrix-core prompts pass went from 128 to 136 us with 8; the plain decode of 256
-// mixed-length texts was unchanged).
+// formats) keeps 4; the vector kernel takes 16, the most that stay resident at its 104
+// VGPRs (the passes' runs are short: more waves keep more bytes in flight). On the 32 x 8
+// sharing workload (bf16) 8 took the forked pairs' pass from 162 to 142 us and the texts'
+// own pass from 24 to 20 us; 16 took the op from 323-327 to 317-320 us (12: no change).
+// (The matrix-core prompts pass went from 128 to 136 us with 8.)
 int pass_waves(int G, int32_t elt) {
   const int gs = heads_per_wave(G);
-  return gs >= 4 && elt == 2 ? kWavesPerCU : 2 * kWavesPerCU;
+  return gs >= 4 && elt == 2 ? kWavesPerCU : 4 * kWavesPerCU;
 }
 
 int prefix_layout(int32_t S, int32_t H, int32_t Hkv, int32_t D, int32_t max_ctx, int32_t levels,
@@ -517,6 +518,235 @@ __global__ void prefix_prep_kernel(const int32_t* __restrict__ vfirst_in,
   }
 }
 
+// ---- the set-up in one launch --------------------------------------------------------
+// For batches of at most kSetupMax texts and kSetupMax groups per level the clear and the
+// per-level set-ups above run as one kernel: workgroup 0 takes every text's starts and
+// outer group from per-text membership arrays it builds in LDS (so no text's entries need
+// clearing first, and no level waits for the one before it), and workgroup 1 + b takes
+// group b of the outer level, then of the inner one: its geometry, its table row and its
+// batch of queries for all key/value heads. Both compute a group's geometry with the same
+// functions, as prefix_prep_kernel computes it; overlapping groups (refused by the debug
+// check) resolve to the highest-numbered group.
+constexpr int kSetupMax = 2048;
+
+struct SetupLevel {
+  const int32_t *first, *count, *prefix;  // the caller's groups
+  int n, max_prefix, cols, maxbp;
+  int32_t *vfirst, *vcount, *vctx, *vtab;  // the level's batch of groups
+  char* vq;
+  int32_t* start;  // each text's start at this level
+};
+
+struct SetupArgs {
+  SetupLevel lv[2];
+  int levels;
+  const int32_t* ctx;
+  const int32_t* tables;
+  const char* q;
+  int S, H, Hkv, row_bytes, maxb, bsz;
+  int32_t* gid;  // two levels: each text's outer group (-1: none)
+};
+
+// Group v's first member, clamped into the batch, and its member count, clamped to the
+// level's width and to the batch's end.
+__device__ __forceinline__ void setup_members(const SetupLevel& g, int v, int S, int Gr, int& f,
+                                              int& n) {
+  int ff = g.first[v];
+  ff = ff < 0 ? 0 : ff >= S ? S - 1 : ff;
+  const int most = g.cols / Gr < S - ff ? g.cols / Gr : S - ff;
+  const int c = g.count[v];
+  n = c < 0 ? 0 : c > most ? most : c;
+  f = ff;
+}
+
+// Shared length of a group with requested length `prefix`, n members whose attended
+// lengths less one token have minimum `keep` (INT32_MAX for none), starting at P0: at most
+// max_prefix and keep, rounded down to a block, not below P0.
+__device__ __forceinline__ int setup_len_from(int64_t prefix, int max_prefix, int64_t keep, int n,
+                                              int P0, int bsz) {
+  int64_t P = prefix;
+  if (P > max_prefix) P = max_prefix;
+  if (P > keep) P = keep;
+  if (P < 0 || n == 0) P = 0;
+  P -= P % bsz;
+  if (P < P0) P = P0;
+  return (int)P;
+}
+
+// A member's attended length less one token (its length clamped into [0, capacity]).
+__device__ __forceinline__ int64_t setup_keep(const SetupArgs& a, int t) {
+  const int64_t capacity = (int64_t)a.maxb * a.bsz;
+  int64_t L = a.ctx[t];
+  L = L < 0 ? 0 : L > capacity ? capacity : L;
+  return L - 1;
+}
+
+// The same for group v over its members f .. f + n - 1 (n <= kPrefixCols), one thread.
+__device__ __forceinline__ int setup_shared_len(const SetupLevel& g, int v, int f, int n, int P0,
+                                                const SetupArgs& a) {
+  int64_t keep = INT32_MAX;
+#pragma unroll
+  for (int m = 0; m < kPrefixCols; ++m) {
+    if (m < n) {
+      const int64_t k = setup_keep(a, f + m);
+      if (k < keep) keep = k;
+    }
+  }
+  return setup_len_from(g.prefix[v], g.max_prefix, keep, n, P0, a.bsz);
+}
+
+// Minimum over the wave of x (64-bit).
+__device__ __forceinline__ int64_t wave_min64(int64_t x) {
+  for (int o = 32; o > 0; o >>= 1) {
+    const int64_t y = __shfl_xor(x, o);
+    x = y < x ? y : x;
+  }
+  return x;
+}
+
+__global__ __launch_bounds__(256) void prefix_setup_kernel(SetupArgs a) {
+  __shared__ int memb0[kSetupMax], memb1[kSetupMax], len0[kSetupMax], len1[kSetupMax];
+  __shared__ int sh[4];
+  const int S = a.S, Gr = a.H / a.Hkv;
+  const SetupLevel& g0 = a.lv[0];
+  if (blockIdx.x == 0) {
+    // every text: the groups holding it, then its starts
+    for (int t = threadIdx.x; t < S; t += blockDim.x) {
+      memb0[t] = -1;
+      memb1[t] = -1;
+    }
+    __syncthreads();
+    for (int u = threadIdx.x; u < g0.n; u += blockDim.x) {
+      int f, n;
+      setup_members(g0, u, S, Gr, f, n);
+      len0[u] = setup_shared_len(g0, u, f, n, 0, a);
+      for (int m = 0; m < n; ++m) atomicMax(&memb0[f + m], u);
+    }
+    __syncthreads();
+    if (a.levels > 1) {
+      const SetupLevel& g1 = a.lv[1];
+      for (int v = threadIdx.x; v < g1.n; v += blockDim.x) {
+        int f, n;
+        setup_members(g1, v, S, Gr, f, n);
+        // members up to the first whose outer group differs from the first member's
+        const int of = n > 0 ? memb0[f] : -1;
+        for (int m = 1; m < n; ++m)
+          if (memb0[f + m] != of) {
+            n = m;
+            break;
+          }
+        // the inner level starts where the first member's outer level ended
+        const int P0 = n > 0 && of >= 0 ? len0[of] : 0;
+        len1[v] = setup_shared_len(g1, v, f, n, P0, a);
+        for (int m = 0; m < n; ++m) atomicMax(&memb1[f + m], v);
+      }
+      __syncthreads();
+    }
+    for (int t = threadIdx.x; t < S; t += blockDim.x) {
+      const int u = memb0[t];
+      const int st0 = u >= 0 ? len0[u] : 0;
+      g0.start[t] = st0;
+      if (a.levels > 1) {
+        a.gid[t] = u;
+        const int v = memb1[t];
+        a.lv[1].start[t] = v >= 0 ? len1[v] : st0;
+      }
+    }
+    return;
+  }
+  // group v of level l
+  const int b = blockIdx.x - 1;
+  const int l = b < g0.n ? 0 : 1;
+  const int v = l == 0 ? b : b - g0.n;
+  const SetupLevel& g = a.lv[l];
+  if (threadIdx.x < 64) {
+    // few dependent memory round trips: the descriptors (this group's and, for the inner
+    // level, the outer groups' one per lane) at once, then every member's length one per
+    // lane, reduced over the wave
+    const int lane = threadIdx.x;
+    int f, n;
+    setup_members(g, v, S, Gr, f, n);
+    const int64_t prefix = g.prefix[v];
+    int P0 = 0;
+    if (l == 1) {
+      // each member's outer group: the highest outer group holding it, by ballots over the
+      // outer groups, 64 at a time; the lane that holds its descriptor hands it over
+      int og[kPrefixCols], ofo = 0, ono = 0;
+#pragma unroll
+      for (int m = 0; m < kPrefixCols; ++m) og[m] = -1;
+      for (int u0 = 0; u0 < g0.n; u0 += 64) {
+        const int u = u0 + lane;
+        int fu = 0, nu = 0;
+        if (u < g0.n) setup_members(g0, u, S, Gr, fu, nu);
+#pragma unroll
+        for (int m = 0; m < kPrefixCols; ++m) {
+          const uint64_t hit = __ballot(m < n && f + m >= fu && f + m < fu + nu);
+          if (hit) {
+            const int src = 63 - __builtin_clzll(hit);
+            og[m] = u0 + src;
+            if (m == 0) {
+              ofo = __shfl(fu, src);
+              ono = __shfl(nu, src);
+            }
+          }
+        }
+      }
+      for (int m = 1; m < n; ++m)
+        if (og[m] != og[0]) {
+          n = m;
+          break;
+        }
+      if (n > 0 && og[0] >= 0) {
+        const int64_t ko = wave_min64(lane < ono ? setup_keep(a, ofo + lane) : INT32_MAX);
+        P0 = setup_len_from(g0.prefix[og[0]], g0.max_prefix, ko, ono, 0, a.bsz);
+      }
+    }
+    const int64_t keep = wave_min64(lane < n ? setup_keep(a, f + lane) : INT32_MAX);
+    const int P = setup_len_from(prefix, g.max_prefix, keep, n, P0, a.bsz);
+    if (lane == 0) {
+      sh[0] = f;
+      sh[1] = n;
+      sh[2] = P;
+      sh[3] = P0;
+      g.vfirst[v] = f;
+      g.vcount[v] = n;
+      g.vctx[v] = P - P0;
+    }
+  }
+  __syncthreads();
+  const int f = sh[0], n = sh[1], P = sh[2], P0 = sh[3];
+  const int nb = (P - P0) / a.bsz, b0 = P0 / a.bsz;
+  for (int k = threadIdx.x; k < g.maxbp; k += blockDim.x)
+    g.vtab[(int64_t)v * g.maxbp + k] = k < nb ? a.tables[(int64_t)f * a.maxb + b0 + k] : 0;
+  // queries: column c of key/value head kvh is member c / Gr's head kvh Gr + c % Gr
+  // (eight pieces per thread in flight at a time: the copy is latency-bound otherwise)
+  const int pieces = a.row_bytes / 16;
+  const int per_head = g.cols * pieces;
+  const int total = a.Hkv * per_head;
+  constexpr int kBatch = 8;
+  for (int i0 = 0; i0 < total; i0 += kBatch * (int)blockDim.x) {
+    uint4 val[kBatch];
+    int64_t dst[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int i = i0 + k * (int)blockDim.x + (int)threadIdx.x;
+      val[k] = make_uint4(0u, 0u, 0u, 0u);
+      dst[k] = -1;
+      if (i < total) {
+        const int kvh = i / per_head, r = i - kvh * per_head;
+        const int c = r / pieces, p = r - c * pieces, m = c / Gr;
+        if (m < n)
+          val[k] = reinterpret_cast<const uint4*>(
+              a.q + ((int64_t)(f + m) * a.H + kvh * Gr + (c - m * Gr)) * a.row_bytes)[p];
+        dst[k] = (((int64_t)v * a.Hkv + kvh) * g.cols + c) * a.row_bytes + (int64_t)p * 16;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+      if (dst[k] >= 0) *reinterpret_cast<uint4*>(g.vq + dst[k]) = val[k];
+  }
+}
+
 }  // namespace
 }  // namespace pagedkv
 
@@ -671,13 +901,38 @@ int prefix_decode(void* out, const void* q, const void* k_cache, const void* v_c
     state[l] = (float*)(ws + pl.lv[l].state_off);
     start[l] = (int32_t*)(ws + pl.lv[l].start_off);
   }
-  {
+  bool one_launch = num_seqs <= kSetupMax;
+  for (int l = 0; l < levels; ++l) one_launch = one_launch && g[l].n <= kSetupMax;
+  if (one_launch) {
+    SetupArgs sa{};
+    for (int l = 0; l < levels; ++l) {
+      const PrefixLevel& v = pl.lv[l];
+      sa.lv[l] = SetupLevel{g[l].first, g[l].count, g[l].prefix, g[l].n, g[l].max_prefix,
+                            (int)cols[l], v.maxbp, (int32_t*)(ws + v.vfirst_off),
+                            (int32_t*)(ws + v.vcount_off), (int32_t*)(ws + v.vctx_off),
+                            (int32_t*)(ws + v.vtab_off), ws + v.vq_off, start[l]};
+    }
+    sa.levels = levels;
+    sa.ctx = context_lens;
+    sa.tables = block_tables;
+    sa.q = (const char*)q;
+    sa.S = num_seqs;
+    sa.H = num_heads;
+    sa.Hkv = num_kv_heads;
+    sa.row_bytes = head_dim * elt_bytes(dtype);
+    sa.maxb = max_blocks_per_seq;
+    sa.bsz = block_size;
+    sa.gid = levels > 1 ? (int32_t*)(ws + pl.gid_off) : nullptr;
+    const int groups = 1 + g[0].n + (levels > 1 ? g[1].n : 0);
+    hipLaunchKernelGGL(prefix_setup_kernel, dim3(groups), dim3(256), 0, st, sa);
+    PA_HIP_CHECK(hipGetLastError());
+  } else {
     const int blocks = (num_seqs + 255) / 256;
     hipLaunchKernelGGL(prefix_clear_starts_kernel, dim3(blocks < 1024 ? blocks : 1024), dim3(256),
                        0, st, start[0], levels > 1 ? start[1] : (int32_t*)nullptr,
                        levels > 1 ? (int32_t*)(ws + pl.gid_off) : (int32_t*)nullptr, num_seqs);
   }
-  for (int l = 0; l < levels; ++l) {
+  for (int l = 0; l < levels && !one_launch; ++l) {
     const PrefixLevel& v = pl.lv[l];
     hipLaunchKernelGGL(prefix_prep_kernel, dim3(g[l].n, num_kv_heads), dim3(256), 0, st,
                        g[l].first, g[l].count, g[l].prefix, context_lens, block_tables,

@@ -219,3 +219,13 @@ def test_nested_graph_replays_match_eager(native):
         assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"replay {rep}"
     ref = decode_attention(q, kc, vc, tables, lens, B)
     assert_close(want, ref, "bf16", "prefix2 eager (graph test)")
+
+
+def test_nested_past_the_one_launch_set_up(native):
+    """More than 2,048 texts: the set-up runs as the clear and the two per-level kernels
+    instead of the single set-up launch; the same attention as over the whole tables."""
+    outer = [(16, [(16, [1 + (i + j) % 5, 2 + (i * j) % 4]) for j in range(4)]) for i in range(263)]
+    case = make_nested(71, outer, 2, 2, 64, 16, "f16")
+    assert case[0].shape[0] == 2104
+    say("prefix2 with 2,104 texts (general set-up path)")
+    check(native, "f16", case, "2,104 texts")
