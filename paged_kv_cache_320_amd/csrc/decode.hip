@@ -352,14 +352,17 @@ struct PrefixLayout {
 
 // Segments per compute unit of one pass of the shared-block decode, whose key/value heads
 // each serve G query heads: the matrix-core kernel (4 or 8 query heads per wave, 16-bit
-// formats) keeps 4; the vector kernel takes 16, the most that stay resident at its 104
-// VGPRs (the passes' runs are short: more waves keep more bytes in flight). On the 32 x 8
-// sharing workload (bf16) 8 took the forked pairs' pass from 162 to 142 us and the texts'
-// own pass from 24 to 20 us; 16 took the op from 323-327 to 317-320 us (12: no change).
-// (The matrix-core prompts pass went from 128 to 136 us with 8.)
+// formats) keeps 4; the vector kernel takes 16 for two heads a wave (a group's columns: the
+// forked pairs' blocks, runs of ~17 chunks; 16 is the most that stay resident at 104
+// VGPRs) and 8 otherwise (the texts' own blocks, runs of one or two chunks, where more
+// segments mostly add partials). On the 32 x 8 sharing workload (bf16): 8 took the pairs'
+// pass from 162 to 142 us and the own pass from 24 to 20 us; 16 for both took the op from
+// 323-327 to 317-320 us (12: no change), and 8 again for the own pass to 312-315 us. (The
+// matrix-core prompts pass went from 128 to 136 us with 8.)
 int pass_waves(int G, int32_t elt) {
   const int gs = heads_per_wave(G);
-  return gs >= 4 && elt == 2 ? kWavesPerCU : 4 * kWavesPerCU;
+  if (gs >= 4 && elt == 2) return kWavesPerCU;
+  return gs == 2 ? 4 * kWavesPerCU : 2 * kWavesPerCU;
 }
 
 int prefix_layout(int32_t S, int32_t H, int32_t Hkv, int32_t D, int32_t max_ctx, int32_t levels,
