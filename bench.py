@@ -458,6 +458,7 @@ def bench_sharing(args, base, K: int, W: int) -> dict:
                 S, H, Hkv, D, B, max_ctx_bound, GMAX, max_ctx_bound, L.dtype_code(outs[0])),
                 dtype=torch.uint8, device="cuda")
     ngroups = [0, 0]
+    nfused = [0]  # timed steps whose new-token writes ran inside the nested decode
 
     def step(i: int, timed: bool):
         for op in step_ops[i]:
@@ -504,13 +505,23 @@ def bench_sharing(args, base, K: int, W: int) -> dict:
                                             d.step_k[i], d.step_v[i], d_slots, d_tables, d_lens,
                                             mctx, ws)
         else:
-            for li in range(NL):
-                L.pa_kv_write(cache.k[li], cache.v[li], d.step_k[i], d.step_v[i], d_slots)
             no, ni = ngroups
             og = [d_groups[k, :no] for k in range(3)]
             ig = [d_groups[3 + k, :ni] for k in range(3)]
+            # the nested call stores the new rows itself (its texts' own pass) unless
+            # --separate-write; otherwise pa_kv_write first
+            fuse = mode == "nested" and ni > 0 and not args.separate_write
+            nfused[0] += int(fuse and timed)
+            if not fuse:
+                for li in range(NL):
+                    L.pa_kv_write(cache.k[li], cache.v[li], d.step_k[i], d.step_v[i], d_slots)
             for li in range(NL):
-                if mode == "nested" and ni > 0:
+                if fuse:
+                    L.pa_decode_attention_prefix2_write(
+                        outs[li], d.step_q[i], cache.k[li], cache.v[li], d.step_k[i],
+                        d.step_v[i], d_slots, d_tables, d_lens, mctx, *og, max_ctx_bound, *ig,
+                        max_ctx_bound, 2, pws)
+                elif mode == "nested" and ni > 0:
                     L.pa_decode_attention_prefix2(outs[li], d.step_q[i], cache.k[li],
                                                   cache.v[li], d_tables, d_lens, mctx, *og,
                                                   max_ctx_bound, *ig, max_ctx_bound, 2, pws)
@@ -549,6 +560,7 @@ def bench_sharing(args, base, K: int, W: int) -> dict:
             f"read + written, {copy_gbps:.0f} GB/s)")
     used_blocks, filled = cache.alloc.stats()
     util = filled / (used_blocks * B) if used_blocks else None
+    fused_nested = nfused[0] == K
     log(f"step {total_ms / K * 1e3:.1f} us ({NL} layers, {np.mean(copies):.0f} block copies "
         f"per layer), decode launch {avg * 1e3:.1f} us: unique {u_launch / 1e9:.2f} GB -> "
         f"{achieved:.0f} GB/s = {achieved / HBM_PEAK_GBPS:.1%} of 8 TB/s; logical "
@@ -563,7 +575,9 @@ def bench_sharing(args, base, K: int, W: int) -> dict:
                    "prompt_len": w.prompt_len, "heads": H, "kv_heads": Hkv, "head_dim": D,
                    "block_size": B, "pool_blocks": w.num_blocks, "layers_per_step": NL,
                    "parallelism": "single GPU",
-                   "new_token_write": "fused into decode" if per_text else "pa_kv_write per layer",
+                   "new_token_write": "fused into decode" if (per_text or fused_nested)
+                                      else ("pa_kv_write per layer" if nfused[0] == 0 else
+                                            f"fused into decode on {nfused[0]} of {K} steps"),
                    "shared_blocks": {"per-text": "read once per text",
                                      "prefix": "prompt read once per group",
                                      "nested": "prompt once per group, a pair's blocks once "
@@ -572,6 +586,9 @@ def bench_sharing(args, base, K: int, W: int) -> dict:
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": ("pa_decode_attention_write = decode_partition (new-token "
                                 "write fused) + decode_merge") if per_text else
+                               ("pa_decode_attention_prefix2_write (set-up, shared blocks once "
+                                "per group, each text's own blocks with the new-token write, "
+                                "merges)") if fused_nested else
                                ("pa_kv_write + pa_decode_attention_prefix" +
                                 ("2" if mode == "nested" else "") + " (set-up, shared blocks "
                                 "once per group, each text's own blocks, merges)"),
@@ -1136,7 +1153,8 @@ def main():
                          "the identity-placement run)")
     ap.add_argument("--separate-write", action="store_true",
                     help="write each layer's new token with pa_kv_write before its decode launch "
-                         "instead of inside it (pa_decode_attention_write)")
+                         "instead of inside it (pa_decode_attention_write, and "
+                         "pa_decode_attention_prefix2_write for the nested shared-block decode)")
     ap.add_argument("--sharing-decode", choices=["nested", "prefix", "per-text"],
                     default="nested",
                     help="shared-prompt workloads: every shared block read once (the prompt per "

@@ -195,8 +195,8 @@ int pa_host_num_free(const pa_alloc* a, int32_t* n_out);
 /* ---------------------------------------------------------------------------
  * Debug re-checks of what the device calls take on trust (on the host, before launch):
  *  - pa_kv_write, pa_kv_write_fp8: the slots inside the pool are distinct;
- *  - pa_decode_attention_write: also, each text's slot is the place of its last attended
- *    position in its table;
+ *  - pa_decode_attention_write, pa_decode_attention_prefix2_write: also, each text's slot
+ *    is the place of its last attended position in its table;
  *  - pa_copy_blocks: destinations distinct, no block both a source and a destination;
  *  - pa_decode_attention_prefix / _prefix2: no text in two groups of one level, and every
  *    member's table holds its group's first member's blocks over the blocks the level
@@ -436,6 +436,32 @@ int pa_decode_attention_prefix2(void* out, const void* q, const void* k_cache,
                                 int32_t max_inner_prefix_len, int32_t inner_members,
                                 float scale, int32_t dtype, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/* pa_decode_attention_prefix2 with the step's new-token write fused in ("Shared, Copied on
+ * Write": forked texts append their own tokens; «KV cache» "How it works": the new
+ * position's key and value join the cache and are attended in the same step).
+ *
+ * Result, bit for bit, that of
+ *   pa_kv_write(k_cache, v_cache, k_new, v_new, slots', num_seqs, ...);
+ *   pa_decode_attention_prefix2(out, q, k_cache, v_cache, ...);
+ * with slots' and the conditions on slots as for pa_decode_attention_write (slots[s] the
+ * place of position context_lens[s] - 1 of text s in its table; no text attends another's
+ * new place). A text's newest token always lies in its own blocks (each level leaves every
+ * member at least that token), so the texts' own pass reads it from k_new / v_new and
+ * stores it into the pools (one wave per text and key/value head); the shared passes never
+ * read it. Slots outside [0, num_blocks * block_size) are skipped. k_new, v_new:
+ * [num_seqs][num_kv_heads][head_dim] in dtype, 16-byte aligned; slots: int64 [num_seqs].
+ * Everything else, the workspace included, as pa_decode_attention_prefix2. */
+int pa_decode_attention_prefix2_write(
+    void* out, const void* q, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+    const int64_t* slots, const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+    int32_t num_groups, const int32_t* group_first, const int32_t* group_count,
+    const int32_t* group_prefix, int32_t max_prefix_len, int32_t num_inner_groups,
+    const int32_t* inner_first, const int32_t* inner_count, const int32_t* inner_prefix,
+    int32_t max_inner_prefix_len, int32_t inner_members, float scale, int32_t dtype,
+    void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Prefix caching ("What Came After": every full block gets a hash of its tokens and

@@ -851,7 +851,8 @@ int prefix_decode(void* out, const void* q, const void* k_cache, const void* v_c
                   int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                   int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                   int levels, const GroupsIn* g, float scale, int32_t dtype, void* workspace,
-                  size_t workspace_bytes, void* stream) {
+                  size_t workspace_bytes, void* stream,
+                  const decode_impl::NewRows& nr = decode_impl::NewRows{}) {
   if (!dtype_ok(dtype)) return fail(PA_EINVAL, "dtype %d is not PA_F32/PA_F16/PA_BF16", dtype);
   for (int l = 0; l < levels; ++l) {
     if (g[l].n < 1) return fail(PA_EINVAL, "num_groups %d < 1 (level %d)", g[l].n, l + 1);
@@ -963,14 +964,16 @@ int prefix_decode(void* out, const void* q, const void* k_cache, const void* v_c
                        decode_impl::NewRows{}, p1, pass_waves(cols[l], elt_bytes(dtype)));
     if (rc != PA_OK) return rc;
   }
-  // every text's own blocks, its states folded in (each level's where it applies)
+  // every text's own blocks, its states folded in (each level's where it applies); with new
+  // rows, this pass also stores them (a text's newest token lies in its own blocks: every
+  // level leaves each member at least that token)
   const decode_impl::Prefix p2{start[levels - 1], state[levels - 1], nullptr, nullptr, num_heads,
                                2, levels > 1 ? start[0] : (const int32_t*)nullptr,
                                levels > 1 ? state[0] : (const float*)nullptr};
   return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
                        num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                        max_context_len, 0, scale, 1.0f, 1.0f, dtype, dtype, workspace,
-                       pl.decode_bytes, stream, decode_impl::NewRows{}, p2,
+                       pl.decode_bytes, stream, nr, p2,
                        pass_waves(num_heads / num_kv_heads, elt_bytes(dtype)));
 }
 
@@ -1051,4 +1054,49 @@ extern "C" int pa_decode_attention_prefix2(
   return prefix_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
                        num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                        max_context_len, 2, g, scale, dtype, workspace, workspace_bytes, stream);
+}
+
+extern "C" int pa_decode_attention_prefix2_write(
+    void* out, const void* q, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+    const int64_t* slots, const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+    int32_t num_groups, const int32_t* group_first, const int32_t* group_count,
+    const int32_t* group_prefix, int32_t max_prefix_len, int32_t num_inner_groups,
+    const int32_t* inner_first, const int32_t* inner_count, const int32_t* inner_prefix,
+    int32_t max_inner_prefix_len, int32_t inner_members, float scale, int32_t dtype,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return fail(PA_EINVAL, "dtype %d is not PA_F32/PA_F16/PA_BF16", dtype);
+  if (!k_new || !v_new || !slots) return fail(PA_EINVAL, "null pointer");
+  if (!aligned16(k_new) || !aligned16(v_new) || ((uintptr_t)slots & 7u))
+    return fail(PA_EINVAL, "k_new and v_new must be 16-byte aligned, slots 8-byte aligned");
+  if (num_groups < 1 || num_inner_groups < 1)
+    return fail(PA_EINVAL, "num_groups %d and num_inner_groups %d must be >= 1", num_groups,
+                num_inner_groups);
+  if (num_kv_heads < 1 || num_heads % num_kv_heads != 0)
+    return fail(PA_EINVAL, "num_heads %d is not a multiple of num_kv_heads %d", num_heads,
+                num_kv_heads);
+  const int32_t icols = prefix_cols(inner_members, num_heads, num_kv_heads);
+  if (icols == 0)
+    return fail(inner_members < 1 ? PA_EINVAL : PA_EUNSUPPORTED,
+                "inner_members %d: 1 .. %d with %d query heads per key/value head",
+                inner_members, kPrefixCols / (num_heads / num_kv_heads),
+                num_heads / num_kv_heads);
+  if (debug_checks() && block_tables && context_lens && num_seqs > 0 && max_blocks_per_seq > 0 &&
+      num_blocks > 0 && block_size > 0) {
+    const int rc = check_new_slots(slots, block_tables, context_lens, num_seqs,
+                                   max_blocks_per_seq, block_size, num_blocks,
+                                   (hipStream_t)stream);
+    if (rc != PA_OK) return rc;
+  }
+  const GroupsIn g[2] = {{num_groups, group_first, group_count, group_prefix, max_prefix_len,
+                          kPrefixCols},
+                         {num_inner_groups, inner_first, inner_count, inner_prefix,
+                          max_inner_prefix_len, icols}};
+  const decode_impl::NewRows nr{(const char*)k_new, (const char*)v_new, slots, (char*)k_cache,
+                                (char*)v_cache};
+  return prefix_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
+                       num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                       max_context_len, 2, g, scale, dtype, workspace, workspace_bytes, stream,
+                       nr);
 }

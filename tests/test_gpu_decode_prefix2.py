@@ -229,3 +229,58 @@ def test_nested_past_the_one_launch_set_up(native):
     assert case[0].shape[0] == 2104
     say("prefix2 with 2,104 texts (general set-up path)")
     check(native, "f16", case, "2,104 texts")
+
+
+@pytest.mark.parametrize("dtype,H,Hkv", [("f16", 8, 4), ("bf16", 8, 8), ("f32", 4, 4)])
+def test_nested_fused_write_equals_write_then_decode(native, dtype, H, Hkv):
+    """pa_decode_attention_prefix2_write: outputs and whole pools bit for bit those of
+    pa_kv_write then pa_decode_attention_prefix2, every text's newest key and value being
+    new rows (stored by the texts' own pass); and the oracle over the written pools."""
+    case = make_nested(81, [(32, [(16, [3, 7]), (16, [1, 17])]), (16, [(32, [2, 5]), (0, [9])])],
+                       H, Hkv, 128, 16, dtype)
+    q, kc, vc, tables, lens, og, ig = case
+    S, _, D = q.shape
+    B = kc.shape[2]
+    say(f"prefix2 fused write {dtype} S={S} H={H} Hkv={Hkv}")
+    g = torch.Generator().manual_seed(82)
+    kn = (torch.randn((S, Hkv, D), generator=g) / math.sqrt(D)).to(TD[dtype])
+    vn = (torch.randn((S, Hkv, D), generator=g) / math.sqrt(D)).to(TD[dtype])
+    slots = torch.tensor([int(tables[s, (lens[s] - 1) // B]) * B + int(lens[s] - 1) % B
+                          for s in range(S)], dtype=torch.int64)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    arr = lambda gs, i: np.array([x[i] for x in gs], dtype=np.int32)
+    max_ctx = int(lens.max())
+    p1, p2 = arr(og, 2), arr(ig, 2)
+    m1, m2, im = int(p1.max()), int(p2.max()), max(x[1] for x in ig)
+    n = native.pa_decode_prefix2_workspace_bytes(S, H, Hkv, D, B, max_ctx, len(og), m1, len(ig),
+                                                 m2, im, CODE[q.dtype])
+    groups = (dev(arr(og, 0)), dev(arr(og, 1)), dev(p1), m1, dev(arr(ig, 0)), dev(arr(ig, 1)),
+              dev(p2), m2, im)
+    qd, knd, vnd, sld = q.cuda(), kn.cuda(), vn.cuda(), slots.cuda()
+    td, ld = dev(tables), dev(lens)
+    # write, then decode
+    ka, va = kc.cuda(), vc.cuda()
+    out_a = torch.full(q.shape, 7.0, dtype=q.dtype, device="cuda")
+    native.pa_kv_write(ka, va, knd, vnd, sld)
+    native.pa_decode_attention_prefix2(out_a, qd, ka, va, td, ld, max_ctx, *groups,
+                                       torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda"))
+    # fused
+    kb, vb = kc.cuda(), vc.cuda()
+    out_b = torch.full(q.shape, 7.0, dtype=q.dtype, device="cuda")
+    native.pa_decode_attention_prefix2_write(out_b, qd, kb, vb, knd, vnd, sld, td, ld, max_ctx,
+                                             *groups,
+                                             torch.full((n,), 0x5A, dtype=torch.uint8,
+                                                        device="cuda"))
+    torch.cuda.synchronize()
+    bits = {torch.float32: torch.int32, torch.float16: torch.int16, torch.bfloat16: torch.int16}
+    iv = lambda t: t.cpu().view(bits[t.dtype])
+    assert torch.equal(iv(out_a), iv(out_b)), "outputs differ from write-then-decode"
+    assert torch.equal(iv(ka), iv(kb)) and torch.equal(iv(va), iv(vb)), "pools differ"
+    # the oracle over the pools with the new rows in place
+    kw, vw = kc.clone(), vc.clone()
+    for s in range(S):
+        blk, off = int(slots[s]) // B, int(slots[s]) % B
+        kw[blk, :, off] = kn[s]
+        vw[blk, :, off] = vn[s]
+    want = decode_attention(q, kw, vw, tables, lens, B)
+    assert_close(out_b.cpu(), want, dtype, f"fused write {dtype}")
