@@ -459,6 +459,7 @@ def bench_sharing(args, base, K: int, W: int) -> dict:
                 dtype=torch.uint8, device="cuda")
     ngroups = [0, 0]
     nfused = [0]  # timed steps whose new-token writes ran inside the nested decode
+    planned_any = mode == "nested" and not args.per_layer_setup
 
     def step(i: int, timed: bool):
         for op in step_ops[i]:
@@ -508,20 +509,34 @@ def bench_sharing(args, base, K: int, W: int) -> dict:
             no, ni = ngroups
             og = [d_groups[k, :no] for k in range(3)]
             ig = [d_groups[3 + k, :ni] for k in range(3)]
-            # the nested call stores the new rows itself (its texts' own pass) unless
+            nested = mode == "nested" and ni > 0
+            # the nested decode stores the new rows itself (its texts' own pass) unless
             # --separate-write; otherwise pa_kv_write first
-            fuse = mode == "nested" and ni > 0 and not args.separate_write
+            fuse = nested and not args.separate_write
             nfused[0] += int(fuse and timed)
             if not fuse:
                 for li in range(NL):
                     L.pa_kv_write(cache.k[li], cache.v[li], d.step_k[i], d.step_v[i], d_slots)
+            planned = nested and not args.per_layer_setup
+            if planned:
+                # the set-up once per step: every layer attends with these tables, lengths
+                # and groups
+                L.pa_decode_prefix2_plan(d.step_q[i], cache.k[0], d_tables, d_lens, mctx, *og,
+                                         max_ctx_bound, *ig, max_ctx_bound, 2, pws)
+            counts = (no, max_ctx_bound, ni, max_ctx_bound, 2)
+            rows = ({"k_new": d.step_k[i], "v_new": d.step_v[i], "slots": d_slots} if fuse
+                    else {})
             for li in range(NL):
-                if fuse:
+                if planned:
+                    L.pa_decode_attention_prefix2_run(outs[li], d.step_q[i], cache.k[li],
+                                                      cache.v[li], d_tables, d_lens, mctx,
+                                                      *counts, pws, **rows)
+                elif fuse:
                     L.pa_decode_attention_prefix2_write(
                         outs[li], d.step_q[i], cache.k[li], cache.v[li], d.step_k[i],
                         d.step_v[i], d_slots, d_tables, d_lens, mctx, *og, max_ctx_bound, *ig,
                         max_ctx_bound, 2, pws)
-                elif mode == "nested" and ni > 0:
+                elif nested:
                     L.pa_decode_attention_prefix2(outs[li], d.step_q[i], cache.k[li],
                                                   cache.v[li], d_tables, d_lens, mctx, *og,
                                                   max_ctx_bound, *ig, max_ctx_bound, 2, pws)
@@ -561,6 +576,21 @@ def bench_sharing(args, base, K: int, W: int) -> dict:
     used_blocks, filled = cache.alloc.stats()
     util = filled / (used_blocks * B) if used_blocks else None
     fused_nested = nfused[0] == K
+    if per_text:
+        kernel_desc = "pa_decode_attention_write = decode_partition (new-token write fused) + " \
+                      "decode_merge"
+    elif mode != "nested":
+        kernel_desc = "pa_kv_write + pa_decode_attention_prefix (set-up, prompt blocks once " \
+                      "per group, each text's own blocks, merges)"
+    else:
+        kernel_desc = (("" if fused_nested else "pa_kv_write + ") +
+                       ("pa_decode_prefix2_plan once per step (set-up) + "
+                        "pa_decode_attention_prefix2_run per layer" if planned_any else
+                        "pa_decode_attention_prefix2" + ("_write" if fused_nested else "") +
+                        " per layer (set-up,") +
+                       (" (" if planned_any else " ") +
+                       "shared blocks once per group, each text's own blocks" +
+                       (" with the new-token write" if fused_nested else "") + ", merges)")
     log(f"step {total_ms / K * 1e3:.1f} us ({NL} layers, {np.mean(copies):.0f} block copies "
         f"per layer), decode launch {avg * 1e3:.1f} us: unique {u_launch / 1e9:.2f} GB -> "
         f"{achieved:.0f} GB/s = {achieved / HBM_PEAK_GBPS:.1%} of 8 TB/s; logical "
@@ -584,14 +614,7 @@ def bench_sharing(args, base, K: int, W: int) -> dict:
                                                "per pair"}[mode]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": ("pa_decode_attention_write = decode_partition (new-token "
-                                "write fused) + decode_merge") if per_text else
-                               ("pa_decode_attention_prefix2_write (set-up, shared blocks once "
-                                "per group, each text's own blocks with the new-token write, "
-                                "merges)") if fused_nested else
-                               ("pa_kv_write + pa_decode_attention_prefix" +
-                                ("2" if mode == "nested" else "") + " (set-up, shared blocks "
-                                "once per group, each text's own blocks, merges)"),
+                     "kernel": kernel_desc,
                      "avg_launch_us": round(avg * 1e3, 2),
                      "median_launch_us": round(float(np.median(launch_ms)) * 1e3, 2),
                      "min_launch_us": round(float(min(launch_ms)) * 1e3, 2),
@@ -1155,6 +1178,11 @@ def main():
                     help="write each layer's new token with pa_kv_write before its decode launch "
                          "instead of inside it (pa_decode_attention_write, and "
                          "pa_decode_attention_prefix2_write for the nested shared-block decode)")
+    ap.add_argument("--per-layer-setup", action="store_true",
+                    help="nested shared-block decode: the set-up in every layer's call "
+                         "(pa_decode_attention_prefix2_write) instead of once per step "
+                         "(pa_decode_prefix2_plan, then pa_decode_attention_prefix2_run per "
+                         "layer)")
     ap.add_argument("--sharing-decode", choices=["nested", "prefix", "per-text"],
                     default="nested",
                     help="shared-prompt workloads: every shared block read once (the prompt per "

@@ -195,12 +195,13 @@ int pa_host_num_free(const pa_alloc* a, int32_t* n_out);
 /* ---------------------------------------------------------------------------
  * Debug re-checks of what the device calls take on trust (on the host, before launch):
  *  - pa_kv_write, pa_kv_write_fp8: the slots inside the pool are distinct;
- *  - pa_decode_attention_write, pa_decode_attention_prefix2_write: also, each text's slot
+ *  - pa_decode_attention_write, pa_decode_attention_prefix2_write, and
+ *    pa_decode_attention_prefix2_run with new rows: also, each text's slot
  *    is the place of its last attended position in its table;
  *  - pa_copy_blocks: destinations distinct, no block both a source and a destination;
- *  - pa_decode_attention_prefix / _prefix2: no text in two groups of one level, and every
- *    member's table holds its group's first member's blocks over the blocks the level
- *    reads once for the group (with the decode's own clamps).
+ *  - pa_decode_attention_prefix / _prefix2 / pa_decode_prefix2_plan: no text in two groups
+ *    of one level, and every member's table holds its group's first member's blocks over
+ *    the blocks the level reads once for the group (with the decode's own clamps).
  * A failed check returns PA_EINVAL naming the offender, and nothing is launched. Each check
  * copies the device arrays it needs to the host and waits for `stream`: for testing, not
  * for the timed path. Off by default; on when PA_DEBUG_CHECKS is set to a value other than
@@ -409,10 +410,11 @@ int pa_decode_attention_prefix(void* out, const void* q, const void* k_cache,
  * outer group and inner_members per inner group (more are left out of the group);
  * inner_members sets the width of the inner pass (its members' query heads per key/value
  * head, rounded up to 1, 2, 4 or 8: pairs of texts with one query head per key/value head
- * take the two-head vector kernel), PA_EUNSUPPORTED past 8. Passes on `stream`: the texts'
- * starts cleared, set-up per level, the outer groups' shared blocks, the inner groups'
- * shared blocks, every text's own blocks with both levels' softmax states folded in (each
- * level's state used only where its start moved past the level before). dtype, limits
+ * take the two-head vector kernel), PA_EUNSUPPORTED past 8. Passes on `stream`: the set-up
+ * (pa_decode_prefix2_plan), then pa_decode_attention_prefix2_run: the outer groups' shared
+ * blocks, the inner groups' shared blocks, every text's own blocks with both levels'
+ * softmax states folded in (each level's state used only where its start moved past the
+ * level before). dtype, limits
  * and errors as pa_decode_attention_prefix; the group
  * arrays are device int32 [num_groups] and [num_inner_groups], both counts >= 1.
  * workspace: pa_decode_prefix2_workspace_bytes(...) bytes, 16-byte aligned, no
@@ -460,6 +462,47 @@ int pa_decode_attention_prefix2_write(
     int32_t num_groups, const int32_t* group_first, const int32_t* group_count,
     const int32_t* group_prefix, int32_t max_prefix_len, int32_t num_inner_groups,
     const int32_t* inner_first, const int32_t* inner_count, const int32_t* inner_prefix,
+    int32_t max_inner_prefix_len, int32_t inner_members, float scale, int32_t dtype,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/* pa_decode_attention_prefix2 (and _write) in two parts, for a model whose layers all
+ * attend with the same block tables, context lengths and groups in a decode step (the
+ * tables map token positions to blocks for every layer: "The Block Table"): the set-up
+ * once per step, then the passes once per layer.
+ *
+ * pa_decode_prefix2_plan writes into `workspace` what the tables, lengths and groups alone
+ * decide: each group's shared length, table row and members, each text's start at both
+ * levels and its outer group. One launch on `stream` (three past 2,048 texts or groups a
+ * level); arguments, clamps and errors as pa_decode_attention_prefix2 (no q, pools or
+ * output are read; the group arrays are read by this call only). With debug checks on it
+ * re-checks the groups as pa_decode_attention_prefix2 does.
+ *
+ * pa_decode_attention_prefix2_run then runs that call's passes over the plan in
+ * `workspace`, any number of times while the tables, lengths and groups stay as planned
+ * (k_cache / v_cache and q may change: one call per layer). With k_new, v_new and slots
+ * (all three, else all null) it also writes the new rows, as pa_decode_attention_prefix2_
+ * write. The shapes, counts, max_prefix_len, max_inner_prefix_len, inner_members, dtype and
+ * workspace_bytes must be those of the plan call. Result, bit for bit, that of
+ * pa_decode_attention_prefix2 (_write) with the planned groups. The run overwrites the
+ * workspace's partials and states but not the plan. A workspace holding no plan for these
+ * arguments gives meaningless outputs without leaving the batch, the pools or the
+ * workspace (the kernels clamp what they read there as they clamp the caller's indices).
+ * A run must not overlap a plan or another run on the same workspace. */
+int pa_decode_prefix2_plan(
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_groups,
+    const int32_t* group_first, const int32_t* group_count, const int32_t* group_prefix,
+    int32_t max_prefix_len, int32_t num_inner_groups, const int32_t* inner_first,
+    const int32_t* inner_count, const int32_t* inner_prefix, int32_t max_inner_prefix_len,
+    int32_t inner_members, int32_t dtype, void* workspace, size_t workspace_bytes,
+    void* stream);
+int pa_decode_attention_prefix2_run(
+    void* out, const void* q, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+    const int64_t* slots, const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+    int32_t num_groups, int32_t max_prefix_len, int32_t num_inner_groups,
     int32_t max_inner_prefix_len, int32_t inner_members, float scale, int32_t dtype,
     void* workspace, size_t workspace_bytes, void* stream);
 

@@ -81,6 +81,13 @@ SIGNATURES = {
                                                          _i32, _i32, _i32, _vp, _vp, _vp, _i32,
                                                          _i32, _vp, _vp, _vp, _i32, _i32,
                                                          ctypes.c_float, _i32, _vp, _sz, _vp]),
+    "pa_decode_prefix2_plan": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                              _i32, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _vp,
+                                              _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "pa_decode_attention_prefix2_run": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                       _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                       _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                       ctypes.c_float, _i32, _vp, _sz, _vp]),
     "pa_hash_blocks": (ctypes.c_int, [_vp, _i32, _i32, ctypes.c_uint64, _vp]),
     "pa_seq_add_cached": (ctypes.c_int, [_vp, _vp, _i32, _c_int32_p, _c_int32_p]),
     "pa_seq_cache_blocks": (ctypes.c_int, [_vp, _i32, _vp, _i32]),
@@ -645,6 +652,66 @@ def pa_decode_attention_prefix2_write(out, q, k_cache, v_cache, k_new, v_new, sl
         _dev(inner_count, "inner_count"), _dev(inner_prefix, "inner_prefix"),
         int(max_inner_prefix_len), int(inner_members), float(scale), dtype_code(q),
         _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def pa_decode_prefix2_plan(q, k_cache, block_tables, context_lens, max_context_len: int,
+                           group_first, group_count, group_prefix, max_prefix_len: int,
+                           inner_first, inner_count, inner_prefix, max_inner_prefix_len: int,
+                           inner_members: int, workspace, stream=None) -> None:
+    """The set-up of pa_decode_attention_prefix2 into `workspace`, once for every call of
+    pa_decode_attention_prefix2_run with these tables, lengths and groups (q and k_cache give
+    the shapes and dtype only; neither is read)."""
+    S, H, D = q.shape
+    N, Hkv, B, Dk = k_cache.shape
+    assert Dk == D and q.dtype == k_cache.dtype
+    assert block_tables.shape[0] == S and context_lens.numel() == S
+    G, G2 = group_first.numel(), inner_first.numel()
+    assert group_count.numel() == G and group_prefix.numel() == G
+    assert inner_count.numel() == G2 and inner_prefix.numel() == G2
+    for t in (group_first, group_count, group_prefix, inner_first, inner_count, inner_prefix):
+        assert str(t.dtype) == "torch.int32", "group arrays must be int32"
+    _check(lib().pa_decode_prefix2_plan(
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), S, H, Hkv, D, B,
+        int(block_tables.shape[1]), int(max_context_len), G, _dev(group_first, "group_first"),
+        _dev(group_count, "group_count"), _dev(group_prefix, "group_prefix"),
+        int(max_prefix_len), G2, _dev(inner_first, "inner_first"),
+        _dev(inner_count, "inner_count"), _dev(inner_prefix, "inner_prefix"),
+        int(max_inner_prefix_len), int(inner_members), dtype_code(q),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def pa_decode_attention_prefix2_run(out, q, k_cache, v_cache, block_tables, context_lens,
+                                    max_context_len: int, num_groups: int, max_prefix_len: int,
+                                    num_inner_groups: int, max_inner_prefix_len: int,
+                                    inner_members: int, workspace, k_new=None, v_new=None,
+                                    slots=None, scale: Optional[float] = None,
+                                    stream=None) -> None:
+    """The passes of pa_decode_attention_prefix2 over the plan in `workspace`
+    (pa_decode_prefix2_plan with the same tables, lengths, groups and shapes); with k_new,
+    v_new [S, Hkv, D] and slots int64 [S] also the new-token write."""
+    S, H, D = q.shape
+    N, Hkv, B, Dk = k_cache.shape
+    assert Dk == D and tuple(out.shape) == (S, H, D) and out.dtype == q.dtype == k_cache.dtype
+    assert block_tables.shape[0] == S and context_lens.numel() == S
+    rows = (k_new, v_new, slots)
+    assert all(t is None for t in rows) or all(t is not None for t in rows), \
+        "k_new, v_new and slots: all three or none"
+    if slots is not None:
+        assert tuple(k_new.shape) == (S, Hkv, D) and tuple(v_new.shape) == (S, Hkv, D)
+        assert k_new.dtype == v_new.dtype == k_cache.dtype and slots.numel() == S
+        assert str(slots.dtype) == "torch.int64", "slots must be int64"
+    if scale is None:
+        scale = D ** -0.5
+    kn, vn, sl = ((None, None, None) if slots is None else
+                  (_dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(slots, "slots")))
+    _check(lib().pa_decode_attention_prefix2_run(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        kn, vn, sl, _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), S,
+        H, Hkv, D, B, N, int(block_tables.shape[1]), int(max_context_len), int(num_groups),
+        int(max_prefix_len), int(num_inner_groups), int(max_inner_prefix_len),
+        int(inner_members), float(scale), dtype_code(q), _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 

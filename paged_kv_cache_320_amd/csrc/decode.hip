@@ -338,9 +338,10 @@ constexpr int kPrefixCols = 8;  // query heads per key/value head in a shared-bl
 
 // Workspace of the shared-prefix decode: the decode workspace (sized for the largest of the
 // passes), then per level the texts' states [S][H][D + 4] and starts [S], and the level's
-// group arrays, table rows and query batch.
+// group arrays and table rows. The set-up writes the starts, group arrays, table rows and
+// outer groups (the plan); the passes write the decode workspace and the states.
 struct PrefixLevel {
-  size_t state_off, start_off, vfirst_off, vcount_off, vctx_off, vtab_off, vq_off;
+  size_t state_off, start_off, vfirst_off, vcount_off, vctx_off, vtab_off;
   int maxbp;  // table entries per group (shared blocks at most)
 };
 struct PrefixLayout {
@@ -403,8 +404,6 @@ int prefix_layout(int32_t S, int32_t H, int32_t Hkv, int32_t D, int32_t max_ctx,
     off = align256(off + sizeof(int32_t) * (size_t)V[l]);
     v.vtab_off = off;
     off = align256(off + sizeof(int32_t) * (size_t)V[l] * v.maxbp);
-    v.vq_off = off;
-    off = align256(off + (size_t)elt * V[l] * Hkv * cols[l] * D);
   }
   pl->gid_off = off;
   if (levels > 1) off = align256(off + sizeof(int32_t) * (size_t)S);
@@ -427,28 +426,25 @@ __global__ void prefix_clear_starts_kernel(int32_t* __restrict__ a, int32_t* __r
 // One workgroup per (group, key/value head): its members (clamped into the batch, at most
 // 8 / (H / Hkv)), its shared length (at most every member's context less one token, so
 // that each keeps its newest token, at most max_prefix, rounded down to a block) and, from
-// the head-0 workgroup, the members' skipped start and the group's table row (its first
-// member's, past the shared blocks zero); every workgroup copies its key/value head's
-// queries into the group's batch of Hkv * 8 query heads (column c of key/value head k:
-// member c / Gr's head k * Gr + c % Gr, Gr = H / Hkv; columns past the members zero).
-// The members' lengths are read by one lane each and reduced across the wave.
+// the members' skipped start and the group's table row (its first member's, past the
+// shared blocks zero). The members' lengths are read by one lane each and reduced across
+// the wave.
 // Two levels: the outer level records each member's group (gid_out); the inner level keeps
 // its members up to the first whose outer group (base_gid) differs from its first member's.
 __global__ void prefix_prep_kernel(const int32_t* __restrict__ vfirst_in,
                                    const int32_t* __restrict__ vcount_in,
                                    const int32_t* __restrict__ vprefix_in,
                                    const int32_t* __restrict__ ctx,
-                                   const int32_t* __restrict__ tables, const char* __restrict__ q,
-                                   int S, int H, int Hkv, int row_bytes, int maxb, int bsz,
-                                   int max_prefix, int maxbp, int32_t* __restrict__ vfirst,
-                                   int32_t* __restrict__ vcount, int32_t* __restrict__ vctx,
-                                   int32_t* __restrict__ vtables, char* __restrict__ vq,
+                                   const int32_t* __restrict__ tables, int S, int H, int Hkv,
+                                   int maxb, int bsz, int max_prefix, int maxbp,
+                                   int32_t* __restrict__ vfirst, int32_t* __restrict__ vcount,
+                                   int32_t* __restrict__ vctx, int32_t* __restrict__ vtables,
                                    int32_t* __restrict__ start,
                                    const int32_t* __restrict__ base_start,
                                    int32_t* __restrict__ start_also, int cols,
                                    int32_t* __restrict__ gid_out,
                                    const int32_t* __restrict__ base_gid) {
-  const int v = blockIdx.x, kvh = blockIdx.y;
+  const int v = blockIdx.x;
   const int Gr = H / Hkv;
   __shared__ int sh[4];
   if (threadIdx.x < 64) {
@@ -489,36 +485,21 @@ __global__ void prefix_prep_kernel(const int32_t* __restrict__ vfirst_in,
       sh[1] = n;
       sh[2] = (int)P;
       sh[3] = P0;
-      if (kvh == 0) {
-        vfirst[v] = f;
-        vcount[v] = n;
-        vctx[v] = (int)P - P0;
-      }
+      vfirst[v] = f;
+      vcount[v] = n;
+      vctx[v] = (int)P - P0;
     }
   }
   __syncthreads();
   const int f = sh[0], n = sh[1], P = sh[2], P0 = sh[3];
-  if (kvh == 0) {
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-      start[f + i] = P;
-      if (start_also) start_also[f + i] = P;
-      if (gid_out) gid_out[f + i] = v;
-    }
-    const int nb = (P - P0) / bsz, b0 = P0 / bsz;
-    for (int k = threadIdx.x; k < maxbp; k += blockDim.x)
-      vtables[(int64_t)v * maxbp + k] = k < nb ? tables[(int64_t)f * maxb + b0 + k] : 0;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    start[f + i] = P;
+    if (start_also) start_also[f + i] = P;
+    if (gid_out) gid_out[f + i] = v;
   }
-  const int pieces = row_bytes / 16;
-  const int total = cols * pieces;
-  for (int i = threadIdx.x; i < total; i += blockDim.x) {
-    const int c = i / pieces, p = i - c * pieces, m = c / Gr;
-    uint4 val = make_uint4(0u, 0u, 0u, 0u);
-    if (m < n)
-      val = reinterpret_cast<const uint4*>(
-          q + ((int64_t)(f + m) * H + kvh * Gr + (c - m * Gr)) * row_bytes)[p];
-    reinterpret_cast<uint4*>(
-        vq + (((int64_t)v * Hkv + kvh) * cols + c) * row_bytes)[p] = val;
-  }
+  const int nb = (P - P0) / bsz, b0 = P0 / bsz;
+  for (int k = threadIdx.x; k < maxbp; k += blockDim.x)
+    vtables[(int64_t)v * maxbp + k] = k < nb ? tables[(int64_t)f * maxb + b0 + k] : 0;
 }
 
 // ---- the set-up in one launch --------------------------------------------------------
@@ -526,8 +507,8 @@ __global__ void prefix_prep_kernel(const int32_t* __restrict__ vfirst_in,
 // per-level set-ups above run as one kernel: workgroup 0 takes every text's starts and
 // outer group from per-text membership arrays it builds in LDS (so no text's entries need
 // clearing first, and no level waits for the one before it), and workgroup 1 + b takes
-// group b of the outer level, then of the inner one: its geometry, its table row and its
-// batch of queries for all key/value heads. Both compute a group's geometry with the same
+// group b of the outer level, then of the inner one: its geometry and its table row. Both
+// compute a group's geometry with the same
 // functions, as prefix_prep_kernel computes it; overlapping groups (refused by the debug
 // check) resolve to the highest-numbered group.
 constexpr int kSetupMax = 2048;
@@ -536,7 +517,6 @@ struct SetupLevel {
   const int32_t *first, *count, *prefix;  // the caller's groups
   int n, max_prefix, cols, maxbp;
   int32_t *vfirst, *vcount, *vctx, *vtab;  // the level's batch of groups
-  char* vq;
   int32_t* start;  // each text's start at this level
 };
 
@@ -545,8 +525,7 @@ struct SetupArgs {
   int levels;
   const int32_t* ctx;
   const int32_t* tables;
-  const char* q;
-  int S, H, Hkv, row_bytes, maxb, bsz;
+  int S, H, Hkv, maxb, bsz;
   int32_t* gid;  // two levels: each text's outer group (-1: none)
 };
 
@@ -708,7 +687,6 @@ __global__ __launch_bounds__(256) void prefix_setup_kernel(SetupArgs a) {
     const int P = setup_len_from(prefix, g.max_prefix, keep, n, P0, a.bsz);
     if (lane == 0) {
       sh[0] = f;
-      sh[1] = n;
       sh[2] = P;
       sh[3] = P0;
       g.vfirst[v] = f;
@@ -717,37 +695,10 @@ __global__ __launch_bounds__(256) void prefix_setup_kernel(SetupArgs a) {
     }
   }
   __syncthreads();
-  const int f = sh[0], n = sh[1], P = sh[2], P0 = sh[3];
+  const int f = sh[0], P = sh[2], P0 = sh[3];
   const int nb = (P - P0) / a.bsz, b0 = P0 / a.bsz;
   for (int k = threadIdx.x; k < g.maxbp; k += blockDim.x)
     g.vtab[(int64_t)v * g.maxbp + k] = k < nb ? a.tables[(int64_t)f * a.maxb + b0 + k] : 0;
-  // queries: column c of key/value head kvh is member c / Gr's head kvh Gr + c % Gr
-  // (eight pieces per thread in flight at a time: the copy is latency-bound otherwise)
-  const int pieces = a.row_bytes / 16;
-  const int per_head = g.cols * pieces;
-  const int total = a.Hkv * per_head;
-  constexpr int kBatch = 8;
-  for (int i0 = 0; i0 < total; i0 += kBatch * (int)blockDim.x) {
-    uint4 val[kBatch];
-    int64_t dst[kBatch];
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int i = i0 + k * (int)blockDim.x + (int)threadIdx.x;
-      val[k] = make_uint4(0u, 0u, 0u, 0u);
-      dst[k] = -1;
-      if (i < total) {
-        const int kvh = i / per_head, r = i - kvh * per_head;
-        const int c = r / pieces, p = r - c * pieces, m = c / Gr;
-        if (m < n)
-          val[k] = reinterpret_cast<const uint4*>(
-              a.q + ((int64_t)(f + m) * a.H + kvh * Gr + (c - m * Gr)) * a.row_bytes)[p];
-        dst[k] = (((int64_t)v * a.Hkv + kvh) * g.cols + c) * a.row_bytes + (int64_t)p * 16;
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k)
-      if (dst[k] >= 0) *reinterpret_cast<uint4*>(g.vq + dst[k]) = val[k];
-  }
 }
 
 }  // namespace
@@ -843,55 +794,65 @@ int check_groups(int levels, const GroupsIn* g, const int32_t* ctx_d, const int3
   return PA_OK;
 }
 
-// The shared-prefix decode over one level of groups or two nested ones: set-up, one pass
-// per level over the groups' shared blocks (states out; with two levels the inner level's
-// states are merged with the outer's), then every text's own blocks with its state folded in.
-int prefix_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-                  const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
-                  int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                  int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
-                  int levels, const GroupsIn* g, float scale, int32_t dtype, void* workspace,
-                  size_t workspace_bytes, void* stream,
-                  const decode_impl::NewRows& nr = decode_impl::NewRows{}) {
+// Checks that the set-up and the passes of the shared-prefix decode share, and the
+// workspace layout they agree on.
+int prefix_check(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                 int32_t block_size, int32_t max_blocks_per_seq, int32_t max_context_len,
+                 int levels, const GroupsIn* g, int32_t dtype, const void* workspace,
+                 size_t workspace_bytes, PrefixLayout* pl) {
   if (!dtype_ok(dtype)) return fail(PA_EINVAL, "dtype %d is not PA_F32/PA_F16/PA_BF16", dtype);
-  for (int l = 0; l < levels; ++l) {
+  for (int l = 0; l < levels; ++l)
     if (g[l].n < 1) return fail(PA_EINVAL, "num_groups %d < 1 (level %d)", g[l].n, l + 1);
-    if (!g[l].first || !g[l].count || !g[l].prefix) return fail(PA_EINVAL, "null pointer");
-    if (((uintptr_t)g[l].first & 3u) || ((uintptr_t)g[l].count & 3u) ||
-        ((uintptr_t)g[l].prefix & 3u))
-      return fail(PA_EINVAL, "group arrays must be 4-byte aligned");
-  }
   if (num_kv_heads < 1 || num_heads % num_kv_heads != 0)
     return fail(PA_EINVAL, "num_heads %d is not a multiple of num_kv_heads %d", num_heads,
                 num_kv_heads);
   if (num_heads / num_kv_heads > kPrefixCols)
     return fail(PA_EUNSUPPORTED, "%d query heads per key/value head (at most %d share a read)",
                 num_heads / num_kv_heads, kPrefixCols);
-  // the plain decode's checks (shapes, pointers, alignment) before anything is launched
   if (head_dim != 64 && head_dim != 128)
     return fail(PA_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
   if (block_size != 4 && block_size != 8 && block_size != 16 && block_size != 32)
     return fail(PA_EUNSUPPORTED, "block_size %d (supported: 4, 8, 16, 32)", block_size);
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !workspace)
-    return fail(PA_EINVAL, "null pointer");
-  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
-      !aligned16(workspace))
-    return fail(PA_EINVAL, "out, q, pools and workspace must be 16-byte aligned");
-  if (num_seqs < 1 || max_blocks_per_seq < 1 || num_blocks < 1 || max_context_len < 0)
-    return fail(PA_EINVAL, "num_seqs, max_blocks_per_seq and num_blocks must be >= 1, "
-                "max_context_len >= 0");
+  if (!workspace) return fail(PA_EINVAL, "null pointer");
+  if (!aligned16(workspace)) return fail(PA_EINVAL, "workspace must be 16-byte aligned");
+  if (num_seqs < 1 || max_blocks_per_seq < 1 || max_context_len < 0)
+    return fail(PA_EINVAL, "num_seqs and max_blocks_per_seq must be >= 1, max_context_len >= 0");
   const int32_t V[2] = {g[0].n, levels > 1 ? g[1].n : 0};
   const int32_t maxp[2] = {g[0].max_prefix, levels > 1 ? g[1].max_prefix : 0};
   const int32_t cols[2] = {g[0].cols, levels > 1 ? g[1].cols : 1};
   for (int l = 0; l < levels; ++l)
     if (cols[l] < num_heads / num_kv_heads || cols[l] > kPrefixCols)
       return fail(PA_EINVAL, "bad group width at level %d", l + 1);
-  PrefixLayout pl;
-  int rc = prefix_layout(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, levels, V,
-                         maxp, cols, block_size, elt_bytes(dtype), &pl);
+  const int rc = prefix_layout(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
+                               levels, V, maxp, cols, block_size, elt_bytes(dtype), pl);
   if (rc != PA_OK) return rc;
-  if (workspace_bytes < pl.bytes)
-    return fail(PA_EINVAL, "workspace_bytes %zu < %zu required", workspace_bytes, pl.bytes);
+  if (workspace_bytes < pl->bytes)
+    return fail(PA_EINVAL, "workspace_bytes %zu < %zu required", workspace_bytes, pl->bytes);
+  return PA_OK;
+}
+
+// The set-up of the shared-prefix decode (the plan): what the block tables, context lengths
+// and groups alone decide, into the workspace. Every layer of a decode step attends with
+// the same tables, lengths and groups, so one set-up serves all of them.
+int prefix_plan(const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                int32_t max_blocks_per_seq, int32_t max_context_len, int levels,
+                const GroupsIn* g, int32_t dtype, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  PrefixLayout pl;
+  int rc = prefix_check(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                        max_blocks_per_seq, max_context_len, levels, g, dtype, workspace,
+                        workspace_bytes, &pl);
+  if (rc != PA_OK) return rc;
+  for (int l = 0; l < levels; ++l) {
+    if (!g[l].first || !g[l].count || !g[l].prefix) return fail(PA_EINVAL, "null pointer");
+    if (((uintptr_t)g[l].first & 3u) || ((uintptr_t)g[l].count & 3u) ||
+        ((uintptr_t)g[l].prefix & 3u))
+      return fail(PA_EINVAL, "group arrays must be 4-byte aligned");
+  }
+  if (!block_tables || !context_lens) return fail(PA_EINVAL, "null pointer");
+  if (((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u))
+    return fail(PA_EINVAL, "tables and context_lens must be 4-byte aligned");
   char* ws = (char*)workspace;
   hipStream_t st = (hipStream_t)stream;
   if (debug_checks()) {
@@ -899,12 +860,8 @@ int prefix_decode(void* out, const void* q, const void* k_cache, const void* v_c
                       max_blocks_per_seq, block_size, st);
     if (rc != PA_OK) return rc;
   }
-  float* state[2];
   int32_t* start[2];
-  for (int l = 0; l < levels; ++l) {
-    state[l] = (float*)(ws + pl.lv[l].state_off);
-    start[l] = (int32_t*)(ws + pl.lv[l].start_off);
-  }
+  for (int l = 0; l < levels; ++l) start[l] = (int32_t*)(ws + pl.lv[l].start_off);
   bool one_launch = num_seqs <= kSetupMax;
   for (int l = 0; l < levels; ++l) one_launch = one_launch && g[l].n <= kSetupMax;
   if (one_launch) {
@@ -912,69 +869,134 @@ int prefix_decode(void* out, const void* q, const void* k_cache, const void* v_c
     for (int l = 0; l < levels; ++l) {
       const PrefixLevel& v = pl.lv[l];
       sa.lv[l] = SetupLevel{g[l].first, g[l].count, g[l].prefix, g[l].n, g[l].max_prefix,
-                            (int)cols[l], v.maxbp, (int32_t*)(ws + v.vfirst_off),
+                            (int)g[l].cols, v.maxbp, (int32_t*)(ws + v.vfirst_off),
                             (int32_t*)(ws + v.vcount_off), (int32_t*)(ws + v.vctx_off),
-                            (int32_t*)(ws + v.vtab_off), ws + v.vq_off, start[l]};
+                            (int32_t*)(ws + v.vtab_off), start[l]};
     }
     sa.levels = levels;
     sa.ctx = context_lens;
     sa.tables = block_tables;
-    sa.q = (const char*)q;
     sa.S = num_seqs;
     sa.H = num_heads;
     sa.Hkv = num_kv_heads;
-    sa.row_bytes = head_dim * elt_bytes(dtype);
     sa.maxb = max_blocks_per_seq;
     sa.bsz = block_size;
     sa.gid = levels > 1 ? (int32_t*)(ws + pl.gid_off) : nullptr;
     const int groups = 1 + g[0].n + (levels > 1 ? g[1].n : 0);
     hipLaunchKernelGGL(prefix_setup_kernel, dim3(groups), dim3(256), 0, st, sa);
     PA_HIP_CHECK(hipGetLastError());
-  } else {
-    const int blocks = (num_seqs + 255) / 256;
-    hipLaunchKernelGGL(prefix_clear_starts_kernel, dim3(blocks < 1024 ? blocks : 1024), dim3(256),
-                       0, st, start[0], levels > 1 ? start[1] : (int32_t*)nullptr,
-                       levels > 1 ? (int32_t*)(ws + pl.gid_off) : (int32_t*)nullptr, num_seqs);
+    return ok();
   }
-  for (int l = 0; l < levels && !one_launch; ++l) {
+  const int blocks = (num_seqs + 255) / 256;
+  hipLaunchKernelGGL(prefix_clear_starts_kernel, dim3(blocks < 1024 ? blocks : 1024), dim3(256),
+                     0, st, start[0], levels > 1 ? start[1] : (int32_t*)nullptr,
+                     levels > 1 ? (int32_t*)(ws + pl.gid_off) : (int32_t*)nullptr, num_seqs);
+  for (int l = 0; l < levels; ++l) {
     const PrefixLevel& v = pl.lv[l];
-    hipLaunchKernelGGL(prefix_prep_kernel, dim3(g[l].n, num_kv_heads), dim3(256), 0, st,
-                       g[l].first, g[l].count, g[l].prefix, context_lens, block_tables,
-                       (const char*)q, num_seqs, num_heads, num_kv_heads,
-                       head_dim * elt_bytes(dtype), max_blocks_per_seq, block_size,
-                       g[l].max_prefix, v.maxbp, (int32_t*)(ws + v.vfirst_off),
-                       (int32_t*)(ws + v.vcount_off), (int32_t*)(ws + v.vctx_off),
-                       (int32_t*)(ws + v.vtab_off), ws + v.vq_off, start[l],
+    hipLaunchKernelGGL(prefix_prep_kernel, dim3(g[l].n), dim3(256), 0, st, g[l].first,
+                       g[l].count, g[l].prefix, context_lens, block_tables, num_seqs, num_heads,
+                       num_kv_heads, max_blocks_per_seq, block_size, g[l].max_prefix, v.maxbp,
+                       (int32_t*)(ws + v.vfirst_off), (int32_t*)(ws + v.vcount_off),
+                       (int32_t*)(ws + v.vctx_off), (int32_t*)(ws + v.vtab_off), start[l],
                        l > 0 ? start[l - 1] : (const int32_t*)nullptr,
-                       l + 1 < levels ? start[l + 1] : (int32_t*)nullptr, (int)cols[l],
+                       l + 1 < levels ? start[l + 1] : (int32_t*)nullptr, (int)g[l].cols,
                        l == 0 && levels > 1 ? (int32_t*)(ws + pl.gid_off) : (int32_t*)nullptr,
                        l > 0 ? (const int32_t*)(ws + pl.gid_off) : (const int32_t*)nullptr);
     PA_HIP_CHECK(hipGetLastError());
   }
-  // a pass per level over the groups' shared blocks, states out
+  return ok();
+}
+
+// The passes of the shared-prefix decode over a workspace that prefix_plan filled: one pass
+// per level over the groups' shared blocks (states out), then every text's own blocks with
+// its states folded in (each level's where it applies). Only g[l].n, .max_prefix and .cols
+// are read here. A workspace holding no plan for these shapes, tables, lengths and groups
+// gives meaningless outputs, with every access still inside the batch, the pools and the
+// workspace: the kernels clamp the plan's members, lengths and starts and bound its table
+// entries as they do the caller's.
+int prefix_run(void* out, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+               int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+               int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+               int levels, const GroupsIn* g, float scale, int32_t dtype, void* workspace,
+               size_t workspace_bytes, void* stream,
+               const decode_impl::NewRows& nr = decode_impl::NewRows{}) {
+  PrefixLayout pl;
+  int rc = prefix_check(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                        max_blocks_per_seq, max_context_len, levels, g, dtype, workspace,
+                        workspace_bytes, &pl);
+  if (rc != PA_OK) return rc;
+  // the plain decode's checks (pointers, alignment) before anything is launched
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PA_EINVAL, "null pointer");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_EINVAL, "out, q, pools and workspace must be 16-byte aligned");
+  if (num_blocks < 1) return fail(PA_EINVAL, "num_blocks must be >= 1");
+  if (!std::isfinite(scale)) return fail(PA_EINVAL, "scale is not finite");
+  char* ws = (char*)workspace;
+  float* state[2];
+  int32_t* start[2];
+  for (int l = 0; l < levels; ++l) {
+    state[l] = (float*)(ws + pl.lv[l].state_off);
+    start[l] = (int32_t*)(ws + pl.lv[l].start_off);
+  }
+  const int Gr = num_heads / num_kv_heads;
   for (int l = 0; l < levels; ++l) {
     const PrefixLevel& v = pl.lv[l];
+    int colm = 0, colh = 0;
+    for (int c = 0; c < g[l].cols; ++c) {
+      colm |= (c / Gr) << (4 * c);
+      colh |= (c % Gr) << (4 * c);
+    }
     const decode_impl::Prefix p1{nullptr, state[l], (const int32_t*)(ws + v.vfirst_off),
                                  (const int32_t*)(ws + v.vcount_off), num_heads, 1, nullptr,
-                                 nullptr};
-    rc = decode_common(out, ws + v.vq_off, k_cache, v_cache, (const int32_t*)(ws + v.vtab_off),
-                       (const int32_t*)(ws + v.vctx_off), g[l].n, num_kv_heads * cols[l],
+                                 nullptr, num_seqs, Gr, g[l].cols / Gr, colm, colh};
+    rc = decode_common(out, q, k_cache, v_cache, (const int32_t*)(ws + v.vtab_off),
+                       (const int32_t*)(ws + v.vctx_off), g[l].n, num_kv_heads * g[l].cols,
                        num_kv_heads, head_dim, block_size, num_blocks, v.maxbp, g[l].max_prefix,
                        0, scale, 1.0f, 1.0f, dtype, dtype, workspace, pl.decode_bytes, stream,
-                       decode_impl::NewRows{}, p1, pass_waves(cols[l], elt_bytes(dtype)));
+                       decode_impl::NewRows{}, p1, pass_waves(g[l].cols, elt_bytes(dtype)));
     if (rc != PA_OK) return rc;
   }
-  // every text's own blocks, its states folded in (each level's where it applies); with new
-  // rows, this pass also stores them (a text's newest token lies in its own blocks: every
-  // level leaves each member at least that token)
+  // with new rows, the own pass also stores them (a text's newest token lies in its own
+  // blocks: every level leaves each member at least that token)
   const decode_impl::Prefix p2{start[levels - 1], state[levels - 1], nullptr, nullptr, num_heads,
                                2, levels > 1 ? start[0] : (const int32_t*)nullptr,
                                levels > 1 ? state[0] : (const float*)nullptr};
   return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
                        num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                        max_context_len, 0, scale, 1.0f, 1.0f, dtype, dtype, workspace,
-                       pl.decode_bytes, stream, nr, p2,
-                       pass_waves(num_heads / num_kv_heads, elt_bytes(dtype)));
+                       pl.decode_bytes, stream, nr, p2, pass_waves(Gr, elt_bytes(dtype)));
+}
+
+// The shared-prefix decode over one level of groups or two nested ones: the set-up, then
+// the passes.
+int prefix_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                  int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                  int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                  int levels, const GroupsIn* g, float scale, int32_t dtype, void* workspace,
+                  size_t workspace_bytes, void* stream,
+                  const decode_impl::NewRows& nr = decode_impl::NewRows{}) {
+  // the passes' own checks first, so that nothing is launched for a call they refuse
+  PrefixLayout pl;
+  int rc = prefix_check(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                        max_blocks_per_seq, max_context_len, levels, g, dtype, workspace,
+                        workspace_bytes, &pl);
+  if (rc != PA_OK) return rc;
+  if (!out || !q || !k_cache || !v_cache) return fail(PA_EINVAL, "null pointer");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_EINVAL, "out, q, pools and workspace must be 16-byte aligned");
+  if (num_blocks < 1) return fail(PA_EINVAL, "num_blocks must be >= 1");
+  if (!std::isfinite(scale)) return fail(PA_EINVAL, "scale is not finite");
+  rc = prefix_plan(block_tables, context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                   block_size, max_blocks_per_seq, max_context_len, levels, g, dtype, workspace,
+                   workspace_bytes, stream);
+  if (rc != PA_OK) return rc;
+  return prefix_run(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
+                    num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                    max_context_len, levels, g, scale, dtype, workspace, workspace_bytes, stream,
+                    nr);
 }
 
 }  // namespace
@@ -1025,16 +1047,16 @@ extern "C" int pa_decode_attention_prefix(
                        max_context_len, 1, g, scale, dtype, workspace, workspace_bytes, stream);
 }
 
-extern "C" int pa_decode_attention_prefix2(
-    void* out, const void* q, const void* k_cache, const void* v_cache,
-    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
-    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-    int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_groups,
-    const int32_t* group_first, const int32_t* group_count, const int32_t* group_prefix,
-    int32_t max_prefix_len, int32_t num_inner_groups, const int32_t* inner_first,
-    const int32_t* inner_count, const int32_t* inner_prefix, int32_t max_inner_prefix_len,
-    int32_t inner_members, float scale, int32_t dtype, void* workspace, size_t workspace_bytes,
-    void* stream) {
+namespace {
+
+// The two levels of the nested shared-block calls as the caller gives them (null arrays
+// where a call reads only the counts and lengths).
+int prefix2_levels(int32_t num_heads, int32_t num_kv_heads, int32_t num_groups,
+                   const int32_t* group_first, const int32_t* group_count,
+                   const int32_t* group_prefix, int32_t max_prefix_len, int32_t num_inner_groups,
+                   const int32_t* inner_first, const int32_t* inner_count,
+                   const int32_t* inner_prefix, int32_t max_inner_prefix_len,
+                   int32_t inner_members, GroupsIn* g) {
   if (num_groups < 1 || num_inner_groups < 1)
     return fail(PA_EINVAL, "num_groups %d and num_inner_groups %d must be >= 1", num_groups,
                 num_inner_groups);
@@ -1047,10 +1069,53 @@ extern "C" int pa_decode_attention_prefix2(
                 "inner_members %d: 1 .. %d with %d query heads per key/value head",
                 inner_members, kPrefixCols / (num_heads / num_kv_heads),
                 num_heads / num_kv_heads);
-  const GroupsIn g[2] = {{num_groups, group_first, group_count, group_prefix, max_prefix_len,
-                          kPrefixCols},
-                         {num_inner_groups, inner_first, inner_count, inner_prefix,
-                          max_inner_prefix_len, icols}};
+  g[0] = GroupsIn{num_groups, group_first, group_count, group_prefix, max_prefix_len,
+                  kPrefixCols};
+  g[1] = GroupsIn{num_inner_groups, inner_first, inner_count, inner_prefix, max_inner_prefix_len,
+                  icols};
+  return PA_OK;
+}
+
+// The new rows of a fused write, checked (nullptr rows: none, all three null).
+int new_rows_of(const void* k_new, const void* v_new, const int64_t* slots, void* k_cache,
+                void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                int32_t num_seqs, int32_t max_blocks_per_seq, int32_t block_size,
+                int32_t num_blocks, void* stream, bool optional, decode_impl::NewRows* nr) {
+  *nr = decode_impl::NewRows{};
+  if (optional && !k_new && !v_new && !slots) return PA_OK;
+  if (!k_new || !v_new || !slots) return fail(PA_EINVAL, "null pointer");
+  if (!aligned16(k_new) || !aligned16(v_new) || ((uintptr_t)slots & 7u))
+    return fail(PA_EINVAL, "k_new and v_new must be 16-byte aligned, slots 8-byte aligned");
+  if (debug_checks() && block_tables && context_lens && num_seqs > 0 && max_blocks_per_seq > 0 &&
+      num_blocks > 0 && block_size > 0) {
+    const int rc = check_new_slots(slots, block_tables, context_lens, num_seqs,
+                                   max_blocks_per_seq, block_size, num_blocks,
+                                   (hipStream_t)stream);
+    if (rc != PA_OK) return rc;
+  }
+  *nr = decode_impl::NewRows{(const char*)k_new, (const char*)v_new, slots, (char*)k_cache,
+                             (char*)v_cache};
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" int pa_decode_attention_prefix2(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_groups,
+    const int32_t* group_first, const int32_t* group_count, const int32_t* group_prefix,
+    int32_t max_prefix_len, int32_t num_inner_groups, const int32_t* inner_first,
+    const int32_t* inner_count, const int32_t* inner_prefix, int32_t max_inner_prefix_len,
+    int32_t inner_members, float scale, int32_t dtype, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  GroupsIn g[2];
+  const int rc = prefix2_levels(num_heads, num_kv_heads, num_groups, group_first, group_count,
+                                group_prefix, max_prefix_len, num_inner_groups, inner_first,
+                                inner_count, inner_prefix, max_inner_prefix_len, inner_members,
+                                g);
+  if (rc != PA_OK) return rc;
   return prefix_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
                        num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                        max_context_len, 2, g, scale, dtype, workspace, workspace_bytes, stream);
@@ -1067,36 +1132,59 @@ extern "C" int pa_decode_attention_prefix2_write(
     int32_t max_inner_prefix_len, int32_t inner_members, float scale, int32_t dtype,
     void* workspace, size_t workspace_bytes, void* stream) {
   if (!dtype_ok(dtype)) return fail(PA_EINVAL, "dtype %d is not PA_F32/PA_F16/PA_BF16", dtype);
-  if (!k_new || !v_new || !slots) return fail(PA_EINVAL, "null pointer");
-  if (!aligned16(k_new) || !aligned16(v_new) || ((uintptr_t)slots & 7u))
-    return fail(PA_EINVAL, "k_new and v_new must be 16-byte aligned, slots 8-byte aligned");
-  if (num_groups < 1 || num_inner_groups < 1)
-    return fail(PA_EINVAL, "num_groups %d and num_inner_groups %d must be >= 1", num_groups,
-                num_inner_groups);
-  if (num_kv_heads < 1 || num_heads % num_kv_heads != 0)
-    return fail(PA_EINVAL, "num_heads %d is not a multiple of num_kv_heads %d", num_heads,
-                num_kv_heads);
-  const int32_t icols = prefix_cols(inner_members, num_heads, num_kv_heads);
-  if (icols == 0)
-    return fail(inner_members < 1 ? PA_EINVAL : PA_EUNSUPPORTED,
-                "inner_members %d: 1 .. %d with %d query heads per key/value head",
-                inner_members, kPrefixCols / (num_heads / num_kv_heads),
-                num_heads / num_kv_heads);
-  if (debug_checks() && block_tables && context_lens && num_seqs > 0 && max_blocks_per_seq > 0 &&
-      num_blocks > 0 && block_size > 0) {
-    const int rc = check_new_slots(slots, block_tables, context_lens, num_seqs,
-                                   max_blocks_per_seq, block_size, num_blocks,
-                                   (hipStream_t)stream);
-    if (rc != PA_OK) return rc;
-  }
-  const GroupsIn g[2] = {{num_groups, group_first, group_count, group_prefix, max_prefix_len,
-                          kPrefixCols},
-                         {num_inner_groups, inner_first, inner_count, inner_prefix,
-                          max_inner_prefix_len, icols}};
-  const decode_impl::NewRows nr{(const char*)k_new, (const char*)v_new, slots, (char*)k_cache,
-                                (char*)v_cache};
+  GroupsIn g[2];
+  int rc = prefix2_levels(num_heads, num_kv_heads, num_groups, group_first, group_count,
+                          group_prefix, max_prefix_len, num_inner_groups, inner_first,
+                          inner_count, inner_prefix, max_inner_prefix_len, inner_members, g);
+  if (rc != PA_OK) return rc;
+  decode_impl::NewRows nr;
+  rc = new_rows_of(k_new, v_new, slots, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                   max_blocks_per_seq, block_size, num_blocks, stream, false, &nr);
+  if (rc != PA_OK) return rc;
   return prefix_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
                        num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                        max_context_len, 2, g, scale, dtype, workspace, workspace_bytes, stream,
                        nr);
+}
+
+extern "C" int pa_decode_prefix2_plan(
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_groups,
+    const int32_t* group_first, const int32_t* group_count, const int32_t* group_prefix,
+    int32_t max_prefix_len, int32_t num_inner_groups, const int32_t* inner_first,
+    const int32_t* inner_count, const int32_t* inner_prefix, int32_t max_inner_prefix_len,
+    int32_t inner_members, int32_t dtype, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  GroupsIn g[2];
+  const int rc = prefix2_levels(num_heads, num_kv_heads, num_groups, group_first, group_count,
+                                group_prefix, max_prefix_len, num_inner_groups, inner_first,
+                                inner_count, inner_prefix, max_inner_prefix_len, inner_members,
+                                g);
+  if (rc != PA_OK) return rc;
+  return prefix_plan(block_tables, context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                     block_size, max_blocks_per_seq, max_context_len, 2, g, dtype, workspace,
+                     workspace_bytes, stream);
+}
+
+extern "C" int pa_decode_attention_prefix2_run(
+    void* out, const void* q, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+    const int64_t* slots, const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+    int32_t num_groups, int32_t max_prefix_len, int32_t num_inner_groups,
+    int32_t max_inner_prefix_len, int32_t inner_members, float scale, int32_t dtype,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  GroupsIn g[2];
+  int rc = prefix2_levels(num_heads, num_kv_heads, num_groups, nullptr, nullptr, nullptr,
+                          max_prefix_len, num_inner_groups, nullptr, nullptr, nullptr,
+                          max_inner_prefix_len, inner_members, g);
+  if (rc != PA_OK) return rc;
+  decode_impl::NewRows nr;
+  rc = new_rows_of(k_new, v_new, slots, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                   max_blocks_per_seq, block_size, num_blocks, stream, true, &nr);
+  if (rc != PA_OK) return rc;
+  return prefix_run(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
+                    num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                    max_context_len, 2, g, scale, dtype, workspace, workspace_bytes, stream, nr);
 }

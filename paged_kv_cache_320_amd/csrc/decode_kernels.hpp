@@ -99,11 +99,12 @@ struct Cursor {
 
 // Shared-prefix decode (pa_decode_attention_prefix) runs the kernels twice. Mode 1 runs over
 // groups of texts whose tables begin with the same blocks: a group is one text of this
-// batch, its queries those of its members (query head c of key/value head k is member
-// c / Gr's head k * Gr + c % Gr, Gr = heads / Hkv), and each member's (m, l, acc) over
-// the shared blocks goes to its row of `state` [texts][heads][D + 4] instead of an
-// output. Mode 2 runs over every text's own blocks, from start[s] on, and folds the
-// text's state in before the output is formed. Mode 0: plain decode.
+// batch, its queries those of its members, read from the real batch's q (query head c of
+// key/value head k is member c / Gr's head k * Gr + c % Gr, Gr = heads / Hkv), and each
+// member's (m, l, acc) over the shared blocks goes to its row of `state`
+// [texts][heads][D + 4] instead of an output. Mode 2 runs over every text's own blocks,
+// from start[s] on, and folds the text's state in before the output is formed. Mode 0:
+// plain decode.
 struct Prefix {
   const int32_t* __restrict__ start;   // mode 2: tokens skipped per text (block multiples)
   float* state;                        // modes 1, 2
@@ -117,7 +118,31 @@ struct Prefix {
   // level); rows that do not apply are never read, so neither array needs clearing.
   const int32_t* __restrict__ start0;
   const float* state0;
+  // mode 1: texts of the real batch, its query heads per key/value head (Gr), members a
+  // group holds at most, and for each column c < 8 of a key/value head its member
+  // (colm >> 4c & 15) and head offset (colh >> 4c & 15)
+  int seqs, gr, members, colm, colh;
 };
+
+// Mode 1: group s's first member and member count as the set-up wrote them, clamped into
+// the real batch (every row the kernels touch through them stays inside it).
+__device__ __forceinline__ void group_members(const Prefix& pf, int s, int& f, int& n) {
+  int ff = pf.vfirst[s];
+  ff = ff < 0 ? 0 : ff >= pf.seqs ? pf.seqs - 1 : ff;
+  const int most = pf.members < pf.seqs - ff ? pf.members : pf.seqs - ff;
+  const int nn = pf.vcount[s];
+  n = nn < 0 ? 0 : nn > most ? most : nn;
+  f = ff;
+}
+
+// Mode 1: the row of the real batch's q (text x heads + head) holding column col of key/value
+// head kvh of a group whose members are vfirst .. vfirst + vcount - 1. A column past the
+// members reads the first member's row: its results are never stored.
+__device__ __forceinline__ int64_t group_q_row(const Prefix& pf, int vfirst, int vcount, int kvh,
+                                               int col) {
+  const int m = (pf.colm >> (4 * col)) & 15, ho = (pf.colh >> (4 * col)) & 15;
+  return (int64_t)(vfirst + (m < vcount ? m : 0)) * pf.heads + kvh * pf.gr + ho;
+}
 
 // Mode 2: which state rows text s folds in (bit 0: the outer level's, bit 1: `state`'s).
 __device__ __forceinline__ int fold_mask(const Prefix& pf, int s) {
@@ -191,8 +216,10 @@ __device__ __forceinline__ void set_text_raw(Cursor& c, const Ctx& x, int s, int
   if (s < x.S) {
     c.L = attended_from(raw, x.pf.start, s, x.capacity, x.bsz, &c.toff, &c.over);
     if (x.pf.mode == 1) {
-      c.vfirst = __builtin_amdgcn_readfirstlane(x.pf.vfirst[s]);
-      c.vcount = __builtin_amdgcn_readfirstlane(x.pf.vcount[s]);
+      int f, n;
+      group_members(x.pf, s, f, n);
+      c.vfirst = __builtin_amdgcn_readfirstlane(f);
+      c.vcount = __builtin_amdgcn_readfirstlane(n);
     } else if (x.pf.mode == 2) {
       c.fold = __builtin_amdgcn_readfirstlane(fold_mask(x.pf, s));
     }
@@ -342,14 +369,26 @@ __device__ __forceinline__ void load_chunk(Buf<KT, QT, D, GS>& b, const Cursor& 
       }
     }
   }
-  // the GS query rows (cache hits after the run's first chunk)
-  const char* qrow =
-      q + ((int64_t)c.s * x.H + first_head_of<GS>(c.r, x)) * kQRowBytes + lp * QP * 16;
+  // the GS query rows (cache hits after the run's first chunk); in shared-prefix mode 1 each
+  // column's row lies in its member's part of the real batch
+  const int h0 = first_head_of<GS>(c.r, x);
+  if (x.pf.mode == 1) {
 #pragma unroll
-  for (int j = 0; j < GS; ++j)
+    for (int j = 0; j < GS; ++j) {
+      const char* qrow = q + group_q_row(x.pf, c.vfirst, c.vcount, kvh, h0 + j - kvh * x.G) *
+                                 kQRowBytes + lp * QP * 16;
 #pragma unroll
-    for (int p = 0; p < QP; ++p)
-      b.q[j][p] = *reinterpret_cast<const uint4*>(qrow + j * kQRowBytes + p * 16);
+      for (int p = 0; p < QP; ++p)
+        b.q[j][p] = *reinterpret_cast<const uint4*>(qrow + p * 16);
+    }
+  } else {
+    const char* qrow = q + ((int64_t)c.s * x.H + h0) * kQRowBytes + lp * QP * 16;
+#pragma unroll
+    for (int j = 0; j < GS; ++j)
+#pragma unroll
+      for (int p = 0; p < QP; ++p)
+        b.q[j][p] = *reinterpret_cast<const uint4*>(qrow + j * kQRowBytes + p * 16);
+  }
 }
 
 // Fused write: when a writing run's last chunk is computed, the lanes holding the new
@@ -1073,7 +1112,9 @@ __global__ __launch_bounds__(kThreads) void decode_merge(
   const int h = (r / NG) * Gq + (r % NG) * GS + lane / (64 / GS);  // the lane's query head
   const int64_t pair = (int64_t)s * H + h;
   if (pf.mode == 1) {
-    float* row = prefix_state_row<D>(pf, Hkv, Gq, pf.vfirst[s], pf.vcount[s], h);
+    int f, n;
+    group_members(pf, s, f, n);
+    float* row = prefix_state_row<D>(pf, Hkv, Gq, f, n, h);
     merge_run<QT, D, GS>(partials, w0, w1, lo, seg, v_scale, nullptr, lane, nullptr, row,
                          nullptr);
     return;
@@ -1391,8 +1432,11 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mma(
     if (c.r == q_run && c.s == q_text) return;
     q_run = c.r;
     q_text = c.s;
+    const int h = first_head_of<GS>(c.r, x) + (col & (GS - 1));
+    const int kvh = kv_head_of<GS>(c.r, x);
     const char* qrow =
-        q + ((int64_t)c.s * x.H + first_head_of<GS>(c.r, x) + (col & (GS - 1))) * D * 2;
+        q + (x.pf.mode == 1 ? group_q_row(x.pf, c.vfirst, c.vcount, kvh, h - kvh * x.G)
+                            : (int64_t)c.s * x.H + h) * D * 2;
 #pragma unroll
     for (int cc = 0; cc < D / 32; ++cc) {
       uint4 v = *reinterpret_cast<const uint4*>(qrow + (8 * grp + 32 * cc) * 2);

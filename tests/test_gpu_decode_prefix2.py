@@ -284,3 +284,94 @@ def test_nested_fused_write_equals_write_then_decode(native, dtype, H, Hkv):
         vw[blk, :, off] = vn[s]
     want = decode_attention(q, kw, vw, tables, lens, B)
     assert_close(out_b.cpu(), want, dtype, f"fused write {dtype}")
+
+
+@pytest.mark.parametrize("dtype,H,Hkv", [("f16", 8, 4), ("bf16", 8, 8), ("f32", 4, 4)])
+def test_nested_plan_once_runs_per_layer(native, dtype, H, Hkv):
+    """pa_decode_prefix2_plan once, then pa_decode_attention_prefix2_run for three layers
+    (each its own queries and pools), without and with new rows: bit for bit the one-call
+    pa_decode_attention_prefix2 / _write of each layer (the runs leave the plan as it was);
+    the last layer also against the oracle."""
+    case = make_nested(83, [(32, [(16, [3, 7]), (16, [1, 17])]), (16, [(32, [2, 5]), (0, [9])])],
+                       H, Hkv, 128, 16, dtype)
+    q, kc, vc, tables, lens, og, ig = case
+    S, _, D = q.shape
+    B = kc.shape[2]
+    say(f"prefix2 plan + runs {dtype} S={S} H={H} Hkv={Hkv}")
+    g = torch.Generator().manual_seed(84)
+    kn = (torch.randn((S, Hkv, D), generator=g) / math.sqrt(D)).to(TD[dtype])
+    vn = (torch.randn((S, Hkv, D), generator=g) / math.sqrt(D)).to(TD[dtype])
+    slots = torch.tensor([int(tables[s, (lens[s] - 1) // B]) * B + int(lens[s] - 1) % B
+                          for s in range(S)], dtype=torch.int64)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    arr = lambda gs, i: np.array([x[i] for x in gs], dtype=np.int32)
+    max_ctx = int(lens.max())
+    p1, p2 = arr(og, 2), arr(ig, 2)
+    m1, m2, im = int(p1.max()), int(p2.max()), max(x[1] for x in ig)
+    n = native.pa_decode_prefix2_workspace_bytes(S, H, Hkv, D, B, max_ctx, len(og), m1, len(ig),
+                                                 m2, im, CODE[q.dtype])
+    groups = (dev(arr(og, 0)), dev(arr(og, 1)), dev(p1), m1, dev(arr(ig, 0)), dev(arr(ig, 1)),
+              dev(p2), m2, im)
+    counts = (len(og), m1, len(ig), m2, im)
+    td, ld = dev(tables), dev(lens)
+    knd, vnd, sld = kn.cuda(), vn.cuda(), slots.cuda()
+    # layer l: heads of q rotated by l, keys negated and values halved on odd layers (exact in
+    # every format; the pools' unused places stay NaN where they were)
+    layers = []
+    for li in range(3):
+        sign, half = (-1.0, 0.5) if li % 2 else (1.0, 1.0)
+        layers.append((q.roll(li, dims=1).contiguous(), kc * sign, vc * half))
+    wsp = torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda")
+    native.pa_decode_prefix2_plan(layers[0][0].cuda(), kc.cuda(), td, ld, max_ctx, *groups, wsp)
+    bits = {torch.float32: torch.int32, torch.float16: torch.int16, torch.bfloat16: torch.int16}
+    iv = lambda t: t.cpu().view(bits[t.dtype])
+    for write in (False, True):
+        for li, (ql, kl, vl) in enumerate(layers):
+            qd = ql.cuda()
+            ka, va, kb, vb = kl.cuda(), vl.cuda(), kl.cuda(), vl.cuda()
+            out_a = torch.full(q.shape, 7.0, dtype=q.dtype, device="cuda")
+            out_b = torch.full(q.shape, 7.0, dtype=q.dtype, device="cuda")
+            ws1 = torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda")
+            if write:
+                native.pa_decode_attention_prefix2_write(out_a, qd, ka, va, knd, vnd, sld, td, ld,
+                                                         max_ctx, *groups, ws1)
+                native.pa_decode_attention_prefix2_run(out_b, qd, kb, vb, td, ld, max_ctx, *counts,
+                                                       wsp, k_new=knd, v_new=vnd, slots=sld)
+            else:
+                native.pa_decode_attention_prefix2(out_a, qd, ka, va, td, ld, max_ctx, *groups,
+                                                   ws1)
+                native.pa_decode_attention_prefix2_run(out_b, qd, kb, vb, td, ld, max_ctx, *counts,
+                                                       wsp)
+            torch.cuda.synchronize()
+            what = f"layer {li}{' with new rows' if write else ''}"
+            assert torch.equal(iv(out_a), iv(out_b)), f"{what}: outputs differ from one call"
+            assert torch.equal(iv(ka), iv(kb)) and torch.equal(iv(va), iv(vb)), \
+                f"{what}: pools differ"
+    ql, kl, vl = layers[2]
+    want = decode_attention(ql, kl, vl, tables, lens, B)
+    assert_close(run_nested(native, ql, kl, vl, tables, lens, og, ig), want, dtype,
+                 f"layer 2 {dtype}")
+
+
+def test_nested_run_on_a_zeroed_workspace_decodes_whole_tables(native):
+    """A zeroed workspace holds a plan of empty groups: every text starts at its first token
+    with no shared state, so pa_decode_attention_prefix2_run without a plan call attends each
+    text over its whole table (the oracle's result) and stays inside its arguments."""
+    case = make_nested(85, [(32, [(16, [3, 7]), (16, [1, 17])]), (16, [(32, [2, 5]), (0, [9])])],
+                       8, 8, 128, 16, "bf16")
+    q, kc, vc, tables, lens, og, ig = case
+    S, H, D = q.shape
+    Hkv, B = kc.shape[1], kc.shape[2]
+    say(f"prefix2 run on a zeroed workspace S={S}")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    max_ctx = int(lens.max())
+    m1, m2, im = max(x[2] for x in og), max(x[2] for x in ig), max(x[1] for x in ig)
+    n = native.pa_decode_prefix2_workspace_bytes(S, H, Hkv, D, B, max_ctx, len(og), m1, len(ig),
+                                                 m2, im, CODE[q.dtype])
+    ws = torch.zeros((n,), dtype=torch.uint8, device="cuda")
+    out = torch.full(q.shape, 7.0, dtype=q.dtype, device="cuda")
+    native.pa_decode_attention_prefix2_run(out, q.cuda(), kc.cuda(), vc.cuda(), dev(tables),
+                                           dev(lens), max_ctx, len(og), m1, len(ig), m2, im, ws)
+    torch.cuda.synchronize()
+    want = decode_attention(q, kc, vc, tables, lens, B)
+    assert_close(out.cpu(), want, "bf16", "zeroed workspace")
