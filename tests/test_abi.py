@@ -3,6 +3,7 @@
 Runs on the CPU: the library loads without a GPU, and the calls below return
 before any HIP runtime call.
 """
+import ctypes
 import os
 import re
 import subprocess
@@ -85,3 +86,32 @@ def test_noalloc_refuses_past_its_workspace_before_any_hip_call(native):
     rc = L.pa_decode_attention_noalloc(None, None, None, None, None, None, 1, 8, 8, 128, 16, 4, 4,
                                        64, 16, 0.1, 9, None)
     assert rc == native.PA_EINVAL
+
+
+def test_shared_block_plan_and_run_validate_before_any_hip_call(native):
+    """pa_decode_prefix2_plan and pa_decode_attention_prefix2_run refuse bad counts, shapes,
+    widths, a missing workspace and a partial set of new rows on the host."""
+    L = native.lib()
+    n = None
+
+    def plan(G=2, H=8, Hkv=8, D=128, B=16, members=2, ws=n):
+        return L.pa_decode_prefix2_plan(n, n, 4, H, Hkv, D, B, 8, 128, G, n, n, n, 64, 1, n, n, n,
+                                        96, members, 1, ws, 0, n)
+
+    def run(kn=n, vn=n, slots=n, G=2, D=128, ws=n):
+        return L.pa_decode_attention_prefix2_run(n, n, n, n, kn, vn, slots, n, n, 4, 8, 8, D, 16,
+                                                 64, 8, 128, G, 64, 1, 96, 2, 0.1, 1, ws, 0, n)
+
+    assert plan(G=0) == native.PA_EINVAL and ">= 1" in native.pa_last_error()
+    assert plan(H=8, Hkv=3) == native.PA_EINVAL and "multiple" in native.pa_last_error()
+    assert plan(members=9) == native.PA_EUNSUPPORTED
+    assert plan(members=0) == native.PA_EINVAL
+    assert plan(D=80) == native.PA_EUNSUPPORTED
+    assert plan(B=12) == native.PA_EUNSUPPORTED
+    assert plan() == native.PA_EINVAL and "null" in native.pa_last_error()
+    assert run(G=0) == native.PA_EINVAL
+    assert run(D=96) == native.PA_EUNSUPPORTED
+    fake = ctypes.c_void_p(16)
+    assert run(kn=fake) == native.PA_EINVAL and "null" in native.pa_last_error()
+    assert run(kn=fake, vn=fake) == native.PA_EINVAL and "null" in native.pa_last_error()
+    assert run() == native.PA_EINVAL and "null" in native.pa_last_error()
