@@ -99,7 +99,7 @@ int decode_common(void* out, const void* q, const void* k_cache, const void* v_c
                   int32_t kv_dtype, int32_t q_dtype, void* workspace, size_t workspace_bytes,
                   void* stream, const decode_impl::NewRows& nr = decode_impl::NewRows{},
                   const decode_impl::Prefix& pf = decode_impl::Prefix{},
-                  int wpc = kWavesPerCU) {
+                  int wpc = kWavesPerCU, bool defer_merge = false) {
   if (head_dim != 64 && head_dim != 128)
     return fail(PA_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
   if (block_size != 4 && block_size != 8 && block_size != 16 && block_size != 32)
@@ -135,7 +135,7 @@ int decode_common(void* out, const void* q, const void* k_cache, const void* v_c
                  max_context_len,
                  // scale * k_scale * log2(e): scores in the exp2 domain, key scale folded in
                  scale * k_scale * 1.4426950408889634f, v_scale,
-                 (char*)workspace, lay, (hipStream_t)stream, nr, pf};
+                 (char*)workspace, lay, (hipStream_t)stream, nr, pf, defer_merge};
   const int GS = heads_per_wave(num_heads / num_kv_heads);
   bool done = false;
   const bool d64 = head_dim == 64;
@@ -337,8 +337,9 @@ namespace {
 constexpr int kPrefixCols = 8;  // query heads per key/value head in a shared-blocks pass, at most
 
 // Workspace of the shared-prefix decode: the decode workspace (sized for the largest of the
-// passes), then per level the texts' states [S][H][D + 4] and starts [S], and the level's
-// group arrays and table rows. The set-up writes the starts, group arrays, table rows and
+// outer level's pass and the own pass), with two levels a second one for the inner level's
+// pass (both levels' partials are merged in one launch after both passes), then per level the
+// texts' states [S][H][D + 4] and starts [S], and the level's group arrays and table rows. The set-up writes the starts, group arrays, table rows and
 // outer groups (the plan); the passes write the decode workspace and the states.
 struct PrefixLevel {
   size_t state_off, start_off, vfirst_off, vcount_off, vctx_off, vtab_off;
@@ -346,6 +347,7 @@ struct PrefixLevel {
 };
 struct PrefixLayout {
   size_t decode_bytes, bytes;
+  size_t decode1_off, decode1_bytes;  // two levels: the inner level's decode workspace
   size_t gid_off;  // two levels: each text's outer group (-1: none) [S]
   int levels;
   PrefixLevel lv[2];
@@ -379,15 +381,19 @@ int prefix_layout(int32_t S, int32_t H, int32_t Hkv, int32_t D, int32_t max_ctx,
   Layout a;
   int rc = layout(S, H, D, max_ctx, 0, &a, pass_waves(H / Hkv, elt));
   if (rc != PA_OK) return rc;
-  size_t need = a.bytes;
+  size_t need = a.bytes, need1 = 0;
   for (int l = 0; l < levels; ++l) {
     Layout b;
     rc = layout(V[l], Hkv * cols[l], D, max_prefix[l], 0, &b, pass_waves(cols[l], elt));
     if (rc != PA_OK) return rc;
-    if (b.bytes > need) need = b.bytes;
+    if (l == 1) need1 = b.bytes;
+    else if (b.bytes > need) need = b.bytes;
   }
   size_t off = align256(need);
   pl->decode_bytes = off;
+  pl->decode1_off = off;
+  pl->decode1_bytes = align256(need1);
+  off += pl->decode1_bytes;
   pl->levels = levels;
   for (int l = 0; l < levels; ++l) {
     PrefixLevel& v = pl->lv[l];
@@ -794,6 +800,37 @@ int check_groups(int levels, const GroupsIn* g, const int32_t* ctx_d, const int3
   return PA_OK;
 }
 
+// The merges of both shared-block levels in one launch (decode_merge_pair), the outer
+// level 8 heads a wave, the inner one GS1.
+template <int QT, int D>
+bool merge_pair_gs(int GS1, const decode_impl::MergePass& a, const decode_impl::MergePass& b,
+                   int Hkv, int bsz, hipStream_t st) {
+  using decode_impl::decode_merge_pair;
+  const dim3 grid(a.groups + b.groups), block(decode_impl::kThreads);
+  switch (GS1) {
+    case 1: hipLaunchKernelGGL((decode_merge_pair<QT, D, 8, 1>), grid, block, 0, st, a, b, Hkv, bsz); return true;
+    case 2: hipLaunchKernelGGL((decode_merge_pair<QT, D, 8, 2>), grid, block, 0, st, a, b, Hkv, bsz); return true;
+    case 4: hipLaunchKernelGGL((decode_merge_pair<QT, D, 8, 4>), grid, block, 0, st, a, b, Hkv, bsz); return true;
+    case 8: hipLaunchKernelGGL((decode_merge_pair<QT, D, 8, 8>), grid, block, 0, st, a, b, Hkv, bsz); return true;
+  }
+  return false;
+}
+
+bool merge_pair(int32_t dtype, int D, int GS1, const decode_impl::MergePass& a,
+                const decode_impl::MergePass& b, int Hkv, int bsz, hipStream_t st) {
+  const bool d64 = D == 64;
+  if (dtype == PA_F32)
+    return d64 ? merge_pair_gs<PA_F32, 64>(GS1, a, b, Hkv, bsz, st)
+               : merge_pair_gs<PA_F32, 128>(GS1, a, b, Hkv, bsz, st);
+  if (dtype == PA_F16)
+    return d64 ? merge_pair_gs<PA_F16, 64>(GS1, a, b, Hkv, bsz, st)
+               : merge_pair_gs<PA_F16, 128>(GS1, a, b, Hkv, bsz, st);
+  if (dtype == PA_BF16)
+    return d64 ? merge_pair_gs<PA_BF16, 64>(GS1, a, b, Hkv, bsz, st)
+               : merge_pair_gs<PA_BF16, 128>(GS1, a, b, Hkv, bsz, st);
+  return false;
+}
+
 // Checks that the set-up and the passes of the shared-prefix decode share, and the
 // workspace layout they agree on.
 int prefix_check(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -941,6 +978,13 @@ int prefix_run(void* out, const void* q, const void* k_cache, const void* v_cach
     start[l] = (int32_t*)(ws + pl.lv[l].start_off);
   }
   const int Gr = num_heads / num_kv_heads;
+  const int elt = elt_bytes(dtype);
+  // With two levels (the outer one 8 heads a wave) the level passes write their partials to
+  // their own decode workspaces and one launch merges both after both passes, instead of a
+  // merge after each.
+  const bool pair = levels == 2 && heads_per_wave(g[0].cols) == 8;
+  decode_impl::MergePass mp[2];
+  decode_impl::Prefix p1[2];
   for (int l = 0; l < levels; ++l) {
     const PrefixLevel& v = pl.lv[l];
     int colm = 0, colh = 0;
@@ -948,15 +992,41 @@ int prefix_run(void* out, const void* q, const void* k_cache, const void* v_cach
       colm |= (c / Gr) << (4 * c);
       colh |= (c % Gr) << (4 * c);
     }
-    const decode_impl::Prefix p1{nullptr, state[l], (const int32_t*)(ws + v.vfirst_off),
-                                 (const int32_t*)(ws + v.vcount_off), num_heads, 1, nullptr,
-                                 nullptr, num_seqs, Gr, g[l].cols / Gr, colm, colh};
+    p1[l] = decode_impl::Prefix{nullptr, state[l], (const int32_t*)(ws + v.vfirst_off),
+                                (const int32_t*)(ws + v.vcount_off), num_heads, 1, nullptr,
+                                nullptr, num_seqs, Gr, g[l].cols / Gr, colm, colh};
+    if (pair) {
+      Layout lay;
+      rc = layout(g[l].n, num_kv_heads * g[l].cols, head_dim, g[l].max_prefix, 0, &lay,
+                  pass_waves(g[l].cols, elt));
+      if (rc != PA_OK) return rc;
+      const char* region = l == 1 ? ws + pl.decode1_off : ws;
+      const int64_t runs = (int64_t)g[l].n * (num_kv_heads * g[l].cols / heads_per_wave(g[l].cols));
+      mp[l] = decode_impl::MergePass{(const int32_t*)(ws + v.vctx_off), g[l].n,
+                                     num_kv_heads * g[l].cols, v.maxbp, (int)lay.W,
+                                     g[l].max_prefix, (const int64_t*)region,
+                                     (const int64_t*)(region + lay.excl_off),
+                                     (const float*)(region + lay.part_off), p1[l],
+                                     (int)((runs + decode_impl::kWavesPerGroup - 1) /
+                                           decode_impl::kWavesPerGroup)};
+    }
+  }
+  for (int l = 0; l < levels; ++l) {
+    const PrefixLevel& v = pl.lv[l];
+    char* region = l == 1 ? ws + pl.decode1_off : ws;
+    const size_t region_bytes = l == 1 ? pl.decode1_bytes : pl.decode_bytes;
     rc = decode_common(out, q, k_cache, v_cache, (const int32_t*)(ws + v.vtab_off),
                        (const int32_t*)(ws + v.vctx_off), g[l].n, num_kv_heads * g[l].cols,
                        num_kv_heads, head_dim, block_size, num_blocks, v.maxbp, g[l].max_prefix,
-                       0, scale, 1.0f, 1.0f, dtype, dtype, workspace, pl.decode_bytes, stream,
-                       decode_impl::NewRows{}, p1, pass_waves(g[l].cols, elt_bytes(dtype)));
+                       0, scale, 1.0f, 1.0f, dtype, dtype, region, region_bytes, stream,
+                       decode_impl::NewRows{}, p1[l], pass_waves(g[l].cols, elt), pair);
     if (rc != PA_OK) return rc;
+  }
+  if (pair) {
+    if (!merge_pair(dtype, head_dim, heads_per_wave(g[1].cols), mp[0], mp[1], num_kv_heads,
+                    block_size, (hipStream_t)stream))
+      return fail(PA_EUNSUPPORTED, "no merge for this shape");
+    PA_HIP_CHECK(hipGetLastError());
   }
   // with new rows, the own pass also stores them (a text's newest token lies in its own
   // blocks: every level leaves each member at least that token)
@@ -966,7 +1036,7 @@ int prefix_run(void* out, const void* q, const void* k_cache, const void* v_cach
   return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
                        num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                        max_context_len, 0, scale, 1.0f, 1.0f, dtype, dtype, workspace,
-                       pl.decode_bytes, stream, nr, p2, pass_waves(Gr, elt_bytes(dtype)));
+                       pl.decode_bytes, stream, nr, p2, pass_waves(Gr, elt));
 }
 
 // The shared-prefix decode over one level of groups or two nested ones: the set-up, then

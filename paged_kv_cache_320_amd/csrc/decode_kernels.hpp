@@ -1053,16 +1053,15 @@ __device__ __forceinline__ void merge_run(const float* __restrict__ partials, in
 // the lengths themselves for small batches, instead of the header and offsets the partition
 // kernel wrote, measured 0.6 us slower per op on the 7 x 2,048 OPT-13B step: loading the
 // partials on a guess beside them, checked against them, is what saves the round trip.)
+// The merge of run `run` (wave-uniform) of one pass.
 template <int QT, int D, int GS>
-__global__ __launch_bounds__(kThreads) void decode_merge(
+__device__ __forceinline__ void merge_one_run(
     char* __restrict__ out, const int32_t* __restrict__ ctx, int S, int H, int Hkv, int maxb,
     int bsz, int W, float v_scale, const int64_t* __restrict__ hdr,
-    const int64_t* __restrict__ excl, const float* __restrict__ partials, Prefix pf,
-    int max_ctx, int seg_fixed) {
+    const int64_t* __restrict__ excl, const float* __restrict__ partials, const Prefix& pf,
+    int max_ctx, int seg_fixed, int64_t run) {
   const int lane = threadIdx.x & 63;
   const int Gq = H / Hkv, NG = Gq / GS, R = Hkv * NG;
-  const int64_t run =
-      (int64_t)blockIdx.x * kWavesPerGroup + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (run >= (int64_t)S * R) return;
   const int s = (int)(run / R), r = (int)(run - (int64_t)s * R);
   const int64_t capacity = (int64_t)maxb * bsz;
@@ -1125,6 +1124,46 @@ __global__ __launch_bounds__(kThreads) void decode_merge(
   const float* init2 = fold & 2 ? pf.state + pair * (D + 4) : nullptr;
   merge_run<QT, D, GS>(partials, w0, w1, lo, seg, v_scale, out + pair * D * elt_size<QT>(),
                        lane, init, nullptr, init2);
+}
+
+template <int QT, int D, int GS>
+__global__ __launch_bounds__(kThreads) void decode_merge(
+    char* __restrict__ out, const int32_t* __restrict__ ctx, int S, int H, int Hkv, int maxb,
+    int bsz, int W, float v_scale, const int64_t* __restrict__ hdr,
+    const int64_t* __restrict__ excl, const float* __restrict__ partials, Prefix pf,
+    int max_ctx, int seg_fixed) {
+  const int64_t run =
+      (int64_t)blockIdx.x * kWavesPerGroup + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  merge_one_run<QT, D, GS>(out, ctx, S, H, Hkv, maxb, bsz, W, v_scale, hdr, excl, partials, pf,
+                           max_ctx, seg_fixed, run);
+}
+
+// One shared-block level's pass as its merge reads it (shared-prefix mode 1: states out).
+struct MergePass {
+  const int32_t* ctx;  // the level's group lengths
+  int S, H, maxb, W, max_ctx;
+  const int64_t* hdr;
+  const int64_t* excl;
+  const float* partials;
+  Prefix pf;
+  int groups;  // workgroups of this pass's merge
+};
+
+// The merges of both levels of the nested shared-block decode in one launch: workgroups
+// below a.groups merge the outer level's runs, the rest the inner level's (each level's
+// passes wrote their own partials, so both run after both passes).
+template <int QT, int D, int GS0, int GS1>
+__global__ __launch_bounds__(kThreads) void decode_merge_pair(MergePass a, MergePass b, int Hkv,
+                                                              int bsz) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if ((int)blockIdx.x < a.groups)
+    merge_one_run<QT, D, GS0>(nullptr, a.ctx, a.S, a.H, Hkv, a.maxb, bsz, a.W, 1.0f, a.hdr,
+                              a.excl, a.partials, a.pf, a.max_ctx, 0,
+                              (int64_t)blockIdx.x * kWavesPerGroup + w);
+  else
+    merge_one_run<QT, D, GS1>(nullptr, b.ctx, b.S, b.H, Hkv, b.maxb, bsz, b.W, 1.0f, b.hdr,
+                              b.excl, b.partials, b.pf, b.max_ctx, 0,
+                              (int64_t)(blockIdx.x - a.groups) * kWavesPerGroup + w);
 }
 
 // ---- shared key/value heads on the matrix cores --------------------------------
@@ -1523,6 +1562,7 @@ struct Launch {
   hipStream_t st;
   NewRows nr;  // fused new-token write when nr.k != nullptr
   Prefix pf;   // shared-prefix passes (mode 0: plain decode)
+  bool defer_merge;  // partition only: the caller launches the merge
 };
 
 template <int KT, int QT, int D, int B, int GS, bool FUSED>
@@ -1553,6 +1593,7 @@ bool launch(const Launch& a) {
   } else {
     launch_partition<KT, QT, D, B, GS, false>(a, hdr, excl, part);
   }
+  if (a.defer_merge) return true;
   const int64_t runs = (int64_t)a.S * (a.H / GS);  // merge waves: one per run
   const int mgroups = (int)((runs + kWavesPerGroup - 1) / kWavesPerGroup);
   hipLaunchKernelGGL((decode_merge<QT, D, GS>), dim3(mgroups), dim3(kThreads), 0, a.st, a.out,
