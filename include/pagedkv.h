@@ -412,9 +412,9 @@ int pa_decode_attention_prefix(void* out, const void* q, const void* k_cache,
  * head, rounded up to 1, 2, 4 or 8: pairs of texts with one query head per key/value head
  * take the two-head vector kernel), PA_EUNSUPPORTED past 8. Passes on `stream`: the set-up
  * (pa_decode_prefix2_plan), then pa_decode_attention_prefix2_run: the outer groups' shared
- * blocks, the inner groups' shared blocks, every text's own blocks with both levels'
- * softmax states folded in (each level's state used only where its start moved past the
- * level before). dtype, limits
+ * blocks, the inner groups' shared blocks, one merge of both levels' partials into the
+ * members' softmax states, every text's own blocks with both levels' states folded in (each
+ * level's state used only where its start moved past the level before), and its merge. dtype, limits
  * and errors as pa_decode_attention_prefix; the group
  * arrays are device int32 [num_groups] and [num_inner_groups], both counts >= 1.
  * workspace: pa_decode_prefix2_workspace_bytes(...) bytes, 16-byte aligned, no
