@@ -40,7 +40,8 @@ int layout(int32_t S, int32_t H, int32_t D, int32_t max_ctx, int32_t T, Layout* 
   if (W > 0x7fffffff / 2) return fail(PA_EINVAL, "too many segments");
   lay->W = W;
   lay->excl_off = kHdrBytes;
-  lay->part_off = align256(lay->excl_off + sizeof(int64_t) * (size_t)S);
+  lay->split_off = align256(lay->excl_off + sizeof(int64_t) * (size_t)S);
+  lay->part_off = align256(lay->split_off + sizeof(int64_t) * (size_t)W);
   lay->bytes = align256(lay->part_off + sizeof(float) * (size_t)W * 2 * kMaxGS * (D + 4));
   return PA_OK;
 }
@@ -1002,12 +1003,17 @@ int prefix_run(void* out, const void* q, const void* k_cache, const void* v_cach
       if (rc != PA_OK) return rc;
       const char* region = l == 1 ? ws + pl.decode1_off : ws;
       const int64_t runs = (int64_t)g[l].n * (num_kv_heads * g[l].cols / heads_per_wave(g[l].cols));
+      const bool by_boundary = decode_impl::merge_by_boundary(runs, lay.W);
+      const int64_t mwaves = by_boundary ? lay.W : runs;
       mp[l] = decode_impl::MergePass{(const int32_t*)(ws + v.vctx_off), g[l].n,
                                      num_kv_heads * g[l].cols, v.maxbp, (int)lay.W,
                                      g[l].max_prefix, (const int64_t*)region,
                                      (const int64_t*)(region + lay.excl_off),
-                                     (const float*)(region + lay.part_off), p1[l],
-                                     (int)((runs + decode_impl::kWavesPerGroup - 1) /
+                                     (const float*)(region + lay.part_off),
+                                     by_boundary ? (const int64_t*)(region + lay.split_off)
+                                                 : (const int64_t*)nullptr,
+                                     p1[l],
+                                     (int)((mwaves + decode_impl::kWavesPerGroup - 1) /
                                            decode_impl::kWavesPerGroup)};
     }
   }

@@ -651,6 +651,7 @@ struct Segment {
   int w;
   int64_t seg_lo, seg_hi;
   int n;
+  int64_t split_run;  // the run this segment's first boundary names to the merge, or -1
 };
 
 // One step of a wave scan: add the value that DPP control CTRL moves into each lane of the
@@ -693,13 +694,18 @@ __device__ __forceinline__ int64_t readlane64(int64_t v, int src) {
 // and values as soon as its own lengths arrive (a workgroup-wide search with two barriers
 // took 3.0 us from the first instruction to the first load on the 7 x 2,048 OPT-13B step,
 // this one 2.2 us). Wave 0 of workgroup 0 also writes every text's first unit (excl_out)
-// and the header (total units, segment length) for the merge.
+// and the header (total units, segment length) for the merge, and a wave w < W whose
+// segment is empty writes split_out[w] = -1; the others leave in sg.split_run the run (text
+// x runs + run) that crosses into their segment from the segment before, or -1, for the
+// kernel to store once its segment is done (a store ahead of the first loads delayed them). A run split over several segments is named once, by the first boundary it
+// crosses, so a merge wave per boundary visits every split run once.
 template <int B, int GS>
 __device__ __forceinline__ bool start_segment(const int32_t* __restrict__ ctx, int S, int H,
                                               int Hkv, int maxb, int num_blocks, int W,
                                               int seg_fixed, const Prefix& pf,
                                               int64_t* __restrict__ hdr,
-                                              int64_t* __restrict__ excl_out, Segment& sg,
+                                              int64_t* __restrict__ excl_out,
+                                              int64_t* __restrict__ split_out, Segment& sg,
                                               Ctx& x, Cursor& cur) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -744,7 +750,11 @@ __device__ __forceinline__ bool start_segment(const int32_t* __restrict__ ctx, i
 
   sg.w = blockIdx.x * kWavesPerGroup + wave;
   sg.seg_lo = (int64_t)sg.w * seg;
-  if (sg.w >= W || sg.seg_lo >= total) return false;
+  if (sg.w >= W) return false;
+  if (sg.seg_lo >= total) {
+    if (lane == 0) split_out[sg.w] = -1;
+    return false;
+  }
   sg.seg_hi = sg.seg_lo + seg < total ? sg.seg_lo + seg : total;
   sg.n = (int)(sg.seg_hi - sg.seg_lo);
 
@@ -773,6 +783,7 @@ __device__ __forceinline__ bool start_segment(const int32_t* __restrict__ ctx, i
   const int64_t off = c0 - f_excl;  // below R * U
   cur.r = off <= 0x7fffffff ? (int)off / cur.U : (int)(off / cur.U);
   cur.u = (int)(off - (int64_t)cur.r * cur.U);
+  sg.split_run = seg::names_split_run(cur.u, seg) ? (int64_t)found * R + cur.r : -1;
   return true;
 }
 
@@ -782,8 +793,9 @@ __global__ __launch_bounds__(kThreads) void decode_partition(
     const char* __restrict__ vc, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ ctx, int S, int H, int Hkv, int maxb, int num_blocks, int W,
     int seg_fixed, float scale_log2, float v_scale, int64_t* __restrict__ hdr,
-    int64_t* __restrict__ excl_out, float* __restrict__ partials, NewRows nr_arg,
-    const int64_t* __restrict__ new_slots, Prefix pf) {
+    int64_t* __restrict__ excl_out, float* __restrict__ partials,
+    int64_t* __restrict__ split_out, NewRows nr_arg, const int64_t* __restrict__ new_slots,
+    Prefix pf) {
   // the slots as a restrict argument: the compiler may then read them through the scalar
   // cache, which keeps the fused write's slot lookup out of the vector wait counts
   NewRows nr = nr_arg;
@@ -793,11 +805,12 @@ __global__ __launch_bounds__(kThreads) void decode_partition(
   Ctx x;
   Cursor cur;
   if (!start_segment<B, GS>(ctx, S, H, Hkv, maxb, num_blocks, W, seg_fixed, pf, hdr, excl_out,
-                            sg, x, cur))
+                            split_out, sg, x, cur))
     return;
   const int w = sg.w;
   const int64_t seg_lo = sg.seg_lo, seg_hi = sg.seg_hi;
   const int n = sg.n;
+  const int64_t split_run = sg.split_run;
   Cursor ld = cur;
   const float sl = scale_log2;
 
@@ -877,6 +890,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition(
       compute(A);
       finish(i + 3);
     }
+    if (lane == 0) split_out[w] = split_run;
     return;
   }
   // steady state: both loads unconditional, so the next chunk's loads stay in
@@ -914,6 +928,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition(
     compute(A);
     finish(i);
   }
+  if (lane == 0) split_out[w] = split_run;
 }
 
 // Combining the partials of one run, left by segments w0..w1, in segment order, for all GS
@@ -1126,14 +1141,24 @@ __device__ __forceinline__ void merge_one_run(
                        lane, init, nullptr, init2);
 }
 
+// The run merge wave i takes: run i, or with `split` (batches with more runs than
+// segments) the run that crosses segment boundary i, if any (-1: none).
+__device__ __forceinline__ int64_t merge_run_of(const int64_t* __restrict__ split, int W,
+                                                int64_t i) {
+  if (!split) return i;
+  return i < W ? split[i] : -1;
+}
+
 template <int QT, int D, int GS>
 __global__ __launch_bounds__(kThreads) void decode_merge(
     char* __restrict__ out, const int32_t* __restrict__ ctx, int S, int H, int Hkv, int maxb,
     int bsz, int W, float v_scale, const int64_t* __restrict__ hdr,
-    const int64_t* __restrict__ excl, const float* __restrict__ partials, Prefix pf,
-    int max_ctx, int seg_fixed) {
-  const int64_t run =
-      (int64_t)blockIdx.x * kWavesPerGroup + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t* __restrict__ excl, const float* __restrict__ partials,
+    const int64_t* __restrict__ split, Prefix pf, int max_ctx, int seg_fixed) {
+  const int64_t run = merge_run_of(
+      split, W,
+      (int64_t)blockIdx.x * kWavesPerGroup + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
+  if (run < 0) return;
   merge_one_run<QT, D, GS>(out, ctx, S, H, Hkv, maxb, bsz, W, v_scale, hdr, excl, partials, pf,
                            max_ctx, seg_fixed, run);
 }
@@ -1145,6 +1170,7 @@ struct MergePass {
   const int64_t* hdr;
   const int64_t* excl;
   const float* partials;
+  const int64_t* split;  // the split runs by segment boundary, or null: a wave per run
   Prefix pf;
   int groups;  // workgroups of this pass's merge
 };
@@ -1156,14 +1182,18 @@ template <int QT, int D, int GS0, int GS1>
 __global__ __launch_bounds__(kThreads) void decode_merge_pair(MergePass a, MergePass b, int Hkv,
                                                               int bsz) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if ((int)blockIdx.x < a.groups)
-    merge_one_run<QT, D, GS0>(nullptr, a.ctx, a.S, a.H, Hkv, a.maxb, bsz, a.W, 1.0f, a.hdr,
-                              a.excl, a.partials, a.pf, a.max_ctx, 0,
-                              (int64_t)blockIdx.x * kWavesPerGroup + w);
-  else
-    merge_one_run<QT, D, GS1>(nullptr, b.ctx, b.S, b.H, Hkv, b.maxb, bsz, b.W, 1.0f, b.hdr,
-                              b.excl, b.partials, b.pf, b.max_ctx, 0,
-                              (int64_t)(blockIdx.x - a.groups) * kWavesPerGroup + w);
+  if ((int)blockIdx.x < a.groups) {
+    const int64_t run = merge_run_of(a.split, a.W, (int64_t)blockIdx.x * kWavesPerGroup + w);
+    if (run >= 0)
+      merge_one_run<QT, D, GS0>(nullptr, a.ctx, a.S, a.H, Hkv, a.maxb, bsz, a.W, 1.0f, a.hdr,
+                                a.excl, a.partials, a.pf, a.max_ctx, 0, run);
+  } else {
+    const int64_t run =
+        merge_run_of(b.split, b.W, (int64_t)(blockIdx.x - a.groups) * kWavesPerGroup + w);
+    if (run >= 0)
+      merge_one_run<QT, D, GS1>(nullptr, b.ctx, b.S, b.H, Hkv, b.maxb, bsz, b.W, 1.0f, b.hdr,
+                                b.excl, b.partials, b.pf, b.max_ctx, 0, run);
+  }
 }
 
 // ---- shared key/value heads on the matrix cores --------------------------------
@@ -1441,8 +1471,9 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mma(
     const char* __restrict__ vc, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ ctx, int S, int H, int Hkv, int maxb, int num_blocks, int W,
     int seg_fixed, float scale_log2, float v_scale, int64_t* __restrict__ hdr,
-    int64_t* __restrict__ excl_out, float* __restrict__ partials, NewRows nr_arg,
-    const int64_t* __restrict__ new_slots, Prefix pf) {
+    int64_t* __restrict__ excl_out, float* __restrict__ partials,
+    int64_t* __restrict__ split_out, NewRows nr_arg, const int64_t* __restrict__ new_slots,
+    Prefix pf) {
   static_assert(GS == 4 || GS == 8, "4 or 8 query heads per wave");
   NewRows nr = nr_arg;
   nr.slots = new_slots;
@@ -1456,11 +1487,12 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mma(
   Ctx x;
   Cursor cur;
   if (!start_segment<B, GS>(ctx, S, H, Hkv, maxb, num_blocks, W, seg_fixed, pf, hdr, excl_out,
-                            sg, x, cur))
+                            split_out, sg, x, cur))
     return;
   const int w = sg.w;
   const int64_t seg_lo = sg.seg_lo, seg_hi = sg.seg_hi;
   const int n = sg.n;
+  const int64_t split_run = sg.split_run;
   uint16_t* vrow = vlds[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
 
   // Q^T operand of the run's 8 heads: lane holds q[h0 + col][8 grp + 32 c .. +7]; the
@@ -1534,17 +1566,22 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mma(
   } else {
     step(A, i);
   }
+  if (lane == 0) split_out[w] = split_run;
 }
 
 // ---- launch ------------------------------------------------------------------
 
 // Workspace: header (total units, segment length), int64 unit offset of each text [S],
-// fp32 partials [W][2][GS][D+4] (sized for GS = 8). Written by decode_partition, read
-// by decode_merge.
+// int64 split run of each segment boundary [W], fp32 partials [W][2][GS][D+4] (sized for
+// GS = 8). Written by decode_partition, read by decode_merge.
 struct Layout {
   int64_t W;  // wavefronts (segments) in the grid
-  size_t excl_off, part_off, bytes;
+  size_t excl_off, split_off, part_off, bytes;
 };
+
+// Merge waves of a pass with `runs` runs over W segments: one per run, or with more runs
+// than segments one per segment boundary (only runs crossing a boundary have partials).
+inline bool merge_by_boundary(int64_t runs, int64_t W) { return runs > W; }
 
 struct Launch {
   char* out;
@@ -1566,17 +1603,18 @@ struct Launch {
 };
 
 template <int KT, int QT, int D, int B, int GS, bool FUSED>
-void launch_partition(const Launch& a, int64_t* hdr, int64_t* excl, float* part) {
+void launch_partition(const Launch& a, int64_t* hdr, int64_t* excl, float* part,
+                      int64_t* split) {
   const int groups = (a.W + kWavesPerGroup - 1) / kWavesPerGroup;
   if constexpr ((GS == 4 || GS == 8) && KT == QT && (KT == PA_F16 || KT == PA_BF16))
     hipLaunchKernelGGL((decode_partition_mma<QT, D, B, GS, FUSED>), dim3(groups), dim3(kThreads),
                        0, a.st, a.out, a.q, a.kc, a.vc, a.tables, a.ctx, a.S, a.H, a.Hkv, a.maxb,
-                       a.nb, a.W, a.seg_fixed, a.sl, a.v_scale, hdr, excl, part, a.nr,
+                       a.nb, a.W, a.seg_fixed, a.sl, a.v_scale, hdr, excl, part, split, a.nr,
                        a.nr.slots, a.pf);
   else
     hipLaunchKernelGGL((decode_partition<KT, QT, D, B, GS, FUSED>), dim3(groups), dim3(kThreads),
                        0, a.st, a.out, a.q, a.kc, a.vc, a.tables, a.ctx, a.S, a.H, a.Hkv, a.maxb,
-                       a.nb, a.W, a.seg_fixed, a.sl, a.v_scale, hdr, excl, part, a.nr,
+                       a.nb, a.W, a.seg_fixed, a.sl, a.v_scale, hdr, excl, part, split, a.nr,
                        a.nr.slots, a.pf);
 }
 
@@ -1585,20 +1623,24 @@ bool launch(const Launch& a) {
   int64_t* hdr = reinterpret_cast<int64_t*>(a.ws);
   int64_t* excl = reinterpret_cast<int64_t*>(a.ws + a.lay.excl_off);
   float* part = reinterpret_cast<float*>(a.ws + a.lay.part_off);
+  int64_t* split = reinterpret_cast<int64_t*>(a.ws + a.lay.split_off);
   if (a.nr.k) {
     // the fused write stores rows in the pools' own format: not for E4M3 pools, whose
     // new rows arrive in 16 bits and are quantized by pa_kv_write_fp8
-    if constexpr (KT == QT) launch_partition<KT, QT, D, B, GS, true>(a, hdr, excl, part);
+    if constexpr (KT == QT) launch_partition<KT, QT, D, B, GS, true>(a, hdr, excl, part, split);
     else return false;
   } else {
-    launch_partition<KT, QT, D, B, GS, false>(a, hdr, excl, part);
+    launch_partition<KT, QT, D, B, GS, false>(a, hdr, excl, part, split);
   }
   if (a.defer_merge) return true;
-  const int64_t runs = (int64_t)a.S * (a.H / GS);  // merge waves: one per run
-  const int mgroups = (int)((runs + kWavesPerGroup - 1) / kWavesPerGroup);
+  const int64_t runs = (int64_t)a.S * (a.H / GS);
+  const bool by_boundary = merge_by_boundary(runs, a.W);
+  const int64_t mwaves = by_boundary ? a.W : runs;
+  const int mgroups = (int)((mwaves + kWavesPerGroup - 1) / kWavesPerGroup);
   hipLaunchKernelGGL((decode_merge<QT, D, GS>), dim3(mgroups), dim3(kThreads), 0, a.st, a.out,
-                     a.ctx, a.S, a.H, a.Hkv, a.maxb, B, a.W, a.v_scale, hdr, excl, part, a.pf,
-                     a.max_ctx, a.seg_fixed);
+                     a.ctx, a.S, a.H, a.Hkv, a.maxb, B, a.W, a.v_scale, hdr, excl, part,
+                     by_boundary ? split : (const int64_t*)nullptr, a.pf, a.max_ctx,
+                     a.seg_fixed);
   return true;
 }
 

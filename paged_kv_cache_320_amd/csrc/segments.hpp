@@ -58,6 +58,12 @@ __host__ __device__ inline int partial_slot(int64_t run_lo, int64_t seg_lo) {
   return run_lo <= seg_lo ? 0 : 1;
 }
 
+// Whether a segment whose first unit lies `u` units into a run names that run to the merge:
+// the run started in the segment before (0 < u <= seg), so a run split over several
+// segments is named once, by the first segment boundary it crosses, and a run that starts
+// at a segment's first unit is not split there.
+__host__ __device__ inline bool names_split_run(int64_t u, int64_t seg) { return u > 0 && u <= seg; }
+
 // Offset, in floats, of the partial of query head j (of a wave's gs heads) in slot `slot`
 // of segment w; a record is stride floats (m, l, two pads, acc[head_dim]).
 __host__ __device__ inline int64_t partial_offset(int64_t w, int slot, int j, int gs, int stride) {

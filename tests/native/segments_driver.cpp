@@ -1,6 +1,7 @@
 // Host check of the decode's segmentation arithmetic (csrc/segments.hpp, the functions the
 // kernels call) over random batches: every unit of a launch lies in exactly one segment
-// below W, every run's merge range [w0, w1] is exactly the segments the run touches, no two
+// below W, every run's merge range [w0, w1] is exactly the segments the run touches, every
+// run split over segments is named to the merge by exactly one segment boundary, no two
 // runs write the same partial record, and every record lies inside the workspace.
 //
 //   segments_driver <seed> <cases> [old]
@@ -72,6 +73,7 @@ bool check(const Case& c, bool old, char* why, size_t n) {
       return false;
     }
   }
+  std::vector<int> named((size_t)c.S * R, 0);  // run -> boundaries naming it
   for (int64_t w = 0; w < W; ++w) {
     const int64_t c0 = w * seg;
     if (c0 >= total) continue;
@@ -113,6 +115,9 @@ bool check(const Case& c, bool old, char* why, size_t n) {
                (long long)w, (long long)c0, text, (long long)off);
       return false;
     }
+    // the run this segment boundary names to the merge (the partition wave's record)
+    const int64_t r = off / U[text], u = off - r * U[text];
+    if (names_split_run(u, seg)) ++named[(int64_t)text * R + r];
   }
   // runs: merge ranges, partial records
   const int64_t records = W * 2 * kMaxGS;  // partial records the workspace holds
@@ -129,8 +134,14 @@ bool check(const Case& c, bool old, char* why, size_t n) {
                  (long long)want0, (long long)want1, (long long)W);
         return false;
       }
-      if (w0 == w1) continue;  // finished inside one segment: no partials
       const int64_t run_id = (int64_t)s * R + r;
+      // a merge wave per boundary visits exactly the runs with partials, each once
+      if (named[run_id] != (w0 == w1 ? 0 : 1)) {
+        snprintf(why, n, "run [%lld, %lld) over segments %lld..%lld named by %d boundaries",
+                 (long long)lo, (long long)hi, (long long)w0, (long long)w1, named[run_id]);
+        return false;
+      }
+      if (w0 == w1) continue;  // finished inside one segment: no partials
       for (int64_t w = w0; w <= w1; ++w) {
         // the partition kernel's slot (flush) and the merge's slot (read) of this record
         const int slot = partial_slot(lo, w * seg);
