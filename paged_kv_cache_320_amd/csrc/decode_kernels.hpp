@@ -1061,7 +1061,8 @@ __device__ __forceinline__ void merge_run(const float* __restrict__ partials, in
   merge_finish<QT, D, GS>(M, den, num, v_scale, dst_row, state_dst, lane);
 }
 
-// Merge pass: one wave per run (a text's head group of GS query heads), all GS heads at
+// Merge pass: one wave per run (a text's head group of GS query heads), or per segment
+// boundary when runs outnumber segments (decode_merge's split array), all GS heads at
 // once; runs finished inside one segment return at once. W: segments of the partition
 // launch (the merge range is clamped to it). (One wave per query head instead launched GS
 // times the waves for the same partials. Taking the first unit and the segment length from
