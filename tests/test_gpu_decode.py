@@ -297,3 +297,27 @@ def test_segment_search_past_4096_texts(native):
     got = run_gpu(native, q, kc, vc, tables, L)
     want = decode_attention(q, kc, vc, tables, L, B)
     assert_close(got, want, "f16", "4,200 texts")
+
+
+def test_merge_by_segment_boundary_with_runs_over_many_segments(native):
+    """More runs than segments (600 texts x 2 heads over the 1,024 segments of a 256-CU
+    part's auto grid), so the merge runs one wave per segment boundary. Three 6,000-token
+    texts among short ones make runs that cross ~90 boundaries each: every such run must be
+    merged once, by the wave of the first boundary it crosses, and every short run split
+    across a boundary too. Sharp scores (q x 32, V ~ N(0,1)): a run merged twice from the
+    wrong partials, or left unmerged (7.0), would show; a second launch gives the same bits."""
+    rng = np.random.default_rng(21)
+    lens = [int(x) for x in rng.integers(1, 21, 600)]
+    for i in (5, 300, 599):
+        lens[i] = 6000
+    H, Hkv, D, B = 2, 2, 128, 16
+    say(f"merge by segment boundary, {len(lens)} texts")
+    q, kc, vc, tables, L = make_case(22, lens, H, Hkv, D, B, "f16", kv_std=1.0 / math.sqrt(D),
+                                     q_std=32.0)
+    vc = torch.where(torch.isnan(vc), vc, vc * math.sqrt(D))
+    want = decode_attention(q, kc, vc, tables, L, B)
+    got = run_gpu(native, q, kc, vc, tables, L)
+    assert torch.isfinite(got.float()).all()
+    assert_close(got, want, "f16", "600 texts, three of 6,000 tokens")
+    again = run_gpu(native, q, kc, vc, tables, L)
+    assert torch.equal(again.view(torch.int16), got.view(torch.int16))
