@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     char* __restrict__ out, const char* __restrict__ q, const char* __restrict__ kc,
     const char* __restrict__ vc, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ ctx, const int32_t* __restrict__ q_start, int T, int H, int Hkv,
-    int maxb, int num_blocks, int qtiles, int nwork, float scale_log2) {
+    int maxb, int num_blocks, int qtiles, int nwork, int round_robin, float scale_log2) {
   using M = Mma<DT>;
   typedef typename M::v8 v8;
   constexpr int CPR = D / 8;                     // 16-byte pieces per key row
@@ -162,17 +162,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
   __shared__ int bad_sh;
 
-  // Work item w = (text, head, query tile), numbered so that one (text, head)'s query
-  // tiles are consecutive. Workgroups are dealt to the 8 XCDs in turn (workgroup b to
-  // XCD b % 8), so w takes b's XCD-major rank: each XCD walks its own contiguous range of
-  // work items and a head's keys and values are read by workgroups sharing one L2.
-  const int per = (nwork + 7) >> 3;
-  const int w = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
-  if (w >= nwork) return;
-  const int qt0 = qtiles - 1 - w % qtiles;  // the longest query tiles of a text first
-  const int s = w / qtiles / H;
-  const int h = w / qtiles % H;
-  const int kvh = h / (H / Hkv);
+  // Work item = (text, head, query tile), a unit being a text's key/value head with the
+  // Gr query heads it serves. Workgroups are dealt to the 8 XCDs in turn (workgroup b to
+  // XCD b % 8), and each XCD walks its items in order (a unit's heads, each head's longest
+  // query tiles first), so the heads sharing a key/value head run on one XCD, whose L2 then
+  // serves their keys and values. Prompts of equal length: XCD x takes the x-th contiguous
+  // eighth of the units. Unequal lengths (round_robin): unit u goes to XCD u % 8, so every
+  // XCD gets an even share of every text's heads and no XCD holds the longest prompts
+  // alone (on 64 prompts of 16-2,048 tokens the contiguous dealing left one XCD ~1.4x the
+  // mean work).
+  const int Gr = H / Hkv;
+  const int per_unit = Gr * qtiles;
+  const int units = nwork / per_unit;  // texts x key/value heads
+  const int upx = (units + 7) >> 3;    // units per XCD
+  const int rank = (int)(blockIdx.x >> 3);
+  const int ui = rank / per_unit;
+  const int x = (int)(blockIdx.x & 7);
+  const int u = round_robin ? x + 8 * ui : x * upx + ui;
+  if (ui >= upx || u >= units) return;
+  const int rem = rank - ui * per_unit;
+  const int qt0 = qtiles - 1 - rem % qtiles;  // the longest query tiles of a head first
+  const int s = u / Hkv;
+  const int kvh = u - s * Hkv;
+  const int h = kvh * Gr + rem / qtiles;
   const int r0 = q_start[s], r1 = q_start[s + 1];
   const int n = r1 - r0;
   if (r0 < 0 || r1 > T || n <= 0) return;  // no rows of `out` to write
@@ -434,17 +446,20 @@ struct Args {
   char* out;
   const char *q, *kc, *vc;
   const int32_t *tables, *ctx, *q_start;
-  int S, T, H, Hkv, maxb, num_blocks, qtiles, nwork;
+  int S, T, H, Hkv, maxb, num_blocks, qtiles, nwork, round_robin;
   float scale_log2;
   hipStream_t st;
 };
 
 template <int DT, int D, int B>
 void launch(const Args& a) {
-  const dim3 grid((unsigned)(8 * ((a.nwork + 7) / 8))), block(kThreads);
+  // 8 XCDs x the units each is dealt (ceil(units / 8)) x the items of a unit
+  const int64_t per_unit = (int64_t)(a.H / a.Hkv) * a.qtiles;
+  const int64_t units = (int64_t)a.S * a.Hkv;
+  const dim3 grid((unsigned)(8 * ((units + 7) / 8) * per_unit)), block(kThreads);
   hipLaunchKernelGGL((prefill_kernel<DT, D, B>), grid, block, 0, a.st, a.out, a.q, a.kc, a.vc,
                      a.tables, a.ctx, a.q_start, a.T, a.H, a.Hkv, a.maxb, a.num_blocks,
-                     a.qtiles, a.nwork, a.scale_log2);
+                     a.qtiles, a.nwork, a.round_robin, a.scale_log2);
 }
 
 template <int DT, int D>
@@ -502,13 +517,15 @@ extern "C" int pa_prefill_attention(void* out, const void* q, const void* k_cach
       ((uintptr_t)q_start & 3u))
     return fail(PA_EINVAL, "tables, context_lens and q_start must be 4-byte aligned");
   const int64_t qtiles = ((int64_t)max_q_len + kQRows - 1) / kQRows;
-  if ((int64_t)num_seqs * num_heads * qtiles > 0x7ffffff0LL)
+  if (((int64_t)num_seqs * num_kv_heads + 7) * (num_heads / num_kv_heads) * qtiles > 0x7ffffff0LL)
     return fail(PA_EINVAL, "num_seqs * num_heads * ceil(max_q_len / %d) exceeds the grid",
                 kQRows);
   const Args a{(char*)out, (const char*)q, (const char*)k_cache, (const char*)v_cache,
                block_tables, context_lens, q_start, num_seqs, num_rows, num_heads,
                num_kv_heads, max_blocks_per_seq, num_blocks, (int)qtiles,
                (int)(num_seqs * num_heads * qtiles),
+               // every prompt max_q_len long exactly when the rows add up to that
+               (int64_t)num_rows != (int64_t)num_seqs * max_q_len,
                scale * 1.4426950408889634f, (hipStream_t)stream};
   if (dtype == PA_F16) launch_d<PA_F16>(head_dim, block_size, a);
   else launch_d<PA_BF16>(head_dim, block_size, a);
