@@ -181,17 +181,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int u = round_robin ? x + 8 * ui : x * upx + ui;
   if (ui >= upx || u >= units) return;
   const int rem = rank - ui * per_unit;
-  // a head's query tiles longest first, in snake order over groups of four (15 14 13 12,
-  // 8 9 10 11, 7 6 5 4, 0 1 2 3 for 16): an XCD starts its workgroups on its shader engines
-  // in turn, and in plain descending order engine k would always get the k-th longest of
-  // every four tiles (40 : 36 : 32 : 28 of the work for 16 tiles); this way each engine gets
-  // the same share. A partial last group keeps descending order.
-  const int p = rem % qtiles, g4 = p >> 2;
-  const int d = (g4 & 1) && 4 * g4 + 4 <= qtiles ? 4 * g4 + 3 - (p & 3) : p;
-  const int qt0 = qtiles - 1 - d;
+  // a head's query tiles longest first, in snake order over groups of four of the XCD's
+  // workgroups (15 14 13 12, 8 9 10 11, 7 6 5 4, 0 1 2 3 for 16 tiles; heads of 4 tiles
+  // alternate direction): an XCD starts its workgroups on its shader engines in turn, and
+  // in plain descending order engine k would always get the k-th longest of every four
+  // tiles (40 : 36 : 32 : 28 of the work for 16 tiles); this way each engine gets the same
+  // share. Only where a unit's items come in whole groups of four (else plain order).
+  int d = rem;
+  if ((per_unit & 3) == 0 && ((rank >> 2) & 1)) d = (rem & ~3) + 3 - (rem & 3);
+  const int qt0 = qtiles - 1 - d % qtiles;
   const int s = u / Hkv;
   const int kvh = u - s * Hkv;
-  const int h = kvh * Gr + rem / qtiles;
+  const int h = kvh * Gr + d / qtiles;
   const int r0 = q_start[s], r1 = q_start[s + 1];
   const int n = r1 - r0;
   if (r0 < 0 || r1 > T || n <= 0) return;  // no rows of `out` to write
